@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of paged decode attention on one MI355X.
+
+One step is one decode step of the 64-request Qwen3-235B-shaped workload
+(one GPU's share under TP8: 8 query heads on 1 KV head, head_dim 128,
+block_size 16, contexts U[1000,2000]):
+  1. cache write of each request's new token into the shuffled KV cache,
+  2. paged GQA decode attention over every request's whole context
+     (split-KV partitions + log-sum-exp merge).
+Steps rotate over several independent KV pools (like the layers of a
+model), together larger than the 256 MB Infinity Cache, so every step reads
+its KV from HBM.  The timed region replays a captured HIP graph of the
+steps; the decode kernels' own duration is measured with HIP events on the
+stream they are launched on.
+
+Prints one JSON line.  Other workloads: --config long_context | mla | extend.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 reqs"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="qwen3",
+                    choices=["qwen3", "long_context", "mla", "mla_bs1", "extend"])
+    ap.add_argument("--pools", type=int, default=0, help="KV pool copies (0: enough to exceed the MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# GQA decode workloads
+# ---------------------------------------------------------------------------
+
+def gqa_algorithmic_bytes(case) -> int:
+    """Bytes the method must move per decode launch: every context token's K
+    and V once, q, out, lse, the used block-table entries and lengths."""
+    S, Hq, Hkv, D, B = case.S, case.Hq, case.Hkv, case.D, case.B
+    n = case.context_lens.astype(np.int64)
+    kv = int(n.sum()) * Hkv * D * 2 * 2
+    blocks = int(((n + B - 1) // B).sum())
+    return kv + S * Hq * D * 2 * 2 + S * Hq * 4 + blocks * 4 + S * 4
+
+
+def gqa_algorithmic_flops(case) -> int:
+    return int(case.context_lens.astype(np.int64).sum()) * case.Hq * case.D * 4
+
+
+def bench_gqa(args, case, label):
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+
+    dev = torch.device("cuda:0")
+    pg = case.paging
+    pool_bytes = pg.num_blocks * case.Hkv * case.D * case.B * 2 * 2
+    pools = args.pools or max(1, math.ceil(2 * MALL_BYTES / pool_bytes))
+    log(f"[bench] {label}: S={case.S} Hq={case.Hq} Hkv={case.Hkv} D={case.D} B={case.B} "
+        f"tokens={pg.total_tokens} pool={pool_bytes / 1e6:.1f} MB x {pools} copies")
+    key = case.key.to(dev)
+    value = case.value.to(dev)
+    slots_all = torch.from_numpy(pg.slot_mapping).to(dev)
+    caches = []
+    for _ in range(pools):
+        kc = torch.zeros((pg.num_blocks, case.Hkv, case.D // 8, case.B, 8), dtype=torch.bfloat16,
+                         device=dev)
+        vc = torch.zeros((pg.num_blocks, case.Hkv, case.B // 8, case.D, 8), dtype=torch.bfloat16,
+                         device=dev)
+        pa.reshape_and_cache(key, value, kc, vc, slots_all)
+        caches.append((kc, vc))
+    rows = torch.from_numpy(case.new_token_rows()).to(dev)
+    new_k = key[rows].contiguous()
+    new_v = value[rows].contiguous()
+    new_slots = slots_all[rows].contiguous()
+    del key, value
+    q = case.query.to(dev)
+    bt = torch.from_numpy(pg.block_table).to(dev)
+    cl = torch.from_numpy(pg.lens).to(dev)
+    max_ctx = int(pg.lens.max())
+    P = case.partition_tokens
+    ws = torch.empty(max(1, pa.decode_workspace_size(case.S, case.Hq, case.Hkv, case.D, max_ctx, P)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def decode(i):
+        kc, vc = caches[i % pools]
+        pa.paged_decode_attn(q, kc, vc, bt, cl, case.scale, max_ctx, partition_tokens=P,
+                             out=out, lse=lse, workspace=ws)
+
+    def step(i):
+        kc, vc = caches[i % pools]
+        pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots)
+        decode(i)
+
+    # eager reference for the graph check
+    step(0)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    if not args.no_graph:
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for i in range(pools):  # warm the capture stream
+                step(i)
+        torch.cuda.synchronize()
+        for i in range(pools):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % pools].replay()
+        else:
+            step(i)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # every replay recomputes pool 0's step output bit for bit
+    run(0 if not graphs else pools * 1000)
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
+
+    # decode kernels' own duration: HIP events on the launch stream
+    cur = torch.cuda.current_stream()
+    n_ev = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for i in range(n_ev):
+        evs[i][0].record(cur)
+        decode(i)
+        evs[i][1].record(cur)
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    algo = gqa_algorithmic_bytes(case)
+    achieved = algo / (dec_ms * 1e-3) / 1e9
+    tok_s = case.S / (ms_per_step * 1e-3)
+    return {
+        "value": tok_s,
+        "ms_per_step": ms_per_step,
+        "graph_replay_matches_eager": graph_ok,
+        "decode_ms": dec_ms,
+        "hbm_gbps": achieved,
+        "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "algo_bytes": algo,
+        "algo_flops": gqa_algorithmic_flops(case),
+        "pools": pools,
+        "partition_tokens": pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P),
+    }
+
+
+def cpu_baseline_gqa(case, seconds):
+    """The oracle as it stands on this host: decode steps (cache write of the
+    new tokens + exact attention through the block table), repeated for
+    about `seconds`."""
+    import oracle
+    from paged_attention_decode_reshape_amd import workloads as W
+
+    orc = oracle.get()
+    kc, vc = orc.empty_shuffled_cache(case.paging.num_blocks, case.Hkv, case.D, case.B)
+    orc.cache_write_shuffled(W.bf16_bits(case.key), W.bf16_bits(case.value),
+                             case.paging.slot_mapping, kc, vc, case.B)
+    rows = case.new_token_rows()
+    nk = W.bf16_bits(case.key)[rows]
+    nv = W.bf16_bits(case.value)[rows]
+    ns = case.paging.slot_mapping[rows]
+    qb = W.bf16_bits(case.query)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.cache_write_shuffled(nk, nv, ns, kc, vc, case.B)
+        orc.paged_decode_gqa(qb, kc, vc, case.paging.block_table, case.context_lens, case.B,
+                             case.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": case.S * reps / el, "unit": "tok/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full decode steps of the same workload ({case.S} requests) "
+                      f"in {el:.1f} s, fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library's "
+              "path has no multi-GPU leg", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    from paged_attention_decode_reshape_amd import workloads as W
+
+    if args.config == "qwen3":
+        case = W.qwen3_decode()
+        r = bench_gqa(args, case, "qwen3_decode_64req")
+        workload = {"workload": "qwen3_235b_tp8_decode_64req", "requests": 64, "q_heads": 8,
+                    "kv_heads": 1, "head_dim": 128, "block_size": 16,
+                    "context_lens": "U[1000,2000]", "kv_layout": "shuffled",
+                    "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"]}
+    elif args.config == "long_context":
+        case = W.long_context_decode()
+        r = bench_gqa(args, case, "long_context_decode")
+        workload = {"workload": "long_context_gqa_decode_8req", "requests": 8, "q_heads": 64,
+                    "kv_heads": 4, "head_dim": 128, "block_size": 16,
+                    "context_lens": "U[32768,131072]", "kv_pool_copies": r["pools"],
+                    "partition_tokens": r["partition_tokens"]}
+    else:
+        print(f"--config {args.config} is not available yet", file=sys.stderr)
+        sys.exit(2)
+
+    line = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": workload,
+        "hbm_gbps": r["hbm_gbps"],
+        "pct_hbm_peak": r["pct_hbm_peak"],
+        "graph_replay_matches_eager": r["graph_replay_matches_eager"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged decode (partition + merge launches)",
+            "achieved": r["hbm_gbps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algo_bytes_per_launch": r["algo_bytes"],
+            "avg_launch_ms": r["decode_ms"],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

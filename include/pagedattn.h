@@ -1,0 +1,231 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged-attention library
+ * (libpagedattn.so).
+ *
+ * The operations are those of the "ROCm attention backends" blog (vLLM on
+ * AMD ROCm; English summary and the vllm.com.cn translation):
+ *   - the cache write that keeps the KV cache in the preshuffled layout
+ *     (ROCM_AITER_FA section, key innovation 4, and the decode-path
+ *     paragraph: the custom cache-write operator always leaves the cache
+ *     shuffled so decode reads it with no layout conversion);
+ *   - memory-bound decode attention over that cache (phase taxonomy:
+ *     decode loads the whole KV cache per step), for GQA/MHA and for
+ *     absorbed MLA over the 576-wide latent (MLA section);
+ *   - log-sum-exp merging of partial results (extend-path pseudocode:
+ *     every chunk yields an output and an LSE and the merge is stable);
+ *   - chunked extend: new-token attention, then a loop of
+ *     gather -> attention -> merge over context chunks within a per-
+ *     iteration token budget, then a final merge (extend-path pseudocode).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are device pointers (HBM) unless the name ends in _host.
+ *    The caller owns every buffer; the library never allocates or frees
+ *    device memory, keeps no mutable global state and is re-entrant.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Work is enqueued
+ *    on it asynchronously; nothing synchronises.
+ *  - Tensors are dense, row-major, no padding.  bf16 is the storage type
+ *    of queries, keys, values, latents and attention outputs; arithmetic is
+ *    fp32.  LSE values are natural-log log-sum-exp of the scaled scores,
+ *    fp32, laid out [tokens, heads]; an empty set of keys gives out = 0 and
+ *    lse = -inf.
+ *  - Argument checks run on the host before anything is enqueued: a bad
+ *    argument returns a status, enqueues nothing and leaves outputs
+ *    untouched.  A failed launch returns PA_ERR_HIP.  Device data (block
+ *    tables, lengths, slots) is range-checked in the kernels so that a bad
+ *    entry never makes a kernel read or write outside the buffers whose
+ *    sizes the arguments describe; the numerical result for such an entry
+ *    is unspecified.
+ *
+ * Shuffled KV layout (x = 16 bytes / sizeof(bf16) = 8 elements):
+ *   k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x]
+ *   v_cache [num_blocks, num_kv_heads, block_size / x, head_dim, x]
+ * A token's slot is physical_block * block_size + offset_in_block.
+ * MLA latent layout: kv_cache [num_blocks, block_size, latent_dim].
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,          /* null pointer, negative size, inconsistent shapes */
+    PA_ERR_UNSUPPORTED = 2,          /* a valid shape outside the supported envelope */
+    PA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < the size query's answer */
+    PA_ERR_HIP = 4                   /* a HIP call or launch failed */
+};
+
+enum { PA_BF16 = 0, PA_F32 = 1 };                           /* element types for merge */
+enum { PA_LAYOUT_SHUFFLED_KV = 0, PA_LAYOUT_MLA_LATENT = 1 }; /* cache layouts */
+
+/* Human-readable name of a status code (static storage). */
+const char *pa_status_string(pa_status s);
+
+/*
+ * Cache write (reshape_and_cache).  Stage 1 of every forward on the pages:
+ * the new tokens' K/V go into the paged cache before attention runs.
+ *
+ * PA_LAYOUT_SHUFFLED_KV: key, value [num_tokens, num_kv_heads, head_dim]
+ *   bf16 are scattered into k_cache / v_cache in the shuffled layout.
+ * PA_LAYOUT_MLA_LATENT: key is the latent [num_tokens, head_dim] bf16
+ *   (head_dim = latent width, e.g. 576); value and v_cache must be NULL,
+ *   num_kv_heads must be 1; k_cache is the latent cache.
+ * slot_mapping [num_tokens] int64: destination slot of each token.  A
+ *   negative slot, or one >= num_blocks * block_size, is skipped.
+ * Supported: shuffled layout needs head_dim in {64, 128} and block_size in
+ *   {16, 32}; the latent layout needs head_dim % 8 == 0 and any
+ *   block_size >= 1.  num_tokens == 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *value,
+                               void *k_cache, void *v_cache, const int64_t *slot_mapping,
+                               int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, void *stream);
+
+/*
+ * Split-KV partition length the decode entry points use for these
+ * arguments: partition_tokens > 0 is rounded up to a multiple of 64;
+ * 0 picks one from the work size; -1 means one partition per sequence.
+ */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                   int32_t max_context_len, int32_t partition_tokens);
+
+/* Bytes of workspace pa_paged_decode_attn needs (0 if no split is needed). */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_tokens);
+
+/*
+ * GQA / MHA paged decode attention (paged_decode_attn): one query token per
+ * sequence attends to all context_lens[s] tokens of its sequence, found
+ * through block_table (decode path: reads the shuffled cache directly).
+ *
+ * out [num_seqs, num_q_heads, head_dim] bf16; lse [num_seqs, num_q_heads]
+ *   f32 (nullable).  query [num_seqs, num_q_heads, head_dim] bf16.
+ * block_table [num_seqs, max_blocks_per_seq] int32 physical block ids;
+ *   entries past ceil(context_lens[s] / block_size) are never read.
+ * context_lens [num_seqs] int32, counting the token the step just wrote;
+ *   values above max_context_len or max_blocks_per_seq * block_size are
+ *   clamped.  max_context_len is a host-side bound used to size the grid.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * scale multiplies q . k before the softmax.
+ * partition_tokens: see pa_decode_partition_tokens.  Sequences longer than
+ *   one partition are split; partial (out, lse) go to the workspace and
+ *   are merged by log-sum-exp.
+ * workspace: device memory of at least pa_decode_workspace_size(...)
+ *   bytes, 256-byte aligned; contents need no initialisation.
+ * Supported: head_dim in {64, 128}, block_size in {16, 32}, group size
+ *   num_q_heads / num_kv_heads in 1..16, max_context_len <= 1 << 20.
+ */
+pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float scale, int32_t partition_tokens,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace pa_mla_decode_attn needs (0 if no split is needed). */
+size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,
+                             int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * Absorbed MLA paged decode attention (mla_decode_attn; MLA section: decode
+ * runs directly on the compressed 576-wide latent).  Every query head reads
+ * the same latent row: keys are whole rows, values their first v_dim
+ * entries.
+ *
+ * out [num_seqs, num_q_heads, v_dim] bf16; lse [num_seqs, num_q_heads] f32
+ *   (nullable).  query [num_seqs, num_q_heads, latent_dim] bf16.
+ * kv_cache [num_blocks, block_size, latent_dim] bf16.
+ * block_table, context_lens, max_context_len, partition_tokens, workspace:
+ *   as for pa_paged_decode_attn.
+ * Supported: latent_dim == 576, v_dim == 512, num_q_heads in 1..16,
+ *   any block_size >= 1.
+ */
+pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const void *kv_cache,
+                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t latent_dim,
+                             int32_t v_dim, int32_t block_size, int64_t num_blocks, float scale,
+                             int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Log-sum-exp merge of two partial attention results (merge_attn_states;
+ * extend-path pseudocode): with M = max(Lp, Ls), wp = exp(Lp - M),
+ * ws = exp(Ls - M): out = (wp * Op + ws * Os) / (wp + ws),
+ * out_lse = M + log(wp + ws).  A part with lse = -inf has weight 0; two
+ * empty parts give out = 0, out_lse = -inf.
+ *
+ * prefix_out, suffix_out [num_tokens, num_heads, head_dim] of in_dtype;
+ * prefix_lse, suffix_lse [num_tokens, num_heads] f32; out of out_dtype,
+ * out_lse f32 (nullable).  out may alias prefix_out or suffix_out when the
+ * dtypes match (each element is read before it is written by the same
+ * thread).  Supported: head_dim % 8 == 0, head_dim <= 1024.
+ */
+pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,
+                               const void *prefix_out, const float *prefix_lse,
+                               const void *suffix_out, const float *suffix_lse, int32_t in_dtype,
+                               int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                               void *stream);
+
+/*
+ * Per-request chunk length one extend iteration gathers: the budget spread
+ * over the requests that still have context, rounded down to a multiple of
+ * block_size (at least block_size).
+ */
+int32_t pa_extend_chunk_tokens(int32_t num_seqs, int32_t block_size,
+                               int32_t chunk_budget_tokens);
+
+/* Bytes of workspace pa_chunked_extend_attn needs. */
+size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t chunk_budget_tokens);
+
+/*
+ * Chunked extend attention (chunked_extend_attn; extend-path pseudocode).
+ * Request r has context_lens[r] cached tokens (in the shuffled cache,
+ * through block_table) and new query tokens at rows
+ * query_start_loc[r] .. query_start_loc[r+1]; new token i attends to every
+ * cached token and to new tokens 0..i.
+ *
+ * Stage 1: causal attention of the new tokens over k_new / v_new.
+ * Stage 2: for each iteration, every request's next chunk of context
+ *   (pa_extend_chunk_tokens tokens) is gathered from the shuffled cache to
+ *   the standard [tokens, kv_heads, head_dim] layout in the workspace,
+ *   attended without a mask, and merged into the running context result.
+ * Stage 3: the context result is merged with the stage-1 result.
+ *
+ * out [total_new_tokens, num_q_heads, head_dim] bf16; lse
+ *   [total_new_tokens, num_q_heads] f32 (nullable).
+ * query [total_new_tokens, num_q_heads, head_dim] bf16; k_new, v_new
+ *   [total_new_tokens, num_kv_heads, head_dim] bf16.
+ * query_start_loc [num_seqs + 1] int32 on the device and the same values in
+ *   query_start_loc_host; context_lens [num_seqs] int32 on the device and
+ *   the same values in context_lens_host (the host copies plan the chunk
+ *   loop without a device read-back).
+ * Supported: head_dim == 128, block_size in {16, 32}, group size 1..16.
+ */
+pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const void *k_new,
+                                 const void *v_new, const int32_t *query_start_loc,
+                                 const int32_t *query_start_loc_host, const void *k_cache,
+                                 const void *v_cache, const int32_t *block_table,
+                                 int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                 const int32_t *context_lens_host, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float scale,
+                                 int32_t chunk_budget_tokens, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,24 @@
+"""MI355X (gfx950) paged attention over a block-table KV cache.
+
+Python binding of libpagedattn.so (C ABI in include/pagedattn.h).  The
+functions below only check and marshal torch tensors into pointers and sizes;
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU fallback: a call fails if the library is not built or the tensors are
+not on a GPU.
+"""
+from .ops import (  # noqa: F401
+    LAYOUT_MLA_LATENT,
+    LAYOUT_SHUFFLED_KV,
+    PagedAttnError,
+    chunked_extend_attn,
+    decode_partition_tokens,
+    decode_workspace_size,
+    extend_chunk_tokens,
+    extend_workspace_size,
+    library,
+    merge_attn_states,
+    mla_decode_attn,
+    mla_workspace_size,
+    paged_decode_attn,
+    reshape_and_cache,
+)

@@ -1,0 +1,240 @@
+// C ABI of libpagedattn (declared in include/pagedattn.h): host-side
+// argument checks, partition / chunk planning and kernel launches.
+// Nothing here allocates device memory or keeps state between calls.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "pagedattn.h"
+
+using namespace pa;
+
+namespace {
+
+constexpr int32_t kMaxContext = 1 << 20;
+constexpr int kAutoTargetWorkgroups = 1024;  // ~4 per CU on 256 CUs
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+int32_t partition_tokens_for(int32_t S, int32_t H, int32_t max_ctx, int32_t requested) {
+    const int32_t ctx = max_ctx > 0 ? max_ctx : 1;
+    if (requested == -1) return (int32_t)cdiv(ctx, 64) * 64;
+    if (requested > 0) return (int32_t)cdiv(requested, 64) * 64;
+    // auto: 256-token partitions (one 64-token step per wave), doubled while
+    // the grid would still hold >= kAutoTargetWorkgroups workgroups
+    int32_t P = 256;
+    while (P < 8192 && (int64_t)S * H * cdiv(ctx, 2 * (int64_t)P) >= kAutoTargetWorkgroups) P *= 2;
+    return P;
+}
+
+struct Split {
+    int32_t P;
+    int32_t parts;
+    size_t out_bytes, lse_bytes;
+};
+
+Split plan_split(int32_t S, int32_t Hq, int32_t H_units, int32_t Dv, int32_t max_ctx,
+                 int32_t requested) {
+    Split sp;
+    sp.P = partition_tokens_for(S, H_units, max_ctx, requested);
+    sp.parts = max_ctx > 0 ? (int32_t)cdiv(max_ctx, sp.P) : 1;
+    if (sp.parts <= 1) {
+        sp.parts = 1;
+        sp.out_bytes = sp.lse_bytes = 0;
+    } else {
+        sp.out_bytes = align256((size_t)S * Hq * sp.parts * Dv * sizeof(float));
+        sp.lse_bytes = align256((size_t)S * Hq * sp.parts * sizeof(float));
+    }
+    return sp;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(pa_status s) {
+    switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *value, void *k_cache,
+                               void *v_cache, const int64_t *slot_mapping, int64_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, void *stream) {
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+        return PA_ERR_INVALID_ARG;
+    if (!key || !k_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!aligned(key, 16) || !aligned(k_cache, 16)) return PA_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (layout == PA_LAYOUT_SHUFFLED_KV) {
+        if (!value || !v_cache || !aligned(value, 16) || !aligned(v_cache, 16))
+            return PA_ERR_INVALID_ARG;
+        if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+        if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+        if (num_tokens == 0) return PA_OK;
+        return from_hip(launch_cache_write_shuffled(key, value, k_cache, v_cache, slot_mapping,
+                                                    num_tokens, num_kv_heads, head_dim, block_size,
+                                                    num_blocks, st));
+    }
+    if (layout == PA_LAYOUT_MLA_LATENT) {
+        if (value || v_cache || num_kv_heads != 1) return PA_ERR_INVALID_ARG;
+        if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;
+        if (num_tokens == 0) return PA_OK;
+        return from_hip(launch_cache_write_latent(key, k_cache, slot_mapping, num_tokens, head_dim,
+                                                  block_size, num_blocks, st));
+    }
+    return PA_ERR_INVALID_ARG;
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                   int32_t partition_tokens) {
+    return partition_tokens_for(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_tokens) {
+    if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+        max_context_len < 0 || partition_tokens < -1)
+        return 0;
+    Split sp = plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_tokens);
+    return sp.out_bytes + sp.lse_bytes;
+}
+
+pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float scale, int32_t partition_tokens,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
+        num_blocks < 1 || max_context_len < 0 || partition_tokens < -1 || !isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (!out || !query || !k_cache || !v_cache || !block_table || !context_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(query, 4) ||
+        !aligned(out, 2) || !aligned(lse, 4))
+        return PA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+    if (max_context_len > kMaxContext || num_seqs > 65535 || num_kv_heads > 65535)
+        return PA_ERR_UNSUPPORTED;
+    Split sp = plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_tokens);
+    if (sp.out_bytes + sp.lse_bytes > 0) {
+        if (!workspace || workspace_bytes < sp.out_bytes + sp.lse_bytes)
+            return PA_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+    }
+    if (num_seqs == 0) return PA_OK;
+    DecodeParams p;
+    p.out = out;
+    p.lse = lse;
+    p.query = query;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.context_lens = context_lens;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.D = head_dim;
+    p.B = block_size;
+    p.num_blocks = num_blocks;
+    p.scale = scale;
+    p.partition = sp.P;
+    p.max_parts = sp.parts;
+    p.part_out = sp.parts > 1 ? (float *)workspace : nullptr;
+    p.part_lse = sp.parts > 1 ? (float *)((char *)workspace + sp.out_bytes) : nullptr;
+    return from_hip(launch_paged_decode(p, (hipStream_t)stream));
+}
+
+size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,
+                             int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs < 0 || num_q_heads < 1 || v_dim < 1 || max_context_len < 0 ||
+        partition_tokens < -1)
+        return 0;
+    Split sp = plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len, partition_tokens);
+    return sp.out_bytes + sp.lse_bytes;
+}
+
+pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const void *kv_cache,
+                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t latent_dim,
+                             int32_t v_dim, int32_t block_size, int64_t num_blocks, float scale,
+                             int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    (void)out; (void)lse; (void)query; (void)kv_cache; (void)block_table;
+    (void)max_blocks_per_seq; (void)context_lens; (void)max_context_len; (void)num_seqs;
+    (void)num_q_heads; (void)latent_dim; (void)v_dim; (void)block_size; (void)num_blocks;
+    (void)scale; (void)partition_tokens; (void)workspace; (void)workspace_bytes; (void)stream;
+    return PA_ERR_UNSUPPORTED;
+}
+
+pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,
+                               const void *prefix_out, const float *prefix_lse,
+                               const void *suffix_out, const float *suffix_lse, int32_t in_dtype,
+                               int64_t num_tokens, int32_t num_heads, int32_t head_dim,
+                               void *stream) {
+    if (num_tokens < 0 || num_heads < 1 || head_dim < 1) return PA_ERR_INVALID_ARG;
+    if ((in_dtype != PA_BF16 && in_dtype != PA_F32) || (out_dtype != PA_BF16 && out_dtype != PA_F32))
+        return PA_ERR_INVALID_ARG;
+    if (!out || !prefix_out || !prefix_lse || !suffix_out || !suffix_lse) return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(prefix_out, 16) || !aligned(suffix_out, 16) ||
+        !aligned(prefix_lse, 4) || !aligned(suffix_lse, 4) || !aligned(out_lse, 4))
+        return PA_ERR_INVALID_ARG;
+    if (head_dim % 8 != 0 || head_dim > 1024) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    return from_hip(launch_merge_pair(out, out_lse, out_dtype == PA_F32, prefix_out, prefix_lse,
+                                      suffix_out, suffix_lse, in_dtype == PA_F32,
+                                      num_tokens * num_heads, head_dim, (hipStream_t)stream));
+}
+
+int32_t pa_extend_chunk_tokens(int32_t num_seqs, int32_t block_size, int32_t chunk_budget_tokens) {
+    if (num_seqs < 1 || block_size < 1 || chunk_budget_tokens < 1) return block_size > 0 ? block_size : 1;
+    int32_t c = chunk_budget_tokens / num_seqs / block_size * block_size;
+    return c < block_size ? block_size : c;
+}
+
+size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t chunk_budget_tokens) {
+    (void)num_seqs; (void)total_new_tokens; (void)num_q_heads; (void)num_kv_heads;
+    (void)head_dim; (void)block_size; (void)chunk_budget_tokens;
+    return 0;
+}
+
+pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const void *k_new,
+                                 const void *v_new, const int32_t *query_start_loc,
+                                 const int32_t *query_start_loc_host, const void *k_cache,
+                                 const void *v_cache, const int32_t *block_table,
+                                 int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                 const int32_t *context_lens_host, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float scale,
+                                 int32_t chunk_budget_tokens, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    (void)out; (void)lse; (void)query; (void)k_new; (void)v_new; (void)query_start_loc;
+    (void)query_start_loc_host; (void)k_cache; (void)v_cache; (void)block_table;
+    (void)max_blocks_per_seq; (void)context_lens; (void)context_lens_host; (void)num_seqs;
+    (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)block_size; (void)num_blocks;
+    (void)scale; (void)chunk_budget_tokens; (void)workspace; (void)workspace_bytes; (void)stream;
+    return PA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Cache write into the preshuffled KV layout and into the MLA latent cache.
+//
+// "ROCm attention backends" blog, ROCM_AITER_FA section (key innovation 4)
+// and the decode-path paragraph: the custom cache-write operator always
+// leaves the cache in the shuffled layout
+//   k_cache [num_blocks, kv_heads, head_dim / x, block_size, x]
+//   v_cache [num_blocks, kv_heads, block_size / x, head_dim, x]
+// so decode never converts it.  x = 8 bf16 = one 16-byte vector.
+//
+// K: one 16-byte source vector (8 consecutive dims of one token) maps to one
+// 16-byte destination vector, so each thread moves one vector with a single
+// dwordx4 load and store.
+// V: a destination vector holds 8 consecutive *tokens* of one dim, so a lone
+// token contributes 2 bytes to each of head_dim vectors.  Each thread loads
+// 8 dims of one token and issues 8 two-byte stores; neighbouring threads hit
+// neighbouring 16-byte vectors, which L2 write-combines.
+#include "common.h"
+#include "launch.h"
+
+namespace pa {
+
+template <int D>
+__global__ __launch_bounds__(256) void cache_write_shuffled_kernel(
+    const uint4 *__restrict__ key, const uint4 *__restrict__ value, uint16_t *__restrict__ k_cache,
+    uint16_t *__restrict__ v_cache, const int64_t *__restrict__ slot_mapping, int64_t num_tokens,
+    int Hkv, int B, int64_t num_blocks) {
+    constexpr int C = D / 8;  // 16-byte vectors per head row
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = num_tokens * Hkv * C;
+    if (idx >= total) return;
+    const int c = (int)(idx % C);
+    const int g = (int)((idx / C) % Hkv);
+    const int64_t i = idx / ((int64_t)C * Hkv);
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * B) return;
+    const int64_t p = slot / B;
+    const int o = (int)(slot % B);
+    const uint4 kv = key[idx];
+    const uint4 vv = value[idx];
+    // K vector (dims c*8 .. c*8+7 of token o) -> k_cache[p][g][c][o][0..8)
+    uint4 *kdst = reinterpret_cast<uint4 *>(k_cache) + ((p * Hkv + g) * C + c) * B + o;
+    *kdst = kv;
+    // V: dim d = c*8 + e of token o -> v_cache[p][g][o / 8][d][o % 8]
+    uint16_t *vdst = v_cache + (((p * Hkv + g) * (B / 8) + o / 8) * D + c * 8) * 8 + (o % 8);
+    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const uint32_t word = w[e / 2];
+        vdst[e * 8] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+    }
+}
+
+// Latent rows are contiguous in both source and cache: one 16-byte vector per thread.
+__global__ __launch_bounds__(256) void cache_write_latent_kernel(
+    const uint4 *__restrict__ latent, uint4 *__restrict__ kv_cache,
+    const int64_t *__restrict__ slot_mapping, int64_t num_tokens, int C, int B,
+    int64_t num_blocks) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= num_tokens * C) return;
+    const int64_t i = idx / C;
+    const int c = (int)(idx % C);
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * B) return;
+    kv_cache[slot * C + c] = latent[idx];
+}
+
+hipError_t launch_cache_write_shuffled(const void *key, const void *value, void *k_cache,
+                                       void *v_cache, const int64_t *slot_mapping,
+                                       int64_t num_tokens, int Hkv, int D, int B,
+                                       int64_t num_blocks, hipStream_t stream) {
+    const int64_t total = num_tokens * Hkv * (D / 8);
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (D == 128)
+        hipLaunchKernelGGL(cache_write_shuffled_kernel<128>, dim3((unsigned)grid), dim3(256), 0,
+                           stream, (const uint4 *)key, (const uint4 *)value, (uint16_t *)k_cache,
+                           (uint16_t *)v_cache, slot_mapping, num_tokens, Hkv, B, num_blocks);
+    else
+        hipLaunchKernelGGL(cache_write_shuffled_kernel<64>, dim3((unsigned)grid), dim3(256), 0,
+                           stream, (const uint4 *)key, (const uint4 *)value, (uint16_t *)k_cache,
+                           (uint16_t *)v_cache, slot_mapping, num_tokens, Hkv, B, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_write_latent(const void *latent, void *kv_cache,
+                                     const int64_t *slot_mapping, int64_t num_tokens, int Dl,
+                                     int B, int64_t num_blocks, hipStream_t stream) {
+    const int C = Dl / 8;
+    const int64_t grid = (num_tokens * C + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cache_write_latent_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4 *)latent, (uint4 *)kv_cache, slot_mapping, num_tokens, C, B,
+                       num_blocks);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,64 @@
+// Host-side launchers of the gfx950 kernels (internal; the public ABI is
+// include/pagedattn.h).  Each launcher enqueues on `stream` and returns
+// hipGetLastError() after the launch.  Arguments are assumed validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+hipError_t launch_cache_write_shuffled(const void *key, const void *value, void *k_cache,
+                                       void *v_cache, const int64_t *slot_mapping,
+                                       int64_t num_tokens, int Hkv, int D, int B,
+                                       int64_t num_blocks, hipStream_t stream);
+
+hipError_t launch_cache_write_latent(const void *latent, void *kv_cache,
+                                     const int64_t *slot_mapping, int64_t num_tokens, int Dl,
+                                     int B, int64_t num_blocks, hipStream_t stream);
+
+struct DecodeParams {
+    void *out;                 // bf16 [S, Hq, D]
+    float *lse;                // f32 [S, Hq] or null
+    const void *query;         // bf16 [S, Hq, D]
+    const void *k_cache;       // shuffled
+    const void *v_cache;       // shuffled
+    const int32_t *block_table;
+    int32_t max_blocks;
+    const int32_t *context_lens;
+    int32_t S, Hq, Hkv, D, B;
+    int64_t num_blocks;
+    float scale;
+    int32_t partition;         // tokens per partition (multiple of 64)
+    int32_t max_parts;         // partitions per sequence in the grid
+    float *part_out;           // f32 [S, Hq, max_parts, D] (when max_parts > 1)
+    float *part_lse;           // f32 [S, Hq, max_parts]
+};
+
+hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
+
+struct MLAParams {
+    void *out;                 // bf16 [S, Hq, Dv]
+    float *lse;                // f32 [S, Hq] or null
+    const void *query;         // bf16 [S, Hq, Dl]
+    const void *kv_cache;      // bf16 [NB, B, Dl]
+    const int32_t *block_table;
+    int32_t max_blocks;
+    const int32_t *context_lens;
+    int32_t S, Hq, Dl, Dv, B;
+    int64_t num_blocks;
+    float scale;
+    int32_t partition;
+    int32_t max_parts;
+    float *part_out;           // f32 [S, Hq, max_parts, Dv]
+    float *part_lse;           // f32 [S, Hq, max_parts]
+};
+
+hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);
+
+hipError_t launch_merge_pair(void *out, float *out_lse, int out_f32, const void *a,
+                             const float *a_lse, const void *b, const float *b_lse, int in_f32,
+                             int64_t rows, int D, hipStream_t stream);
+
+}  // namespace pa

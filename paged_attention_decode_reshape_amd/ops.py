@@ -1,0 +1,336 @@
+"""ctypes binding of libpagedattn.so: tensor checks and argument marshalling.
+
+Names match the C entry points without their ``pa_`` prefix.  Each call
+enqueues on the current torch stream of the tensors' device and returns
+without synchronising.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
+
+LAYOUT_SHUFFLED_KV = 0
+LAYOUT_MLA_LATENT = 1
+_BF16, _F32 = 0, 1
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
+           4: "HIP error"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "pa_status_string": ([_i32], ctypes.c_char_p),
+    "pa_reshape_and_cache": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp], _i32),
+    "pa_decode_partition_tokens": ([_i32, _i32, _i32, _i32], _i32),
+    "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pa_paged_decode_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                              _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
+    "pa_mla_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
+    "pa_mla_decode_attn": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                            _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
+    "pa_merge_attn_states": ([_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp],
+                             _i32),
+    "pa_extend_chunk_tokens": ([_i32, _i32, _i32], _i32),
+    "pa_extend_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pa_chunked_extend_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp],
+                               _i32),
+}
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libpagedattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m paged_attention_decode_reshape_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PagedAttnError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _gpu(name: str, t: torch.Tensor, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _gpu("workspace", workspace)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace
+
+
+# ---------------------------------------------------------------------------
+
+def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], k_cache: torch.Tensor,
+                      v_cache: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+                      layout: int = LAYOUT_SHUFFLED_KV) -> None:
+    """Write new tokens into the paged cache.
+
+    Shuffled: key/value [T, Hkv, D] bf16, k_cache [NB, Hkv, D/8, B, 8],
+    v_cache [NB, Hkv, B/8, D, 8].  MLA latent: key [T, Dl], value None,
+    k_cache [NB, B, Dl], v_cache None.  slot_mapping [T] int64.
+    """
+    lib = library()
+    _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    if layout == LAYOUT_SHUFFLED_KV:
+        _gpu("key", key, torch.bfloat16, 3)
+        _gpu("value", value, torch.bfloat16, 3)
+        _gpu("k_cache", k_cache, torch.bfloat16, 5)
+        _gpu("v_cache", v_cache, torch.bfloat16, 5)
+        T, Hkv, D = key.shape
+        NB, B = k_cache.shape[0], k_cache.shape[3]
+        if (value.shape != key.shape or tuple(k_cache.shape) != (NB, Hkv, D // 8, B, 8)
+                or tuple(v_cache.shape) != (NB, Hkv, B // 8, D, 8)):
+            raise ValueError("cache shapes do not match key/value")
+        vptr, vcptr = value.data_ptr(), v_cache.data_ptr()
+    elif layout == LAYOUT_MLA_LATENT:
+        _gpu("key", key, torch.bfloat16, 2)
+        _gpu("k_cache", k_cache, torch.bfloat16, 3)
+        T, D = key.shape
+        Hkv = 1
+        NB, B = k_cache.shape[0], k_cache.shape[1]
+        if k_cache.shape[2] != D or value is not None or v_cache is not None:
+            raise ValueError("latent cache must be [NB, B, Dl]; value and v_cache must be None")
+        vptr = vcptr = None
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    st = lib.pa_reshape_and_cache(layout, key.data_ptr(), vptr, k_cache.data_ptr(), vcptr,
+                                  slot_mapping.data_ptr(), T, Hkv, D, B, NB, _stream(key))
+    _check("reshape_and_cache", st)
+
+
+def decode_partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                            partition_tokens: int = 0) -> int:
+    return int(library().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len,
+                                                    partition_tokens))
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          max_context_len: int, partition_tokens: int = 0) -> int:
+    return int(library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len, partition_tokens))
+
+
+def paged_decode_attn(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      max_context_len: int, partition_tokens: int = 0,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """GQA paged decode: query [S, Hq, D] bf16 -> (out [S, Hq, D] bf16, lse [S, Hq] f32)."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("k_cache", k_cache, torch.bfloat16, 5)
+    _gpu("v_cache", v_cache, torch.bfloat16, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, D = query.shape
+    NB, Hkv, _, B, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_paged_decode_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), k_cache.data_ptr(),
+                                  v_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+                                  context_lens.data_ptr(), int(max_context_len), S, Hq, Hkv, D, B,
+                                  NB, float(scale), int(partition_tokens), _ptr(ws), nbytes,
+                                  _stream(query))
+    _check("paged_decode_attn", st)
+    return out, lse
+
+
+def mla_workspace_size(num_seqs: int, num_q_heads: int, v_dim: int, max_context_len: int,
+                       partition_tokens: int = 0) -> int:
+    return int(library().pa_mla_workspace_size(num_seqs, num_q_heads, v_dim, max_context_len,
+                                               partition_tokens))
+
+
+def mla_decode_attn(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                    context_lens: torch.Tensor, scale: float, max_context_len: int,
+                    v_dim: int = 512, partition_tokens: int = 0,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Absorbed MLA decode: query [S, Hq, Dl] -> (out [S, Hq, v_dim], lse [S, Hq])."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("kv_cache", kv_cache, torch.bfloat16, 3)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, Dl = query.shape
+    NB, B, Dl2 = kv_cache.shape
+    if Dl2 != Dl:
+        raise ValueError("kv_cache latent width differs from the query's")
+    if out is None:
+        out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_mla_decode_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), kv_cache.data_ptr(),
+                                block_table.data_ptr(), block_table.shape[1],
+                                context_lens.data_ptr(), int(max_context_len), S, Hq, Dl, v_dim, B,
+                                NB, float(scale), int(partition_tokens), _ptr(ws), nbytes,
+                                _stream(query))
+    _check("mla_decode_attn", st)
+    return out, lse
+
+
+def merge_attn_states(prefix_out: torch.Tensor, prefix_lse: torch.Tensor,
+                      suffix_out: torch.Tensor, suffix_lse: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None, return_lse: bool = True
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """LSE merge of two partial results [T, H, D] (bf16 or f32) with lse [T, H] f32."""
+    lib = library()
+    dt = prefix_out.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise ValueError("outputs must be bf16 or f32")
+    _gpu("prefix_out", prefix_out, dt, 3)
+    _gpu("suffix_out", suffix_out, dt, 3)
+    _gpu("prefix_lse", prefix_lse, torch.float32, 2)
+    _gpu("suffix_lse", suffix_lse, torch.float32, 2)
+    T, H, D = prefix_out.shape
+    if suffix_out.shape != prefix_out.shape or prefix_lse.shape != (T, H) or \
+            suffix_lse.shape != (T, H):
+        raise ValueError("shape mismatch")
+    odt = out_dtype or (out.dtype if out is not None else dt)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=odt, device=prefix_out.device)
+    _gpu("out", out, odt, 3)
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((T, H), dtype=torch.float32, device=prefix_out.device)
+    if out_lse is not None:
+        _gpu("out_lse", out_lse, torch.float32, 2)
+    code = {torch.bfloat16: _BF16, torch.float32: _F32}
+    st = lib.pa_merge_attn_states(out.data_ptr(), _ptr(out_lse), code[odt], prefix_out.data_ptr(),
+                                  prefix_lse.data_ptr(), suffix_out.data_ptr(),
+                                  suffix_lse.data_ptr(), code[dt], T, H, D, _stream(prefix_out))
+    _check("merge_attn_states", st)
+    return out, out_lse
+
+
+def extend_chunk_tokens(num_seqs: int, block_size: int, chunk_budget_tokens: int) -> int:
+    return int(library().pa_extend_chunk_tokens(num_seqs, block_size, chunk_budget_tokens))
+
+
+def extend_workspace_size(num_seqs: int, total_new_tokens: int, num_q_heads: int,
+                          num_kv_heads: int, head_dim: int, block_size: int,
+                          chunk_budget_tokens: int) -> int:
+    return int(library().pa_extend_workspace_size(num_seqs, total_new_tokens, num_q_heads,
+                                                  num_kv_heads, head_dim, block_size,
+                                                  chunk_budget_tokens))
+
+
+def chunked_extend_attn(query: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        query_start_loc: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, query_start_loc_host,
+                        context_lens_host, chunk_budget_tokens: int = 32768,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked extend: query [Tn, Hq, D], k_new/v_new [Tn, Hkv, D] -> (out, lse).
+
+    ``query_start_loc_host`` and ``context_lens_host`` are host copies (lists
+    or CPU int32 tensors/arrays) of the device tensors, used to plan chunks.
+    """
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("k_new", k_new, torch.bfloat16, 3)
+    _gpu("v_new", v_new, torch.bfloat16, 3)
+    _gpu("query_start_loc", query_start_loc, torch.int32, 1)
+    _gpu("k_cache", k_cache, torch.bfloat16, 5)
+    _gpu("v_cache", v_cache, torch.bfloat16, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    Tn, Hq, D = query.shape
+    NB, Hkv, _, B, _ = k_cache.shape
+    S = context_lens.shape[0]
+    qsl_h = torch.as_tensor(query_start_loc_host, dtype=torch.int32).contiguous()
+    cl_h = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous()
+    if qsl_h.device.type != "cpu" or cl_h.device.type != "cpu":
+        raise ValueError("host copies must be on the CPU")
+    if qsl_h.numel() != S + 1 or cl_h.numel() != S:
+        raise ValueError("host copies have the wrong length")
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((Tn, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = extend_workspace_size(S, Tn, Hq, Hkv, D, B, chunk_budget_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_chunked_extend_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), k_new.data_ptr(),
+                                    v_new.data_ptr(), query_start_loc.data_ptr(),
+                                    qsl_h.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    block_table.data_ptr(), block_table.shape[1],
+                                    context_lens.data_ptr(), cl_h.data_ptr(), S, Hq, Hkv, D, B, NB,
+                                    float(scale), int(chunk_budget_tokens), _ptr(ws), nbytes,
+                                    _stream(query))
+    _check("chunked_extend_attn", st)
+    return out, lse

@@ -1,0 +1,111 @@
+"""The C ABI on the CPU: every declared symbol is exported, and argument
+checks return their status before anything is enqueued (no GPU needed; only
+argument combinations that fail validation are passed, so no kernel is
+ever launched from these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_attention_decode_reshape_amd as pa
+from paged_attention_decode_reshape_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+FAKE = 0x10000  # aligned non-null address; never dereferenced by a failing call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_operations():
+    names = declared_functions()
+    for op in ("reshape_and_cache", "paged_decode_attn", "mla_decode_attn",
+               "chunked_extend_attn", "merge_attn_states"):
+        assert f"pa_{op}" in names
+        assert hasattr(pa, op)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) <= set(ops._SIGS)
+
+
+def test_status_strings():
+    lib = pa.library()
+    assert lib.pa_status_string(0) == b"ok"
+    assert lib.pa_status_string(3) == b"workspace too small"
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, lse=None, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxb=8, cl=FAKE, maxctx=100,
+             S=4, Hq=8, Hkv=1, D=128, B=16, NB=64, scale=0.1, P=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pa_paged_decode_attn(a["out"], a["lse"], a["query"], a["k"], a["v"], a["bt"],
+                                    a["maxb"], a["cl"], a["maxctx"], a["S"], a["Hq"], a["Hkv"],
+                                    a["D"], a["B"], a["NB"], a["scale"], a["P"], a["ws"], a["wsb"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), INVALID),
+    (dict(k=FAKE + 8), INVALID),                      # cache not 16-byte aligned
+    (dict(Hq=6, Hkv=4), INVALID),                     # group not integral
+    (dict(scale=float("inf")), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(B=8), UNSUPPORTED),
+    (dict(Hq=32, Hkv=1), UNSUPPORTED),                # group 32 > 16
+    (dict(maxctx=(1 << 20) + 1, P=-1), UNSUPPORTED),
+    (dict(P=-2), INVALID),
+    (dict(maxctx=1000, P=128), WS_SMALL),             # 8 partitions need a workspace
+    (dict(maxctx=1000, P=128, ws=FAKE, wsb=100), WS_SMALL),
+])
+def test_decode_validation(kw, status):
+    assert _decode(pa.library(), **kw) == status
+
+
+def test_decode_workspace_sizes():
+    assert pa.decode_partition_tokens(4, 1, 511, 128) == 128
+    assert pa.decode_partition_tokens(4, 1, 511, 100) == 128   # rounded up to 64
+    assert pa.decode_partition_tokens(4, 1, 511, -1) == 512
+    assert pa.decode_partition_tokens(64, 1, 2000, 0) == 256
+    assert pa.decode_workspace_size(4, 4, 1, 128, 511, -1) == 0
+    parts = 4  # 511 tokens in 128-token partitions
+    want = (4 * 4 * parts * 128 * 4 + 255) // 256 * 256 + (4 * 4 * parts * 4 + 255) // 256 * 256
+    assert pa.decode_workspace_size(4, 4, 1, 128, 511, 128) == want
+
+
+def test_cache_write_validation():
+    lib = pa.library()
+    f = lib.pa_reshape_and_cache
+    assert f(0, FAKE, None, FAKE, FAKE, FAKE, 4, 1, 128, 16, 8, None) == INVALID   # value NULL
+    assert f(0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 96, 16, 8, None) == UNSUPPORTED
+    assert f(0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 128, 24, 8, None) == UNSUPPORTED
+    assert f(1, FAKE, FAKE, FAKE, None, FAKE, 4, 1, 576, 1, 8, None) == INVALID    # MLA + value
+    assert f(1, FAKE, None, FAKE, None, FAKE, 4, 2, 576, 1, 8, None) == INVALID    # MLA Hkv != 1
+    assert f(7, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 128, 16, 8, None) == INVALID   # bad layout
+    assert f(0, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, 128, 16, 8, None) == INVALID
+    assert f(0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 128, 16, 8, None) == OK        # no-op
+
+
+def test_merge_validation():
+    f = pa.library().pa_merge_attn_states
+    assert f(FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 12, None) == UNSUPPORTED
+    assert f(FAKE, None, 5, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 128, None) == INVALID
+    assert f(None, None, 0, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 128, None) == INVALID
+    assert f(FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, 2, 128, None) == OK     # no rows
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.paged_decode_attn(q, q, q, q, q, 0.1, 1)

@@ -1,0 +1,201 @@
+"""GPU parity: cache write (bit-exact) and GQA paged decode (tolerance) vs the oracle.
+
+Every call goes through the C ABI (libpagedattn.so) via the Python binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_decode_reshape_amd as pa
+from paged_attention_decode_reshape_amd import workloads as W
+import oracle_pins
+from gpu_util import GpuGQA, assert_attn_close, device, oracle_gqa, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# cache write
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mk", [
+    lambda: W.tiny_gqa(),
+    lambda: W.gqa_decode_case("d64b32", 201, [1, 31, 32, 33, 200], Hq=8, Hkv=4, D=64,
+                              block_size=32),
+    lambda: W.gqa_decode_case("h3", 202, [5, 17, 64, 65], Hq=6, Hkv=3, D=128, block_size=16),
+], ids=["tiny", "d64b32_hkv4", "hkv3"])
+def test_cache_write_bitexact(orc, mk):
+    case = mk()
+    say(f"cache write {case.name}")
+    g = GpuGQA(case)
+    kc, vc = oracle_pins.oracle_cache(orc, case)
+    assert np.array_equal(_bits(g.kc), kc.reshape(-1).reshape(kc.shape))
+    assert np.array_equal(_bits(g.vc), vc)
+
+
+def test_cache_write_skips_bad_slots(orc):
+    dev = device()
+    case = W.gqa_decode_case("skip", 203, [20], Hq=2, Hkv=2, D=128, block_size=16)
+    g = GpuGQA(case)
+    before_k, before_v = g.kc.clone(), g.vc.clone()
+    nb = case.paging.num_blocks
+    key = torch.randn(4, 2, 128, device=dev).to(torch.bfloat16)
+    slots = torch.tensor([-1, nb * 16, nb * 16 + 100, -7], dtype=torch.int64, device=dev)
+    pa.reshape_and_cache(key, key.clone(), g.kc, g.vc, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(_t(g.kc), _t(before_k)) and torch.equal(_t(g.vc), _t(before_v))
+
+
+def _t(x):
+    return x.view(torch.int16)
+
+
+def test_cache_write_decode_step_overwrite(orc):
+    """A decode step rewrites each sequence's newest token; bytes stay identical."""
+    case = W.tiny_gqa()
+    g = GpuGQA(case)
+    dev = device()
+    rows = torch.from_numpy(case.new_token_rows())
+    pa.reshape_and_cache(case.key[rows].to(dev), case.value[rows].to(dev), g.kc, g.vc,
+                         g.slots[rows.to(dev)])
+    kc, vc = oracle_pins.oracle_cache(orc, case)
+    assert np.array_equal(_bits(g.kc), kc) and np.array_equal(_bits(g.vc), vc)
+
+
+def test_latent_cache_write_bitexact(orc):
+    cases = W.mla_decode_cases("lat", 204, S=3, lens_range=None, lens=[1, 70, 129], Hq=2, Dl=576,
+                               Dv=512, block_sizes=(1, 64, 5), scale=0.1)
+    dev = device()
+    for B, case in cases.items():
+        kv = torch.full((case.paging.num_blocks, B, 576), float("nan"), dtype=torch.bfloat16,
+                        device=dev)
+        pa.reshape_and_cache(case.latent.to(dev), None, kv, None,
+                             torch.from_numpy(case.paging.slot_mapping).to(dev),
+                             layout=pa.LAYOUT_MLA_LATENT)
+        ref = np.full((case.paging.num_blocks, B, 576), 0x7FC0, dtype=np.uint16)
+        orc.cache_write_latent(W.bf16_bits(case.latent), case.paging.slot_mapping, ref, B)
+        assert np.array_equal(_bits(kv), ref), f"block size {B}"
+
+
+# ---------------------------------------------------------------------------
+# GQA decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("partition", [-1, 128, 0, 64])
+def test_decode_tiny(orc, partition):
+    case = W.tiny_gqa(partition_tokens=partition)
+    say(f"decode tiny partition={partition}")
+    g = GpuGQA(case)
+    out, lse = g.decode()
+    ref_out, ref_lse = oracle_gqa(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what=f"tiny P={partition}")
+
+
+def test_decode_split_matches_unsplit():
+    """128-token partitions + LSE merge equal the unsplit result."""
+    case = W.tiny_gqa()
+    g = GpuGQA(case)
+    o1, l1 = g.decode(partition_tokens=-1)
+    o2, l2 = g.decode(partition_tokens=128)
+    torch.cuda.synchronize()
+    d = (o1.float() - o2.float()).abs().max().item()
+    dl = (l1 - l2).abs().max().item()
+    say(f"  split vs unsplit: out {d:.3e} lse {dl:.3e}")
+    assert d <= 1e-2 and dl <= 1e-4
+
+
+EDGE_LENS = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 0, 300, 511]
+
+
+@pytest.mark.parametrize("D,B,Hq,Hkv", [
+    (128, 16, 4, 1), (128, 32, 8, 1), (64, 16, 2, 2), (64, 32, 16, 1),
+    (128, 16, 3, 1), (128, 16, 12, 2), (128, 32, 64, 4), (128, 16, 5, 5),
+])
+@pytest.mark.parametrize("partition", [-1, 64, 256])
+def test_decode_edges(orc, D, B, Hq, Hkv, partition):
+    case = W.gqa_decode_case(f"edge_{D}_{B}_{Hq}_{Hkv}", 300 + D + B + Hq, EDGE_LENS, Hq=Hq,
+                             Hkv=Hkv, D=D, block_size=B, partition_tokens=partition)
+    say(f"decode edges D={D} B={B} Hq={Hq} Hkv={Hkv} P={partition}")
+    g = GpuGQA(case)
+    out, lse = g.decode()
+    ref_out, ref_lse = oracle_gqa(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what=case.name)
+    # the empty sequence: zero output, -inf lse
+    s0 = EDGE_LENS.index(0)
+    assert torch.all(out[s0] == 0) and torch.all(torch.isneginf(lse[s0]))
+
+
+def test_decode_block_permutation_bitexact():
+    """Relabelling physical blocks changes no output bit."""
+    case = W.tiny_gqa()
+    g = GpuGQA(case)
+    o1, l1 = g.decode(partition_tokens=128)
+    dev = device()
+    nb = case.paging.num_blocks
+    perm = torch.from_numpy(np.random.default_rng(8).permutation(nb)).to(dev)
+    kc2 = torch.empty_like(g.kc)
+    vc2 = torch.empty_like(g.vc)
+    kc2[perm] = g.kc
+    vc2[perm] = g.vc
+    bt2 = perm[g.bt.long()].to(torch.int32).contiguous()
+    o2, l2 = pa.paged_decode_attn(g.q, kc2, vc2, bt2, g.cl, case.scale, g.max_ctx,
+                                  partition_tokens=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_decode_deterministic():
+    case = W.qwen3_decode(S=8)
+    g = GpuGQA(case)
+    o1, l1 = g.decode()
+    o2, l2 = g.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_decode_qwen3_full(orc):
+    """64 requests, GQA 8:1, lengths U[1000,2000]: every output vs the oracle."""
+    case = W.qwen3_decode()
+    say("decode qwen3 64-request full")
+    g = GpuGQA(case)
+    out, lse = g.decode()
+    ref_out, ref_lse = oracle_gqa(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what="qwen3 full")
+
+
+def test_decode_long_context_sampled(orc):
+    """8 requests up to 131072 tokens, 2048-token partitions, K outliers:
+    sampled (seq, head) rows vs the oracle, plus partition-size invariance."""
+    case = W.long_context_decode()
+    say(f"decode long context, lens {case.context_lens.tolist()}")
+    g = GpuGQA(case)
+    out, lse = g.decode()
+    rng = np.random.default_rng(31)
+    mask = np.zeros((case.S, case.Hq), dtype=np.uint8)
+    for s in range(case.S):
+        mask[s, rng.choice(case.Hq, size=3, replace=False)] = 1
+    ref_out, ref_lse = oracle_gqa(orc, case, row_mask=mask)
+    rows = np.nonzero(mask)
+    assert_attn_close(out, lse, ref_out, ref_lse, rows=rows, what="long context sampled")
+    o2, l2 = g.decode(partition_tokens=8192)
+    torch.cuda.synchronize()
+    d = (out.float() - o2.float()).abs().max().item()
+    say(f"  P=2048 vs P=8192: {d:.3e}")
+    assert d <= 1e-2 and (lse - l2).abs().max().item() <= 1e-3
+
+
+def test_decode_rejects_bad_args():
+    case = W.tiny_gqa()
+    g = GpuGQA(case)
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.paged_decode_attn(g.q, g.kc, g.vc, g.bt, g.cl, float("nan"), g.max_ctx)
+    assert e.value.status == 1
+    with pytest.raises(ValueError):
+        pa.paged_decode_attn(g.q, g.kc, g.vc, g.bt, g.cl, 0.1, g.max_ctx, partition_tokens=128,
+                             workspace=torch.empty(16, dtype=torch.uint8, device=device()))
+    with pytest.raises(ValueError):
+        pa.paged_decode_attn(g.q.cpu(), g.kc, g.vc, g.bt, g.cl, 0.1, g.max_ctx)
