@@ -101,7 +101,7 @@ def bench_gqa(args, case, label):
     cl = torch.from_numpy(pg.lens).to(dev)
     max_ctx = int(pg.lens.max())
     P = case.partition_tokens
-    ws = torch.empty(max(1, pa.decode_workspace_size(case.S, case.Hq, case.Hkv, case.D, max_ctx, P)),
+    ws = torch.zeros(max(1, pa.decode_workspace_size(case.S, case.Hq, case.Hkv, case.D, max_ctx, P)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
@@ -265,7 +265,7 @@ def main():
         "graph_replay_matches_eager": r["graph_replay_matches_eager"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged decode (partition + merge launches)",
+            "kernel": "paged_decode_partition_kernel (partitions + fused merge)",
             "achieved": r["hbm_gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

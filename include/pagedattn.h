@@ -91,7 +91,8 @@ pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *valu
 /*
  * Split-KV partition length the decode entry points use for these
  * arguments: partition_tokens > 0 is rounded up to a multiple of 64;
- * 0 picks one from the work size; -1 means one partition per sequence.
+ * 0 picks one from the work size; -1 asks for as few partitions as
+ * possible.  Partitions are capped at 4096 tokens.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_context_len, int32_t partition_tokens);
@@ -119,7 +120,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *   one partition are split; partial (out, lse) go to the workspace and
  *   are merged by log-sum-exp.
  * workspace: device memory of at least pa_decode_workspace_size(...)
- *   bytes, 256-byte aligned; contents need no initialisation.
+ *   bytes, 256-byte aligned.  It starts with a region of completion
+ *   counters that must be zero-filled before the workspace is first used
+ *   (e.g. one hipMemset at allocation); every call leaves it zero again.
+ *   Calls that run concurrently must not share a workspace.
  * Supported: head_dim in {64, 128}, block_size in {16, 32}, group size
  *   num_q_heads / num_kv_heads in 1..16, max_context_len <= 1 << 20.
  */

@@ -19,21 +19,33 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// A workgroup's 4 waves take 16-token sub-blocks round-robin and a wave
+// tracks at most 64 of them, so a partition holds at most 4096 tokens.
+constexpr int32_t kMaxPartition = 4096;
+
 int32_t partition_tokens_for(int32_t S, int32_t H, int32_t max_ctx, int32_t requested) {
     const int32_t ctx = max_ctx > 0 ? max_ctx : 1;
-    if (requested == -1) return (int32_t)cdiv(ctx, 64) * 64;
-    if (requested > 0) return (int32_t)cdiv(requested, 64) * 64;
-    // auto: 256-token partitions (one 64-token step per wave), doubled while
-    // the grid would still hold >= kAutoTargetWorkgroups workgroups
-    int32_t P = 256;
-    while (P < 8192 && (int64_t)S * H * cdiv(ctx, 2 * (int64_t)P) >= kAutoTargetWorkgroups) P *= 2;
-    return P;
+    int32_t P;
+    if (requested == -1)
+        P = (int32_t)cdiv(ctx, 64) * 64;
+    else if (requested > 0)
+        P = (int32_t)cdiv(requested, 64) * 64;
+    else {
+        // auto: 256-token partitions, doubled while the grid would still hold
+        // >= kAutoTargetWorkgroups workgroups
+        P = 256;
+        while (P < kMaxPartition &&
+               (int64_t)S * H * cdiv(ctx, 2 * (int64_t)P) >= kAutoTargetWorkgroups)
+            P *= 2;
+    }
+    return P < kMaxPartition ? P : kMaxPartition;
 }
 
 struct Split {
     int32_t P;
     int32_t parts;
-    size_t out_bytes, lse_bytes;
+    size_t counter_bytes, out_bytes, lse_bytes;
+    size_t total() const { return counter_bytes + out_bytes + lse_bytes; }
 };
 
 Split plan_split(int32_t S, int32_t Hq, int32_t H_units, int32_t Dv, int32_t max_ctx,
@@ -43,8 +55,9 @@ Split plan_split(int32_t S, int32_t Hq, int32_t H_units, int32_t Dv, int32_t max
     sp.parts = max_ctx > 0 ? (int32_t)cdiv(max_ctx, sp.P) : 1;
     if (sp.parts <= 1) {
         sp.parts = 1;
-        sp.out_bytes = sp.lse_bytes = 0;
+        sp.counter_bytes = sp.out_bytes = sp.lse_bytes = 0;
     } else {
+        sp.counter_bytes = align256((size_t)S * H_units * sizeof(int32_t));
         sp.out_bytes = align256((size_t)S * Hq * sp.parts * Dv * sizeof(float));
         sp.lse_bytes = align256((size_t)S * Hq * sp.parts * sizeof(float));
     }
@@ -108,7 +121,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
         return 0;
     Split sp = plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           partition_tokens);
-    return sp.out_bytes + sp.lse_bytes;
+    return sp.total();
 }
 
 pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
@@ -134,9 +147,8 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
         return PA_ERR_UNSUPPORTED;
     Split sp = plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           partition_tokens);
-    if (sp.out_bytes + sp.lse_bytes > 0) {
-        if (!workspace || workspace_bytes < sp.out_bytes + sp.lse_bytes)
-            return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (sp.total() > 0) {
+        if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
     }
     if (num_seqs == 0) return PA_OK;
@@ -158,8 +170,10 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
     p.scale = scale;
     p.partition = sp.P;
     p.max_parts = sp.parts;
-    p.part_out = sp.parts > 1 ? (float *)workspace : nullptr;
-    p.part_lse = sp.parts > 1 ? (float *)((char *)workspace + sp.out_bytes) : nullptr;
+    char *ws = (char *)workspace;
+    p.counters = sp.parts > 1 ? (int *)ws : nullptr;
+    p.part_out = sp.parts > 1 ? (float *)(ws + sp.counter_bytes) : nullptr;
+    p.part_lse = sp.parts > 1 ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
     return from_hip(launch_paged_decode(p, (hipStream_t)stream));
 }
 
@@ -169,7 +183,7 @@ size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_di
         partition_tokens < -1)
         return 0;
     Split sp = plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len, partition_tokens);
-    return sp.out_bytes + sp.lse_bytes;
+    return sp.total();
 }
 
 pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const void *kv_cache,

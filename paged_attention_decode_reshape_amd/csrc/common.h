@@ -44,6 +44,19 @@ __device__ __forceinline__ cptr<T> as_const(const void *p) {
     return (cptr<T>)(p);
 }
 
+// Device-coherent (agent-scope) 4-byte accesses for data one workgroup
+// writes and another, possibly on another XCD, reads in the same kernel.
+// They bypass the per-XCD L2's write-back, so no cache-wide fence is needed.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding stores have completed (been
+// acknowledged); also a compiler barrier for memory.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // A zero the compiler cannot see through.  Adding it to an address keeps a
 // loop-invariant scalar load inside the loop (re-read from the scalar cache
 // each iteration) instead of being hoisted and spilled.

@@ -20,15 +20,19 @@
 //       folded into the scale.
 //   PV  lane l owns dims l (and l + 64).  A V vector
 //       (v_cache[p][g][j][d][0..8), 8 consecutive tokens of one dim) makes
-//       P.V a reduction over tokens inside a lane.  p is split as
-//       hi + lo (two bf16) so that bf16 dot2 keeps ~2^-17 relative accuracy
-//       per weight; the pairs are permuted (ds_bpermute) so that lane n of
-//       every row holds token pair n and are broadcast by DPP as above.
+//       P.V a reduction over tokens inside a lane.  It runs as fp32 FMAs
+//       (on gfx950 a wave64 fp32 FMA issues in half the cycles of a bf16
+//       dot2, so fp32 weights cost no more than bf16 ones): each V vector is
+//       widened once and shared by every head; the weights are permuted
+//       (ds_bpermute) so that lane n of every row holds token 16 k + n and
+//       are broadcast by DPP as above.
 // Groups of more than 8 query heads are processed 8 heads at a time with
 // the queries re-read from LDS.  The 4 waves' states merge in LDS.  A
 // sequence longer than one partition writes fp32 partials (normalised
-// output, LSE) that a second kernel merges by log-sum-exp in partition
-// order, so results are deterministic.
+// output, LSE); the last workgroup of the sequence to finish merges them by
+// log-sum-exp in partition order, so results are deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -142,80 +146,315 @@ __device__ __forceinline__ void qk_slice_1h(bool last, float &a0, float &a1, uin
         qk_1h<false>(a0, a1, qa, k0, k1, k2, k3);
 }
 
-// PV for one head over one group of 8 tokens: acc += sum over the group's
-// 4 token pairs of (hi + lo) . v, where pair k sits in lane N0 + k of
-// every row of rh / rl.  v holds the group's 8 tokens of one dim as pairs.
-#define PA_PV2_BODY                                                                         \
-    "s_nop 1\n\t"                                                                           \
-    PA_DOT2_BC("%0", "%2", "%4", "%12") PA_DOT2_BC("%1", "%2", "%8", "%12")                 \
-    PA_DOT2_BC("%0", "%3", "%4", "%12") PA_DOT2_BC("%1", "%3", "%8", "%12")                 \
-    PA_DOT2_BC("%0", "%2", "%5", "%13") PA_DOT2_BC("%1", "%2", "%9", "%13")                 \
-    PA_DOT2_BC("%0", "%3", "%5", "%13") PA_DOT2_BC("%1", "%3", "%9", "%13")                 \
-    PA_DOT2_BC("%0", "%2", "%6", "%14") PA_DOT2_BC("%1", "%2", "%10", "%14")                \
-    PA_DOT2_BC("%0", "%3", "%6", "%14") PA_DOT2_BC("%1", "%3", "%10", "%14")                \
-    PA_DOT2_BC("%0", "%2", "%7", "%15") PA_DOT2_BC("%1", "%2", "%11", "%15")                \
-    PA_DOT2_BC("%0", "%3", "%7", "%15") PA_DOT2_BC("%1", "%3", "%11", "%15")
-#define PA_PV2_OPERANDS                                                                     \
-    : "+v"(a0), "+v"(a1)                                                                    \
-    : "v"(rh), "v"(rl), "v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w), "v"(v1.x), "v"(v1.y),   \
-      "v"(v1.z), "v"(v1.w), "n"(N0), "n"(N0 + 1), "n"(N0 + 2), "n"(N0 + 3)
 
-template <int N0, bool TAIL>
-__device__ __forceinline__ void pv_bcast2(float &a0, float &a1, uint32_t rh, uint32_t rl,
-                                          const uint4 &v0, const uint4 &v1) {
-    if constexpr (TAIL)
-        asm volatile(PA_PV2_BODY "s_nop 4\n\t" PA_PV2_OPERANDS);
-    else
-        asm volatile(PA_PV2_BODY PA_PV2_OPERANDS);
+// head_dim 64: a lane holds 2 K vectors (8 dwords) and lane n (< 8) of its
+// row holds the matching query dword.
+#define PA_QK2H8_BODY                                                                       \
+    "s_nop 1\n\t"                                                                           \
+    PA_DOT2_BC("%0", "%4", "%6", "0") PA_DOT2_BC("%2", "%5", "%6", "0")                     \
+    PA_DOT2_BC("%1", "%4", "%7", "1") PA_DOT2_BC("%3", "%5", "%7", "1")                     \
+    PA_DOT2_BC("%0", "%4", "%8", "2") PA_DOT2_BC("%2", "%5", "%8", "2")                     \
+    PA_DOT2_BC("%1", "%4", "%9", "3") PA_DOT2_BC("%3", "%5", "%9", "3")                     \
+    PA_DOT2_BC("%0", "%4", "%10", "4") PA_DOT2_BC("%2", "%5", "%10", "4")                   \
+    PA_DOT2_BC("%1", "%4", "%11", "5") PA_DOT2_BC("%3", "%5", "%11", "5")                   \
+    PA_DOT2_BC("%0", "%4", "%12", "6") PA_DOT2_BC("%2", "%5", "%12", "6")                   \
+    PA_DOT2_BC("%1", "%4", "%13", "7") PA_DOT2_BC("%3", "%5", "%13", "7") "s_nop 4\n\t"
+#define PA_QK1H8_BODY                                                                       \
+    "s_nop 1\n\t"                                                                           \
+    PA_DOT2_BC("%0", "%2", "%3", "0") PA_DOT2_BC("%1", "%2", "%4", "1")                     \
+    PA_DOT2_BC("%0", "%2", "%5", "2") PA_DOT2_BC("%1", "%2", "%6", "3")                     \
+    PA_DOT2_BC("%0", "%2", "%7", "4") PA_DOT2_BC("%1", "%2", "%8", "5")                     \
+    PA_DOT2_BC("%0", "%2", "%9", "6") PA_DOT2_BC("%1", "%2", "%10", "7") "s_nop 4\n\t"
+
+__device__ __forceinline__ void qk8_2h(float &a0, float &a1, float &b0, float &b1, uint32_t qa,
+                                       uint32_t qb, const uint4 &k0, const uint4 &k1) {
+    asm volatile(PA_QK2H8_BODY
+                 : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1)
+                 : "v"(qa), "v"(qb), "v"(k0.x), "v"(k0.y), "v"(k0.z), "v"(k0.w), "v"(k1.x),
+                   "v"(k1.y), "v"(k1.z), "v"(k1.w));
 }
 
-#define PA_PV1_BODY                                                                         \
-    "s_nop 1\n\t"                                                                           \
-    PA_DOT2_BC("%0", "%1", "%3", "%7") PA_DOT2_BC("%0", "%2", "%3", "%7")                   \
-    PA_DOT2_BC("%0", "%1", "%4", "%8") PA_DOT2_BC("%0", "%2", "%4", "%8")                   \
-    PA_DOT2_BC("%0", "%1", "%5", "%9") PA_DOT2_BC("%0", "%2", "%5", "%9")                   \
-    PA_DOT2_BC("%0", "%1", "%6", "%10") PA_DOT2_BC("%0", "%2", "%6", "%10")
-#define PA_PV1_OPERANDS                                                                     \
-    : "+v"(a0)                                                                              \
-    : "v"(rh), "v"(rl), "v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w), "n"(N0), "n"(N0 + 1),   \
-      "n"(N0 + 2), "n"(N0 + 3)
-
-template <int N0, bool TAIL>
-__device__ __forceinline__ void pv_bcast1(float &a0, uint32_t rh, uint32_t rl, const uint4 &v0) {
-    if constexpr (TAIL)
-        asm volatile(PA_PV1_BODY "s_nop 4\n\t" PA_PV1_OPERANDS);
-    else
-        asm volatile(PA_PV1_BODY PA_PV1_OPERANDS);
+__device__ __forceinline__ void qk8_1h(float &a0, float &a1, uint32_t qa, const uint4 &k0,
+                                       const uint4 &k1) {
+    asm volatile(PA_QK1H8_BODY
+                 : "+v"(a0), "+v"(a1)
+                 : "v"(qa), "v"(k0.x), "v"(k0.y), "v"(k0.z), "v"(k0.w), "v"(k1.x), "v"(k1.y),
+                   "v"(k1.z), "v"(k1.w));
 }
 
-// Dispatch on the (unrolled, hence constant) first pair index of the group.
-template <int DV, bool TAIL>
-__device__ __forceinline__ void pv_group(int n0, float (&a)[DV], uint32_t rh, uint32_t rl,
-                                         const uint4 (&v)[DV]) {
-    if constexpr (DV == 2) {
-        switch (n0) {
-        case 0: pv_bcast2<0, TAIL>(a[0], a[1], rh, rl, v[0], v[1]); break;
-        case 4: pv_bcast2<4, TAIL>(a[0], a[1], rh, rl, v[0], v[1]); break;
-        case 8: pv_bcast2<8, TAIL>(a[0], a[1], rh, rl, v[0], v[1]); break;
-        default: pv_bcast2<12, TAIL>(a[0], a[1], rh, rl, v[0], v[1]); break;
-        }
+// One v_fmac_f32 whose first operand is lane `n` of the same 16-lane row.
+#define PA_FMA_BC(acc, r, v, n) \
+    "v_fmac_f32_dpp " acc ", " r ", " v " row_newbcast:" n " row_mask:0xf bank_mask:0xf\n\t"
+
+// PV over one group of 8 tokens: acc += p(token e) * v(token e), e = 0..7,
+// where p of token e sits in lane N0 + e of every row of the p register
+// (N0 = 0 or 8) and vf0 / vf1 hold the 8 tokens' values of dims lane and
+// lane + 64 as fp32.  Bodies for two heads (a, b) and / or two dims.
+#define PA_PV22_N0                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%4", "%6", "0") PA_FMA_BC("%2", "%5", "%6", "0")                       \
+    PA_FMA_BC("%1", "%4", "%14", "0") PA_FMA_BC("%3", "%5", "%14", "0")                     \
+    PA_FMA_BC("%0", "%4", "%7", "1") PA_FMA_BC("%2", "%5", "%7", "1")                       \
+    PA_FMA_BC("%1", "%4", "%15", "1") PA_FMA_BC("%3", "%5", "%15", "1")                     \
+    PA_FMA_BC("%0", "%4", "%8", "2") PA_FMA_BC("%2", "%5", "%8", "2")                       \
+    PA_FMA_BC("%1", "%4", "%16", "2") PA_FMA_BC("%3", "%5", "%16", "2")                     \
+    PA_FMA_BC("%0", "%4", "%9", "3") PA_FMA_BC("%2", "%5", "%9", "3")                       \
+    PA_FMA_BC("%1", "%4", "%17", "3") PA_FMA_BC("%3", "%5", "%17", "3")                     \
+    PA_FMA_BC("%0", "%4", "%10", "4") PA_FMA_BC("%2", "%5", "%10", "4")                     \
+    PA_FMA_BC("%1", "%4", "%18", "4") PA_FMA_BC("%3", "%5", "%18", "4")                     \
+    PA_FMA_BC("%0", "%4", "%11", "5") PA_FMA_BC("%2", "%5", "%11", "5")                     \
+    PA_FMA_BC("%1", "%4", "%19", "5") PA_FMA_BC("%3", "%5", "%19", "5")                     \
+    PA_FMA_BC("%0", "%4", "%12", "6") PA_FMA_BC("%2", "%5", "%12", "6")                     \
+    PA_FMA_BC("%1", "%4", "%20", "6") PA_FMA_BC("%3", "%5", "%20", "6")                     \
+    PA_FMA_BC("%0", "%4", "%13", "7") PA_FMA_BC("%2", "%5", "%13", "7")                     \
+    PA_FMA_BC("%1", "%4", "%21", "7") PA_FMA_BC("%3", "%5", "%21", "7")
+#define PA_PV22_N8                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%4", "%6", "8") PA_FMA_BC("%2", "%5", "%6", "8")                       \
+    PA_FMA_BC("%1", "%4", "%14", "8") PA_FMA_BC("%3", "%5", "%14", "8")                     \
+    PA_FMA_BC("%0", "%4", "%7", "9") PA_FMA_BC("%2", "%5", "%7", "9")                       \
+    PA_FMA_BC("%1", "%4", "%15", "9") PA_FMA_BC("%3", "%5", "%15", "9")                     \
+    PA_FMA_BC("%0", "%4", "%8", "10") PA_FMA_BC("%2", "%5", "%8", "10")                     \
+    PA_FMA_BC("%1", "%4", "%16", "10") PA_FMA_BC("%3", "%5", "%16", "10")                   \
+    PA_FMA_BC("%0", "%4", "%9", "11") PA_FMA_BC("%2", "%5", "%9", "11")                     \
+    PA_FMA_BC("%1", "%4", "%17", "11") PA_FMA_BC("%3", "%5", "%17", "11")                   \
+    PA_FMA_BC("%0", "%4", "%10", "12") PA_FMA_BC("%2", "%5", "%10", "12")                   \
+    PA_FMA_BC("%1", "%4", "%18", "12") PA_FMA_BC("%3", "%5", "%18", "12")                   \
+    PA_FMA_BC("%0", "%4", "%11", "13") PA_FMA_BC("%2", "%5", "%11", "13")                   \
+    PA_FMA_BC("%1", "%4", "%19", "13") PA_FMA_BC("%3", "%5", "%19", "13")                   \
+    PA_FMA_BC("%0", "%4", "%12", "14") PA_FMA_BC("%2", "%5", "%12", "14")                   \
+    PA_FMA_BC("%1", "%4", "%20", "14") PA_FMA_BC("%3", "%5", "%20", "14")                   \
+    PA_FMA_BC("%0", "%4", "%13", "15") PA_FMA_BC("%2", "%5", "%13", "15")                   \
+    PA_FMA_BC("%1", "%4", "%21", "15") PA_FMA_BC("%3", "%5", "%21", "15")
+#define PA_PV12_N0                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%2", "%3", "0") PA_FMA_BC("%1", "%2", "%11", "0")                      \
+    PA_FMA_BC("%0", "%2", "%4", "1") PA_FMA_BC("%1", "%2", "%12", "1")                      \
+    PA_FMA_BC("%0", "%2", "%5", "2") PA_FMA_BC("%1", "%2", "%13", "2")                      \
+    PA_FMA_BC("%0", "%2", "%6", "3") PA_FMA_BC("%1", "%2", "%14", "3")                      \
+    PA_FMA_BC("%0", "%2", "%7", "4") PA_FMA_BC("%1", "%2", "%15", "4")                      \
+    PA_FMA_BC("%0", "%2", "%8", "5") PA_FMA_BC("%1", "%2", "%16", "5")                      \
+    PA_FMA_BC("%0", "%2", "%9", "6") PA_FMA_BC("%1", "%2", "%17", "6")                      \
+    PA_FMA_BC("%0", "%2", "%10", "7") PA_FMA_BC("%1", "%2", "%18", "7")
+#define PA_PV12_N8                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%2", "%3", "8") PA_FMA_BC("%1", "%2", "%11", "8")                      \
+    PA_FMA_BC("%0", "%2", "%4", "9") PA_FMA_BC("%1", "%2", "%12", "9")                      \
+    PA_FMA_BC("%0", "%2", "%5", "10") PA_FMA_BC("%1", "%2", "%13", "10")                    \
+    PA_FMA_BC("%0", "%2", "%6", "11") PA_FMA_BC("%1", "%2", "%14", "11")                    \
+    PA_FMA_BC("%0", "%2", "%7", "12") PA_FMA_BC("%1", "%2", "%15", "12")                    \
+    PA_FMA_BC("%0", "%2", "%8", "13") PA_FMA_BC("%1", "%2", "%16", "13")                    \
+    PA_FMA_BC("%0", "%2", "%9", "14") PA_FMA_BC("%1", "%2", "%17", "14")                    \
+    PA_FMA_BC("%0", "%2", "%10", "15") PA_FMA_BC("%1", "%2", "%18", "15")
+#define PA_PV21_N0                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%2", "%4", "0") PA_FMA_BC("%1", "%3", "%4", "0")                       \
+    PA_FMA_BC("%0", "%2", "%5", "1") PA_FMA_BC("%1", "%3", "%5", "1")                       \
+    PA_FMA_BC("%0", "%2", "%6", "2") PA_FMA_BC("%1", "%3", "%6", "2")                       \
+    PA_FMA_BC("%0", "%2", "%7", "3") PA_FMA_BC("%1", "%3", "%7", "3")                       \
+    PA_FMA_BC("%0", "%2", "%8", "4") PA_FMA_BC("%1", "%3", "%8", "4")                       \
+    PA_FMA_BC("%0", "%2", "%9", "5") PA_FMA_BC("%1", "%3", "%9", "5")                       \
+    PA_FMA_BC("%0", "%2", "%10", "6") PA_FMA_BC("%1", "%3", "%10", "6")                     \
+    PA_FMA_BC("%0", "%2", "%11", "7") PA_FMA_BC("%1", "%3", "%11", "7")
+#define PA_PV21_N8                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%2", "%4", "8") PA_FMA_BC("%1", "%3", "%4", "8")                       \
+    PA_FMA_BC("%0", "%2", "%5", "9") PA_FMA_BC("%1", "%3", "%5", "9")                       \
+    PA_FMA_BC("%0", "%2", "%6", "10") PA_FMA_BC("%1", "%3", "%6", "10")                     \
+    PA_FMA_BC("%0", "%2", "%7", "11") PA_FMA_BC("%1", "%3", "%7", "11")                     \
+    PA_FMA_BC("%0", "%2", "%8", "12") PA_FMA_BC("%1", "%3", "%8", "12")                     \
+    PA_FMA_BC("%0", "%2", "%9", "13") PA_FMA_BC("%1", "%3", "%9", "13")                     \
+    PA_FMA_BC("%0", "%2", "%10", "14") PA_FMA_BC("%1", "%3", "%10", "14")                   \
+    PA_FMA_BC("%0", "%2", "%11", "15") PA_FMA_BC("%1", "%3", "%11", "15")
+#define PA_PV11_N0                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%1", "%2", "0")                                                        \
+    PA_FMA_BC("%0", "%1", "%3", "1")                                                        \
+    PA_FMA_BC("%0", "%1", "%4", "2")                                                        \
+    PA_FMA_BC("%0", "%1", "%5", "3")                                                        \
+    PA_FMA_BC("%0", "%1", "%6", "4")                                                        \
+    PA_FMA_BC("%0", "%1", "%7", "5")                                                        \
+    PA_FMA_BC("%0", "%1", "%8", "6")                                                        \
+    PA_FMA_BC("%0", "%1", "%9", "7")
+#define PA_PV11_N8                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_FMA_BC("%0", "%1", "%2", "8")                                                        \
+    PA_FMA_BC("%0", "%1", "%3", "9")                                                        \
+    PA_FMA_BC("%0", "%1", "%4", "10")                                                       \
+    PA_FMA_BC("%0", "%1", "%5", "11")                                                       \
+    PA_FMA_BC("%0", "%1", "%6", "12")                                                       \
+    PA_FMA_BC("%0", "%1", "%7", "13")                                                       \
+    PA_FMA_BC("%0", "%1", "%8", "14")                                                       \
+    PA_FMA_BC("%0", "%1", "%9", "15")
+#define PA_VF8(v) "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
+#define PA_PV_ASM(BODY, ...)                             \
+    do {                                                 \
+        if constexpr (TAIL)                              \
+            asm volatile(BODY "s_nop 4\n\t" __VA_ARGS__); \
+        else                                             \
+            asm volatile(BODY __VA_ARGS__);              \
+    } while (0)
+
+template <bool N8, bool TAIL>
+__device__ __forceinline__ void pv22(float &a0, float &a1, float &b0, float &b1, uint32_t pa,
+                                     uint32_t pb, const float (&v0)[8], const float (&v1)[8]) {
+    if constexpr (N8)
+        PA_PV_ASM(PA_PV22_N8, : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1) : "v"(pa), "v"(pb), PA_VF8(v0), PA_VF8(v1));
+    else
+        PA_PV_ASM(PA_PV22_N0, : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1) : "v"(pa), "v"(pb), PA_VF8(v0), PA_VF8(v1));
+}
+
+template <bool N8, bool TAIL>
+__device__ __forceinline__ void pv12(float &a0, float &a1, uint32_t pa, const float (&v0)[8],
+                                     const float (&v1)[8]) {
+    if constexpr (N8)
+        PA_PV_ASM(PA_PV12_N8, : "+v"(a0), "+v"(a1) : "v"(pa), PA_VF8(v0), PA_VF8(v1));
+    else
+        PA_PV_ASM(PA_PV12_N0, : "+v"(a0), "+v"(a1) : "v"(pa), PA_VF8(v0), PA_VF8(v1));
+}
+
+template <bool N8, bool TAIL>
+__device__ __forceinline__ void pv21(float &a0, float &b0, uint32_t pa, uint32_t pb,
+                                     const float (&v0)[8]) {
+    if constexpr (N8)
+        PA_PV_ASM(PA_PV21_N8, : "+v"(a0), "+v"(b0) : "v"(pa), "v"(pb), PA_VF8(v0));
+    else
+        PA_PV_ASM(PA_PV21_N0, : "+v"(a0), "+v"(b0) : "v"(pa), "v"(pb), PA_VF8(v0));
+}
+
+template <bool N8, bool TAIL>
+__device__ __forceinline__ void pv11(float &a0, uint32_t pa, const float (&v0)[8]) {
+    if constexpr (N8)
+        PA_PV_ASM(PA_PV11_N8, : "+v"(a0) : "v"(pa), PA_VF8(v0));
+    else
+        PA_PV_ASM(PA_PV11_N0, : "+v"(a0) : "v"(pa), PA_VF8(v0));
+}
+
+// fp32 values of the 8 tokens in a V vector (token 2w in the low half of word w)
+__device__ __forceinline__ void widen8(const uint4 &v, float (&f)[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// PV of one token group for one head pair (PAIRS) or one head; `odd`
+// selects lanes 8..15 of the p registers, `last` ends the block with the
+// wait that plain code reading the accumulators needs.
+template <int DV, bool PAIRS>
+__device__ __forceinline__ void pv_step(int odd, bool last, float (&a)[DV], float (&b)[DV],
+                                        uint32_t pa, uint32_t pb, const float (&vf)[DV][8]) {
+#define PA_PV_CALL(N8, T)                                                  \
+    do {                                                                   \
+        if constexpr (PAIRS && DV == 2) pv22<N8, T>(a[0], a[1], b[0], b[1], pa, pb, vf[0], vf[1]); \
+        else if constexpr (PAIRS) pv21<N8, T>(a[0], b[0], pa, pb, vf[0]);  \
+        else if constexpr (DV == 2) pv12<N8, T>(a[0], a[1], pa, vf[0], vf[1]); \
+        else pv11<N8, T>(a[0], pa, vf[0]);                                 \
+    } while (0)
+    if (odd) {
+        if (last) PA_PV_CALL(true, true);
+        else PA_PV_CALL(true, false);
     } else {
-        switch (n0) {
-        case 0: pv_bcast1<0, TAIL>(a[0], rh, rl, v[0]); break;
-        case 4: pv_bcast1<4, TAIL>(a[0], rh, rl, v[0]); break;
-        case 8: pv_bcast1<8, TAIL>(a[0], rh, rl, v[0]); break;
-        default: pv_bcast1<12, TAIL>(a[0], rh, rl, v[0]); break;
+        if (last) PA_PV_CALL(false, true);
+        else PA_PV_CALL(false, false);
+    }
+#undef PA_PV_CALL
+}
+
+// Log-sum-exp merge of one (sequence, q head) row over its partitions, in
+// partition order, by one wave: lane i holds partition i's LSE, weights are
+// broadcast with readlane and 4 partitions' outputs are read together.
+template <int D>
+__device__ __forceinline__ void merge_partitions(const DecodeParams &p, size_t row, int nparts,
+                                                 int lane) {
+    constexpr int DV = D / 64;
+    const float *pl = p.part_lse + row * p.max_parts;
+    float M = kNegInf;
+    for (int b = 0; b < nparts; b += 64) {
+        const float v = b + lane < nparts ? load_coherent(&pl[b + lane]) : kNegInf;
+        M = fmax_nc(M, wave_max(v));
+    }
+    float den = 0.f, o[DV];
+#pragma unroll
+    for (int jj = 0; jj < DV; jj++) o[jj] = 0.f;
+    const float *po = p.part_out + row * p.max_parts * D + lane;
+    for (int b = 0; b < nparts; b += 64) {
+        const float w =
+            b + lane < nparts ? fast_exp2((load_coherent(&pl[b + lane]) - M) * kLog2e) : 0.f;
+        den += wave_sum(w);
+        const int n = min(64, nparts - b);
+        int k = 0;
+        for (; k + 4 <= n; k += 4) {
+            float x[4][DV];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+#pragma unroll
+                for (int jj = 0; jj < DV; jj++)
+                    x[u][jj] = load_coherent(&po[(size_t)(b + k + u) * D + 64 * jj]);
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float wk = __int_as_float(readlane_i32(__float_as_int(w), k + u));
+#pragma unroll
+                for (int jj = 0; jj < DV; jj++) o[jj] += wk * x[u][jj];
+            }
+        }
+        for (; k < n; k++) {
+            const float wk = __int_as_float(readlane_i32(__float_as_int(w), k));
+#pragma unroll
+            for (int jj = 0; jj < DV; jj++)
+                o[jj] += wk * load_coherent(&po[(size_t)(b + k) * D + 64 * jj]);
         }
     }
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + row * D + lane;
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int jj = 0; jj < DV; jj++) out[64 * jj] = f32_to_bf16(o[jj] * inv);
+    if (lane == 0 && p.lse) p.lse[row] = M + fast_log2(den) * kLn2;
 }
 
-template <int D, int B, int G>
+// Sum over the 4 rows of the wave (lanes n, n + 16, n + 32, n + 48); every
+// lane gets the sum for its column.
+__device__ __forceinline__ float row_sum4(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Max over the 16 lanes of each row (v must not be NaN).
+__device__ __forceinline__ float row_max16(float v) {
+    int k = f2ord(v);
+    k = max(k, dpp_i<kQuadXor1>(k));
+    k = max(k, dpp_i<kQuadXor2>(k));
+    k = max(k, dpp_i<kRowRor4>(k));
+    k = max(k, dpp_i<kRowRor8>(k));
+    return ord2f(k);
+}
+
+constexpr int kSub = 16;  // tokens per sub-block: one row of lanes
+
+// Loads of one 16-token sub-block: K of token `col` (quarter `row` of the
+// dims: vectors row * CQ .. row * CQ + CQ - 1) and the two V token groups
+// of the sub-block for dims lane + 64 jj.  `half` selects the 16-token half
+// of a 32-token block.
+template <int D, int B>
+__device__ __forceinline__ void load_sub(const uint4 *kc, const uint4 *vc, size_t tile, int half,
+                                         int row, int col, int lane, uint4 (&kq)[D / 32],
+                                         uint4 (&vv)[2][D / 64]) {
+    constexpr int C = D / 8, CQ = D / 32, DV = D / 64;
+    const uint4 *kt = kc + tile * (size_t)(C * B) + half * kSub + col;
+#pragma unroll
+    for (int i = 0; i < CQ; i++) kq[i] = kt[(row * CQ + i) * B];
+    const uint4 *vt = vc + (tile * (B / 8) + half * 2) * D + lane;
+#pragma unroll
+    for (int tg = 0; tg < 2; tg++)
+#pragma unroll
+        for (int jj = 0; jj < DV; jj++) vv[tg][jj] = vt[tg * D + 64 * jj];
+}
+
+template <int D, int B, int G, int DEPTH>
 __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParams p) {
-    constexpr int C = D / 8;          // K vectors per token
+    constexpr int CQ = D / 32;        // K vectors per lane (a quarter of the dims)
     constexpr int DV = D / 64;        // output dims per lane
-    constexpr int HG = G < 8 ? G : 8; // heads per pass
-    constexpr int NPASS = G / HG;
-    constexpr int QR = D / 32;        // query VGPRs per head (16 dwords each)
+    constexpr int QW = 4 * CQ;        // query dwords per row
 
     const int units = p.S * p.Hkv;
     const int part = blockIdx.x / units;
@@ -227,6 +466,7 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
         clamp_ctx(as_const<int32_t>(p.context_lens)[s], p.max_blocks, B, p.max_parts, P);
     const int start = part * P;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = lane >> 4, col = lane & 15;
     uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
 
     if (start >= ctx) {
@@ -244,34 +484,28 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
     const int nparts = (ctx + P - 1) / P;
     const float sl2 = p.scale * kLog2e;
 
-    // the group's queries in LDS; padded heads (h >= Ga) repeat real ones
-    __shared__ uint32_t q_sm[G * D / 2];
+    // queries: lane (row r, column n) holds dword r * QW + n of each head;
+    // padded heads (h >= Ga) repeat real ones
+    uint32_t qreg[G];
     {
         const uint32_t *qg = reinterpret_cast<const uint32_t *>(p.query) +
-                             ((size_t)s * p.Hq + (size_t)g * Ga) * (D / 2);
-        for (int i = threadIdx.x; i < G * D / 2; i += blockDim.x) {
-            const int h = i / (D / 2);
-            q_sm[i] = qg[(h < Ga ? h : h - Ga) * (D / 2) + i % (D / 2)];
-        }
+                             ((size_t)s * p.Hq + (size_t)g * Ga) * (D / 2) + row * QW + (col % QW);
+#pragma unroll
+        for (int h = 0; h < G; h++) qreg[h] = qg[(h < Ga ? h : h - Ga) * (D / 2)];
     }
-    __syncthreads();
 
-    // ds_bpermute byte addresses: lane L reads pair L % 16 (lane 2 * (L % 16))
-    // and pair 16 + L % 16 (lane 32 + 2 * (L % 16))
-    const int src_pair0 = (2 * (lane & 15)) * 4;
-    const int src_pair1 = (32 + 2 * (lane & 15)) * 4;
-    const cptr<int32_t> bt = as_const<int32_t>(p.block_table) + (size_t)s * p.max_blocks;
+    // This wave's sub-blocks are k = 0, 1, ...: tokens start + 16 (wave + 4 k).
+    // Lane k holds the physical block of sub-block k (-1: out of range).
+    const int nsub = (end - start + kSub - 1) / kSub;
+    const int nmine = nsub > wave ? (nsub - wave + 3) / 4 : 0;
+    int bid = 0;
+    if (lane < nmine) {
+        const int b = as_const<int32_t>(p.block_table)[(size_t)s * p.max_blocks +
+                                                       (start + kSub * (wave + 4 * lane)) / B];
+        bid = (b < 0 || (int64_t)b >= p.num_blocks) ? -1 : b;
+    }
     const uint4 *kc = reinterpret_cast<const uint4 *>(p.k_cache);
     const uint4 *vc = reinterpret_cast<const uint4 *>(p.v_cache);
-
-    // query slices: qr[h][i] holds, in lane n of every row, dword 16 i + n of head h
-    uint32_t qr[HG][QR];
-    if constexpr (NPASS == 1) {
-#pragma unroll
-        for (int h = 0; h < HG; h++)
-#pragma unroll
-            for (int i = 0; i < QR; i++) qr[h][i] = q_sm[h * (D / 2) + 16 * i + (lane & 15)];
-    }
 
     float m[G], lsum[G], acc[G][DV];
 #pragma unroll
@@ -282,139 +516,116 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
         for (int jj = 0; jj < DV; jj++) acc[h][jj] = 0.f;
     }
 
-    for (int t0 = start + wave * kStep; t0 < end; t0 += kWaves * kStep) {
-        const int tok = t0 + lane;
-        bool valid = tok < end;
-        int phys = 0;
-        if (valid) {
-            phys = bt[tok / B];
-            if (phys < 0 || (int64_t)phys >= p.num_blocks) {
-                valid = false;
-                phys = 0;
-            }
-        }
-        // K: this lane's token, all head_dim / 8 vectors
-        uint4 kx[C];
-        {
-            const uint4 *kp = kc + ((size_t)phys * p.Hkv + g) * (size_t)(C * B) + (tok % B);
-            if (valid) {
+    // a DEPTH-deep ring of sub-blocks in flight; past the end the last
+    // sub-block is re-read (a cache hit) so every iteration issues the same loads
+    uint4 kb[DEPTH][CQ], vb[DEPTH][2][DV];
+    auto issue = [&](auto slot_c, int k) {
+        constexpr int slot = decltype(slot_c)::value;
+        const int kk = min(k, nmine - 1);
+        const int b = readlane_i32(bid, kk);
+        const int t0 = start + kSub * (wave + 4 * kk);
+        load_sub<D, B>(kc, vc, (size_t)(b < 0 ? 0 : b) * p.Hkv + g, (t0 % B) / kSub, row, col,
+                       lane, kb[slot], vb[slot]);
+    };
+    auto compute = [&](auto slot_c, int k) {
+        constexpr int slot = decltype(slot_c)::value;
+        const int t0 = start + kSub * (wave + 4 * k);
+        const int nvalid = readlane_i32(bid, k) < 0 ? 0 : min(kSub, end - t0);
+        const bool tok_ok = col < nvalid;
+        // QK: a quarter of each dot product per lane, summed over the rows
+        float sc[G];
 #pragma unroll
-                for (int c = 0; c < C; c++) kx[c] = kp[c * B];
+        for (int h = 0; h < G; h += (G >= 2 ? 2 : 1)) {
+            float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+            if constexpr (G >= 2) {
+                if constexpr (CQ == 4)
+                    qk_2h<true>(a0, a1, b0, b1, qreg[h], qreg[h + 1], kb[slot][0], kb[slot][1],
+                                kb[slot][2], kb[slot][3]);
+                else
+                    qk8_2h(a0, a1, b0, b1, qreg[h], qreg[h + 1], kb[slot][0], kb[slot][1]);
+                const float zb = row_sum4(b0 + b1);
+                sc[h + 1] = tok_ok ? zb * sl2 : kNegInf;
             } else {
-#pragma unroll
-                for (int c = 0; c < C; c++) kx[c] = make_uint4(0, 0, 0, 0);
+                if constexpr (CQ == 4)
+                    qk_1h<true>(a0, a1, qreg[h], kb[slot][0], kb[slot][1], kb[slot][2],
+                                kb[slot][3]);
+                else
+                    qk8_1h(a0, a1, qreg[h], kb[slot][0], kb[slot][1]);
             }
+            const float za = row_sum4(a0 + a1);
+            sc[h] = tok_ok ? za * sl2 : kNegInf;
         }
-        // V: 8 token groups of 8; this lane's dims lane + 64 * jj
-        uint4 vx[8][DV];
+        // online softmax; the weight of token n lands in lane n of every row
+        uint32_t pw[G];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int tg0 = t0 + 8 * j;
-            if (tg0 < end) {
-                const int pj = readlane_i32(phys, 8 * j);
-                const uint4 *vp =
-                    vc + (((size_t)pj * p.Hkv + g) * (B / 8) + ((8 * j) % B) / 8) * D + lane;
+        for (int h = 0; h < G; h++) {
+            const float mx = uniform_f(row_max16(sc[h]));
+            const float mn = fmax_nc(m[h], mx);
+            const float mref = mn == kNegInf ? 0.f : mn;
+            const float alpha = fast_exp2(m[h] - mref);
+            m[h] = mn;
+            const float pr = fast_exp2(sc[h] - mref);
+            lsum[h] = lsum[h] * alpha + pr;
 #pragma unroll
-                for (int jj = 0; jj < DV; jj++) vx[j][jj] = vp[64 * jj];
-            } else {
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++) vx[j][jj] = make_uint4(0, 0, 0, 0);
-            }
+            for (int jj = 0; jj < DV; jj++) acc[h][jj] *= alpha;
+            pw[h] = __float_as_uint(pr);
         }
-        // zero the V of tokens past the end (their weight is 0; the data may be anything)
-        if (t0 + kStep > end) {
+        // PV: zero the V of tokens past the end (weight 0, data may be anything)
+        if (nvalid < kSub) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int nv = end - (t0 + 8 * j);
-                if (nv > 0 && nv < 8) {
+            for (int tg = 0; tg < 2; tg++) {
+                const int nv = nvalid - 8 * tg;
 #pragma unroll
-                    for (int jj = 0; jj < DV; jj++) {
-                        vx[j][jj].x = mask_pair(vx[j][jj].x, 0, nv);
-                        vx[j][jj].y = mask_pair(vx[j][jj].y, 2, nv);
-                        vx[j][jj].z = mask_pair(vx[j][jj].z, 4, nv);
-                        vx[j][jj].w = mask_pair(vx[j][jj].w, 6, nv);
-                    }
+                for (int jj = 0; jj < DV; jj++) {
+                    uint4 &v = vb[slot][tg][jj];
+                    v.x = mask_pair(v.x, 0, nv);
+                    v.y = mask_pair(v.y, 2, nv);
+                    v.z = mask_pair(v.z, 4, nv);
+                    v.w = mask_pair(v.w, 6, nv);
                 }
             }
         }
+#pragma unroll
+        for (int tg = 0; tg < 2; tg++) {
+            float vf[DV][8];
+#pragma unroll
+            for (int jj = 0; jj < DV; jj++) widen8(vb[slot][tg][jj], vf[jj]);
+            constexpr bool kPairs = G >= 2;
+#pragma unroll
+            for (int h = 0; h < G; h += (kPairs ? 2 : 1)) {
+                const bool last = tg == 1 && h + (kPairs ? 2 : 1) >= G;
+                pv_step<DV, kPairs>(tg, last, acc[h], acc[h + (kPairs ? 1 : 0)], pw[h],
+                                    pw[h + (kPairs ? 1 : 0)], vf);
+            }
+        }
+    };
 
-#pragma unroll
-        for (int pass = 0; pass < NPASS; pass++) {
-            const int hb = pass * HG;
-            if constexpr (NPASS > 1) {
-#pragma unroll
-                for (int h = 0; h < HG; h++)
-#pragma unroll
-                    for (int i = 0; i < QR; i++)
-                        qr[h][i] = q_sm[(hb + h) * (D / 2) + 16 * i + (lane & 15)];
-            }
-            // QK: whole dot products per lane
-            float sc[HG];
-            if constexpr (HG == 1) {
-                float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-                for (int i = 0; i < QR; i++)
-                    qk_slice_1h(i == QR - 1, a0, a1, qr[0][i], kx[4 * i], kx[4 * i + 1],
-                                kx[4 * i + 2], kx[4 * i + 3]);
-                sc[0] = valid ? (a0 + a1) * sl2 : kNegInf;
-            } else {
-#pragma unroll
-                for (int h = 0; h < HG; h += 2) {
-                    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-#pragma unroll
-                    for (int i = 0; i < QR; i++)
-                        qk_slice_2h(i == QR - 1, a0, a1, b0, b1, qr[h][i], qr[h + 1][i], kx[4 * i],
-                                    kx[4 * i + 1], kx[4 * i + 2], kx[4 * i + 3]);
-                    sc[h] = valid ? (a0 + a1) * sl2 : kNegInf;
-                    sc[h + 1] = valid ? (b0 + b1) * sl2 : kNegInf;
-                }
-            }
-            // online softmax and the hi / lo pairs for P.V
-            uint32_t r0hi[HG], r1hi[HG], r0lo[HG], r1lo[HG];
-#pragma unroll
-            for (int h = 0; h < HG; h++) {
-                const int H = hb + h;
-                const float mx = uniform_f(wave_max(sc[h]));
-                const float mn = fmax_nc(m[H], mx);
-                const float mref = mn == kNegInf ? 0.f : mn;
-                const float alpha = fast_exp2(m[H] - mref);
-                m[H] = mn;
-                const float pr = fast_exp2(sc[h] - mref);
-                lsum[H] = lsum[H] * alpha + pr;
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++) acc[H][jj] *= alpha;
-                const float pn = dpp_f<kQuadXor1>(pr);
-                const uint32_t hi = pack_bf16x2(pr, pn);
-                const uint32_t lo = pack_bf16x2(pr - bf16_lo(hi), pn - bf16_hi(hi));
-                r0hi[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_pair0, (int)hi);
-                r1hi[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_pair1, (int)hi);
-                r0lo[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_pair0, (int)lo);
-                r1lo[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_pair1, (int)lo);
-            }
-            // PV: token group j holds pairs 4j .. 4j+3
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                if (t0 + 8 * j < end) {
-#pragma unroll
-                    for (int h = 0; h < HG; h++) {
-                        const uint32_t rh = j < 4 ? r0hi[h] : r1hi[h];
-                        const uint32_t rl = j < 4 ? r0lo[h] : r1lo[h];
-                        if (h == HG - 1)
-                            pv_group<DV, true>((4 * j) % 16, acc[hb + h], rh, rl, vx[j]);
-                        else
-                            pv_group<DV, false>((4 * j) % 16, acc[hb + h], rh, rl, vx[j]);
-                    }
-                }
-            }
+    // step U of an unrolled group: prefetch sub-block k + DEPTH - 1 into the
+    // slot freed by the previous step, then compute sub-block k from slot U
+    auto step = [&](auto u_c, int k) {
+        constexpr int U = decltype(u_c)::value;
+        if (k < nmine) {
+            issue(std::integral_constant<int, (U + DEPTH - 1) % DEPTH>{}, k + DEPTH - 1);
+            compute(std::integral_constant<int, U>{}, k);
+        }
+    };
+    if (nmine > 0) {
+        issue(std::integral_constant<int, 0>{}, 0);
+        if constexpr (DEPTH > 2) issue(std::integral_constant<int, 1>{}, 1);
+        for (int i = 0; i < nmine; i += DEPTH) {
+            step(std::integral_constant<int, 0>{}, i);
+            if constexpr (DEPTH > 1) step(std::integral_constant<int, 1>{}, i + 1);
+            if constexpr (DEPTH > 2) step(std::integral_constant<int, 2>{}, i + 2);
         }
     }
 
-    // merge the 4 waves of the workgroup
+    // merge the 4 waves of the workgroup (each column holds every row's copy
+    // of its token weights, so a wave's sum is 4 x the row sum)
     __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
     __shared__ float sm_acc[kWaves][G][D];
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const float l = wave_sum(lsum[h]);
+        const float l = wave_sum(lsum[h]) * 0.25f;
         if (lane == 0) {
             sm_m[wave][h] = m[h];
             sm_l[wave][h] = l;
@@ -442,74 +653,39 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
             out[row * D + d] = f32_to_bf16(o);
             if (d == 0 && p.lse) p.lse[row] = L;
         } else {
-            p.part_out[(row * p.max_parts + part) * D + d] = o;
-            if (d == 0) p.part_lse[row * p.max_parts + part] = L;
+            store_coherent(&p.part_out[(row * p.max_parts + part) * D + d], o);
+            if (d == 0) store_coherent(&p.part_lse[row * p.max_parts + part], L);
         }
     }
-}
+    if (nparts == 1) return;
 
-// Log-sum-exp merge of a sequence's partitions, one wave per (seq, q head),
-// in partition order: lane i holds partition i's LSE, the weights are
-// broadcast with readlane and the partial outputs of 4 partitions are read
-// together.
-template <int D>
-__global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeParams p, int B) {
-    constexpr int DV = D / 64;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= p.S * p.Hq) return;
-    const int lane = threadIdx.x & 63;
-    const int s = row / p.Hq;
-    const int P = p.partition;
-    const int ctx = clamp_ctx(p.context_lens[s], p.max_blocks, B, p.max_parts, P);
-    const int nparts = (ctx + P - 1) / P;
-    if (nparts <= 1) return;
-    const float *pl = p.part_lse + (size_t)row * p.max_parts;
-    float M = kNegInf;
-    for (int b = 0; b < nparts; b += 64) {
-        const float v = b + lane < nparts ? pl[b + lane] : kNegInf;
-        M = fmax_nc(M, wave_max(v));
-    }
-    float den = 0.f, o[DV];
-#pragma unroll
-    for (int jj = 0; jj < DV; jj++) o[jj] = 0.f;
-    const float *po = p.part_out + (size_t)row * p.max_parts * D + lane;
-    for (int b = 0; b < nparts; b += 64) {
-        const float w = b + lane < nparts ? fast_exp2((pl[b + lane] - M) * kLog2e) : 0.f;
-        den += wave_sum(w);
-        const int n = min(64, nparts - b);
-        int k = 0;
-        for (; k + 4 <= n; k += 4) {
-            float x[4][DV];
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++) x[u][jj] = po[(size_t)(b + k + u) * D + 64 * jj];
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const float wk = __int_as_float(readlane_i32(__float_as_int(w), k + u));
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++) o[jj] += wk * x[u][jj];
-            }
-        }
-        for (; k < n; k++) {
-            const float wk = __int_as_float(readlane_i32(__float_as_int(w), k));
-#pragma unroll
-            for (int jj = 0; jj < DV; jj++) o[jj] += wk * po[(size_t)(b + k) * D + 64 * jj];
-        }
-    }
-    uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + (size_t)row * D + lane;
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int jj = 0; jj < DV; jj++) out[64 * jj] = f32_to_bf16(o[jj] * inv);
-    if (lane == 0 && p.lse) p.lse[row] = M + fast_log2(den) * kLn2;
+    // The last workgroup of this (sequence, kv head) to finish merges all of
+    // its partitions, in partition order, so the result does not depend on
+    // which one is last.  Partials are written and read with device-coherent
+    // (agent-scope) accesses, so no cache-wide fence is needed: each thread
+    // waits for its partial stores to complete, then one thread counts.
+    __shared__ int sm_last;
+    wait_stores();
+    __syncthreads();
+    int *counter = p.counters + (size_t)s * p.Hkv + g;
+    if (threadIdx.x == 0)
+        sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  nparts - 1;
+    __syncthreads();
+    if (!sm_last) return;
+    if (threadIdx.x == 0)  // leave the counter zero for the next call
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int h = wave; h < Ga; h += kWaves)
+        merge_partitions<D>(p, (size_t)s * p.Hq + (size_t)g * Ga + h, nparts, lane);
 }
 
 template <int D, int B, int G>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
     const int64_t units = (int64_t)p.max_parts * p.S * p.Hkv;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((paged_decode_partition_kernel<D, B, G>), dim3((unsigned)units), dim3(256),
-                       0, stream, p);
+    constexpr int kDepth = G >= 16 ? 2 : 3;
+    hipLaunchKernelGGL((paged_decode_partition_kernel<D, B, G, kDepth>), dim3((unsigned)units),
+                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -526,19 +702,9 @@ hipError_t dispatch_group(const DecodeParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
-    hipError_t e;
     if (p.D == 128)
-        e = p.B == 16 ? dispatch_group<128, 16>(p, stream) : dispatch_group<128, 32>(p, stream);
-    else
-        e = p.B == 16 ? dispatch_group<64, 16>(p, stream) : dispatch_group<64, 32>(p, stream);
-    if (e != hipSuccess || p.max_parts <= 1) return e;
-    const unsigned rows = (unsigned)p.S * (unsigned)p.Hq;
-    dim3 grid((rows + 3) / 4);
-    if (p.D == 128)
-        hipLaunchKernelGGL(paged_decode_reduce_kernel<128>, grid, dim3(256), 0, stream, p, p.B);
-    else
-        hipLaunchKernelGGL(paged_decode_reduce_kernel<64>, grid, dim3(256), 0, stream, p, p.B);
-    return hipGetLastError();
+        return p.B == 16 ? dispatch_group<128, 16>(p, stream) : dispatch_group<128, 32>(p, stream);
+    return p.B == 16 ? dispatch_group<64, 16>(p, stream) : dispatch_group<64, 32>(p, stream);
 }
 
 }  // namespace pa

@@ -34,6 +34,7 @@ struct DecodeParams {
     int32_t max_parts;         // partitions per sequence in the grid
     float *part_out;           // f32 [S, Hq, max_parts, D] (when max_parts > 1)
     float *part_lse;           // f32 [S, Hq, max_parts]
+    int *counters;             // [S, Hkv] partitions finished; zero between calls
 };
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);

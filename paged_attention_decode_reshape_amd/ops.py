@@ -102,10 +102,13 @@ def _stream(t: torch.Tensor):
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    """A caller-supplied workspace, or a fresh zero-filled one.  Workspaces
+    start with completion counters that must be zero before first use; the
+    library leaves them zero after every call, so a workspace can be reused."""
     if nbytes == 0:
         return None
     if workspace is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
     _gpu("workspace", workspace)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")

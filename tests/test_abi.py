@@ -77,9 +77,12 @@ def test_decode_workspace_sizes():
     assert pa.decode_partition_tokens(4, 1, 511, 100) == 128   # rounded up to 64
     assert pa.decode_partition_tokens(4, 1, 511, -1) == 512
     assert pa.decode_partition_tokens(64, 1, 2000, 0) == 256
+    assert pa.decode_partition_tokens(8, 4, 131072, 8192) == 4096
+    assert pa.decode_partition_tokens(1, 1, 100000, -1) == 4096
     assert pa.decode_workspace_size(4, 4, 1, 128, 511, -1) == 0
     parts = 4  # 511 tokens in 128-token partitions
-    want = (4 * 4 * parts * 128 * 4 + 255) // 256 * 256 + (4 * 4 * parts * 4 + 255) // 256 * 256
+    a256 = lambda n: (n + 255) // 256 * 256
+    want = a256(4 * 1 * 4) + a256(4 * 4 * parts * 128 * 4) + a256(4 * 4 * parts * 4)
     assert pa.decode_workspace_size(4, 4, 1, 128, 511, 128) == want
 
 
