@@ -359,57 +359,6 @@ __device__ __forceinline__ void pv_step(int odd, bool last, float (&a)[DV], floa
 #undef PA_PV_CALL
 }
 
-// Log-sum-exp merge of one (sequence, q head) row over its partitions, in
-// partition order, by one wave: lane i holds partition i's LSE, weights are
-// broadcast with readlane and 4 partitions' outputs are read together.
-template <int D>
-__device__ __forceinline__ void merge_partitions(const DecodeParams &p, size_t row, int nparts,
-                                                 int lane) {
-    constexpr int DV = D / 64;
-    const float *pl = p.part_lse + row * p.max_parts;
-    float M = kNegInf;
-    for (int b = 0; b < nparts; b += 64) {
-        const float v = b + lane < nparts ? load_coherent(&pl[b + lane]) : kNegInf;
-        M = fmax_nc(M, wave_max(v));
-    }
-    float den = 0.f, o[DV];
-#pragma unroll
-    for (int jj = 0; jj < DV; jj++) o[jj] = 0.f;
-    const float *po = p.part_out + row * p.max_parts * D + lane;
-    for (int b = 0; b < nparts; b += 64) {
-        const float w =
-            b + lane < nparts ? fast_exp2((load_coherent(&pl[b + lane]) - M) * kLog2e) : 0.f;
-        den += wave_sum(w);
-        const int n = min(64, nparts - b);
-        int k = 0;
-        for (; k + 4 <= n; k += 4) {
-            float x[4][DV];
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++)
-                    x[u][jj] = load_coherent(&po[(size_t)(b + k + u) * D + 64 * jj]);
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const float wk = __int_as_float(readlane_i32(__float_as_int(w), k + u));
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++) o[jj] += wk * x[u][jj];
-            }
-        }
-        for (; k < n; k++) {
-            const float wk = __int_as_float(readlane_i32(__float_as_int(w), k));
-#pragma unroll
-            for (int jj = 0; jj < DV; jj++)
-                o[jj] += wk * load_coherent(&po[(size_t)(b + k) * D + 64 * jj]);
-        }
-    }
-    uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + row * D + lane;
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int jj = 0; jj < DV; jj++) out[64 * jj] = f32_to_bf16(o[jj] * inv);
-    if (lane == 0 && p.lse) p.lse[row] = M + fast_log2(den) * kLn2;
-}
-
 // Sum over the 4 rows of the wave (lanes n, n + 16, n + 32, n + 48); every
 // lane gets the sum for its column.
 __device__ __forceinline__ float row_sum4(float v) {
@@ -429,20 +378,37 @@ __device__ __forceinline__ float row_max16(float v) {
     return ord2f(k);
 }
 
+// Two adjacent floats read / written as one 8-byte device-coherent access.
+__device__ __forceinline__ float2 load_coherent2(const float *p) {
+    const uint64_t w = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+}
+__device__ __forceinline__ void store_coherent2(float *p, float a, float b) {
+    const uint64_t w = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), w, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int kSub = 16;  // tokens per sub-block: one row of lanes
 
-// Loads of one 16-token sub-block: K of token `col` (quarter `row` of the
-// dims: vectors row * CQ .. row * CQ + CQ - 1) and the two V token groups
-// of the sub-block for dims lane + 64 jj.  `half` selects the 16-token half
-// of a 32-token block.
+// K of one 16-token sub-block: lane (row, col) loads token `col`'s vectors
+// row * CQ .. row * CQ + CQ - 1 (a quarter of the dims).  `half` selects the
+// 16-token half of a 32-token block.
 template <int D, int B>
-__device__ __forceinline__ void load_sub(const uint4 *kc, const uint4 *vc, size_t tile, int half,
-                                         int row, int col, int lane, uint4 (&kq)[D / 32],
-                                         uint4 (&vv)[2][D / 64]) {
-    constexpr int C = D / 8, CQ = D / 32, DV = D / 64;
+__device__ __forceinline__ void load_k_sub(const uint4 *kc, size_t tile, int half, int row,
+                                           int col, uint4 (&kq)[D / 32]) {
+    constexpr int C = D / 8, CQ = D / 32;
     const uint4 *kt = kc + tile * (size_t)(C * B) + half * kSub + col;
 #pragma unroll
     for (int i = 0; i < CQ; i++) kq[i] = kt[(row * CQ + i) * B];
+}
+
+// V of one 16-token sub-block: its two 8-token groups for dims lane + 64 jj.
+template <int D, int B>
+__device__ __forceinline__ void load_v_sub(const uint4 *vc, size_t tile, int half, int lane,
+                                           uint4 (&vv)[2][D / 64]) {
+    constexpr int DV = D / 64;
     const uint4 *vt = vc + (tile * (B / 8) + half * 2) * D + lane;
 #pragma unroll
     for (int tg = 0; tg < 2; tg++)
@@ -450,11 +416,79 @@ __device__ __forceinline__ void load_sub(const uint4 *kc, const uint4 *vc, size_
         for (int jj = 0; jj < DV; jj++) vv[tg][jj] = vt[tg * D + 64 * jj];
 }
 
-template <int D, int B, int G, int DEPTH>
-__global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParams p) {
-    constexpr int CQ = D / 32;        // K vectors per lane (a quarter of the dims)
+// Log-sum-exp merge of the partitions of one (sequence, kv head), run by the
+// workgroup that finished last.  Thread -> (head, DPT consecutive dims); all
+// partitions' LSEs and outputs of a batch are fetched before any is used, so
+// a batch costs one memory round trip.  Partitions combine in index order,
+// so the result does not depend on which workgroup merges.
+template <int D, int G>
+__device__ __forceinline__ void merge_partitions(const DecodeParams &p, size_t row0, int Ga,
+                                                 int nparts) {
+    constexpr int DPT = G * D / 256 > 4 ? G * D / 256 : 4;
+    constexpr int kBatch = DPT > 4 ? 4 : 8;
+    const int it = threadIdx.x;
+    if (it >= Ga * (D / DPT)) return;
+    const int h = it / (D / DPT), d0 = (it % (D / DPT)) * DPT;
+    const size_t row = row0 + h;
+    const float *pl = p.part_lse + row * p.max_parts;
+    const float *po = p.part_out + row * p.max_parts * D + d0;
+    float M = kNegInf, den = 0.f, o[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; e++) o[e] = 0.f;
+    for (int b = 0; b < nparts; b += kBatch) {
+        float L[kBatch], x[kBatch][DPT];
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int pu = b + u < nparts ? b + u : b;  // always an in-range address
+            L[u] = load_coherent(&pl[pu]);
+#pragma unroll
+            for (int e = 0; e < DPT; e += 2) {
+                const float2 v = load_coherent2(&po[(size_t)pu * D + e]);
+                x[u][e] = v.x;
+                x[u][e + 1] = v.y;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; u++)
+            if (b + u >= nparts) L[u] = kNegInf;
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) Mb = fmax_nc(Mb, L[u]);
+        const float Mr = Mb == kNegInf ? 0.f : Mb;
+        const float r = fast_exp2((M - Mr) * kLog2e);
+        den *= r;
+#pragma unroll
+        for (int e = 0; e < DPT; e++) o[e] *= r;
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const float w = fast_exp2((L[u] - Mr) * kLog2e);
+            den += w;
+#pragma unroll
+            for (int e = 0; e < DPT; e++) o[e] += w * x[u][e];
+        }
+        M = Mb;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint32_t *out = reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(p.out) + row * D + d0);
+#pragma unroll
+    for (int e = 0; e < DPT; e += 2) out[e / 2] = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+    if (d0 == 0 && p.lse) p.lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
+}
+
+// One workgroup (4 waves) per (partition, kv head, sequence).  A wave owns
+// every 4th chunk of SUBS 16-token sub-blocks of the partition.  Per chunk
+// it loads the sub-blocks' K (one 16-byte vector per lane per load) and V,
+// computes all SUBS x G scores, takes their exact max, and accumulates P.V;
+// the next chunk's K loads are issued as soon as the current K is consumed,
+// and its V loads as soon as the current V is.
+template <int D, int B, int G, int SUBS>
+__global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
+    constexpr int CQ = D / 32;        // K vectors per lane per sub-block
     constexpr int DV = D / 64;        // output dims per lane
     constexpr int QW = 4 * CQ;        // query dwords per row
+    constexpr int kChunk = kSub * SUBS;
+    constexpr bool kPairs = G >= 2;
+    constexpr int HS = kPairs ? 2 : 1;
 
     const int units = p.S * p.Hkv;
     const int part = blockIdx.x / units;
@@ -462,12 +496,29 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
     const int s = rem / p.Hkv, g = rem - s * p.Hkv;
     const int Ga = p.Hq / p.Hkv;
     const int P = p.partition;
-    const int ctx =
-        clamp_ctx(as_const<int32_t>(p.context_lens)[s], p.max_blocks, B, p.max_parts, P);
     const int start = part * P;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index as a scalar, so per-wave token offsets stay in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int row = lane >> 4, col = lane & 15;
     uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+
+    // Issued together, before anything waits: the context length, the
+    // block-table entry of this wave's sub-block `lane` (index clamped into
+    // the table, validity decided once the length is known) and the queries.
+    // Sub-block k of the wave is sub-block k % SUBS of its chunk k / SUBS.
+    const int ctx_raw = as_const<int32_t>(p.context_lens)[s];
+    const int t0_lane = start + (kWaves * (lane / SUBS) + wave) * kChunk + kSub * (lane % SUBS);
+    const int bt_raw =
+        p.block_table[(size_t)s * p.max_blocks + min(t0_lane / B, p.max_blocks - 1)];
+    uint32_t qreg[G];
+    {
+        const uint32_t *qg = reinterpret_cast<const uint32_t *>(p.query) +
+                             ((size_t)s * p.Hq + (size_t)g * Ga) * (D / 2) + row * QW + (col % QW);
+#pragma unroll
+        for (int h = 0; h < G; h++) qreg[h] = qg[(h < Ga ? h : h - Ga) * (D / 2)];
+    }
+    const int ctx = clamp_ctx(ctx_raw, p.max_blocks, B, p.max_parts, P);
 
     if (start >= ctx) {
         if (ctx == 0 && part == 0) {
@@ -484,26 +535,12 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
     const int nparts = (ctx + P - 1) / P;
     const float sl2 = p.scale * kLog2e;
 
-    // queries: lane (row r, column n) holds dword r * QW + n of each head;
-    // padded heads (h >= Ga) repeat real ones
-    uint32_t qreg[G];
-    {
-        const uint32_t *qg = reinterpret_cast<const uint32_t *>(p.query) +
-                             ((size_t)s * p.Hq + (size_t)g * Ga) * (D / 2) + row * QW + (col % QW);
-#pragma unroll
-        for (int h = 0; h < G; h++) qreg[h] = qg[(h < Ga ? h : h - Ga) * (D / 2)];
-    }
-
-    // This wave's sub-blocks are k = 0, 1, ...: tokens start + 16 (wave + 4 k).
-    // Lane k holds the physical block of sub-block k (-1: out of range).
-    const int nsub = (end - start + kSub - 1) / kSub;
-    const int nmine = nsub > wave ? (nsub - wave + 3) / 4 : 0;
-    int bid = 0;
-    if (lane < nmine) {
-        const int b = as_const<int32_t>(p.block_table)[(size_t)s * p.max_blocks +
-                                                       (start + kSub * (wave + 4 * lane)) / B];
-        bid = (b < 0 || (int64_t)b >= p.num_blocks) ? -1 : b;
-    }
+    // lane k: physical block of sub-block k, -1 past the end or out of range.
+    // Validity is monotone in k, so the valid sub-blocks are 0 .. nmine - 1.
+    const bool lane_ok = t0_lane < end;
+    const int bid = lane_ok && bt_raw >= 0 && (int64_t)bt_raw < p.num_blocks ? bt_raw : -1;
+    const int nmine = __popcll(__ballot(lane_ok));
+    const int nch = (nmine + SUBS - 1) / SUBS;
     const uint4 *kc = reinterpret_cast<const uint4 *>(p.k_cache);
     const uint4 *vc = reinterpret_cast<const uint4 *>(p.v_cache);
 
@@ -516,111 +553,147 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
         for (int jj = 0; jj < DV; jj++) acc[h][jj] = 0.f;
     }
 
-    // a DEPTH-deep ring of sub-blocks in flight; past the end the last
-    // sub-block is re-read (a cache hit) so every iteration issues the same loads
-    uint4 kb[DEPTH][CQ], vb[DEPTH][2][DV];
-    auto issue = [&](auto slot_c, int k) {
-        constexpr int slot = decltype(slot_c)::value;
+    uint4 kb[SUBS][CQ], vb[SUBS][2][DV];
+    // Sub-block k's block and token offset; a sub-block past the end re-reads
+    // the wave's last valid one (a cache hit) so every chunk issues the same loads.
+    auto locate = [&](int k, size_t &tile, int &half) {
         const int kk = min(k, nmine - 1);
         const int b = readlane_i32(bid, kk);
-        const int t0 = start + kSub * (wave + 4 * kk);
-        load_sub<D, B>(kc, vc, (size_t)(b < 0 ? 0 : b) * p.Hkv + g, (t0 % B) / kSub, row, col,
-                       lane, kb[slot], vb[slot]);
+        const int t0 = start + (kWaves * (kk / SUBS) + wave) * kChunk + kSub * (kk % SUBS);
+        tile = (size_t)(b < 0 ? 0 : b) * p.Hkv + g;
+        half = (t0 % B) / kSub;
     };
-    auto compute = [&](auto slot_c, int k) {
-        constexpr int slot = decltype(slot_c)::value;
-        const int t0 = start + kSub * (wave + 4 * k);
-        const int nvalid = readlane_i32(bid, k) < 0 ? 0 : min(kSub, end - t0);
-        const bool tok_ok = col < nvalid;
-        // QK: a quarter of each dot product per lane, summed over the rows
-        float sc[G];
+    auto issue_k = [&](int c) {
 #pragma unroll
-        for (int h = 0; h < G; h += (G >= 2 ? 2 : 1)) {
-            float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-            if constexpr (G >= 2) {
-                if constexpr (CQ == 4)
-                    qk_2h<true>(a0, a1, b0, b1, qreg[h], qreg[h + 1], kb[slot][0], kb[slot][1],
-                                kb[slot][2], kb[slot][3]);
-                else
-                    qk8_2h(a0, a1, b0, b1, qreg[h], qreg[h + 1], kb[slot][0], kb[slot][1]);
-                const float zb = row_sum4(b0 + b1);
-                sc[h + 1] = tok_ok ? zb * sl2 : kNegInf;
-            } else {
-                if constexpr (CQ == 4)
-                    qk_1h<true>(a0, a1, qreg[h], kb[slot][0], kb[slot][1], kb[slot][2],
-                                kb[slot][3]);
-                else
-                    qk8_1h(a0, a1, qreg[h], kb[slot][0], kb[slot][1]);
-            }
-            const float za = row_sum4(a0 + a1);
-            sc[h] = tok_ok ? za * sl2 : kNegInf;
+        for (int j = 0; j < SUBS; j++) {
+            size_t tile;
+            int half;
+            locate(c * SUBS + j, tile, half);
+            load_k_sub<D, B>(kc, tile, half, row, col, kb[j]);
         }
-        // online softmax; the weight of token n lands in lane n of every row
-        uint32_t pw[G];
+    };
+    auto issue_v = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < SUBS; j++) {
+            size_t tile;
+            int half;
+            locate(c * SUBS + j, tile, half);
+            load_v_sub<D, B>(vc, tile, half, lane, vb[j]);
+        }
+    };
+
+    // One chunk: all of its K and V loads are issued first (V lands while
+    // the scores are computed), then QK, softmax, PV.  Buffers are not
+    // carried across chunks; the other waves of the SIMD cover the latency.
+    auto chunk = [&](int c) {
+        issue_k(c);
+        issue_v(c);
+        int nvalid[SUBS];
+#pragma unroll
+        for (int j = 0; j < SUBS; j++) {
+            const int k = c * SUBS + j;
+            const int t0 = start + (kWaves * c + wave) * kChunk + kSub * j;
+            nvalid[j] = readlane_i32(bid, k) < 0 ? 0 : min(kSub, end - t0);
+        }
+        // QK: each lane sums a quarter of the dims; the rows are then summed,
+        // leaving every row with the 16 scores of the sub-block
+        float sc[SUBS][G];
+#pragma unroll
+        for (int j = 0; j < SUBS; j++) {
+            float a[G][2];
+#pragma unroll
+            for (int h = 0; h < G; h++) a[h][0] = a[h][1] = 0.f;
+#pragma unroll
+            for (int h = 0; h < G; h += HS) {
+                if constexpr (kPairs) {
+                    if constexpr (CQ == 4) {
+                        if (h + 2 >= G)
+                            qk_2h<true>(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
+                                        qreg[h + 1], kb[j][0], kb[j][1], kb[j][2], kb[j][3]);
+                        else
+                            qk_2h<false>(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
+                                         qreg[h + 1], kb[j][0], kb[j][1], kb[j][2], kb[j][3]);
+                    } else {
+                        qk8_2h(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h], qreg[h + 1],
+                               kb[j][0], kb[j][1]);
+                    }
+                } else {
+                    if constexpr (CQ == 4)
+                        qk_1h<true>(a[h][0], a[h][1], qreg[h], kb[j][0], kb[j][1], kb[j][2],
+                                    kb[j][3]);
+                    else
+                        qk8_1h(a[h][0], a[h][1], qreg[h], kb[j][0], kb[j][1]);
+                }
+            }
+            const bool ok = col < nvalid[j];
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float z = row_sum4(a[h][0] + a[h][1]);
+                sc[j][h] = ok ? z * sl2 : kNegInf;
+            }
+        }
+        // softmax: exact max over the chunk, one rescale of the running state
+        uint32_t pw[SUBS][G];
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            const float mx = uniform_f(row_max16(sc[h]));
+            float mx = sc[0][h];
+#pragma unroll
+            for (int j = 1; j < SUBS; j++) mx = fmax_nc(mx, sc[j][h]);
+            mx = uniform_f(row_max16(mx));
             const float mn = fmax_nc(m[h], mx);
             const float mref = mn == kNegInf ? 0.f : mn;
             const float alpha = fast_exp2(m[h] - mref);
             m[h] = mn;
-            const float pr = fast_exp2(sc[h] - mref);
-            lsum[h] = lsum[h] * alpha + pr;
+            float l = lsum[h] * alpha;
+#pragma unroll
+            for (int j = 0; j < SUBS; j++) {
+                const float pr = fast_exp2(sc[j][h] - mref);
+                l += pr;
+                pw[j][h] = __float_as_uint(pr);
+            }
+            lsum[h] = l;
 #pragma unroll
             for (int jj = 0; jj < DV; jj++) acc[h][jj] *= alpha;
-            pw[h] = __float_as_uint(pr);
         }
-        // PV: zero the V of tokens past the end (weight 0, data may be anything)
-        if (nvalid < kSub) {
+        // PV: the V of tokens past the end is zeroed (weight 0, data may be anything)
 #pragma unroll
-            for (int tg = 0; tg < 2; tg++) {
-                const int nv = nvalid - 8 * tg;
+        for (int j = 0; j < SUBS; j++) {
+            if (nvalid[j] < kSub) {
 #pragma unroll
-                for (int jj = 0; jj < DV; jj++) {
-                    uint4 &v = vb[slot][tg][jj];
-                    v.x = mask_pair(v.x, 0, nv);
-                    v.y = mask_pair(v.y, 2, nv);
-                    v.z = mask_pair(v.z, 4, nv);
-                    v.w = mask_pair(v.w, 6, nv);
+                for (int tg = 0; tg < 2; tg++) {
+                    const int nv = nvalid[j] - 8 * tg;
+#pragma unroll
+                    for (int jj = 0; jj < DV; jj++) {
+                        uint4 &v = vb[j][tg][jj];
+                        v.x = mask_pair(v.x, 0, nv);
+                        v.y = mask_pair(v.y, 2, nv);
+                        v.z = mask_pair(v.z, 4, nv);
+                        v.w = mask_pair(v.w, 6, nv);
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int tg = 0; tg < 2; tg++) {
-            float vf[DV][8];
+        for (int j = 0; j < SUBS; j++) {
 #pragma unroll
-            for (int jj = 0; jj < DV; jj++) widen8(vb[slot][tg][jj], vf[jj]);
-            constexpr bool kPairs = G >= 2;
+            for (int tg = 0; tg < 2; tg++) {
+                float vf[DV][8];
 #pragma unroll
-            for (int h = 0; h < G; h += (kPairs ? 2 : 1)) {
-                const bool last = tg == 1 && h + (kPairs ? 2 : 1) >= G;
-                pv_step<DV, kPairs>(tg, last, acc[h], acc[h + (kPairs ? 1 : 0)], pw[h],
-                                    pw[h + (kPairs ? 1 : 0)], vf);
+                for (int jj = 0; jj < DV; jj++) widen8(vb[j][tg][jj], vf[jj]);
+#pragma unroll
+                for (int h = 0; h < G; h += HS) {
+                    const bool last = j == SUBS - 1 && tg == 1 && h + HS >= G;
+                    pv_step<DV, kPairs>(tg, last, acc[h], acc[h + HS - 1], pw[j][h],
+                                        pw[j][h + HS - 1], vf);
+                }
             }
         }
     };
 
-    // step U of an unrolled group: prefetch sub-block k + DEPTH - 1 into the
-    // slot freed by the previous step, then compute sub-block k from slot U
-    auto step = [&](auto u_c, int k) {
-        constexpr int U = decltype(u_c)::value;
-        if (k < nmine) {
-            issue(std::integral_constant<int, (U + DEPTH - 1) % DEPTH>{}, k + DEPTH - 1);
-            compute(std::integral_constant<int, U>{}, k);
-        }
-    };
-    if (nmine > 0) {
-        issue(std::integral_constant<int, 0>{}, 0);
-        if constexpr (DEPTH > 2) issue(std::integral_constant<int, 1>{}, 1);
-        for (int i = 0; i < nmine; i += DEPTH) {
-            step(std::integral_constant<int, 0>{}, i);
-            if constexpr (DEPTH > 1) step(std::integral_constant<int, 1>{}, i + 1);
-            if constexpr (DEPTH > 2) step(std::integral_constant<int, 2>{}, i + 2);
-        }
-    }
+    for (int c = 0; c < nch; c++) chunk(c);
 
-    // merge the 4 waves of the workgroup (each column holds every row's copy
-    // of its token weights, so a wave's sum is 4 x the row sum)
+    // merge the 4 waves of the workgroup (every row holds the same token
+    // weights, so a wave's sum is 4 x the row sum)
     __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
     __shared__ float sm_acc[kWaves][G][D];
 #pragma unroll
@@ -634,34 +707,35 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
         for (int jj = 0; jj < DV; jj++) sm_acc[wave][h][lane + 64 * jj] = acc[h][jj];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < Ga * D; idx += blockDim.x) {
-        const int h = idx / D, d = idx % D;
+    for (int idx = threadIdx.x; idx < Ga * (D / 2); idx += blockDim.x) {
+        const int h = idx / (D / 2), d = 2 * (idx % (D / 2));
         float M = kNegInf;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm_m[w][h]);
-        float num = 0.f, den = 0.f;
+        const float Mr = M == kNegInf ? 0.f : M;
+        float n0 = 0.f, n1 = 0.f, den = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
-            const float wt = fast_exp2(sm_m[w][h] - M);
-            num += wt * sm_acc[w][h][d];
+            const float wt = fast_exp2(sm_m[w][h] - Mr);
+            n0 += wt * sm_acc[w][h][d];
+            n1 += wt * sm_acc[w][h][d + 1];
             den += wt * sm_l[w][h];
         }
-        const float o = num / den;
-        const float L = (M + fast_log2(den)) * kLn2;
-        const size_t row = (size_t)s * p.Hq + (size_t)g * Ga + h;
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
+        const size_t orow = (size_t)s * p.Hq + (size_t)g * Ga + h;
         if (nparts == 1) {
-            out[row * D + d] = f32_to_bf16(o);
-            if (d == 0 && p.lse) p.lse[row] = L;
+            reinterpret_cast<uint32_t *>(out + orow * D)[d / 2] = pack_bf16x2(n0 * inv, n1 * inv);
+            if (d == 0 && p.lse) p.lse[orow] = L;
         } else {
-            store_coherent(&p.part_out[(row * p.max_parts + part) * D + d], o);
-            if (d == 0) store_coherent(&p.part_lse[row * p.max_parts + part], L);
+            store_coherent2(&p.part_out[(orow * p.max_parts + part) * D + d], n0 * inv, n1 * inv);
+            if (d == 0) store_coherent(&p.part_lse[orow * p.max_parts + part], L);
         }
     }
     if (nparts == 1) return;
 
     // The last workgroup of this (sequence, kv head) to finish merges all of
-    // its partitions, in partition order, so the result does not depend on
-    // which one is last.  Partials are written and read with device-coherent
+    // its partitions.  Partials are written and read with device-coherent
     // (agent-scope) accesses, so no cache-wide fence is needed: each thread
     // waits for its partial stores to complete, then one thread counts.
     __shared__ int sm_last;
@@ -675,17 +749,16 @@ __global__ __launch_bounds__(256) void paged_decode_partition_kernel(DecodeParam
     if (!sm_last) return;
     if (threadIdx.x == 0)  // leave the counter zero for the next call
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int h = wave; h < Ga; h += kWaves)
-        merge_partitions<D>(p, (size_t)s * p.Hq + (size_t)g * Ga + h, nparts, lane);
+    merge_partitions<D, G>(p, (size_t)s * p.Hq + (size_t)g * Ga, Ga, nparts);
 }
 
 template <int D, int B, int G>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
     const int64_t units = (int64_t)p.max_parts * p.S * p.Hkv;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    constexpr int kDepth = G >= 16 ? 2 : 3;
-    hipLaunchKernelGGL((paged_decode_partition_kernel<D, B, G, kDepth>), dim3((unsigned)units),
-                       dim3(256), 0, stream, p);
+    constexpr int kSubs = G >= 16 ? 2 : 4;
+    hipLaunchKernelGGL((paged_decode_kernel<D, B, G, kSubs>), dim3((unsigned)units), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
