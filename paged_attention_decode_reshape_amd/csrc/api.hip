@@ -138,7 +138,7 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
     if (!out || !query || !k_cache || !v_cache || !block_table || !context_lens)
         return PA_ERR_INVALID_ARG;
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(query, 4) ||
-        !aligned(out, 2) || !aligned(lse, 4))
+        !aligned(out, 4) || !aligned(lse, 4))
         return PA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
@@ -193,11 +193,45 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
                              int32_t v_dim, int32_t block_size, int64_t num_blocks, float scale,
                              int32_t partition_tokens, void *workspace, size_t workspace_bytes,
                              void *stream) {
-    (void)out; (void)lse; (void)query; (void)kv_cache; (void)block_table;
-    (void)max_blocks_per_seq; (void)context_lens; (void)max_context_len; (void)num_seqs;
-    (void)num_q_heads; (void)latent_dim; (void)v_dim; (void)block_size; (void)num_blocks;
-    (void)scale; (void)partition_tokens; (void)workspace; (void)workspace_bytes; (void)stream;
-    return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_q_heads < 1 || block_size < 1 || num_blocks < 1 ||
+        max_blocks_per_seq < 1 || max_context_len < 0 || partition_tokens < -1 ||
+        !isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (!out || !query || !kv_cache || !block_table || !context_lens) return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(query, 4) || !aligned(kv_cache, 16) || !aligned(lse, 4) ||
+        !aligned(block_table, 4) || !aligned(context_lens, 4))
+        return PA_ERR_INVALID_ARG;
+    if (latent_dim != 576 || v_dim != 512 || num_q_heads > 16 || max_context_len > kMaxContext ||
+        num_seqs > 65535)
+        return PA_ERR_UNSUPPORTED;
+    Split sp = plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len, partition_tokens);
+    if (sp.total() > 0) {
+        if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+    }
+    if (num_seqs == 0) return PA_OK;
+    MLAParams p;
+    p.out = out;
+    p.lse = lse;
+    p.query = query;
+    p.kv_cache = kv_cache;
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.context_lens = context_lens;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Dl = latent_dim;
+    p.Dv = v_dim;
+    p.B = block_size;
+    p.num_blocks = num_blocks;
+    p.scale = scale;
+    p.partition = sp.P;
+    p.max_parts = sp.parts;
+    char *ws = (char *)workspace;
+    p.counters = sp.parts > 1 ? (int *)ws : nullptr;
+    p.part_out = sp.parts > 1 ? (float *)(ws + sp.counter_bytes) : nullptr;
+    p.part_lse = sp.parts > 1 ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
+    return from_hip(launch_mla_decode(p, (hipStream_t)stream));
 }
 
 pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,

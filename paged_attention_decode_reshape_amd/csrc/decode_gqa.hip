@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "decode_common.h"
 #include "launch.h"
 
 namespace pa {
@@ -54,9 +55,6 @@ __device__ __forceinline__ uint32_t mask_pair(uint32_t w, int first, int nvalid)
     return first >= nvalid ? 0u : (first + 1 >= nvalid ? (w & 0xffffu) : w);
 }
 
-// One v_dot2c whose first operand is lane `n` of the same 16-lane row.
-#define PA_DOT2_BC(acc, r, v, n) \
-    "v_dot2c_f32_bf16_dpp " acc ", " r ", " v " row_newbcast:" n " row_mask:0xf bank_mask:0xf\n\t"
 
 // Hazards the compiler cannot see inside inline asm:
 //  - the leading s_nop covers the VALU-write -> DPP-read hazard on the
@@ -378,18 +376,6 @@ __device__ __forceinline__ float row_max16(float v) {
     return ord2f(k);
 }
 
-// Two adjacent floats read / written as one 8-byte device-coherent access.
-__device__ __forceinline__ float2 load_coherent2(const float *p) {
-    const uint64_t w = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)),
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
-}
-__device__ __forceinline__ void store_coherent2(float *p, float a, float b) {
-    const uint64_t w = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), w, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
 constexpr int kSub = 16;  // tokens per sub-block: one row of lanes
 
 // K of one 16-token sub-block: lane (row, col) loads token `col`'s vectors
@@ -414,65 +400,6 @@ __device__ __forceinline__ void load_v_sub(const uint4 *vc, size_t tile, int hal
     for (int tg = 0; tg < 2; tg++)
 #pragma unroll
         for (int jj = 0; jj < DV; jj++) vv[tg][jj] = vt[tg * D + 64 * jj];
-}
-
-// Log-sum-exp merge of the partitions of one (sequence, kv head), run by the
-// workgroup that finished last.  Thread -> (head, DPT consecutive dims); all
-// partitions' LSEs and outputs of a batch are fetched before any is used, so
-// a batch costs one memory round trip.  Partitions combine in index order,
-// so the result does not depend on which workgroup merges.
-template <int D, int G>
-__device__ __forceinline__ void merge_partitions(const DecodeParams &p, size_t row0, int Ga,
-                                                 int nparts) {
-    constexpr int DPT = G * D / 256 > 4 ? G * D / 256 : 4;
-    constexpr int kBatch = DPT > 4 ? 4 : 8;
-    const int it = threadIdx.x;
-    if (it >= Ga * (D / DPT)) return;
-    const int h = it / (D / DPT), d0 = (it % (D / DPT)) * DPT;
-    const size_t row = row0 + h;
-    const float *pl = p.part_lse + row * p.max_parts;
-    const float *po = p.part_out + row * p.max_parts * D + d0;
-    float M = kNegInf, den = 0.f, o[DPT];
-#pragma unroll
-    for (int e = 0; e < DPT; e++) o[e] = 0.f;
-    for (int b = 0; b < nparts; b += kBatch) {
-        float L[kBatch], x[kBatch][DPT];
-#pragma unroll
-        for (int u = 0; u < kBatch; u++) {
-            const int pu = b + u < nparts ? b + u : b;  // always an in-range address
-            L[u] = load_coherent(&pl[pu]);
-#pragma unroll
-            for (int e = 0; e < DPT; e += 2) {
-                const float2 v = load_coherent2(&po[(size_t)pu * D + e]);
-                x[u][e] = v.x;
-                x[u][e + 1] = v.y;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; u++)
-            if (b + u >= nparts) L[u] = kNegInf;
-        float Mb = M;
-#pragma unroll
-        for (int u = 0; u < kBatch; u++) Mb = fmax_nc(Mb, L[u]);
-        const float Mr = Mb == kNegInf ? 0.f : Mb;
-        const float r = fast_exp2((M - Mr) * kLog2e);
-        den *= r;
-#pragma unroll
-        for (int e = 0; e < DPT; e++) o[e] *= r;
-#pragma unroll
-        for (int u = 0; u < kBatch; u++) {
-            const float w = fast_exp2((L[u] - Mr) * kLog2e);
-            den += w;
-#pragma unroll
-            for (int e = 0; e < DPT; e++) o[e] += w * x[u][e];
-        }
-        M = Mb;
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint32_t *out = reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(p.out) + row * D + d0);
-#pragma unroll
-    for (int e = 0; e < DPT; e += 2) out[e / 2] = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
-    if (d0 == 0 && p.lse) p.lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
 }
 
 // One workgroup (4 waves) per (partition, kv head, sequence).  A wave owns
@@ -625,6 +552,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
                         qk8_1h(a[h][0], a[h][1], qreg[h], kb[j][0], kb[j][1]);
                 }
             }
+            dpp_result_fence<2 * G>(&a[0][0]);
             const bool ok = col < nvalid[j];
 #pragma unroll
             for (int h = 0; h < G; h++) {
@@ -688,6 +616,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
                 }
             }
         }
+        dpp_result_fence<G * DV>(&acc[0][0]);
     };
 
     for (int c = 0; c < nch; c++) chunk(c);
@@ -749,7 +678,10 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     if (!sm_last) return;
     if (threadIdx.x == 0)  // leave the counter zero for the next call
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_partitions<D, G>(p, (size_t)s * p.Hq + (size_t)g * Ga, Ga, nparts);
+    constexpr int kDPT = G * D / 256 > 4 ? G * D / 256 : 4;
+    merge_partition_rows<D, kDPT, (kDPT > 4 ? 4 : 8)>(p.part_out, p.part_lse, p.max_parts,
+                                                      reinterpret_cast<uint16_t *>(p.out), p.lse,
+                                                      (size_t)s * p.Hq + (size_t)g * Ga, Ga, nparts);
 }
 
 template <int D, int B, int G>

@@ -54,6 +54,7 @@ struct MLAParams {
     int32_t max_parts;
     float *part_out;           // f32 [S, Hq, max_parts, Dv]
     float *part_lse;           // f32 [S, Hq, max_parts]
+    int *counters;             // [S] partitions finished; zero between calls
 };
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);
