@@ -188,6 +188,26 @@ pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,
 int32_t pa_extend_chunk_tokens(int32_t num_seqs, int32_t block_size,
                                int32_t chunk_budget_tokens);
 
+/*
+ * Context gather of one extend iteration (extend-path pseudocode: each
+ * chunk of cached context is copied out of the shuffled cache into the
+ * standard [tokens, kv_heads, head_dim] layout before attention).
+ * Request r contributes its context tokens
+ *   [iteration * chunk_tokens, min((iteration + 1) * chunk_tokens, context_lens[r]))
+ * in order; requests follow each other, so request r's first row is the sum
+ * of the earlier requests' lengths.  k_out, v_out [rows, num_kv_heads,
+ * head_dim] bf16 with rows <= num_seqs * chunk_tokens.  The copy is exact
+ * (bit for bit).  A block-table entry outside [0, num_blocks) gathers
+ * zeros.  Supported: head_dim == 128, block_size and chunk_tokens multiples
+ * of 8, chunk_tokens a multiple of block_size.
+ */
+pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table,
+                                int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, int32_t iteration,
+                                int32_t chunk_tokens, void *stream);
+
 /* Bytes of workspace pa_chunked_extend_attn needs. */
 size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     decode_workspace_size,
     extend_chunk_tokens,
     extend_workspace_size,
+    gather_cache_chunk,
     library,
     merge_attn_states,
     mla_decode_attn,

@@ -259,12 +259,52 @@ int32_t pa_extend_chunk_tokens(int32_t num_seqs, int32_t block_size, int32_t chu
     return c < block_size ? block_size : c;
 }
 
+pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table,
+                                int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, int32_t iteration,
+                                int32_t chunk_tokens, void *stream) {
+    if (num_seqs < 0 || num_kv_heads < 1 || block_size < 1 || num_blocks < 1 ||
+        max_blocks_per_seq < 1 || iteration < 0 || chunk_tokens < 1)
+        return PA_ERR_INVALID_ARG;
+    if (!k_out || !v_out || !k_cache || !v_cache || !block_table || !context_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16))
+        return PA_ERR_INVALID_ARG;
+    if (head_dim != 128 || block_size % 8 != 0 || chunk_tokens % block_size != 0 ||
+        num_seqs > 65535 || (int64_t)iteration * chunk_tokens > kMaxContext)
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    GatherParams gp;
+    gp.k_cache = k_cache;
+    gp.v_cache = v_cache;
+    gp.block_table = block_table;
+    gp.max_blocks = max_blocks_per_seq;
+    gp.context_lens = context_lens;
+    gp.S = num_seqs;
+    gp.Hkv = num_kv_heads;
+    gp.B = block_size;
+    gp.num_blocks = num_blocks;
+    gp.iteration = iteration;
+    gp.chunk = chunk_tokens;
+    gp.k_out = k_out;
+    gp.v_out = v_out;
+    return from_hip(launch_gather_chunk(gp, chunk_tokens, (hipStream_t)stream));
+}
+
 size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                 int32_t chunk_budget_tokens) {
-    (void)num_seqs; (void)total_new_tokens; (void)num_q_heads; (void)num_kv_heads;
-    (void)head_dim; (void)block_size; (void)chunk_budget_tokens;
-    return 0;
+    if (num_seqs < 1 || total_new_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+        head_dim < 1 || block_size < 1 || chunk_budget_tokens < 1)
+        return 0;
+    const int64_t c = pa_extend_chunk_tokens(num_seqs, block_size, chunk_budget_tokens);
+    const size_t kv = align256((size_t)num_seqs * c * num_kv_heads * head_dim * 2);
+    const size_t run_o = align256((size_t)total_new_tokens * num_q_heads * head_dim * 4);
+    const size_t run_l = align256((size_t)total_new_tokens * num_q_heads * 4);
+    return 2 * kv + run_o + run_l;
 }
 
 pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const void *k_new,
@@ -277,12 +317,96 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
                                  int32_t block_size, int64_t num_blocks, float scale,
                                  int32_t chunk_budget_tokens, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-    (void)out; (void)lse; (void)query; (void)k_new; (void)v_new; (void)query_start_loc;
-    (void)query_start_loc_host; (void)k_cache; (void)v_cache; (void)block_table;
-    (void)max_blocks_per_seq; (void)context_lens; (void)context_lens_host; (void)num_seqs;
-    (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)block_size; (void)num_blocks;
-    (void)scale; (void)chunk_budget_tokens; (void)workspace; (void)workspace_bytes; (void)stream;
-    return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || block_size < 1 ||
+        num_blocks < 1 || max_blocks_per_seq < 1 || chunk_budget_tokens < 1 || !isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (!out || !query || !k_new || !v_new || !query_start_loc || !query_start_loc_host ||
+        !k_cache || !v_cache || !block_table || !context_lens || !context_lens_host)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+        !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lse, 4))
+        return PA_ERR_INVALID_ARG;
+    if (head_dim != 128 || block_size % 8 != 0 || num_seqs > 65535 || num_q_heads > 65535)
+        return PA_ERR_UNSUPPORTED;
+    // plan on the host copies: lengths, iterations, largest query / chunk extents
+    if (query_start_loc_host[0] != 0) return PA_ERR_INVALID_ARG;
+    int32_t max_new = 0, max_ctx = 0;
+    for (int32_t r = 0; r < num_seqs; r++) {
+        const int32_t n = query_start_loc_host[r + 1] - query_start_loc_host[r];
+        const int32_t c = context_lens_host[r];
+        if (n < 0 || c < 0 || (int64_t)c > (int64_t)max_blocks_per_seq * block_size)
+            return PA_ERR_INVALID_ARG;
+        max_new = n > max_new ? n : max_new;
+        max_ctx = c > max_ctx ? c : max_ctx;
+    }
+    const int32_t total_new = query_start_loc_host[num_seqs];
+    const size_t need = pa_extend_workspace_size(num_seqs, total_new, num_q_heads, num_kv_heads,
+                                                 head_dim, block_size, chunk_budget_tokens);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+    if (total_new == 0) return PA_OK;
+
+    const int32_t c = pa_extend_chunk_tokens(num_seqs, block_size, chunk_budget_tokens);
+    const int32_t n_iter = (int32_t)cdiv(max_ctx, c);
+    char *ws = (char *)workspace;
+    const size_t kv = align256((size_t)num_seqs * c * num_kv_heads * head_dim * 2);
+    void *k_chunk = ws, *v_chunk = ws + kv;
+    float *run_o = (float *)(ws + 2 * kv);
+    float *run_l = (float *)(ws + 2 * kv + align256((size_t)total_new * num_q_heads * head_dim * 4));
+    hipStream_t st = (hipStream_t)stream;
+
+    FAParams f;
+    f.q = query;
+    f.q_start = query_start_loc;
+    f.context_lens = context_lens;
+    f.S = num_seqs;
+    f.Hq = num_q_heads;
+    f.Hkv = num_kv_heads;
+    f.scale = scale;
+    f.run_out = run_o;
+    f.run_lse = run_l;
+    f.out = out;
+    f.lse = lse;
+    // stage 1: causal attention of the new tokens over their own K / V
+    f.k = k_new;
+    f.v = v_new;
+    f.iteration = 0;
+    f.chunk = 0;
+    hipError_t e = launch_fa(f, max_new, true, 0, n_iter == 0, st);
+    if (e != hipSuccess) return PA_ERR_HIP;
+    // stage 2: context chunks, gathered to the standard layout, merged in
+    GatherParams gp;
+    gp.k_cache = k_cache;
+    gp.v_cache = v_cache;
+    gp.block_table = block_table;
+    gp.max_blocks = max_blocks_per_seq;
+    gp.context_lens = context_lens;
+    gp.S = num_seqs;
+    gp.Hkv = num_kv_heads;
+    gp.B = block_size;
+    gp.num_blocks = num_blocks;
+    gp.chunk = c;
+    gp.k_out = k_chunk;
+    gp.v_out = v_chunk;
+    f.k = k_chunk;
+    f.v = v_chunk;
+    f.chunk = c;
+    for (int32_t it = 0; it < n_iter; it++) {
+        int32_t max_len = 0;
+        for (int32_t r = 0; r < num_seqs; r++) {
+            const int64_t rest = (int64_t)context_lens_host[r] - (int64_t)it * c;
+            const int32_t len = rest <= 0 ? 0 : (rest < c ? (int32_t)rest : c);
+            max_len = len > max_len ? len : max_len;
+        }
+        gp.iteration = it;
+        if ((e = launch_gather_chunk(gp, max_len, st)) != hipSuccess) return PA_ERR_HIP;
+        f.iteration = it;
+        // stage 3 is the last iteration's merge, which writes the output
+        if ((e = launch_fa(f, max_new, false, 1, it == n_iter - 1, st)) != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    return PA_OK;
 }
 
 }  // extern "C"

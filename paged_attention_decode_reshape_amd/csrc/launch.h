@@ -59,6 +59,40 @@ struct MLAParams {
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);
 
+// Chunked extend (extend.hip).
+struct GatherParams {
+    const void *k_cache;       // shuffled [NB, Hkv, D/8, B, 8]
+    const void *v_cache;       // shuffled [NB, Hkv, B/8, D, 8]
+    const int32_t *block_table;
+    int32_t max_blocks;
+    const int32_t *context_lens;  // [S] cached tokens per request
+    int32_t S, Hkv, B;         // head_dim 128
+    int64_t num_blocks;
+    int32_t iteration, chunk;  // gathers context tokens [iteration * chunk, +chunk)
+    void *k_out, *v_out;       // standard [rows, Hkv, D] bf16, request-major
+};
+
+hipError_t launch_gather_chunk(const GatherParams &p, int max_chunk_len, hipStream_t stream);
+
+struct FAParams {
+    const void *q;             // bf16 [Tn, Hq, 128]
+    const void *k, *v;         // bf16 standard [rows, Hkv, 128]
+    const int32_t *q_start;    // [S + 1] query rows of request r
+    const int32_t *context_lens;  // chunk > 0: keys are the gathered chunk rows of request r
+    int32_t iteration, chunk;  // chunk == 0: keys are the request's new tokens (rows of q)
+    int32_t S, Hq, Hkv;
+    float scale;
+    float *run_out;            // fp32 [Tn, Hq, 128] running output
+    float *run_lse;            // fp32 [Tn, Hq]
+    void *out;                 // bf16 [Tn, Hq, 128] (final step)
+    float *lse;                // fp32 [Tn, Hq] or null (final step)
+};
+
+// mode 0: result -> running state; mode 1: merged into it.  final_: write
+// out / lse instead of the running state.
+hipError_t launch_fa(const FAParams &p, int max_q_len, bool causal, int mode, bool final_,
+                     hipStream_t stream);
+
 hipError_t launch_merge_pair(void *out, float *out_lse, int out_f32, const void *a,
                              const float *a_lse, const void *b, const float *b_lse, int in_f32,
                              int64_t rows, int D, hipStream_t stream);

@@ -48,6 +48,8 @@ _SIGS = {
                             _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
     "pa_merge_attn_states": ([_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp],
                              _i32),
+    "pa_gather_cache_chunk": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i64,
+                               _i32, _i32, _vp], _i32),
     "pa_extend_chunk_tokens": ([_i32, _i32, _i32], _i32),
     "pa_extend_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_chunked_extend_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
@@ -274,6 +276,38 @@ def merge_attn_states(prefix_out: torch.Tensor, prefix_lse: torch.Tensor,
                                   suffix_lse.data_ptr(), code[dt], T, H, D, _stream(prefix_out))
     _check("merge_attn_states", st)
     return out, out_lse
+
+
+def gather_cache_chunk(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                       context_lens: torch.Tensor, iteration: int, chunk_tokens: int,
+                       k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Copy every request's context tokens [iteration * chunk_tokens, +chunk_tokens)
+    out of the shuffled caches into standard [rows, kv_heads, head_dim] tensors
+    (requests one after another; rows <= num_seqs * chunk_tokens)."""
+    lib = library()
+    _gpu("k_cache", k_cache, torch.bfloat16, 5)
+    _gpu("v_cache", v_cache, torch.bfloat16, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    NB, Hkv, C, B, x = k_cache.shape
+    D = C * x
+    S = context_lens.shape[0]
+    rows = S * chunk_tokens
+    if k_out is None:
+        k_out = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=k_cache.device)
+    _gpu("k_out", k_out, torch.bfloat16, 3)
+    _gpu("v_out", v_out, torch.bfloat16, 3)
+    if k_out.shape[0] < rows or v_out.shape[0] < rows:
+        raise ValueError("output tensors need num_seqs * chunk_tokens rows")
+    st = lib.pa_gather_cache_chunk(k_out.data_ptr(), v_out.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), block_table.data_ptr(),
+                                   block_table.shape[1], context_lens.data_ptr(), S, Hkv, D, B, NB,
+                                   int(iteration), int(chunk_tokens), _stream(k_cache))
+    _check("gather_cache_chunk", st)
+    return k_out, v_out
 
 
 def extend_chunk_tokens(num_seqs: int, block_size: int, chunk_budget_tokens: int) -> int:
