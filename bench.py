@@ -70,6 +70,22 @@ def gqa_algorithmic_flops(case) -> int:
     return int(case.context_lens.astype(np.int64).sum()) * case.Hq * case.D * 4
 
 
+def time_launches(launch, n):
+    """Average per-launch time (ms) of n back-to-back launches, measured with
+    HIP events recorded on the stream the launches use."""
+    import torch
+    cur = torch.cuda.current_stream()
+    for i in range(5):
+        launch(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for i in range(n):
+        launch(i)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def bench_gqa(args, case, label):
     import torch
     import paged_attention_decode_reshape_amd as pa
@@ -157,17 +173,9 @@ def bench_gqa(args, case, label):
     torch.cuda.synchronize()
     graph_ok = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
 
-    # decode kernels' own duration: HIP events on the launch stream
-    cur = torch.cuda.current_stream()
-    n_ev = min(args.steps, 200)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    for i in range(n_ev):
-        evs[i][0].record(cur)
-        decode(i)
-        evs[i][1].record(cur)
-    torch.cuda.synchronize()
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # the decode kernel's own duration: HIP events on the launch stream around
+    # back-to-back launches (rotating pools), averaged per launch
+    dec_ms = time_launches(decode, min(args.steps, 400))
 
     algo = gqa_algorithmic_bytes(case)
     achieved = algo / (dec_ms * 1e-3) / 1e9
@@ -218,6 +226,188 @@ def cpu_baseline_gqa(case, seconds):
                       f"in {el:.1f} s, fp64"}
 
 
+# ---------------------------------------------------------------------------
+# MLA decode
+# ---------------------------------------------------------------------------
+
+VALU_PEAK_TFLOPS = 157.3  # fp32 vector (bf16 dot2 issues at the same rate)
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def mla_algorithmic_bytes(case) -> int:
+    n = case.context_lens.astype(np.int64)
+    lat = int(n.sum()) * case.Dl * 2
+    blocks = int(((n + case.B - 1) // case.B).sum())
+    return lat + case.S * case.Hq * (case.Dl + case.Dv) * 2 + case.S * case.Hq * 4 + blocks * 4 + case.S * 4
+
+
+def mla_algorithmic_flops(case) -> int:
+    return int(case.context_lens.astype(np.int64).sum()) * case.Hq * (case.Dl + case.Dv) * 2
+
+
+def bench_mla(args, case, label):
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+
+    dev = torch.device("cuda:0")
+    pg = case.paging
+    pool_bytes = pg.num_blocks * case.B * case.Dl * 2
+    pools = args.pools or max(1, math.ceil(2 * MALL_BYTES / pool_bytes))
+    log(f"[bench] {label}: S={case.S} Hq={case.Hq} B={case.B} tokens={pg.total_tokens} "
+        f"pool={pool_bytes / 1e6:.1f} MB x {pools} copies")
+    lat = case.latent.to(dev)
+    slots_all = torch.from_numpy(pg.slot_mapping).to(dev)
+    caches = []
+    for _ in range(pools):
+        kv = torch.zeros((pg.num_blocks, case.B, case.Dl), dtype=torch.bfloat16, device=dev)
+        pa.reshape_and_cache(lat, None, kv, None, slots_all, layout=pa.LAYOUT_MLA_LATENT)
+        caches.append(kv)
+    rows = torch.from_numpy(case.new_token_rows()).to(dev)
+    new_lat = lat[rows].contiguous()
+    new_slots = slots_all[rows].contiguous()
+    del lat
+    q = case.query.to(dev)
+    bt = torch.from_numpy(pg.block_table).to(dev)
+    cl = torch.from_numpy(pg.lens).to(dev)
+    max_ctx = int(pg.lens.max())
+    ws = torch.zeros(max(1, pa.mla_workspace_size(case.S, case.Hq, case.Dv, max_ctx, 0)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((case.S, case.Hq, case.Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
+
+    def decode(i):
+        pa.mla_decode_attn(q, caches[i % pools], bt, cl, case.scale, max_ctx, v_dim=case.Dv,
+                           out=out, lse=lse, workspace=ws)
+
+    def step(i):
+        pa.reshape_and_cache(new_lat, None, caches[i % pools], None, new_slots,
+                             layout=pa.LAYOUT_MLA_LATENT)
+        decode(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    dec_ms = time_launches(decode, min(args.steps, 200))
+    algo = mla_algorithmic_bytes(case)
+    flops = mla_algorithmic_flops(case)
+    return {"value": case.S / (ms_per_step * 1e-3), "ms_per_step": ms_per_step,
+            "decode_ms": dec_ms, "algo_bytes": algo, "algo_flops": flops,
+            "hbm_gbps": algo / (dec_ms * 1e-3) / 1e9, "tflops": flops / (dec_ms * 1e-3) / 1e12,
+            "pools": pools}
+
+
+def cpu_baseline_mla(case, seconds):
+    import oracle
+    from paged_attention_decode_reshape_amd import workloads as W
+
+    orc = oracle.get()
+    kv = np.zeros((case.paging.num_blocks, case.B, case.Dl), dtype=np.uint16)
+    orc.cache_write_latent(W.bf16_bits(case.latent), case.paging.slot_mapping, kv, case.B)
+    qb = W.bf16_bits(case.query)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.paged_decode_mla(qb, kv, case.paging.block_table, case.context_lens, case.B, case.Dv,
+                             case.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": case.S * reps / el, "unit": "tok/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full MLA decode steps of the same workload ({case.S} requests) "
+                      f"in {el:.1f} s, fp64"}
+
+
+# ---------------------------------------------------------------------------
+# chunked extend
+# ---------------------------------------------------------------------------
+
+def extend_algorithmic_flops(case) -> int:
+    n = case.new_lens.astype(np.int64)
+    c = case.ctx_lens.astype(np.int64)
+    pairs = int((n * c).sum() + (n * (n + 1) // 2).sum())
+    return pairs * case.Hq * case.D * 4
+
+
+def bench_extend(args, case, label):
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+
+    dev = torch.device("cuda:0")
+    pg = case.paging
+    log(f"[bench] {label}: S={case.S} new={int(case.new_lens.sum())} "
+        f"context={int(case.ctx_lens.sum())} tokens, budget {case.chunk_budget_tokens}")
+    kc = torch.zeros((pg.num_blocks, case.Hkv, case.D // 8, case.B, 8), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros((pg.num_blocks, case.Hkv, case.B // 8, case.D, 8), dtype=torch.bfloat16, device=dev)
+    pa.reshape_and_cache(case.key.to(dev), case.value.to(dev), kc, vc,
+                         torch.from_numpy(pg.slot_mapping).to(dev))
+    rows = torch.from_numpy(case.new_rows())
+    k_new = case.key[rows].to(dev).contiguous()
+    v_new = case.value[rows].to(dev).contiguous()
+    q = case.query.to(dev)
+    qsl = torch.from_numpy(case.query_start_loc).to(dev)
+    bt = torch.from_numpy(pg.block_table).to(dev)
+    cl = torch.from_numpy(case.ctx_lens).to(dev)
+    Tn = int(case.query_start_loc[-1])
+    ws = torch.zeros(pa.extend_workspace_size(case.S, Tn, case.Hq, case.Hkv, case.D, case.B,
+                                              case.chunk_budget_tokens), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((Tn, case.Hq), dtype=torch.float32, device=dev)
+
+    def call(i):
+        pa.chunked_extend_attn(q, k_new, v_new, qsl, kc, vc, bt, cl, case.scale,
+                               case.query_start_loc, case.ctx_lens,
+                               chunk_budget_tokens=case.chunk_budget_tokens, out=out, lse=lse,
+                               workspace=ws)
+
+    for i in range(max(1, args.warmup)):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = time_launches(call, args.steps)
+    flops = extend_algorithmic_flops(case)
+    return {"value": Tn / (ms * 1e-3), "ms_per_step": ms, "call_ms": ev_ms, "algo_flops": flops,
+            "tflops": flops / (ev_ms * 1e-3) / 1e12}
+
+
+def cpu_baseline_extend(case, seconds):
+    """The oracle's extend (the definition, fp64) on a bounded sample: the
+    first request's first new tokens, as many as fit the time budget."""
+    import oracle
+    from paged_attention_decode_reshape_amd import workloads as W
+
+    orc = oracle.get()
+    sub = W.extend_case("extend_sample", 1005, ctx_lens=[int(case.ctx_lens[0])], new_tokens=[8],
+                        Hq=case.Hq, Hkv=case.Hkv, D=case.D, block_size=case.B)
+    rows = sub.new_rows()
+    kc, vc = orc.empty_shuffled_cache(sub.paging.num_blocks, sub.Hkv, sub.D, sub.B)
+    orc.cache_write_shuffled(W.bf16_bits(sub.key), W.bf16_bits(sub.value), sub.paging.slot_mapping,
+                             kc, vc, sub.B)
+    kn, vn, qb = W.bf16_bits(sub.key)[rows], W.bf16_bits(sub.value)[rows], W.bf16_bits(sub.query)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.extend(qb, kn, vn, sub.query_start_loc, kc, vc, sub.paging.block_table, sub.ctx_lens,
+                   sub.B, sub.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": 8 * reps / el, "unit": "new tok/s", "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"{reps} runs of 8 new tokens over a {int(case.ctx_lens[0])}-token context "
+                      f"(64 q heads) in {el:.1f} s, fp64"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,14 +432,72 @@ def main():
                     "kv_heads": 4, "head_dim": 128, "block_size": 16,
                     "context_lens": "U[32768,131072]", "kv_pool_copies": r["pools"],
                     "partition_tokens": r["partition_tokens"]}
-    else:
-        print(f"--config {args.config} is not available yet", file=sys.stderr)
-        sys.exit(2)
+    elif args.config in ("mla", "mla_bs1"):
+        B = 1 if args.config == "mla_bs1" else 64
+        case = W.deepseek_mla_decode(block_sizes=(B,))[B]
+        r = bench_mla(args, case, f"deepseek_mla_decode_bs{B}")
+        workload = {"workload": f"deepseek_r1_tp8_mla_decode_64req_bs{B}", "requests": 64,
+                    "q_heads": 16, "latent_dim": 576, "v_dim": 512, "block_size": B,
+                    "context_lens": "U[1024,4096]", "kv_pool_copies": r["pools"]}
+        line = base_line(args, r, workload)
+        line["hbm_gbps"] = r["hbm_gbps"]
+        line["pct_hbm_peak"] = 100.0 * r["hbm_gbps"] / HBM_PEAK_GBPS
+        line["roofline"] = {"bound": "alu", "kernel": "mla_decode_kernel", "achieved": r["tflops"],
+                            "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": r["tflops"] / VALU_PEAK_TFLOPS, "traffic": None,
+                            "algo_flops_per_launch": r["algo_flops"],
+                            "algo_bytes_per_launch": r["algo_bytes"], "avg_launch_ms": r["decode_ms"]}
+        if not args.no_cpu_baseline:
+            log("[bench] timing the oracle on the host cores")
+            line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+        return
+    else:  # extend
+        case = W.chunked_extend()
+        r = bench_extend(args, case, "chunked_extend")
+        workload = {"workload": "chunked_extend_16req_256new", "requests": 16, "new_tokens": 256,
+                    "q_heads": 64, "kv_heads": 4, "head_dim": 128, "block_size": 16,
+                    "context_lens": "U[8192,40960]", "chunk_budget_tokens": case.chunk_budget_tokens}
+        line = base_line(args, r, workload, unit="new tok/s")
+        line["roofline"] = {"bound": "mfma", "kernel": "fa_kernel (+ gather_chunk_kernel)",
+                            "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                            "traffic": None, "algo_flops_per_call": r["algo_flops"],
+                            "avg_call_ms": r["call_ms"]}
+        if not args.no_cpu_baseline:
+            log("[bench] timing the oracle on the host cores")
+            line["cpu_baseline"] = cpu_baseline_extend(case, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+        return
 
-    line = {
+    line = base_line(args, r, workload)
+    line.update({
+        "hbm_gbps": r["hbm_gbps"],
+        "pct_hbm_peak": r["pct_hbm_peak"],
+        "graph_replay_matches_eager": r["graph_replay_matches_eager"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel (partitions + fused merge)",
+            "achieved": r["hbm_gbps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algo_bytes_per_launch": r["algo_bytes"],
+            "avg_launch_ms": r["decode_ms"],
+        },
+    })
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def base_line(args, r, workload, unit="tok/s"):
+    return {
         "metric": METRIC,
         "value": r["value"],
-        "unit": "tok/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -260,26 +508,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": workload,
-        "hbm_gbps": r["hbm_gbps"],
-        "pct_hbm_peak": r["pct_hbm_peak"],
-        "graph_replay_matches_eager": r["graph_replay_matches_eager"],
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "paged_decode_partition_kernel (partitions + fused merge)",
-            "achieved": r["hbm_gbps"],
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-            "traffic": None,
-            "algo_bytes_per_launch": r["algo_bytes"],
-            "avg_launch_ms": r["decode_ms"],
-        },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host cores")
-        line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
