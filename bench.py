@@ -30,6 +30,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 reqs"
+
+# HBM traffic per decode launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+# plain copy of known size (summary and commands in profiles/), valid only for the
+# kernel sources it was measured on: (sha256 prefix of those sources, bytes).
+DECODE_SOURCES = ("paged_attention_decode_reshape_amd/csrc/decode_gqa.hip",
+                  "paged_attention_decode_reshape_amd/csrc/decode_common.h")
+MEASURED_TRAFFIC = {"qwen3": ("105f75e4648c7c5c", 52.30e6)}
+
+
+def measured_traffic(config):
+    """The counter-measured bytes per launch, or None once the kernel changed."""
+    import hashlib
+    if config not in MEASURED_TRAFFIC:
+        return None
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    sha, nbytes = MEASURED_TRAFFIC[config]
+    return nbytes if h.hexdigest()[:16] == sha else None
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -45,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after the bench, run plain device copies of this many MiB (a known "
+                         "byte count for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -408,6 +431,19 @@ def cpu_baseline_extend(case, seconds):
                       f"(64 q heads) in {el:.1f} s, fp64"}
 
 
+def copy_calibration(mb):
+    """Plain device-to-device copies of a known size: rocprofv3 memory counters
+    read on them give the scale between counter units and bytes."""
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 5 copies of {mb} MiB")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -470,6 +506,8 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
     line = base_line(args, r, workload)
     line.update({
         "hbm_gbps": r["hbm_gbps"],
@@ -482,7 +520,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.config),
             "algo_bytes_per_launch": r["algo_bytes"],
             "avg_launch_ms": r["decode_ms"],
         },
