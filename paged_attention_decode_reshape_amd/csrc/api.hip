@@ -202,7 +202,7 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
         !aligned(block_table, 4) || !aligned(context_lens, 4))
         return PA_ERR_INVALID_ARG;
     if (latent_dim != 576 || v_dim != 512 || num_q_heads > 16 || max_context_len > kMaxContext ||
-        num_seqs > 65535)
+        num_seqs > 65535 || num_blocks * (int64_t)block_size > 0x7fffffff)
         return PA_ERR_UNSUPPORTED;
     Split sp = plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len, partition_tokens);
     if (sp.total() > 0) {

@@ -77,6 +77,27 @@ __device__ __forceinline__ void store_coherent2(float *p, float a, float b) {
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte device-coherent global accesses (cache policy sc1: the access is
+// coherent at agent scope, so data written by one workgroup is seen by
+// another on any XCD) through a buffer resource covering `bytes` bytes from
+// `base`.  0x00020000 is the gfx9 descriptor word 3 for raw (untyped)
+// buffer access.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kCoherentSC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCoherentSC1);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                       __uint_as_float(v[3]));
+}
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                                float a, float b, float c, float d) {
+    const u32x4_t v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kCoherentSC1);
+}
+
 // Log-sum-exp merge of a split-KV partition set ("ROCm attention backends"
 // blog, extend-path pseudocode: each chunk yields an output and an LSE and
 // merge_attn_states combines them; the same merge combines decode

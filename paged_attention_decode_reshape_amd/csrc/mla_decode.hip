@@ -43,6 +43,7 @@ constexpr int kHalfDw = kDl / 4;          // dwords per half row (144)
 constexpr int kSlices = kHalfDw / 16;     // 16-dword query slices per half (9)
 constexpr int kRowVec = kDl / 8;          // 16-byte vectors per latent row (72)
 constexpr int kLoadVec = kTile * kRowVec / 256;  // vectors each thread loads per tile (9)
+constexpr int kMaxPartition = 4096;       // tokens per partition, at most
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int B, int max_parts, int P) {
     const int64_t cap = min((int64_t)max_blocks * B, (int64_t)max_parts * P);
@@ -69,6 +70,72 @@ __device__ __forceinline__ float row_max16(float v) {
     return ord2f(k);
 }
 
+// Log-sum-exp merge of a sequence's partitions (in partition order), by the
+// workgroup that finished last: thread -> (head tid / 16, 16-byte vectors
+// v = 16 k + tid % 16, k < 8) of the partial rows; a batch of 4 partitions is
+// fetched before any is used.
+__device__ __forceinline__ void merge_mla_partitions(const MLAParams &p, int s, int nparts) {
+    constexpr int kBatch = 4;
+    const int h = threadIdx.x >> 4, c = threadIdx.x & 15;
+    if (h >= p.Hq) return;
+    const size_t row = (size_t)s * p.Hq + h;
+    const auto rs = coherent_rsrc(p.part_out + row * p.max_parts * kDv, p.max_parts * kDv * 4);
+    const float *pl = p.part_lse + row * p.max_parts;
+    float M = kNegInf, den = 0.f, o[8][4];
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[k][e] = 0.f;
+    for (int b = 0; b < nparts; b += kBatch) {
+        float L[kBatch];
+        float4 x[kBatch][8];
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int pu = b + u < nparts ? b + u : b;  // always an in-range address
+            L[u] = load_coherent(&pl[pu]);
+#pragma unroll
+            for (int k = 0; k < 8; k++) x[u][k] = load_coherent4(rs, (pu * kDv + 4 * (16 * k + c)) * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; u++)
+            if (b + u >= nparts) L[u] = kNegInf;
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) Mb = fmax_nc(Mb, L[u]);
+        const float Mr = Mb == kNegInf ? 0.f : Mb;
+        const float r = fast_exp2((M - Mr) * kLog2e);
+        den *= r;
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[k][e] *= r;
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const float w = fast_exp2((L[u] - Mr) * kLog2e);
+            den += w;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                o[k][0] += w * x[u][k].x;
+                o[k][1] += w * x[u][k].y;
+                o[k][2] += w * x[u][k].z;
+                o[k][3] += w * x[u][k].w;
+            }
+        }
+        M = Mb;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + row * kDv;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int v = 16 * k + c, d = 8 * (v & 63) + 4 * (v >> 6);  // vector v -> its 4 dims
+        uint2 w;
+        w.x = pack_bf16x2(o[k][0] * inv, o[k][1] * inv);
+        w.y = pack_bf16x2(o[k][2] * inv, o[k][3] * inv);
+        *reinterpret_cast<uint2 *>(out + d) = w;
+    }
+    if (c == 0 && p.lse) p.lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
+}
+
 __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int part = blockIdx.x / p.S;
     const int s = blockIdx.x - part * p.S;
@@ -82,6 +149,10 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
 
     __shared__ __align__(16) uint32_t sm_tile[kTile * kRowDw];
+    // latent row of every token of the partition (-1: past the end or an
+    // out-of-range block id), resolved once so that the tile loop issues no
+    // dependent block-table reads
+    __shared__ int32_t sm_row[kMaxPartition];
 
     const int ctx = clamp_ctx(as_const<int32_t>(p.context_lens)[s], p.max_blocks, p.B,
                               p.max_parts, P);
@@ -98,6 +169,12 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int end = min(start + P, ctx);
     const int nparts = (ctx + P - 1) / P;
     const float sl2 = p.scale * kLog2e;
+
+    for (int i = threadIdx.x; i < end - start; i += blockDim.x) {
+        const int t = start + i;
+        const int b = p.block_table[(size_t)s * p.max_blocks + t / p.B];
+        sm_row[i] = b >= 0 && (int64_t)b < p.num_blocks ? b * p.B + t % p.B : -1;
+    }
 
     // this wave's heads (past num_q_heads: repeats of real heads, not stored)
     int head[kHPW];
@@ -121,16 +198,11 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int ld_tok = 8 * wave + (lane >> 3), ld_vec = lane & 7;
     auto load_tile = [&](int t0, uint4 (&r)[kLoadVec]) {
         const int t = t0 + ld_tok;
-        int64_t rowi = -1;
-        if (t < end) {
-            const int b = p.block_table[(size_t)s * p.max_blocks + t / p.B];
-            if (b >= 0 && (int64_t)b < p.num_blocks) rowi = (int64_t)b * p.B + t % p.B;
-        }
-        const uint4 *src = kv + (rowi < 0 ? 0 : rowi) * kRowVec + ld_vec;
+        const int rowi = t < end ? sm_row[t - start] : -1;
+        const uint4 *src = kv + (size_t)(rowi < 0 ? 0 : rowi) * kRowVec + ld_vec;
 #pragma unroll
         for (int i = 0; i < kLoadVec; i++)
             r[i] = rowi < 0 ? make_uint4(0, 0, 0, 0) : src[8 * i];
-        return rowi >= 0;
     };
     auto store_tile = [&](const uint4 (&r)[kLoadVec]) {
         uint4 *dst = reinterpret_cast<uint4 *>(&sm_tile[ld_tok * kRowDw]) + ld_vec;
@@ -140,9 +212,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     // validity of QK token tk of the tile starting at t0 (same test as the loader)
     auto token_ok = [&](int t0) {
         const int t = t0 + tk;
-        if (t >= end) return false;
-        const int b = p.block_table[(size_t)s * p.max_blocks + t / p.B];
-        return b >= 0 && (int64_t)b < p.num_blocks;
+        return t < end && sm_row[t - start] >= 0;
     };
 
     float m[kHPW], lsum[kHPW], acc[kHPW][8];
@@ -154,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
         for (int i = 0; i < 8; i++) acc[j][i] = 0.f;
     }
 
+    __syncthreads();  // sm_row complete
     uint4 next[kLoadVec];
     load_tile(start, next);
     for (int t0 = start; t0 < end; t0 += kTile) {
@@ -235,10 +306,14 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
             reinterpret_cast<uint4 *>(out + orow * kDv)[lane] = o;
             if (lane == 0 && p.lse) p.lse[orow] = L[j];
         } else {
-            float *po = p.part_out + (orow * p.max_parts + part) * kDv + 8 * lane;
+            // partial row stored as 16-byte vectors v = 64 i + lane (dims
+            // 8 lane + 4 i .. + 3), so each store instruction writes 1 KB
+            const auto rs = coherent_rsrc(p.part_out + (orow * p.max_parts + part) * kDv, kDv * 4);
 #pragma unroll
-            for (int i = 0; i < 8; i += 2)
-                store_coherent2(po + i, acc[j][i] * inv[j], acc[j][i + 1] * inv[j]);
+            for (int i = 0; i < 2; i++)
+                store_coherent4(rs, (64 * i + lane) * 16, acc[j][4 * i] * inv[j],
+                                acc[j][4 * i + 1] * inv[j], acc[j][4 * i + 2] * inv[j],
+                                acc[j][4 * i + 3] * inv[j]);
             if (lane == 0) store_coherent(&p.part_lse[orow * p.max_parts + part], L[j]);
         }
     }
@@ -258,9 +333,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     if (!sm_last) return;
     if (threadIdx.x == 0)  // leave the counter zero for the next call
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // 16 heads x 512 dims over 256 threads: 32 dims each
-    merge_partition_rows<kDv, 32, 4>(p.part_out, p.part_lse, p.max_parts, out, p.lse,
-                                     (size_t)s * p.Hq, p.Hq, nparts);
+    merge_mla_partitions(p, s, nparts);
 }
 
 }  // namespace
