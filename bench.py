@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="GQA decode split: 0 auto, -2 balanced, > 0 fixed partitions, "
+                         "-1 unsplit (default: the workload's own)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after the bench, run plain device copies of this many MiB (a known "
                          "byte count for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -139,7 +142,7 @@ def bench_gqa(args, case, label):
     bt = torch.from_numpy(pg.block_table).to(dev)
     cl = torch.from_numpy(pg.lens).to(dev)
     max_ctx = int(pg.lens.max())
-    P = case.partition_tokens
+    P = case.partition_tokens if args.partition_tokens is None else args.partition_tokens
     ws = torch.zeros(max(1, pa.decode_workspace_size(case.S, case.Hq, case.Hkv, case.D, max_ctx, P)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -213,7 +216,8 @@ def bench_gqa(args, case, label):
         "algo_bytes": algo,
         "algo_flops": gqa_algorithmic_flops(case),
         "pools": pools,
-        "partition_tokens": pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P),
+        "partition_tokens": ("balanced" if pa.decode_uses_balanced_split(case.S, case.Hkv, max_ctx, P)
+                             else pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P)),
     }
 
 

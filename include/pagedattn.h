@@ -91,13 +91,24 @@ pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *valu
 /*
  * Split-KV partition length the decode entry points use for these
  * arguments: partition_tokens > 0 is rounded up to a multiple of 64;
- * 0 picks one from the work size; -1 asks for as few partitions as
- * possible.  Partitions are capped at 4096 tokens.
+ * 0 picks one from the work size (MLA decode; GQA decode uses the balanced
+ * split instead, see pa_paged_decode_attn); -1 asks for as few partitions
+ * as possible.  Partitions are capped at 4096 tokens.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_context_len, int32_t partition_tokens);
 
-/* Bytes of workspace pa_paged_decode_attn needs (0 if no split is needed). */
+/*
+ * 1 if pa_paged_decode_attn with these arguments uses the balanced split
+ * (partition_tokens == -2, or 0 when fixed auto-sized partitions would
+ * need more than one wave of workgroups on the current device), else 0.
+ */
+int32_t pa_decode_uses_balanced_split(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t max_context_len, int32_t partition_tokens);
+
+/* Bytes of workspace pa_paged_decode_attn needs (0 if no split is needed).
+ * For partition_tokens 0 and -2 the size depends on the current device's
+ * compute-unit count. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len,
                                 int32_t partition_tokens);
@@ -116,9 +127,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *   clamped.  max_context_len is a host-side bound used to size the grid.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  * scale multiplies q . k before the softmax.
- * partition_tokens: see pa_decode_partition_tokens.  Sequences longer than
- *   one partition are split; partial (out, lse) go to the workspace and
- *   are merged by log-sum-exp.
+ * partition_tokens: > 0 or -1: fixed-length partitions, see
+ *   pa_decode_partition_tokens; -2: balanced split: a grid of as many
+ *   workgroups as the device holds at once shares all 16-token sub-blocks
+ *   of all (sequence, kv head) pairs in near-equal pieces, whatever the
+ *   length mix; 0: auto-sized partitions when they fit in one wave of
+ *   workgroups, the balanced split otherwise.  A (sequence, kv head) pair
+ *   whose tokens are split writes partial (out, lse) to the workspace;
+ *   they are merged by log-sum-exp in token order.
  * workspace: device memory of at least pa_decode_workspace_size(...)
  *   bytes, 256-byte aligned.  It starts with a region of completion
  *   counters that must be zero-filled before the workspace is first used

@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     PagedAttnError,
     chunked_extend_attn,
     decode_partition_tokens,
+    decode_uses_balanced_split,
     decode_workspace_size,
     extend_chunk_tokens,
     extend_workspace_size,

@@ -64,6 +64,46 @@ Split plan_split(int32_t S, int32_t Hq, int32_t H_units, int32_t Dv, int32_t max
     return sp;
 }
 
+// Balanced split (GQA decode): a grid of as many workgroups as fit on the
+// device at once (at most kBalancedMaxPerCU per compute unit) shares all
+// sub-blocks evenly; each workgroup leaves at most one partial result, so
+// the workspace is sized for the maximum.  partition_tokens == -2 asks for
+// it; 0 takes it when fixed auto-sized partitions would need more than
+// one wave of workgroups (kAutoPartitionedPerCU per compute unit), where
+// unequal sequence lengths leave a tail of lone workgroups.
+constexpr int kBalancedMaxPerCU = 4;
+constexpr int kAutoPartitionedPerCU = 2;
+constexpr int32_t kRequestBalanced = -2;
+
+int32_t device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    return cus;
+}
+int32_t balanced_workgroups() { return kBalancedMaxPerCU * device_cus(); }
+
+bool decode_uses_balanced(int32_t S, int32_t Hkv, int32_t max_ctx, int32_t requested) {
+    if (requested == kRequestBalanced) return true;
+    if (requested != 0) return false;
+    const int32_t P = partition_tokens_for(S, Hkv, max_ctx, 0);
+    const int64_t grid = (int64_t)S * Hkv * (max_ctx > 0 ? cdiv(max_ctx, P) : 1);
+    return grid > (int64_t)kAutoPartitionedPerCU * device_cus();
+}
+
+Split plan_balanced(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t NW) {
+    Split sp;
+    sp.P = 0;
+    sp.parts = 0;
+    const size_t Ga = (size_t)(Hq / Hkv);
+    sp.counter_bytes = align256((size_t)S * Hkv * sizeof(int32_t));
+    sp.out_bytes = align256((size_t)NW * Ga * D * sizeof(float));
+    sp.lse_bytes = align256((size_t)NW * Ga * sizeof(float));
+    return sp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,12 +153,20 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32
     return partition_tokens_for(num_seqs, num_kv_heads, max_context_len, partition_tokens);
 }
 
+int32_t pa_decode_uses_balanced_split(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t max_context_len, int32_t partition_tokens) {
+    return decode_uses_balanced(num_seqs, num_kv_heads, max_context_len, partition_tokens) ? 1 : 0;
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len,
                                 int32_t partition_tokens) {
     if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-        max_context_len < 0 || partition_tokens < -1)
+        max_context_len < 0 || partition_tokens < kRequestBalanced)
         return 0;
+    if (decode_uses_balanced(num_seqs, num_kv_heads, max_context_len, partition_tokens))
+        return plan_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, balanced_workgroups())
+            .total();
     Split sp = plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           partition_tokens);
     return sp.total();
@@ -132,7 +180,8 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
                                int64_t num_blocks, float scale, int32_t partition_tokens,
                                void *workspace, size_t workspace_bytes, void *stream) {
     if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
-        num_blocks < 1 || max_context_len < 0 || partition_tokens < -1 || !isfinite(scale))
+        num_blocks < 1 || max_context_len < 0 || partition_tokens < kRequestBalanced ||
+        !isfinite(scale))
         return PA_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (!out || !query || !k_cache || !v_cache || !block_table || !context_lens)
@@ -145,8 +194,13 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
     if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
     if (max_context_len > kMaxContext || num_seqs > 65535 || num_kv_heads > 65535)
         return PA_ERR_UNSUPPORTED;
-    Split sp = plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                          partition_tokens);
+    const bool balanced =
+        decode_uses_balanced(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    const int32_t cus = balanced ? device_cus() : 0;
+    const int32_t NW = kBalancedMaxPerCU * cus;
+    Split sp = balanced ? plan_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, NW)
+                        : plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                     max_context_len, partition_tokens);
     if (sp.total() > 0) {
         if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
@@ -161,6 +215,7 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
     p.block_table = block_table;
     p.max_blocks = max_blocks_per_seq;
     p.context_lens = context_lens;
+    p.max_ctx = max_context_len;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;
@@ -170,10 +225,13 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
     p.scale = scale;
     p.partition = sp.P;
     p.max_parts = sp.parts;
+    p.balanced_workgroups = NW;
+    p.num_cus = cus;
     char *ws = (char *)workspace;
-    p.counters = sp.parts > 1 ? (int *)ws : nullptr;
-    p.part_out = sp.parts > 1 ? (float *)(ws + sp.counter_bytes) : nullptr;
-    p.part_lse = sp.parts > 1 ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
+    const bool split = balanced || sp.parts > 1;
+    p.counters = split ? (int *)ws : nullptr;
+    p.part_out = split ? (float *)(ws + sp.counter_bytes) : nullptr;
+    p.part_lse = split ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
     return from_hip(launch_paged_decode(p, (hipStream_t)stream));
 }
 

@@ -6,31 +6,34 @@
 // exactly once, as a 16-byte vector, and the arithmetic runs on the VALU as
 // bf16 dot2 instructions whose broadcast operand comes through DPP.
 //
-// Work unit: one workgroup of 4 waves per (partition, kv head, sequence);
-// the 1-D grid is ordered partition-major so the units of one partition
-// index spread over all XCDs.  A wave processes 64 tokens per step:
-//   QK  lane l owns token t0 + l and loads its head_dim / 8 K vectors
-//       (k_cache[p][g][c][o][0..8), 8 consecutive dims of one token), so a
-//       lane accumulates whole dot products with no cross-lane reduction.
-//       The group's queries sit in VGPRs laid out so that lane n of every
-//       16-lane row holds query dword n of a 16-dword slice; DPP
-//       row_newbcast hands it to the whole row inside v_dot2c.
-//   softmax  one wave max per head (integer-ordered DPP max + gfx950
-//       permlane swaps), online rescale, p = exp2(z - m) with log2(e)
-//       folded into the scale.
+// Two ways to split the work over workgroups of 4 waves:
+//   balanced  a fixed grid (a few workgroups per CU) shares the 16-token
+//       sub-blocks of all (sequence, kv head) units equally, so every CU
+//       streams the same number of bytes whatever the length mix;
+//   partitioned  one workgroup per (fixed-length partition, kv head,
+//       sequence), the 1-D grid ordered partition-major so the units of one
+//       partition index spread over all XCDs.
+// Within a range, the waves take chunks of SUBS 16-token sub-blocks
+// round-robin.  A sub-block occupies a wave as 4 rows x 16 lanes:
+//   QK  lane (row r, column n) loads token n's K vectors for a quarter of
+//       head_dim (k_cache[p][g][c][o][0..8), 8 consecutive dims of one
+//       token, as 16-byte loads).  The group's queries sit in VGPRs laid out
+//       so that lane n of a row holds query dword n of the row's slice; DPP
+//       row_newbcast hands it to the whole row inside v_dot2c.  The 4 rows'
+//       partial dots are added with permlane swaps, which leaves every row
+//       holding the 16 scores (column n: token n).
+//   softmax  exact max over the chunk (integer-ordered DPP max), one online
+//       rescale per chunk, p = exp2(z - m) with log2(e) folded into the
+//       scale; the weights stay fp32.
 //   PV  lane l owns dims l (and l + 64).  A V vector
 //       (v_cache[p][g][j][d][0..8), 8 consecutive tokens of one dim) makes
-//       P.V a reduction over tokens inside a lane.  It runs as fp32 FMAs
-//       (on gfx950 a wave64 fp32 FMA issues in half the cycles of a bf16
-//       dot2, so fp32 weights cost no more than bf16 ones): each V vector is
-//       widened once and shared by every head; the weights are permuted
-//       (ds_bpermute) so that lane n of every row holds token 16 k + n and
-//       are broadcast by DPP as above.
-// Groups of more than 8 query heads are processed 8 heads at a time with
-// the queries re-read from LDS.  The 4 waves' states merge in LDS.  A
-// sequence longer than one partition writes fp32 partials (normalised
-// output, LSE); the last workgroup of the sequence to finish merges them by
-// log-sum-exp in partition order, so results are deterministic.
+//       P.V a reduction over tokens inside a lane: fp32 FMAs whose weight
+//       operand (token n's p, in column n of every row) comes through DPP
+//       row_newbcast.  Each V vector is widened once and shared by every head.
+// The 4 waves' states merge in LDS.  A unit split over several workgroups
+// writes fp32 partials (normalised output, LSE); the last workgroup of the
+// unit to finish merges them by log-sum-exp in token order, so results are
+// deterministic.
 #include <type_traits>
 
 #include "common.h"
@@ -44,9 +47,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kStep = 64;  // tokens per wave step
 
-// context length limited to what the block table and the grid can cover
-__device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int B, int max_parts, int P) {
-    const int64_t cap = min((int64_t)max_blocks * B, (int64_t)max_parts * P);
+// context length limited to the host's bound and what the block table covers
+template <int B>
+__device__ __forceinline__ int clamp_ctx(const DecodeParams &p, int ctx) {
+    const int64_t cap = min((int64_t)p.max_blocks * B, (int64_t)p.max_ctx);
     return ctx < 0 ? 0 : ((int64_t)ctx > cap ? (int)cap : ctx);
 }
 
@@ -376,102 +380,287 @@ __device__ __forceinline__ float row_max16(float v) {
     return ord2f(k);
 }
 
-constexpr int kSub = 16;  // tokens per sub-block: one row of lanes
-
-// K of one 16-token sub-block: lane (row, col) loads token `col`'s vectors
-// row * CQ .. row * CQ + CQ - 1 (a quarter of the dims).  `half` selects the
-// 16-token half of a 32-token block.
-template <int D, int B>
-__device__ __forceinline__ void load_k_sub(const uint4 *kc, size_t tile, int half, int row,
-                                           int col, uint4 (&kq)[D / 32]) {
-    constexpr int C = D / 8, CQ = D / 32;
-    const uint4 *kt = kc + tile * (size_t)(C * B) + half * kSub + col;
-#pragma unroll
-    for (int i = 0; i < CQ; i++) kq[i] = kt[(row * CQ + i) * B];
+// s_waitcnt vmcnt(N) as a builtin, so the compiler's own wait insertion
+// knows about it (expcnt and lgkmcnt left at their maximum: no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// V of one 16-token sub-block: its two 8-token groups for dims lane + 64 jj.
+constexpr int kSub = 16;  // tokens per sub-block: one row of lanes
+constexpr float kLazyLog2 = 8.f;  // softmax reference lag allowed (log2 units)
+
+// K and V of one 16-token sub-block come through buffer loads: the block's
+// address is a scalar descriptor base and each lane's offset inside the
+// block is the same for every sub-block, so no address register is
+// rewritten while earlier loads are in flight (which would make the
+// compiler wait for them).  `half` selects the 16-token half of a
+// 32-token block.  The descriptor covers exactly the sub-block's bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// K: lane (row, col) loads token `col`'s vectors row * CQ .. row * CQ + CQ - 1
+// (a quarter of the dims) from k_cache[tile][c][o][0..8).
+// A load that is not `live` gets a descriptor of 0 bytes: it is issued (so
+// the buffers are redefined on every path) but touches no memory and
+// returns zeros.
 template <int D, int B>
-__device__ __forceinline__ void load_v_sub(const uint4 *vc, size_t tile, int half, int lane,
-                                           uint4 (&vv)[2][D / 64]) {
+__device__ __forceinline__ void load_k_sub(const char *k_cache, size_t tile, int half, bool live,
+                                           uint32_t lane_off, uint4 (&kq)[D / 32]) {
+    constexpr int CQ = D / 32;
+    const char *base = k_cache + (tile * (size_t)(D * B) + half * kSub * 8) * 2;
+    const auto r = tile_rsrc(base, live ? (uint32_t)(D * B * 2 - half * kSub * 16) : 0u);
+#pragma unroll
+    for (int i = 0; i < CQ; i++) kq[i] = buf_load16(r, lane_off + i * B * 16);
+}
+// byte offset of lane (row, col) inside a K tile
+template <int D, int B>
+__device__ __forceinline__ uint32_t k_lane_off(int row, int col) {
+    return (uint32_t)((row * (D / 32) * B + col) * 16);
+}
+
+// V: the sub-block's two 8-token groups for dims lane + 64 jj, from
+// v_cache[tile][j][d][0..8).
+template <int D, int B>
+__device__ __forceinline__ void load_v_sub(const char *v_cache, size_t tile, int half, bool live,
+                                           uint32_t lane_off, uint4 (&vv)[2][D / 64]) {
     constexpr int DV = D / 64;
-    const uint4 *vt = vc + (tile * (B / 8) + half * 2) * D + lane;
+    const char *base = v_cache + ((tile * (B / 8) + half * 2) * (size_t)D) * 16;
+    const auto r = tile_rsrc(base, live ? (uint32_t)(2 * D * 16) : 0u);
 #pragma unroll
     for (int tg = 0; tg < 2; tg++)
 #pragma unroll
-        for (int jj = 0; jj < DV; jj++) vv[tg][jj] = vt[tg * D + 64 * jj];
+        for (int jj = 0; jj < DV; jj++) vv[tg][jj] = buf_load16(r, lane_off + (tg * D + 64 * jj) * 16);
 }
 
-// One workgroup (4 waves) per (partition, kv head, sequence).  A wave owns
-// every 4th chunk of SUBS 16-token sub-blocks of the partition.  Per chunk
-// it loads the sub-blocks' K (one 16-byte vector per lane per load) and V,
-// computes all SUBS x G scores, takes their exact max, and accumulates P.V;
-// the next chunk's K loads are issued as soon as the current K is consumed,
-// and its V loads as soon as the current V is.
-template <int D, int B, int G, int SUBS>
-__global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
+// Token offset, from `start`, of a wave's sub-block k.  SHARED: the 4 waves
+// of the workgroup take SUBS-sub-block chunks of the range round-robin
+// (sub-block k of a wave is sub-block k % SUBS of its chunk k / SUBS);
+// otherwise the wave owns the range and its sub-blocks are consecutive.
+template <int SUBS, bool SHARED>
+__device__ __forceinline__ int sub_t0(int k, int wave) {
+    if constexpr (SHARED)
+        return (kWaves * (k / SUBS) + wave) * (kSub * SUBS) + kSub * (k % SUBS);
+    else
+        return kSub * k;
+}
+
+// Raw block-table entry of the wave's sub-block `lane` in the window that
+// starts at token `start` (index clamped into the table; the caller decides
+// validity).
+template <int B, int SUBS, bool SHARED>
+__device__ __forceinline__ int bt_entry(const DecodeParams &p, int s, int start) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int t0 = start + sub_t0<SUBS, SHARED>(lane, wave);
+    return p.block_table[(size_t)s * p.max_blocks + min(t0 / B, p.max_blocks - 1)];
+}
+
+// The work of one wave on tokens [start, end) of sequence s, kv head g (start
+// a multiple of 16), in chunks of SUBS sub-blocks; the online-softmax state
+// (m, lsum, acc) accumulates across calls.  Per chunk a wave loads its
+// sub-blocks' K (one 16-byte vector per lane per load) and V, computes all
+// SUBS x G scores, takes their exact max and accumulates P.V.  A wave
+// tracks the block ids of 64 sub-blocks at a time, so longer ranges are
+// taken in windows; bt_first is bt_entry() of the first window, loaded
+// early by the caller.
+template <int D, int B, int G, int SUBS, bool SHARED>
+__device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g, int range_start,
+                                             int range_end, int bt_first, const uint32_t (&qreg)[G],
+                                             float (&m)[G], float (&lsum)[G],
+                                             float (&acc)[G][D / 64]) {
     constexpr int CQ = D / 32;        // K vectors per lane per sub-block
     constexpr int DV = D / 64;        // output dims per lane
-    constexpr int QW = 4 * CQ;        // query dwords per row
-    constexpr int kChunk = kSub * SUBS;
     constexpr bool kPairs = G >= 2;
     constexpr int HS = kPairs ? 2 : 1;
-
-    const int units = p.S * p.Hkv;
-    const int part = blockIdx.x / units;
-    const int rem = blockIdx.x - part * units;
-    const int s = rem / p.Hkv, g = rem - s * p.Hkv;
-    const int Ga = p.Hq / p.Hkv;
-    const int P = p.partition;
-    const int start = part * P;
-    // the wave index as a scalar, so per-wave token offsets stay in SGPRs
+    constexpr int kWindow = (SHARED ? kWaves : 1) * 64 * kSub;  // tokens per window
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int row = lane >> 4, col = lane & 15;
-    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-
-    // Issued together, before anything waits: the context length, the
-    // block-table entry of this wave's sub-block `lane` (index clamped into
-    // the table, validity decided once the length is known) and the queries.
-    // Sub-block k of the wave is sub-block k % SUBS of its chunk k / SUBS.
-    const int ctx_raw = as_const<int32_t>(p.context_lens)[s];
-    const int t0_lane = start + (kWaves * (lane / SUBS) + wave) * kChunk + kSub * (lane % SUBS);
-    const int bt_raw =
-        p.block_table[(size_t)s * p.max_blocks + min(t0_lane / B, p.max_blocks - 1)];
-    uint32_t qreg[G];
-    {
-        const uint32_t *qg = reinterpret_cast<const uint32_t *>(p.query) +
-                             ((size_t)s * p.Hq + (size_t)g * Ga) * (D / 2) + row * QW + (col % QW);
-#pragma unroll
-        for (int h = 0; h < G; h++) qreg[h] = qg[(h < Ga ? h : h - Ga) * (D / 2)];
-    }
-    const int ctx = clamp_ctx(ctx_raw, p.max_blocks, B, p.max_parts, P);
-
-    if (start >= ctx) {
-        if (ctx == 0 && part == 0) {
-            // no keys: out = 0, lse = -inf
-            for (int idx = threadIdx.x; idx < Ga * D; idx += blockDim.x) {
-                const int hq = g * Ga + idx / D;
-                out[((size_t)s * p.Hq + hq) * D + idx % D] = 0;
-                if (idx % D == 0 && p.lse) p.lse[(size_t)s * p.Hq + hq] = kNegInf;
-            }
-        }
-        return;
-    }
-    const int end = min(start + P, ctx);
-    const int nparts = (ctx + P - 1) / P;
     const float sl2 = p.scale * kLog2e;
+    const char *kc = reinterpret_cast<const char *>(p.k_cache);
+    const char *vc = reinterpret_cast<const char *>(p.v_cache);
+    const uint32_t k_off = k_lane_off<D, B>(row, col), v_off = (uint32_t)lane * 16;
 
-    // lane k: physical block of sub-block k, -1 past the end or out of range.
-    // Validity is monotone in k, so the valid sub-blocks are 0 .. nmine - 1.
-    const bool lane_ok = t0_lane < end;
-    const int bid = lane_ok && bt_raw >= 0 && (int64_t)bt_raw < p.num_blocks ? bt_raw : -1;
-    const int nmine = __popcll(__ballot(lane_ok));
-    const int nch = (nmine + SUBS - 1) / SUBS;
-    const uint4 *kc = reinterpret_cast<const uint4 *>(p.k_cache);
-    const uint4 *vc = reinterpret_cast<const uint4 *>(p.v_cache);
+    int bt_raw = bt_first;
+    for (int start = range_start; start < range_end; start += kWindow) {
+        const int end = min(start + kWindow, range_end);
+        if (start != range_start) bt_raw = bt_entry<B, SUBS, SHARED>(p, s, start);
+        // lane k: physical block of this wave's sub-block k, -1 past the end or
+        // out of range.  Validity is monotone in k, so the sub-blocks in range
+        // are 0 .. nmine - 1.
+        const int t0_lane = start + sub_t0<SUBS, SHARED>(lane, wave);
+        const bool lane_ok = t0_lane < end;
+        const int bid = lane_ok && bt_raw >= 0 && (int64_t)bt_raw < p.num_blocks ? bt_raw : -1;
+        const int nmine = __popcll(__ballot(lane_ok));
 
-    float m[G], lsum[G], acc[G][DV];
+        // Sub-block k's block and token offset (k clamped into the window);
+        // an invalid block id reads block 0 and is masked.
+        auto locate = [&](int k, size_t &tile, int &half) {
+            k = min(k, 63);
+            const int b = readlane_i32(bid, k);
+            const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
+            tile = (size_t)(b < 0 ? 0 : b) * p.Hkv + g;
+            half = (t0 % B) / kSub;
+        };
+        auto load_k = [&](int k, uint4 (&kq)[CQ]) {
+            size_t tile;
+            int half;
+            locate(k, tile, half);
+            load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
+        };
+        auto load_v = [&](int k, uint4 (&vv)[2][DV]) {
+            size_t tile;
+            int half;
+            locate(k, tile, half);
+            load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
+        };
+
+        // One sub-block: QK, a lazy softmax update, PV (skipped, by uniform
+        // branches, for sub-blocks past the end or with an invalid block).
+        // When it starts, the loads in flight are, oldest first: this
+        // sub-block's K and V, then the other buffer's K and V; the explicit
+        // waits say exactly that to the compiler.
+        constexpr int LK = CQ, LV = 2 * DV;  // load instructions per sub-block
+        auto compute_sub = [&](int k, const uint4 (&kq)[CQ], const uint4 (&vv)[2][DV]) {
+            const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
+            const int nvalid =
+                k < nmine && readlane_i32(bid, min(k, 63)) >= 0 ? min(kSub, end - t0) : 0;
+            float z[G];
+            if (nvalid > 0) {
+                wait_vm_loads<LV + LK + LV>();
+                // QK: each lane sums a quarter of the dims; the rows are then
+                // summed, leaving every row with the 16 scores of the sub-block
+                float a[G][2];
+#pragma unroll
+                for (int h = 0; h < G; h++) a[h][0] = a[h][1] = 0.f;
+#pragma unroll
+                for (int h = 0; h < G; h += HS) {
+                    if constexpr (kPairs) {
+                        if constexpr (CQ == 4) {
+                            if (h + 2 >= G)
+                                qk_2h<true>(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
+                                            qreg[h + 1], kq[0], kq[1], kq[2], kq[3]);
+                            else
+                                qk_2h<false>(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
+                                             qreg[h + 1], kq[0], kq[1], kq[2], kq[3]);
+                        } else {
+                            qk8_2h(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
+                                   qreg[h + 1], kq[0], kq[1]);
+                        }
+                    } else {
+                        if constexpr (CQ == 4)
+                            qk_1h<true>(a[h][0], a[h][1], qreg[h], kq[0], kq[1], kq[2], kq[3]);
+                        else
+                            qk8_1h(a[h][0], a[h][1], qreg[h], kq[0], kq[1]);
+                    }
+                }
+                dpp_result_fence<2 * G>(&a[0][0]);
+                const bool ok = col < nvalid;
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    const float t = row_sum4(a[h][0] + a[h][1]);
+                    z[h] = ok ? t * sl2 : kNegInf;
+                }
+            }
+            if (nvalid > 0) {
+                // Lazy softmax: the reference m[h] (log2 units) moves only when
+                // a score exceeds it by more than kLazyLog2, so weights stay
+                // <= 2^kLazyLog2 and most sub-blocks need no rescale.
+                uint64_t over = 0;
+#pragma unroll
+                for (int h = 0; h < G; h++) over |= __ballot(z[h] > m[h] + kLazyLog2);
+                if (over) {
+                    dpp_result_fence<G * DV>(&acc[0][0]);
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        const float mx = uniform_f(row_max16(z[h]));
+                        if (mx > m[h] + kLazyLog2) {
+                            const float alpha = fast_exp2(m[h] - mx);  // 0 from -inf
+                            lsum[h] *= alpha;
+#pragma unroll
+                            for (int jj = 0; jj < DV; jj++) acc[h][jj] *= alpha;
+                            m[h] = mx;
+                        }
+                    }
+                }
+                uint32_t pw[G];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    const float mref = m[h] == kNegInf ? 0.f : m[h];
+                    const float pr = fast_exp2(z[h] - mref);
+                    lsum[h] += pr;
+                    pw[h] = __float_as_uint(pr);
+                }
+                // PV: the V of tokens past the end is zeroed (weight 0, data may
+                // be anything); the buffers themselves are only read
+                wait_vm_loads<LK + LV>();
+#pragma unroll
+                for (int tg = 0; tg < 2; tg++) {
+                    const int nv = nvalid - 8 * tg;
+                    float vf[DV][8];
+#pragma unroll
+                    for (int jj = 0; jj < DV; jj++) {
+                        uint4 v = vv[tg][jj];
+                        if (nvalid < kSub) {
+                            v.x = mask_pair(v.x, 0, nv);
+                            v.y = mask_pair(v.y, 2, nv);
+                            v.z = mask_pair(v.z, 4, nv);
+                            v.w = mask_pair(v.w, 6, nv);
+                        }
+                        widen8(v, vf[jj]);
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; h += HS) {
+                        const bool last = tg == 1 && h + HS >= G;
+                        pv_step<DV, kPairs>(tg, last, acc[h], acc[h + HS - 1], pw[h],
+                                            pw[h + HS - 1], vf);
+                    }
+                }
+                dpp_result_fence<G * DV>(&acc[0][0]);
+            }
+        };
+
+        // Two buffers: sub-block k + 1 is requested before k is computed, so
+        // requests reach memory spread over the wave's work and computation
+        // overlaps the stream (loads complete in issue order).  Every load is
+        // issued on every path (a load past the end touches no memory), so
+        // the buffers are plain loop-carried registers.
+        uint4 kA[CQ], vA[2][DV], kB[CQ], vB[2][DV];
+        load_k(0, kA);
+        load_v(0, vA);
+        for (int k = 0; k < nmine; k += 2) {
+            load_k(k + 1, kB);
+            load_v(k + 1, vB);
+            compute_sub(k, kA, vA);
+            load_k(k + 2, kA);
+            load_v(k + 2, vA);
+            compute_sub(k + 1, kB, vB);
+        }
+    }
+}
+
+// Query registers of kv head g's query heads: lane (row r, column n) holds
+// dword r * QW + n of each head's query; padded heads (h >= Ga) repeat real ones.
+template <int D, int G>
+__device__ __forceinline__ void load_queries(const DecodeParams &p, int s, int g, int Ga,
+                                             uint32_t (&qreg)[G]) {
+    constexpr int QW = D / 8;
+    const int lane = threadIdx.x & 63, row = lane >> 4, col = lane & 15;
+    const uint32_t *qg = reinterpret_cast<const uint32_t *>(p.query) +
+                         ((size_t)s * p.Hq + (size_t)g * Ga) * (D / 2) + row * QW + (col % QW);
+#pragma unroll
+    for (int h = 0; h < G; h++) qreg[h] = qg[(h < Ga ? h : h - Ga) * (D / 2)];
+}
+
+template <int G, int DV>
+__device__ __forceinline__ void reset_state(float (&m)[G], float (&lsum)[G], float (&acc)[G][DV]) {
 #pragma unroll
     for (int h = 0; h < G; h++) {
         m[h] = kNegInf;
@@ -479,216 +668,326 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int jj = 0; jj < DV; jj++) acc[h][jj] = 0.f;
     }
+}
 
-    uint4 kb[SUBS][CQ], vb[SUBS][2][DV];
-    // Sub-block k's block and token offset; a sub-block past the end re-reads
-    // the wave's last valid one (a cache hit) so every chunk issues the same loads.
-    auto locate = [&](int k, size_t &tile, int &half) {
-        const int kk = min(k, nmine - 1);
-        const int b = readlane_i32(bid, kk);
-        const int t0 = start + (kWaves * (kk / SUBS) + wave) * kChunk + kSub * (kk % SUBS);
-        tile = (size_t)(b < 0 ? 0 : b) * p.Hkv + g;
-        half = (t0 % B) / kSub;
-    };
-    auto issue_k = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < SUBS; j++) {
-            size_t tile;
-            int half;
-            locate(c * SUBS + j, tile, half);
-            load_k_sub<D, B>(kc, tile, half, row, col, kb[j]);
-        }
-    };
-    auto issue_v = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < SUBS; j++) {
-            size_t tile;
-            int half;
-            locate(c * SUBS + j, tile, half);
-            load_v_sub<D, B>(vc, tile, half, lane, vb[j]);
-        }
-    };
+template <int D, int G>
+struct WaveMergeLDS {
+    float m[kWaves][G], l[kWaves][G];
+    float acc[kWaves][G][D];
+};
 
-    // One chunk: all of its K and V loads are issued first (V lands while
-    // the scores are computed), then QK, softmax, PV.  Buffers are not
-    // carried across chunks; the other waves of the SIMD cover the latency.
-    auto chunk = [&](int c) {
-        issue_k(c);
-        issue_v(c);
-        int nvalid[SUBS];
-#pragma unroll
-        for (int j = 0; j < SUBS; j++) {
-            const int k = c * SUBS + j;
-            const int t0 = start + (kWaves * c + wave) * kChunk + kSub * j;
-            nvalid[j] = readlane_i32(bid, k) < 0 ? 0 : min(kSub, end - t0);
-        }
-        // QK: each lane sums a quarter of the dims; the rows are then summed,
-        // leaving every row with the 16 scores of the sub-block
-        float sc[SUBS][G];
-#pragma unroll
-        for (int j = 0; j < SUBS; j++) {
-            float a[G][2];
-#pragma unroll
-            for (int h = 0; h < G; h++) a[h][0] = a[h][1] = 0.f;
-#pragma unroll
-            for (int h = 0; h < G; h += HS) {
-                if constexpr (kPairs) {
-                    if constexpr (CQ == 4) {
-                        if (h + 2 >= G)
-                            qk_2h<true>(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
-                                        qreg[h + 1], kb[j][0], kb[j][1], kb[j][2], kb[j][3]);
-                        else
-                            qk_2h<false>(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h],
-                                         qreg[h + 1], kb[j][0], kb[j][1], kb[j][2], kb[j][3]);
-                    } else {
-                        qk8_2h(a[h][0], a[h][1], a[h + 1][0], a[h + 1][1], qreg[h], qreg[h + 1],
-                               kb[j][0], kb[j][1]);
-                    }
-                } else {
-                    if constexpr (CQ == 4)
-                        qk_1h<true>(a[h][0], a[h][1], qreg[h], kb[j][0], kb[j][1], kb[j][2],
-                                    kb[j][3]);
-                    else
-                        qk8_1h(a[h][0], a[h][1], qreg[h], kb[j][0], kb[j][1]);
-                }
-            }
-            dpp_result_fence<2 * G>(&a[0][0]);
-            const bool ok = col < nvalid[j];
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                const float z = row_sum4(a[h][0] + a[h][1]);
-                sc[j][h] = ok ? z * sl2 : kNegInf;
-            }
-        }
-        // softmax: exact max over the chunk, one rescale of the running state
-        uint32_t pw[SUBS][G];
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            float mx = sc[0][h];
-#pragma unroll
-            for (int j = 1; j < SUBS; j++) mx = fmax_nc(mx, sc[j][h]);
-            mx = uniform_f(row_max16(mx));
-            const float mn = fmax_nc(m[h], mx);
-            const float mref = mn == kNegInf ? 0.f : mn;
-            const float alpha = fast_exp2(m[h] - mref);
-            m[h] = mn;
-            float l = lsum[h] * alpha;
-#pragma unroll
-            for (int j = 0; j < SUBS; j++) {
-                const float pr = fast_exp2(sc[j][h] - mref);
-                l += pr;
-                pw[j][h] = __float_as_uint(pr);
-            }
-            lsum[h] = l;
-#pragma unroll
-            for (int jj = 0; jj < DV; jj++) acc[h][jj] *= alpha;
-        }
-        // PV: the V of tokens past the end is zeroed (weight 0, data may be anything)
-#pragma unroll
-        for (int j = 0; j < SUBS; j++) {
-            if (nvalid[j] < kSub) {
-#pragma unroll
-                for (int tg = 0; tg < 2; tg++) {
-                    const int nv = nvalid[j] - 8 * tg;
-#pragma unroll
-                    for (int jj = 0; jj < DV; jj++) {
-                        uint4 &v = vb[j][tg][jj];
-                        v.x = mask_pair(v.x, 0, nv);
-                        v.y = mask_pair(v.y, 2, nv);
-                        v.z = mask_pair(v.z, 4, nv);
-                        v.w = mask_pair(v.w, 6, nv);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < SUBS; j++) {
-#pragma unroll
-            for (int tg = 0; tg < 2; tg++) {
-                float vf[DV][8];
-#pragma unroll
-                for (int jj = 0; jj < DV; jj++) widen8(vb[j][tg][jj], vf[jj]);
-#pragma unroll
-                for (int h = 0; h < G; h += HS) {
-                    const bool last = j == SUBS - 1 && tg == 1 && h + HS >= G;
-                    pv_step<DV, kPairs>(tg, last, acc[h], acc[h + HS - 1], pw[j][h],
-                                        pw[j][h + HS - 1], vf);
-                }
-            }
-        }
-        dpp_result_fence<G * DV>(&acc[0][0]);
-    };
-
-    for (int c = 0; c < nch; c++) chunk(c);
-
-    // merge the 4 waves of the workgroup (every row holds the same token
-    // weights, so a wave's sum is 4 x the row sum)
-    __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
-    __shared__ float sm_acc[kWaves][G][D];
+// Merge the 4 waves' states in LDS; thread (head h, dim pair d) then calls
+// emit(h, d, o0, o1, L) with the normalised output of dims d, d + 1 and the
+// LSE (natural log).  Every row holds the same token weights, so a wave's
+// sum of weights is 4 x the row sum.  Ends with the workgroup synchronised
+// only before the emits: callers that reuse the LDS must synchronise again.
+template <int D, int G, typename Emit>
+__device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G> &sm, int Ga, const float (&m)[G],
+                                            const float (&lsum)[G], const float (&acc)[G][D / 64],
+                                            Emit emit) {
+    constexpr int DV = D / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int h = 0; h < G; h++) {
         const float l = wave_sum(lsum[h]) * 0.25f;
         if (lane == 0) {
-            sm_m[wave][h] = m[h];
-            sm_l[wave][h] = l;
+            sm.m[wave][h] = m[h];
+            sm.l[wave][h] = l;
         }
 #pragma unroll
-        for (int jj = 0; jj < DV; jj++) sm_acc[wave][h][lane + 64 * jj] = acc[h][jj];
+        for (int jj = 0; jj < DV; jj++) sm.acc[wave][h][lane + 64 * jj] = acc[h][jj];
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < Ga * (D / 2); idx += blockDim.x) {
         const int h = idx / (D / 2), d = 2 * (idx % (D / 2));
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm_m[w][h]);
+        for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
         const float Mr = M == kNegInf ? 0.f : M;
         float n0 = 0.f, n1 = 0.f, den = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
-            const float wt = fast_exp2(sm_m[w][h] - Mr);
-            n0 += wt * sm_acc[w][h][d];
-            n1 += wt * sm_acc[w][h][d + 1];
-            den += wt * sm_l[w][h];
+            const float wt = fast_exp2(sm.m[w][h] - Mr);
+            n0 += wt * sm.acc[w][h][d];
+            n1 += wt * sm.acc[w][h][d + 1];
+            den += wt * sm.l[w][h];
         }
         const float inv = den > 0.f ? 1.f / den : 0.f;
         const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
-        const size_t orow = (size_t)s * p.Hq + (size_t)g * Ga + h;
-        if (nparts == 1) {
-            reinterpret_cast<uint32_t *>(out + orow * D)[d / 2] = pack_bf16x2(n0 * inv, n1 * inv);
-            if (d == 0 && p.lse) p.lse[orow] = L;
-        } else {
-            store_coherent2(&p.part_out[(orow * p.max_parts + part) * D + d], n0 * inv, n1 * inv);
-            if (d == 0) store_coherent(&p.part_lse[orow * p.max_parts + part], L);
-        }
+        emit(h, d, n0 * inv, n1 * inv, L);
     }
-    if (nparts == 1) return;
+}
 
-    // The last workgroup of this (sequence, kv head) to finish merges all of
-    // its partitions.  Partials are written and read with device-coherent
-    // (agent-scope) accesses, so no cache-wide fence is needed: each thread
-    // waits for its partial stores to complete, then one thread counts.
+// Counts one finished piece of a split unit; true in the one workgroup that
+// finished last (which then merges).  Each thread first waits for its
+// partial stores to complete (they are device-coherent, so no cache-wide
+// fence is needed).  The last workgroup leaves the counter zero.
+__device__ __forceinline__ bool count_finished(int *counter, int nparts) {
     __shared__ int sm_last;
     wait_stores();
     __syncthreads();
-    int *counter = p.counters + (size_t)s * p.Hkv + g;
-    if (threadIdx.x == 0)
-        sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  nparts - 1;
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = prev == nparts - 1;
+        if (prev == nparts - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
-    if (!sm_last) return;
-    if (threadIdx.x == 0)  // leave the counter zero for the next call
-        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return sm_last;
+}
+
+__device__ __forceinline__ void write_empty(const DecodeParams &p, int s, int g, int Ga, int D) {
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    for (int idx = threadIdx.x; idx < Ga * D; idx += blockDim.x) {
+        const int hq = g * Ga + idx / D;
+        out[((size_t)s * p.Hq + hq) * D + idx % D] = 0;
+        if (idx % D == 0 && p.lse) p.lse[(size_t)s * p.Hq + hq] = kNegInf;
+    }
+}
+
+// Explicit partitions: one workgroup per (partition, kv head, sequence),
+// partition-major grid; partials in [S, Hq, max_parts, D].
+template <int D, int B, int G, int SUBS>
+__global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
+    constexpr int DV = D / 64;
+    const int units = p.S * p.Hkv;
+    const int part = blockIdx.x / units;
+    const int rem = blockIdx.x - part * units;
+    const int s = rem / p.Hkv, g = rem - s * p.Hkv;
+    const int Ga = p.Hq / p.Hkv;
+    const int P = p.partition;
+    const int start = part * P;
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+
+    // issued together, before anything waits: the context length, the
+    // block-table entries of the partition's first piece and the queries
+    const int ctx_raw = as_const<int32_t>(p.context_lens)[s];
+    const int bt_first = bt_entry<B, SUBS, true>(p, s, start);
+    uint32_t qreg[G];
+    load_queries<D, G>(p, s, g, Ga, qreg);
+    const int ctx = clamp_ctx<B>(p, ctx_raw);
+    if (start >= ctx) {
+        if (ctx == 0 && part == 0) write_empty(p, s, g, Ga, D);
+        return;
+    }
+    const int end = min(start + P, ctx);
+    const int nparts = (ctx + P - 1) / P;
+    float m[G], lsum[G], acc[G][DV];
+    reset_state<G, DV>(m, lsum, acc);
+    attend_range<D, B, G, SUBS, true>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
+
+    __shared__ WaveMergeLDS<D, G> sm;
+    merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, float o0, float o1, float L) {
+        const size_t orow = (size_t)s * p.Hq + (size_t)g * Ga + h;
+        if (nparts == 1) {
+            reinterpret_cast<uint32_t *>(out + orow * D)[d / 2] = pack_bf16x2(o0, o1);
+            if (d == 0 && p.lse) p.lse[orow] = L;
+        } else {
+            store_coherent2(&p.part_out[(orow * p.max_parts + part) * D + d], o0, o1);
+            if (d == 0) store_coherent(&p.part_lse[orow * p.max_parts + part], L);
+        }
+    });
+    if (nparts == 1) return;
+    if (!count_finished(p.counters + (size_t)s * p.Hkv + g, nparts)) return;
     constexpr int kDPT = G * D / 256 > 4 ? G * D / 256 : 4;
-    merge_partition_rows<D, kDPT, (kDPT > 4 ? 4 : 8)>(p.part_out, p.part_lse, p.max_parts,
-                                                      reinterpret_cast<uint16_t *>(p.out), p.lse,
-                                                      (size_t)s * p.Hq + (size_t)g * Ga, Ga, nparts);
+    merge_partition_rows<D, kDPT, (kDPT > 4 ? 4 : 8)>(p.part_out, p.part_lse, p.max_parts, out,
+                                                      p.lse, (size_t)s * p.Hq + (size_t)g * Ga,
+                                                      Ga, nparts);
+}
+
+// Balanced split.  The grid has NW workgroups (as many as are resident at
+// once).  Every non-empty (sequence, kv head) unit u, of nsb_u 16-token
+// sub-blocks, is cut into n_u contiguous pieces of near-equal size, one per
+// workgroup: with U non-empty units and SB sub-blocks in all,
+//   n_u = min(nsb_u, 1 + floor(nsb_u (NW - U) / SB))   if U <= NW,
+// so that sum n_u <= NW and every piece holds about SB / NW sub-blocks
+// whatever the length mix; with more units than workgroups every unit is
+// one piece and the workgroups take several.  Pieces are numbered
+// unit-major (unit u = s Hkv + g); workgroup w takes piece w (+ NW, ...),
+// and its 4 waves take the piece's sub-blocks in turn.  A unit cut into
+// pieces P_u .. P_u + n_u - 1 leaves their partials in slots P_u ..
+// P_u + n_u - 1 of [NW, Ga, D] and [NW, Ga]; the last to finish merges them
+// in piece order.
+
+// Inclusive prefix sum over the wave's lanes (Hillis-Steele over ds_bpermute).
+__device__ __forceinline__ int wave_prefix_sum_i(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// Merge of a unit's piece partials (slots P_u .. P_u + nparts - 1, in that
+// order) into rows row0 .. row0 + Ga - 1: thread -> (head, 4 dims), 8
+// partials per round trip.
+template <int D>
+__device__ __forceinline__ void merge_unit_partials(const DecodeParams &p, size_t row0, int Ga,
+                                                    int P_u, int nparts, int NW) {
+    constexpr int kBatch = 8;
+    const auto rs = coherent_rsrc(p.part_out, (uint32_t)NW * Ga * D * 4);
+    for (int it = threadIdx.x; it < Ga * (D / 4); it += blockDim.x) {
+        const int h = it / (D / 4), d0 = (it % (D / 4)) * 4;
+        float M = kNegInf, den = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < nparts; b += kBatch) {
+            float L[kBatch];
+            float4 x[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; u++) {
+                const int slot = P_u + (b + u < nparts ? b + u : b);
+                L[u] = load_coherent(&p.part_lse[(size_t)slot * Ga + h]);
+                x[u] = load_coherent4(rs, (uint32_t)(((size_t)slot * Ga + h) * D + d0) * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; u++)
+                if (b + u >= nparts) L[u] = kNegInf;
+            float Mb = M;
+#pragma unroll
+            for (int u = 0; u < kBatch; u++) Mb = fmax_nc(Mb, L[u]);
+            const float Mr = Mb == kNegInf ? 0.f : Mb;
+            const float r = fast_exp2((M - Mr) * kLog2e);
+            den *= r;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] *= r;
+#pragma unroll
+            for (int u = 0; u < kBatch; u++) {
+                const float wt = fast_exp2((L[u] - Mr) * kLog2e);
+                den += wt;
+                o[0] += wt * x[u].x;
+                o[1] += wt * x[u].y;
+                o[2] += wt * x[u].z;
+                o[3] += wt * x[u].w;
+            }
+            M = Mb;
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const size_t orow = row0 + h;
+        uint2 v;
+        v.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+        v.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + orow * D + d0) = v;
+        if (d0 == 0 && p.lse) p.lse[orow] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
+    }
+}
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
+    constexpr int DV = D / 64;
+    const int NW = gridDim.x, w = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int Ga = p.Hq / p.Hkv, Hkv = p.Hkv;
+    // clamped context length of sequence s (lane-wise; 0 past the end); the
+    // first 64 are kept in a register
+    auto ctx_of = [&](int s) { return s < p.S ? clamp_ctx<B>(p, p.context_lens[min(s, p.S - 1)]) : 0; };
+    const int ctx_w0 = ctx_of(lane);
+    auto ctx_in = [&](int c0) { return c0 == 0 ? ctx_w0 : ctx_of(c0 + lane); };
+
+    // empty sequences: workgroup s % NW writes out = 0, lse = -inf
+    for (int s = w; s < p.S; s += NW)
+        if (readlane_i32(ctx_in(s & ~63), s & 63) == 0)
+            for (int g = 0; g < Hkv; g++) write_empty(p, s, g, Ga, D);
+
+    // pass 1 (every wave): sub-blocks and non-empty sequences
+    int64_t SBs = 0;
+    int Ns = 0;
+    for (int c0 = 0; c0 < p.S; c0 += 64) {
+        const int nsb = (ctx_in(c0) + kSub - 1) / kSub;
+        SBs += readlane_i32(wave_prefix_sum_i(nsb), 63);
+        Ns += __popcll(__ballot(nsb > 0));
+    }
+    if (Ns == 0) return;
+    const int64_t SB = SBs * Hkv;
+    const int64_t U = (int64_t)Ns * Hkv;
+    const bool split = U <= NW;
+    // pieces per unit of a sequence; when split, SB <= NW * 2^16 and the
+    // arithmetic fits 32 bits
+    const uint32_t spare = split ? (uint32_t)(NW - U) : 0u, SB32 = split ? (uint32_t)SB : 1u;
+    auto pieces_of = [&](int nsb) -> int {
+        if (nsb == 0) return 0;
+        if (!split) return 1;
+        const uint32_t n = 1u + (uint32_t)nsb * spare / SB32;
+        return n < (uint32_t)nsb ? (int)n : nsb;
+    };
+
+    __shared__ WaveMergeLDS<D, G> sm;
+    for (int64_t v = w; ; v += NW) {
+        // find piece v (every wave computes the same)
+        int s = -1, g = 0, k = 0, n = 1, a = 0, b = 0, ctx = 0, P_u = 0;
+        int64_t base = 0;  // pieces of the sequences before window c0
+        for (int c0 = 0; c0 < p.S; c0 += 64) {
+            const int ctx_l = ctx_in(c0);
+            const int nsb_l = (ctx_l + kSub - 1) / kSub;
+            const int np_l = pieces_of(nsb_l) * Hkv;
+            const int incl = wave_prefix_sum_i(np_l);
+            const uint64_t past = __ballot(base + incl > v);
+            if (past) {
+                const int i = __builtin_ctzll(past);
+                const int np = readlane_i32(np_l, i);
+                const int nsb = readlane_i32(nsb_l, i);
+                n = np / Hkv;
+                const int64_t first = base + readlane_i32(incl, i) - np;  // sequence's first piece
+                const int r = (int)(v - first);
+                s = c0 + i;
+                g = r / n;
+                k = r - g * n;
+                a = (int)((uint32_t)k * (uint32_t)nsb / (uint32_t)n);
+                b = (int)((uint32_t)(k + 1) * (uint32_t)nsb / (uint32_t)n);
+                P_u = (int)(first + (int64_t)g * n);  // < NW when split
+                ctx = readlane_i32(ctx_l, i);
+                break;
+            }
+            base += readlane_i32(incl, 63);
+        }
+        if (s < 0) break;  // no piece left for this workgroup
+        if (v != w) __syncthreads();  // the LDS of the previous piece has been read
+
+        const int tb = a * kSub, te = min(b * kSub, ctx);
+        const int bt_first = bt_entry<B, 1, true>(p, s, tb);
+        uint32_t qreg[G];
+        load_queries<D, G>(p, s, g, Ga, qreg);
+        float m[G], lsum[G], acc[G][DV];
+        reset_state<G, DV>(m, lsum, acc);
+        attend_range<D, B, G, 1, true>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
+
+        const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
+        merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, float o0, float o1, float L) {
+            if (n == 1) {
+                reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(p.out) + (row0 + h) * D)[d / 2] =
+                    pack_bf16x2(o0, o1);
+                if (d == 0 && p.lse) p.lse[row0 + h] = L;
+            } else {
+                store_coherent2(&p.part_out[((size_t)v * Ga + h) * D + d], o0, o1);
+                if (d == 0) store_coherent(&p.part_lse[(size_t)v * Ga + h], L);
+            }
+        });
+        if (n > 1 && count_finished(p.counters + (size_t)s * Hkv + g, n))
+            merge_unit_partials<D>(p, row0, Ga, P_u, n, NW);
+        if (split) break;  // one piece per workgroup
+    }
 }
 
 template <int D, int B, int G>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
+    constexpr int kSubs = G >= 16 ? 2 : 4;
+    if (p.balanced_workgroups > 0) {
+        // one wave of workgroups: as many as are resident together
+        static const int per_cu = [] {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, reinterpret_cast<const void *>(&paged_decode_balanced_kernel<D, B, G>),
+                    256, 0) != hipSuccess || n < 1)
+                n = 1;
+            return n;
+        }();
+        const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G>), dim3((unsigned)nw),
+                           dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     const int64_t units = (int64_t)p.max_parts * p.S * p.Hkv;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    constexpr int kSubs = G >= 16 ? 2 : 4;
     hipLaunchKernelGGL((paged_decode_kernel<D, B, G, kSubs>), dim3((unsigned)units), dim3(256), 0,
                        stream, p);
     return hipGetLastError();

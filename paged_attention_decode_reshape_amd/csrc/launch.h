@@ -27,14 +27,18 @@ struct DecodeParams {
     const int32_t *block_table;
     int32_t max_blocks;
     const int32_t *context_lens;
+    int32_t max_ctx;           // context lengths are clamped to this and max_blocks * B
     int32_t S, Hq, Hkv, D, B;
     int64_t num_blocks;
     float scale;
     int32_t partition;         // tokens per partition (multiple of 64)
     int32_t max_parts;         // partitions per sequence in the grid
-    float *part_out;           // f32 [S, Hq, max_parts, D] (when max_parts > 1)
-    float *part_lse;           // f32 [S, Hq, max_parts]
-    int *counters;             // [S, Hkv] partitions finished; zero between calls
+    float *part_out;           // f32 [S, Hq, max_parts, D] (when max_parts > 1),
+                               //   [balanced_workgroups, Hq / Hkv, D] (balanced)
+    float *part_lse;           // f32 [S, Hq, max_parts] / [balanced_workgroups, Hq / Hkv]
+    int *counters;             // [S, Hkv] pieces finished; zero between calls
+    int32_t balanced_workgroups;  // > 0: balanced split over at most this many workgroups
+    int32_t num_cus;              // compute units of the device (balanced split)
 };
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);

@@ -40,6 +40,7 @@ _SIGS = {
     "pa_status_string": ([_i32], ctypes.c_char_p),
     "pa_reshape_and_cache": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp], _i32),
     "pa_decode_partition_tokens": ([_i32, _i32, _i32, _i32], _i32),
+    "pa_decode_uses_balanced_split": ([_i32, _i32, _i32, _i32], _i32),
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_paged_decode_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                               _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
@@ -163,6 +164,12 @@ def decode_partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: i
                             partition_tokens: int = 0) -> int:
     return int(library().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len,
                                                     partition_tokens))
+
+
+def decode_uses_balanced_split(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                               partition_tokens: int = 0) -> bool:
+    return bool(library().pa_decode_uses_balanced_split(num_seqs, num_kv_heads, max_context_len,
+                                                        partition_tokens))
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

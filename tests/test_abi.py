@@ -64,7 +64,8 @@ def _decode(lib, **kw):
     (dict(B=8), UNSUPPORTED),
     (dict(Hq=32, Hkv=1), UNSUPPORTED),                # group 32 > 16
     (dict(maxctx=(1 << 20) + 1, P=-1), UNSUPPORTED),
-    (dict(P=-2), INVALID),
+    (dict(P=-3), INVALID),
+    (dict(P=-2), WS_SMALL),                           # the balanced split needs a workspace
     (dict(maxctx=1000, P=128), WS_SMALL),             # 8 partitions need a workspace
     (dict(maxctx=1000, P=128, ws=FAKE, wsb=100), WS_SMALL),
 ])
@@ -80,6 +81,25 @@ def test_decode_workspace_sizes():
     assert pa.decode_partition_tokens(8, 4, 131072, 8192) == 4096
     assert pa.decode_partition_tokens(1, 1, 100000, -1) == 4096
     assert pa.decode_workspace_size(4, 4, 1, 128, 511, -1) == 0
+    # balanced split: counters [S, Hkv] + one partial per workgroup
+    # (at most four workgroups per compute unit; 256 CUs where no device is visible)
+    cus = 256
+    try:
+        import torch
+        if torch.cuda.is_available():
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+    except Exception:
+        pass
+    a256 = lambda n: (n + 255) // 256 * 256
+    nw = 4 * cus
+    assert pa.decode_workspace_size(64, 8, 1, 128, 2000, -2) == \
+        a256(64 * 4) + a256(nw * 8 * 128 * 4) + a256(nw * 8 * 4)
+    # auto: 64 x 8 partitions of 256 tokens fit in one wave of workgroups;
+    # 32 x 32 partitions of 4096 tokens do not
+    assert not pa.decode_uses_balanced_split(64, 1, 2000, 0)
+    assert pa.decode_uses_balanced_split(8, 4, 131072, 0)
+    assert pa.decode_uses_balanced_split(8, 4, 131072, -2)
+    assert not pa.decode_uses_balanced_split(8, 4, 131072, 2048)
     parts = 4  # 511 tokens in 128-token partitions
     a256 = lambda n: (n + 255) // 256 * 256
     want = a256(4 * 1 * 4) + a256(4 * 4 * parts * 128 * 4) + a256(4 * 4 * parts * 4)

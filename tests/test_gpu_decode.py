@@ -115,7 +115,7 @@ EDGE_LENS = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 0, 300, 51
     (128, 16, 4, 1), (128, 32, 8, 1), (64, 16, 2, 2), (64, 32, 16, 1),
     (128, 16, 3, 1), (128, 16, 12, 2), (128, 32, 64, 4), (128, 16, 5, 5),
 ])
-@pytest.mark.parametrize("partition", [-1, 64, 256])
+@pytest.mark.parametrize("partition", [-1, 64, 256, 0, -2])
 def test_decode_edges(orc, D, B, Hq, Hkv, partition):
     case = W.gqa_decode_case(f"edge_{D}_{B}_{Hq}_{Hkv}", 300 + D + B + Hq, EDGE_LENS, Hq=Hq,
                              Hkv=Hkv, D=D, block_size=B, partition_tokens=partition)
@@ -127,6 +127,44 @@ def test_decode_edges(orc, D, B, Hq, Hkv, partition):
     # the empty sequence: zero output, -inf lse
     s0 = EDGE_LENS.index(0)
     assert torch.all(out[s0] == 0) and torch.all(torch.isneginf(lse[s0]))
+
+
+def test_decode_balanced_many_sequences(orc):
+    """200 sequences (several 64-sequence scan windows of the balanced split),
+    lengths U[0, 700] with a run of empty ones: every output vs the oracle."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 701, size=200)
+    lens[50:60] = 0
+    case = W.gqa_decode_case("many", 305, lens.tolist(), Hq=8, Hkv=2, D=128, block_size=16)
+    say("decode balanced 200 sequences")
+    g = GpuGQA(case)
+    out, lse = g.decode(partition_tokens=-2)
+    ref_out, ref_lse = oracle_gqa(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what="balanced many sequences")
+
+
+def test_decode_balanced_more_units_than_waves(orc):
+    """1100 sequences x 4 kv heads: more (sequence, kv head) units than the
+    grid has workgroups, so every unit is one piece and workgroups take several."""
+    rng = np.random.default_rng(78)
+    lens = rng.integers(0, 120, size=1100)
+    case = W.gqa_decode_case("units", 306, lens.tolist(), Hq=8, Hkv=4, D=64, block_size=32)
+    say("decode balanced 1100 sequences x 4 kv heads")
+    g = GpuGQA(case)
+    out, lse = g.decode(partition_tokens=-2)
+    ref_out, ref_lse = oracle_gqa(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what="balanced, units > workgroups")
+
+
+def test_decode_balanced_matches_partitioned():
+    case = W.qwen3_decode(S=16)
+    g = GpuGQA(case)
+    o1, l1 = g.decode(partition_tokens=-2)
+    o2, l2 = g.decode(partition_tokens=256)
+    torch.cuda.synchronize()
+    d = (o1.float() - o2.float()).abs().max().item()
+    say(f"  balanced vs 256-token partitions: {d:.3e}")
+    assert d <= 1e-2 and (l1 - l2).abs().max().item() <= 1e-4
 
 
 def test_decode_block_permutation_bitexact():
@@ -181,11 +219,12 @@ def test_decode_long_context_sampled(orc):
     ref_out, ref_lse = oracle_gqa(orc, case, row_mask=mask)
     rows = np.nonzero(mask)
     assert_attn_close(out, lse, ref_out, ref_lse, rows=rows, what="long context sampled")
-    o2, l2 = g.decode(partition_tokens=8192)
-    torch.cuda.synchronize()
-    d = (out.float() - o2.float()).abs().max().item()
-    say(f"  P=2048 vs P=8192: {d:.3e}")
-    assert d <= 1e-2 and (lse - l2).abs().max().item() <= 1e-3
+    for P in (8192, -2):
+        o2, l2 = g.decode(partition_tokens=P)
+        torch.cuda.synchronize()
+        d = (out.float() - o2.float()).abs().max().item()
+        say(f"  P=2048 vs P={P}: {d:.3e}")
+        assert d <= 1e-2 and (lse - l2).abs().max().item() <= 1e-3
 
 
 def test_decode_rejects_bad_args():
