@@ -809,24 +809,27 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
 // P_u + n_u - 1 of [NW, Ga, D] and [NW, Ga]; the last to finish merges them
 // in piece order.
 
-// Inclusive prefix sum over the wave's lanes (Hillis-Steele over ds_bpermute).
+// Inclusive prefix sum over the wave's lanes: Hillis-Steele inside each
+// 16-lane row (DPP row shifts, zero shifted in), then row 1 and 3 add the
+// last lane of the row before (row_bcast:15) and rows 2 and 3 that of row 1
+// (row_bcast:31).
 __device__ __forceinline__ int wave_prefix_sum_i(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return v;
 }
 
 // Merge of a unit's piece partials (slots P_u .. P_u + nparts - 1, in that
-// order) into rows row0 .. row0 + Ga - 1: thread -> (head, 4 dims), 8
+// order) into rows row0 .. row0 + Ga - 1: thread -> (head, 4 dims), 16
 // partials per round trip.
 template <int D>
 __device__ __forceinline__ void merge_unit_partials(const DecodeParams &p, size_t row0, int Ga,
                                                     int P_u, int nparts, int NW) {
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const auto rs = coherent_rsrc(p.part_out, (uint32_t)NW * Ga * D * 4);
     for (int it = threadIdx.x; it < Ga * (D / 4); it += blockDim.x) {
         const int h = it / (D / 4), d0 = (it % (D / 4)) * 4;
@@ -936,6 +939,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
                 b = (int)((uint32_t)(k + 1) * (uint32_t)nsb / (uint32_t)n);
                 P_u = (int)(first + (int64_t)g * n);  // < NW when split
                 ctx = readlane_i32(ctx_l, i);
+                if (s >= p.S || n < 1 || g >= Hkv || (split && (int64_t)P_u + n > NW)) s = -1;
                 break;
             }
             base += readlane_i32(incl, 63);
