@@ -104,62 +104,68 @@ __device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32
 // partitions).  Rows row0 .. row0 + nrows - 1 of the output, each with
 // nparts partials of D floats at part_out[(row * max_parts + k) * D] and
 // LSEs at part_lse[row * max_parts + k].  Thread -> (row, DPT consecutive
-// dims); all partitions of a batch are fetched before any is used, so a
-// batch costs one memory round trip.  Partitions combine in index order, so
-// the result does not depend on which workgroup merges.  Partials are read
-// with device-coherent loads (they were written by other workgroups of the
-// same kernel).
+// dims, DPT a multiple of 4); all partitions of a batch are fetched before
+// any is used, so a batch costs one memory round trip.  Partitions combine
+// in index order, so the result does not depend on which workgroup merges.
+// Partials are read with device-coherent 16-byte loads (they were written by
+// other workgroups of the same kernel), addressed from the first row so the
+// offsets fit 32 bits.
 template <int D, int DPT, int BATCH>
 __device__ __forceinline__ void merge_partition_rows(const float *part_out, const float *part_lse,
                                                      int max_parts, uint16_t *outp, float *lse,
                                                      size_t row0, int nrows, int nparts) {
-    const int it = threadIdx.x;
-    if (it >= nrows * (D / DPT)) return;
-    const int h = it / (D / DPT), d0 = (it % (D / DPT)) * DPT;
-    const size_t row = row0 + h;
-    const float *pl = part_lse + row * max_parts;
-    const float *po = part_out + row * max_parts * D + d0;
-    float M = kNegInf, den = 0.f, o[DPT];
+    static_assert(DPT % 4 == 0, "16-byte partial loads");
+    const auto rs = coherent_rsrc(part_out + row0 * max_parts * D,
+                                  (uint32_t)nrows * max_parts * D * 4);
+    for (int it = threadIdx.x; it < nrows * (D / DPT); it += blockDim.x) {
+        const int h = it / (D / DPT), d0 = (it % (D / DPT)) * DPT;
+        const size_t row = row0 + h;
+        const float *pl = part_lse + row * max_parts;
+        float M = kNegInf, den = 0.f, o[DPT];
 #pragma unroll
-    for (int e = 0; e < DPT; e++) o[e] = 0.f;
-    for (int b = 0; b < nparts; b += BATCH) {
-        float L[BATCH], x[BATCH][DPT];
+        for (int e = 0; e < DPT; e++) o[e] = 0.f;
+        for (int b = 0; b < nparts; b += BATCH) {
+            float L[BATCH], x[BATCH][DPT];
 #pragma unroll
-        for (int u = 0; u < BATCH; u++) {
-            const int pu = b + u < nparts ? b + u : b;  // always an in-range address
-            L[u] = load_coherent(&pl[pu]);
+            for (int u = 0; u < BATCH; u++) {
+                const int pu = b + u < nparts ? b + u : b;  // always an in-range address
+                L[u] = load_coherent(&pl[pu]);
 #pragma unroll
-            for (int e = 0; e < DPT; e += 2) {
-                const float2 v = load_coherent2(&po[(size_t)pu * D + e]);
-                x[u][e] = v.x;
-                x[u][e + 1] = v.y;
+                for (int e = 0; e < DPT; e += 4) {
+                    const float4 v = load_coherent4(
+                        rs, (uint32_t)(((h * max_parts + pu) * D + d0 + e) * 4));
+                    x[u][e] = v.x;
+                    x[u][e + 1] = v.y;
+                    x[u][e + 2] = v.z;
+                    x[u][e + 3] = v.w;
+                }
             }
+#pragma unroll
+            for (int u = 0; u < BATCH; u++)
+                if (b + u >= nparts) L[u] = kNegInf;
+            float Mb = M;
+#pragma unroll
+            for (int u = 0; u < BATCH; u++) Mb = fmax_nc(Mb, L[u]);
+            const float Mr = Mb == kNegInf ? 0.f : Mb;
+            const float r = fast_exp2((M - Mr) * kLog2e);
+            den *= r;
+#pragma unroll
+            for (int e = 0; e < DPT; e++) o[e] *= r;
+#pragma unroll
+            for (int u = 0; u < BATCH; u++) {
+                const float w = fast_exp2((L[u] - Mr) * kLog2e);
+                den += w;
+#pragma unroll
+                for (int e = 0; e < DPT; e++) o[e] += w * x[u][e];
+            }
+            M = Mb;
         }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        uint32_t *out = reinterpret_cast<uint32_t *>(outp + row * D + d0);
 #pragma unroll
-        for (int u = 0; u < BATCH; u++)
-            if (b + u >= nparts) L[u] = kNegInf;
-        float Mb = M;
-#pragma unroll
-        for (int u = 0; u < BATCH; u++) Mb = fmax_nc(Mb, L[u]);
-        const float Mr = Mb == kNegInf ? 0.f : Mb;
-        const float r = fast_exp2((M - Mr) * kLog2e);
-        den *= r;
-#pragma unroll
-        for (int e = 0; e < DPT; e++) o[e] *= r;
-#pragma unroll
-        for (int u = 0; u < BATCH; u++) {
-            const float w = fast_exp2((L[u] - Mr) * kLog2e);
-            den += w;
-#pragma unroll
-            for (int e = 0; e < DPT; e++) o[e] += w * x[u][e];
-        }
-        M = Mb;
+        for (int e = 0; e < DPT; e += 2) out[e / 2] = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+        if (d0 == 0 && lse) lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint32_t *out = reinterpret_cast<uint32_t *>(outp + row * D + d0);
-#pragma unroll
-    for (int e = 0; e < DPT; e += 2) out[e / 2] = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
-    if (d0 == 0 && lse) lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
 }
 
 }  // namespace pa

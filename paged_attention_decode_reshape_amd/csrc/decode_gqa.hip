@@ -673,14 +673,14 @@ __device__ __forceinline__ void reset_state(float (&m)[G], float (&lsum)[G], flo
 template <int D, int G>
 struct WaveMergeLDS {
     float m[kWaves][G], l[kWaves][G];
-    float acc[kWaves][G][D];
+    __align__(16) float acc[kWaves][G][D];
 };
 
-// Merge the 4 waves' states in LDS; thread (head h, dim pair d) then calls
-// emit(h, d, o0, o1, L) with the normalised output of dims d, d + 1 and the
-// LSE (natural log).  Every row holds the same token weights, so a wave's
-// sum of weights is 4 x the row sum.  Ends with the workgroup synchronised
-// only before the emits: callers that reuse the LDS must synchronise again.
+// Merge the 4 waves' states in LDS; thread (head h, dims d .. d + 3) then
+// calls emit(h, d, o, L) with the normalised output o[0..3] and the LSE
+// (natural log).  Every row holds the same token weights, so a wave's sum
+// of weights is 4 x the row sum.  Ends with the workgroup synchronised only
+// before the emits: callers that reuse the LDS must synchronise again.
 template <int D, int G, typename Emit>
 __device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G> &sm, int Ga, const float (&m)[G],
                                             const float (&lsum)[G], const float (&acc)[G][D / 64],
@@ -699,24 +699,37 @@ __device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G> &sm, int Ga, cons
         for (int jj = 0; jj < DV; jj++) sm.acc[wave][h][lane + 64 * jj] = acc[h][jj];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < Ga * (D / 2); idx += blockDim.x) {
-        const int h = idx / (D / 2), d = 2 * (idx % (D / 2));
+    for (int idx = threadIdx.x; idx < Ga * (D / 4); idx += blockDim.x) {
+        const int h = idx / (D / 4), d = 4 * (idx % (D / 4));
         float M = kNegInf;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
         const float Mr = M == kNegInf ? 0.f : M;
-        float n0 = 0.f, n1 = 0.f, den = 0.f;
+        float o[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
             const float wt = fast_exp2(sm.m[w][h] - Mr);
-            n0 += wt * sm.acc[w][h][d];
-            n1 += wt * sm.acc[w][h][d + 1];
+            const float4 a = *reinterpret_cast<const float4 *>(&sm.acc[w][h][d]);
+            o[0] += wt * a.x;
+            o[1] += wt * a.y;
+            o[2] += wt * a.z;
+            o[3] += wt * a.w;
             den += wt * sm.l[w][h];
         }
         const float inv = den > 0.f ? 1.f / den : 0.f;
         const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
-        emit(h, d, n0 * inv, n1 * inv, L);
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] *= inv;
+        emit(h, d, o, L);
     }
+}
+
+// bf16 x 4 output store
+__device__ __forceinline__ void store_out4(uint16_t *dst, const float (&o)[4]) {
+    uint2 v;
+    v.x = pack_bf16x2(o[0], o[1]);
+    v.y = pack_bf16x2(o[2], o[3]);
+    *reinterpret_cast<uint2 *>(dst) = v;
 }
 
 // Counts one finished piece of a split unit; true in the one workgroup that
@@ -777,22 +790,25 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     attend_range<D, B, G, SUBS, true>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
 
     __shared__ WaveMergeLDS<D, G> sm;
-    merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, float o0, float o1, float L) {
-        const size_t orow = (size_t)s * p.Hq + (size_t)g * Ga + h;
+    const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
+    // partials of this unit's rows, addressed from its first row (32-bit offsets)
+    const auto prs = coherent_rsrc(p.part_out + row0 * p.max_parts * D,
+                                   (uint32_t)Ga * p.max_parts * D * 4);
+    merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, const float (&o)[4], float L) {
+        const size_t orow = row0 + h;
         if (nparts == 1) {
-            reinterpret_cast<uint32_t *>(out + orow * D)[d / 2] = pack_bf16x2(o0, o1);
+            store_out4(out + orow * D + d, o);
             if (d == 0 && p.lse) p.lse[orow] = L;
         } else {
-            store_coherent2(&p.part_out[(orow * p.max_parts + part) * D + d], o0, o1);
+            store_coherent4(prs, (uint32_t)(((h * p.max_parts + part) * D + d) * 4), o[0], o[1],
+                            o[2], o[3]);
             if (d == 0) store_coherent(&p.part_lse[orow * p.max_parts + part], L);
         }
     });
     if (nparts == 1) return;
     if (!count_finished(p.counters + (size_t)s * p.Hkv + g, nparts)) return;
-    constexpr int kDPT = G * D / 256 > 4 ? G * D / 256 : 4;
-    merge_partition_rows<D, kDPT, (kDPT > 4 ? 4 : 8)>(p.part_out, p.part_lse, p.max_parts, out,
-                                                      p.lse, (size_t)s * p.Hq + (size_t)g * Ga,
-                                                      Ga, nparts);
+    merge_partition_rows<D, 4, 16>(p.part_out, p.part_lse, p.max_parts, out, p.lse, row0, Ga,
+                                   nparts);
 }
 
 // Balanced split.  The grid has NW workgroups (as many as are resident at
@@ -956,13 +972,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
         attend_range<D, B, G, 1, true>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
 
         const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
-        merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, float o0, float o1, float L) {
+        const auto prs = coherent_rsrc(p.part_out + (size_t)v * Ga * D, (uint32_t)Ga * D * 4);
+        merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, const float (&o)[4], float L) {
             if (n == 1) {
-                reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(p.out) + (row0 + h) * D)[d / 2] =
-                    pack_bf16x2(o0, o1);
+                store_out4(reinterpret_cast<uint16_t *>(p.out) + (row0 + h) * D + d, o);
                 if (d == 0 && p.lse) p.lse[row0 + h] = L;
             } else {
-                store_coherent2(&p.part_out[((size_t)v * Ga + h) * D + d], o0, o1);
+                store_coherent4(prs, (uint32_t)((h * D + d) * 4), o[0], o[1], o[2], o[3]);
                 if (d == 0) store_coherent(&p.part_lse[(size_t)v * Ga + h], L);
             }
         });
@@ -974,7 +990,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
 
 template <int D, int B, int G>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
-    constexpr int kSubs = G >= 16 ? 2 : 4;
+    constexpr int kSubs = 1;  // waves take single sub-blocks in turn
     if (p.balanced_workgroups > 0) {
         // one wave of workgroups: as many as are resident together
         static const int per_cu = [] {
