@@ -66,8 +66,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--partition-tokens", type=int, default=None,
-                    help="GQA decode split: 0 auto, -2 balanced, > 0 fixed partitions, "
-                         "-1 unsplit (default: the workload's own)")
+                    help="decode split (GQA and MLA): 0 auto, -2 balanced, > 0 fixed "
+                         "partitions, -1 unsplit (default: the workload's own)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after the bench, run plain device copies of this many MiB (a known "
                          "byte count for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -297,14 +297,15 @@ def bench_mla(args, case, label):
     bt = torch.from_numpy(pg.block_table).to(dev)
     cl = torch.from_numpy(pg.lens).to(dev)
     max_ctx = int(pg.lens.max())
-    ws = torch.zeros(max(1, pa.mla_workspace_size(case.S, case.Hq, case.Dv, max_ctx, 0)),
+    P = 0 if args.partition_tokens is None else args.partition_tokens
+    ws = torch.zeros(max(1, pa.mla_workspace_size(case.S, case.Hq, case.Dv, max_ctx, P)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((case.S, case.Hq, case.Dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
 
     def decode(i):
         pa.mla_decode_attn(q, caches[i % pools], bt, cl, case.scale, max_ctx, v_dim=case.Dv,
-                           out=out, lse=lse, workspace=ws)
+                           partition_tokens=P, out=out, lse=lse, workspace=ws)
 
     def step(i):
         pa.reshape_and_cache(new_lat, None, caches[i % pools], None, new_slots,

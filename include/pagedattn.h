@@ -90,10 +90,11 @@ pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *valu
 
 /*
  * Split-KV partition length the decode entry points use for these
- * arguments: partition_tokens > 0 is rounded up to a multiple of 64;
- * 0 picks one from the work size (MLA decode; GQA decode uses the balanced
- * split instead, see pa_paged_decode_attn); -1 asks for as few partitions
- * as possible.  Partitions are capped at 4096 tokens.
+ * arguments when they use fixed partitions: partition_tokens > 0 is rounded
+ * up to a multiple of 64; 0 picks one from the work size; -1 asks for as few
+ * partitions as possible.  Partitions are capped at 4096 tokens.  (With 0
+ * the entry points may use the balanced split instead, see
+ * pa_decode_uses_balanced_split.)
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_context_len, int32_t partition_tokens);
@@ -151,7 +152,9 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
                                int64_t num_blocks, float scale, int32_t partition_tokens,
                                void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace pa_mla_decode_attn needs (0 if no split is needed). */
+/* Bytes of workspace pa_mla_decode_attn needs (0 if no split is needed).
+ * For partition_tokens 0 and -2 the size depends on the current device's
+ * compute-unit count. */
 size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,
                              int32_t max_context_len, int32_t partition_tokens);
 
@@ -165,7 +168,9 @@ size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_di
  *   (nullable).  query [num_seqs, num_q_heads, latent_dim] bf16.
  * kv_cache [num_blocks, block_size, latent_dim] bf16.
  * block_table, context_lens, max_context_len, partition_tokens, workspace:
- *   as for pa_paged_decode_attn.
+ *   as for pa_paged_decode_attn (with one kv head: the balanced split cuts
+ *   each sequence into 32-token-tile pieces; pa_decode_uses_balanced_split
+ *   with num_kv_heads = 1 tells which split the call uses).
  * Supported: latent_dim == 576, v_dim == 512, num_q_heads in 1..16,
  *   any block_size >= 1.
  */

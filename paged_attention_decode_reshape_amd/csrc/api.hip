@@ -238,8 +238,10 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
 size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,
                              int32_t max_context_len, int32_t partition_tokens) {
     if (num_seqs < 0 || num_q_heads < 1 || v_dim < 1 || max_context_len < 0 ||
-        partition_tokens < -1)
+        partition_tokens < kRequestBalanced)
         return 0;
+    if (decode_uses_balanced(num_seqs, 1, max_context_len, partition_tokens))
+        return plan_balanced(num_seqs, num_q_heads, 1, v_dim, balanced_workgroups()).total();
     Split sp = plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len, partition_tokens);
     return sp.total();
 }
@@ -252,7 +254,7 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
                              int32_t partition_tokens, void *workspace, size_t workspace_bytes,
                              void *stream) {
     if (num_seqs < 0 || num_q_heads < 1 || block_size < 1 || num_blocks < 1 ||
-        max_blocks_per_seq < 1 || max_context_len < 0 || partition_tokens < -1 ||
+        max_blocks_per_seq < 1 || max_context_len < 0 || partition_tokens < kRequestBalanced ||
         !isfinite(scale))
         return PA_ERR_INVALID_ARG;
     if (!out || !query || !kv_cache || !block_table || !context_lens) return PA_ERR_INVALID_ARG;
@@ -262,7 +264,12 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
     if (latent_dim != 576 || v_dim != 512 || num_q_heads > 16 || max_context_len > kMaxContext ||
         num_seqs > 65535 || num_blocks * (int64_t)block_size > 0x7fffffff)
         return PA_ERR_UNSUPPORTED;
-    Split sp = plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len, partition_tokens);
+    const bool balanced = decode_uses_balanced(num_seqs, 1, max_context_len, partition_tokens);
+    const int32_t cus = balanced ? device_cus() : 0;
+    const int32_t NW = kBalancedMaxPerCU * cus;
+    Split sp = balanced ? plan_balanced(num_seqs, num_q_heads, 1, v_dim, NW)
+                        : plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len,
+                                     partition_tokens);
     if (sp.total() > 0) {
         if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
@@ -283,12 +290,16 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
     p.B = block_size;
     p.num_blocks = num_blocks;
     p.scale = scale;
+    p.max_ctx = max_context_len;
     p.partition = sp.P;
     p.max_parts = sp.parts;
+    p.balanced_workgroups = NW;
+    p.num_cus = cus;
     char *ws = (char *)workspace;
-    p.counters = sp.parts > 1 ? (int *)ws : nullptr;
-    p.part_out = sp.parts > 1 ? (float *)(ws + sp.counter_bytes) : nullptr;
-    p.part_lse = sp.parts > 1 ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
+    const bool split = balanced || sp.parts > 1;
+    p.counters = split ? (int *)ws : nullptr;
+    p.part_out = split ? (float *)(ws + sp.counter_bytes) : nullptr;
+    p.part_lse = split ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
     return from_hip(launch_mla_decode(p, (hipStream_t)stream));
 }
 

@@ -54,11 +54,14 @@ struct MLAParams {
     int32_t S, Hq, Dl, Dv, B;
     int64_t num_blocks;
     float scale;
+    int32_t max_ctx;           // context lengths are clamped to this and max_blocks * B
     int32_t partition;
     int32_t max_parts;
-    float *part_out;           // f32 [S, Hq, max_parts, Dv]
-    float *part_lse;           // f32 [S, Hq, max_parts]
-    int *counters;             // [S] partitions finished; zero between calls
+    float *part_out;           // f32 [S, Hq, max_parts, Dv] / [balanced_workgroups, Hq, Dv]
+    float *part_lse;           // f32 [S, Hq, max_parts] / [balanced_workgroups, Hq]
+    int *counters;             // [S] pieces finished; zero between calls
+    int32_t balanced_workgroups;  // > 0: balanced split over at most this many workgroups
+    int32_t num_cus;              // compute units of the device (balanced split)
 };
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);

@@ -20,9 +20,12 @@
 //       resident (9 per head); one permlane swap adds the halves.
 //   PV  lane l: output dims 8l .. 8l + 7; per token one 16-byte LDS read,
 //       the weight taken from the token's lane with v_readlane, fp32 FMAs.
-// A sequence longer than one partition writes fp32 partials (normalised
-// output, LSE); the last workgroup of the sequence to finish merges them by
-// log-sum-exp in partition order.
+// Two ways to split the sequences over workgroups: fixed-length partitions
+// (one workgroup per (partition, sequence)) or the balanced split (a grid of
+// the resident workgroups, each sequence cut into pieces proportional to its
+// length, as for GQA decode).  A sequence split over several workgroups
+// writes fp32 partials (normalised output, LSE); the last workgroup of the
+// sequence to finish merges them by log-sum-exp in token order.
 #include <type_traits>
 
 #include "common.h"
@@ -45,8 +48,9 @@ constexpr int kRowVec = kDl / 8;          // 16-byte vectors per latent row (72)
 constexpr int kLoadVec = kTile * kRowVec / 256;  // vectors each thread loads per tile (9)
 constexpr int kMaxPartition = 4096;       // tokens per partition, at most
 
-__device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int B, int max_parts, int P) {
-    const int64_t cap = min((int64_t)max_blocks * B, (int64_t)max_parts * P);
+// context length limited to the host's bound and what the block table covers
+__device__ __forceinline__ int clamp_ctx(const MLAParams &p, int ctx) {
+    const int64_t cap = min((int64_t)p.max_blocks * p.B, (int64_t)p.max_ctx);
     return ctx < 0 ? 0 : ((int64_t)ctx > cap ? (int)cap : ctx);
 }
 
@@ -70,17 +74,21 @@ __device__ __forceinline__ float row_max16(float v) {
     return ord2f(k);
 }
 
-// Log-sum-exp merge of a sequence's partitions (in partition order), by the
-// workgroup that finished last: thread -> (head tid / 16, 16-byte vectors
-// v = 16 k + tid % 16, k < 8) of the partial rows; a batch of 4 partitions is
-// fetched before any is used.
-__device__ __forceinline__ void merge_mla_partitions(const MLAParams &p, int s, int nparts) {
+// Log-sum-exp merge of a sequence's partials (in token order), by the
+// workgroup that finished last.  Partial k of head h sits at
+// po + h * hs + k * ks (floats, rows of 512 stored as 16-byte vectors
+// v = 64 i + lane holding dims 8 lane + 4 i .. + 3) with its LSE at
+// pl + h * lhs + k * lks; `extent` floats from po are readable.  Thread ->
+// (head tid / 16, vectors 16 k + tid % 16, k < 8); 4 partials per round trip.
+__device__ __forceinline__ void merge_mla_partials(const MLAParams &p, int s, const float *po,
+                                                   size_t hs, size_t ks, uint32_t extent,
+                                                   const float *pl, size_t lhs, size_t lks,
+                                                   int nparts) {
     constexpr int kBatch = 4;
     const int h = threadIdx.x >> 4, c = threadIdx.x & 15;
     if (h >= p.Hq) return;
     const size_t row = (size_t)s * p.Hq + h;
-    const auto rs = coherent_rsrc(p.part_out + row * p.max_parts * kDv, p.max_parts * kDv * 4);
-    const float *pl = p.part_lse + row * p.max_parts;
+    const auto rs = coherent_rsrc(po, extent * 4);
     float M = kNegInf, den = 0.f, o[8][4];
 #pragma unroll
     for (int k = 0; k < 8; k++)
@@ -92,9 +100,10 @@ __device__ __forceinline__ void merge_mla_partitions(const MLAParams &p, int s, 
 #pragma unroll
         for (int u = 0; u < kBatch; u++) {
             const int pu = b + u < nparts ? b + u : b;  // always an in-range address
-            L[u] = load_coherent(&pl[pu]);
+            L[u] = load_coherent(&pl[h * lhs + pu * lks]);
+            const uint32_t base = (uint32_t)(h * hs + pu * ks);
 #pragma unroll
-            for (int k = 0; k < 8; k++) x[u][k] = load_coherent4(rs, (pu * kDv + 4 * (16 * k + c)) * 4);
+            for (int k = 0; k < 8; k++) x[u][k] = load_coherent4(rs, (base + 4 * (16 * k + c)) * 4);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; u++)
@@ -136,155 +145,148 @@ __device__ __forceinline__ void merge_mla_partitions(const MLAParams &p, int s, 
     if (c == 0 && p.lse) p.lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
 }
 
-__global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
-    const int part = blockIdx.x / p.S;
-    const int s = blockIdx.x - part * p.S;
-    const int P = p.partition;
-    const int start = part * P;
+struct MLASmem {
+    __align__(16) uint32_t tile[kTile * kRowDw];
+    // latent row of every token of the current window (-1: past the end or
+    // an out-of-range block id), resolved once per window so that the tile
+    // loop issues no dependent block-table reads
+    int32_t row[kMaxPartition];
+};
+
+// Query registers of the wave's heads (past num_q_heads: repeats of real
+// heads, not stored): slice k of head j, lane n of a row of half f holds
+// dword 144 f + 16 k + n of the head's query.
+__device__ __forceinline__ void mla_load_queries(const MLAParams &p, int s,
+                                                 uint32_t (&qreg)[kHPW][kSlices]) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int col = lane & 15;
-    const int hf = lane >> 5;  // QK: half of the latent row
-    const int tk = lane & 31;  // QK: token of the tile
-    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-
-    __shared__ __align__(16) uint32_t sm_tile[kTile * kRowDw];
-    // latent row of every token of the partition (-1: past the end or an
-    // out-of-range block id), resolved once so that the tile loop issues no
-    // dependent block-table reads
-    __shared__ int32_t sm_row[kMaxPartition];
-
-    const int ctx = clamp_ctx(as_const<int32_t>(p.context_lens)[s], p.max_blocks, p.B,
-                              p.max_parts, P);
-    if (start >= ctx) {
-        if (ctx == 0 && part == 0) {
-            // no keys: out = 0, lse = -inf
-            for (int idx = threadIdx.x; idx < p.Hq * kDv; idx += blockDim.x) {
-                out[((size_t)s * p.Hq + idx / kDv) * kDv + idx % kDv] = 0;
-                if (idx % kDv == 0 && p.lse) p.lse[(size_t)s * p.Hq + idx / kDv] = kNegInf;
-            }
-        }
-        return;
-    }
-    const int end = min(start + P, ctx);
-    const int nparts = (ctx + P - 1) / P;
-    const float sl2 = p.scale * kLog2e;
-
-    for (int i = threadIdx.x; i < end - start; i += blockDim.x) {
-        const int t = start + i;
-        const int b = p.block_table[(size_t)s * p.max_blocks + t / p.B];
-        sm_row[i] = b >= 0 && (int64_t)b < p.num_blocks ? b * p.B + t % p.B : -1;
-    }
-
-    // this wave's heads (past num_q_heads: repeats of real heads, not stored)
-    int head[kHPW];
-#pragma unroll
-    for (int j = 0; j < kHPW; j++) head[j] = (kHPW * wave + j) % p.Hq;
-    // query slice k of head j: lane n of a row of half f holds dword
-    // 144 f + 16 k + n of the head's query
-    uint32_t qreg[kHPW][kSlices];
+    const int lane = threadIdx.x & 63, col = lane & 15, hf = lane >> 5;
 #pragma unroll
     for (int j = 0; j < kHPW; j++) {
+        const int head = (kHPW * wave + j) % p.Hq;
         const uint32_t *qh = reinterpret_cast<const uint32_t *>(p.query) +
-                             ((size_t)s * p.Hq + head[j]) * (kDl / 2) + kHalfDw * hf + col;
+                             ((size_t)s * p.Hq + head) * (kDl / 2) + kHalfDw * hf + col;
 #pragma unroll
         for (int k = 0; k < kSlices; k++) qreg[j][k] = qh[16 * k];
     }
+}
 
-    // Tile loader: thread (wave w, lane) moves vectors (lane & 7) + 8 i of
-    // the latent row of tile token 8 w + (lane >> 3); tokens past the end
-    // (or with an out-of-range block id) become zero rows.
+// Attention of the wave's heads over tokens [start, end) of sequence s,
+// accumulated into (m, lsum, acc): windows of at most kMaxPartition tokens
+// whose latent rows are resolved into LDS, then 32-token tiles.
+__device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int s, int start,
+                                           int end, const uint32_t (&qreg)[kHPW][kSlices],
+                                           float (&m)[kHPW], float (&lsum)[kHPW],
+                                           float (&acc)[kHPW][8]) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int hf = lane >> 5;  // QK: half of the latent row
+    const int tk = lane & 31;  // QK: token of the tile
+    const float sl2 = p.scale * kLog2e;
     const uint4 *kv = reinterpret_cast<const uint4 *>(p.kv_cache);
     const int ld_tok = 8 * wave + (lane >> 3), ld_vec = lane & 7;
-    auto load_tile = [&](int t0, uint4 (&r)[kLoadVec]) {
-        const int t = t0 + ld_tok;
-        const int rowi = t < end ? sm_row[t - start] : -1;
-        const uint4 *src = kv + (size_t)(rowi < 0 ? 0 : rowi) * kRowVec + ld_vec;
-#pragma unroll
-        for (int i = 0; i < kLoadVec; i++)
-            r[i] = rowi < 0 ? make_uint4(0, 0, 0, 0) : src[8 * i];
-    };
-    auto store_tile = [&](const uint4 (&r)[kLoadVec]) {
-        uint4 *dst = reinterpret_cast<uint4 *>(&sm_tile[ld_tok * kRowDw]) + ld_vec;
-#pragma unroll
-        for (int i = 0; i < kLoadVec; i++) dst[8 * i] = r[i];
-    };
-    // validity of QK token tk of the tile starting at t0 (same test as the loader)
-    auto token_ok = [&](int t0) {
-        const int t = t0 + tk;
-        return t < end && sm_row[t - start] >= 0;
-    };
 
-    float m[kHPW], lsum[kHPW], acc[kHPW][8];
-#pragma unroll
-    for (int j = 0; j < kHPW; j++) {
-        m[j] = kNegInf;
-        lsum[j] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) acc[j][i] = 0.f;
-    }
-
-    __syncthreads();  // sm_row complete
-    uint4 next[kLoadVec];
-    load_tile(start, next);
-    for (int t0 = start; t0 < end; t0 += kTile) {
-        __syncthreads();  // the previous tile is no longer read
-        store_tile(next);
-        const bool tok_ok = token_ok(t0);
-        __syncthreads();
-        if (t0 + kTile < end) load_tile(t0 + kTile, next);
-
-        // QK: half f of the row of token tk against the wave's heads
-        float za[kHPW], zb[kHPW];
-#pragma unroll
-        for (int j = 0; j < kHPW; j++) za[j] = zb[j] = 0.f;
-        const uint4 *kr = reinterpret_cast<const uint4 *>(&sm_tile[tk * kRowDw + kHalfDw * hf]);
-#pragma unroll
-        for (int k = 0; k < kSlices; k++) {
-            const uint4 k0 = kr[4 * k], k1 = kr[4 * k + 1], k2 = kr[4 * k + 2], k3 = kr[4 * k + 3];
-#pragma unroll
-            for (int j = 0; j < kHPW; j++) qk16<false>(za[j], zb[j], qreg[j][k], k0, k1, k2, k3);
+    for (int w0 = start; w0 < end; w0 += kMaxPartition) {
+        const int wend = min(w0 + kMaxPartition, end);
+        __syncthreads();  // the previous window's rows and tile are no longer read
+        for (int i = threadIdx.x; i < wend - w0; i += blockDim.x) {
+            const int t = w0 + i;
+            const int b = p.block_table[(size_t)s * p.max_blocks + t / p.B];
+            sm.row[i] = b >= 0 && (int64_t)b < p.num_blocks ? b * p.B + t % p.B : -1;
         }
-        dpp_result_fence<kHPW>(za);
-        dpp_result_fence<kHPW>(zb);
-        // softmax: exact max of the tile, one rescale of the running state
-        float pw[kHPW];
+        // Tile loader: thread (wave w, lane) moves vectors (lane & 7) + 8 i of
+        // the latent row of tile token 8 w + (lane >> 3); tokens past the end
+        // (or with an out-of-range block id) become zero rows.
+        auto load_tile = [&](int t0, uint4 (&r)[kLoadVec]) {
+            const int t = t0 + ld_tok;
+            const int rowi = t < wend ? sm.row[t - w0] : -1;
+            const uint4 *src = kv + (size_t)(rowi < 0 ? 0 : rowi) * kRowVec + ld_vec;
 #pragma unroll
-        for (int j = 0; j < kHPW; j++) {
-            const float z = za[j] + zb[j];
-            const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z),
-                                                             false, false);
-            const float sc = tok_ok ? (__uint_as_float(zz[0]) + __uint_as_float(zz[1])) * sl2 : kNegInf;
-            const float rm = row_max16(sc);
-            const auto mm = __builtin_amdgcn_permlane16_swap(__float_as_uint(rm),
-                                                             __float_as_uint(rm), false, false);
-            const float mx = uniform_f(fmax_nc(__uint_as_float(mm[0]), __uint_as_float(mm[1])));
-            const float mn = fmax_nc(m[j], mx);
-            const float mref = mn == kNegInf ? 0.f : mn;
-            const float alpha = fast_exp2(m[j] - mref);
-            m[j] = mn;
-            pw[j] = fast_exp2(sc - mref);
-            lsum[j] = lsum[j] * alpha + pw[j];
+            for (int i = 0; i < kLoadVec; i++)
+                r[i] = rowi < 0 ? make_uint4(0, 0, 0, 0) : src[8 * i];
+        };
+        auto store_tile = [&](const uint4 (&r)[kLoadVec]) {
+            uint4 *dst = reinterpret_cast<uint4 *>(&sm.tile[ld_tok * kRowDw]) + ld_vec;
 #pragma unroll
-            for (int i = 0; i < 8; i++) acc[j][i] *= alpha;
-        }
-        // PV: dims 8 lane .. 8 lane + 7 of every token of the tile
-        const uint4 *vr = reinterpret_cast<const uint4 *>(sm_tile) + lane;
-        static_for<kTile>([&](auto t_c) {
-            constexpr int t = decltype(t_c)::value;
-            const uint4 v = vr[t * (kRowDw / 4)];
-            const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+            for (int i = 0; i < kLoadVec; i++) dst[8 * i] = r[i];
+        };
+        // validity of QK token tk of the tile starting at t0 (same test as the loader)
+        auto token_ok = [&](int t0) {
+            const int t = t0 + tk;
+            return t < wend && sm.row[t - w0] >= 0;
+        };
+
+        __syncthreads();  // rows complete
+        uint4 next[kLoadVec];
+        load_tile(w0, next);
+        for (int t0 = w0; t0 < wend; t0 += kTile) {
+            __syncthreads();  // the previous tile is no longer read
+            store_tile(next);
+            const bool tok_ok = token_ok(t0);
+            __syncthreads();
+            if (t0 + kTile < wend) load_tile(t0 + kTile, next);
+
+            // QK: half f of the row of token tk against the wave's heads
+            float za[kHPW], zb[kHPW];
+#pragma unroll
+            for (int j = 0; j < kHPW; j++) za[j] = zb[j] = 0.f;
+            const uint4 *kr = reinterpret_cast<const uint4 *>(&sm.tile[tk * kRowDw + kHalfDw * hf]);
+#pragma unroll
+            for (int k = 0; k < kSlices; k++) {
+                const uint4 k0 = kr[4 * k], k1 = kr[4 * k + 1], k2 = kr[4 * k + 2], k3 = kr[4 * k + 3];
+#pragma unroll
+                for (int j = 0; j < kHPW; j++) qk16<false>(za[j], zb[j], qreg[j][k], k0, k1, k2, k3);
+            }
+            dpp_result_fence<kHPW>(za);
+            dpp_result_fence<kHPW>(zb);
+            // softmax: exact max of the tile, one rescale of the running state
+            float pw[kHPW];
 #pragma unroll
             for (int j = 0; j < kHPW; j++) {
-                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[j]), t));
+                const float z = za[j] + zb[j];
+                const auto zz = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z),
+                                                                 false, false);
+                const float sc = tok_ok ? (__uint_as_float(zz[0]) + __uint_as_float(zz[1])) * sl2 : kNegInf;
+                const float rm = row_max16(sc);
+                const auto mm = __builtin_amdgcn_permlane16_swap(__float_as_uint(rm),
+                                                                 __float_as_uint(rm), false, false);
+                const float mx = uniform_f(fmax_nc(__uint_as_float(mm[0]), __uint_as_float(mm[1])));
+                const float mn = fmax_nc(m[j], mx);
+                const float mref = mn == kNegInf ? 0.f : mn;
+                const float alpha = fast_exp2(m[j] - mref);
+                m[j] = mn;
+                pw[j] = fast_exp2(sc - mref);
+                lsum[j] = lsum[j] * alpha + pw[j];
 #pragma unroll
-                for (int i = 0; i < 8; i++) acc[j][i] = __builtin_fmaf(w, vf[i], acc[j][i]);
+                for (int i = 0; i < 8; i++) acc[j][i] *= alpha;
             }
-        });
+            // PV: dims 8 lane .. 8 lane + 7 of every token of the tile
+            const uint4 *vr = reinterpret_cast<const uint4 *>(sm.tile) + lane;
+            static_for<kTile>([&](auto t_c) {
+                constexpr int t = decltype(t_c)::value;
+                const uint4 v = vr[t * (kRowDw / 4)];
+                const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+                for (int j = 0; j < kHPW; j++) {
+                    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[j]), t));
+#pragma unroll
+                    for (int i = 0; i < 8; i++) acc[j][i] = __builtin_fmaf(w, vf[i], acc[j][i]);
+                }
+            });
+        }
     }
+}
 
-    // every wave finishes its own heads (lanes 32-63 repeat the weights of 0-31)
+// Normalise the wave's heads and write them: as output rows (whole = true)
+// or as partials at po + h * hs (floats) with LSEs at pl + h * lhs.
+__device__ __forceinline__ void mla_emit(const MLAParams &p, int s, bool whole,
+                                         const float (&m)[kHPW], const float (&lsum)[kHPW],
+                                         const float (&acc)[kHPW][8], float *po, size_t hs,
+                                         float *pl, size_t lhs) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    // lanes 32-63 repeat the weights of 0-31
     float L[kHPW], inv[kHPW];
 #pragma unroll
     for (int j = 0; j < kHPW; j++) {
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
         const int h = kHPW * wave + j;
         if (h >= p.Hq) continue;
         const size_t orow = (size_t)s * p.Hq + h;
-        if (nparts == 1) {
+        if (whole) {
             uint4 o;
             o.x = pack_bf16x2(acc[j][0] * inv[j], acc[j][1] * inv[j]);
             o.y = pack_bf16x2(acc[j][2] * inv[j], acc[j][3] * inv[j]);
@@ -308,37 +310,193 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
         } else {
             // partial row stored as 16-byte vectors v = 64 i + lane (dims
             // 8 lane + 4 i .. + 3), so each store instruction writes 1 KB
-            const auto rs = coherent_rsrc(p.part_out + (orow * p.max_parts + part) * kDv, kDv * 4);
+            const auto rs = coherent_rsrc(po + h * hs, kDv * 4);
 #pragma unroll
             for (int i = 0; i < 2; i++)
                 store_coherent4(rs, (64 * i + lane) * 16, acc[j][4 * i] * inv[j],
                                 acc[j][4 * i + 1] * inv[j], acc[j][4 * i + 2] * inv[j],
                                 acc[j][4 * i + 3] * inv[j]);
-            if (lane == 0) store_coherent(&p.part_lse[orow * p.max_parts + part], L[j]);
+            if (lane == 0) store_coherent(&pl[h * lhs], L[j]);
         }
     }
-    if (nparts == 1) return;
+}
 
-    // The last workgroup of the sequence to finish merges all partitions
-    // (partials are written and read with device-coherent accesses; each
-    // thread waits for its stores to complete before one thread counts).
+// Counts one finished piece of sequence s; true in the workgroup that
+// finished last (which then merges).  Each thread first waits for its
+// partial stores to complete.  The last workgroup leaves the counter zero.
+__device__ __forceinline__ bool mla_count(const MLAParams &p, int s, int nparts) {
     __shared__ int sm_last;
     wait_stores();
     __syncthreads();
     int *counter = p.counters + s;
-    if (threadIdx.x == 0)
-        sm_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  nparts - 1;
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = prev == nparts - 1;
+        if (prev == nparts - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
-    if (!sm_last) return;
-    if (threadIdx.x == 0)  // leave the counter zero for the next call
-        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_mla_partitions(p, s, nparts);
+    return sm_last;
+}
+
+__device__ __forceinline__ void mla_write_empty(const MLAParams &p, int s) {
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    for (int idx = threadIdx.x; idx < p.Hq * kDv; idx += blockDim.x) {
+        out[((size_t)s * p.Hq + idx / kDv) * kDv + idx % kDv] = 0;
+        if (idx % kDv == 0 && p.lse) p.lse[(size_t)s * p.Hq + idx / kDv] = kNegInf;
+    }
+}
+
+__device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW], float (&acc)[kHPW][8]) {
+#pragma unroll
+    for (int j = 0; j < kHPW; j++) {
+        m[j] = kNegInf;
+        lsum[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[j][i] = 0.f;
+    }
+}
+
+// Fixed partitions: one workgroup per (partition, sequence).
+__global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
+    const int part = blockIdx.x / p.S;
+    const int s = blockIdx.x - part * p.S;
+    const int P = p.partition;
+    const int start = part * P;
+    __shared__ MLASmem sm;
+
+    const int ctx = clamp_ctx(p, as_const<int32_t>(p.context_lens)[s]);
+    if (start >= ctx) {
+        if (ctx == 0 && part == 0) mla_write_empty(p, s);
+        return;
+    }
+    const int end = min(start + P, ctx);
+    const int nparts = (ctx + P - 1) / P;
+    uint32_t qreg[kHPW][kSlices];
+    mla_load_queries(p, s, qreg);
+    float m[kHPW], lsum[kHPW], acc[kHPW][8];
+    mla_reset(m, lsum, acc);
+    mla_attend(p, sm, s, start, end, qreg, m, lsum, acc);
+    // partials [S, Hq, max_parts, Dv] and [S, Hq, max_parts]
+    float *po = p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
+    float *pl = p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
+    mla_emit(p, s, nparts == 1, m, lsum, acc, po, (size_t)p.max_parts * kDv, pl, p.max_parts);
+    if (nparts == 1) return;
+    if (!mla_count(p, s, nparts)) return;
+    merge_mla_partials(p, s, p.part_out + (size_t)s * p.Hq * p.max_parts * kDv,
+                       (size_t)p.max_parts * kDv, kDv, (uint32_t)p.Hq * p.max_parts * kDv,
+                       p.part_lse + (size_t)s * p.Hq * p.max_parts, p.max_parts, 1, nparts);
+}
+
+// Inclusive prefix sum over the wave's lanes: Hillis-Steele inside each
+// 16-lane row (DPP row shifts, zero shifted in), then rows 1 and 3 add the
+// last lane of the row before (row_bcast:15) and rows 2 and 3 that of row 1
+// (row_bcast:31).
+__device__ __forceinline__ int wave_prefix_sum_i(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Balanced split: NW resident workgroups; every non-empty sequence (U of
+// them, SB 32-token tiles in all) is cut into
+//   n_s = min(nsb_s, 1 + floor(nsb_s (NW - U) / SB))   pieces if U <= NW,
+// else one, numbered sequence-major; workgroup w takes piece w (+ NW, ...).
+// Pieces P_u .. P_u + n - 1 of a sequence leave partials in those slots of
+// [NW, Hq, Dv] and [NW, Hq]; the last to finish merges them in order.
+__global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p) {
+    const int NW = gridDim.x, w = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    __shared__ MLASmem sm;
+    auto ctx_of = [&](int s) { return s < p.S ? clamp_ctx(p, p.context_lens[min(s, p.S - 1)]) : 0; };
+    const int ctx_w0 = ctx_of(lane);
+    auto ctx_in = [&](int c0) { return c0 == 0 ? ctx_w0 : ctx_of(c0 + lane); };
+
+    for (int s = w; s < p.S; s += NW)
+        if (readlane_i32(ctx_in(s & ~63), s & 63) == 0) mla_write_empty(p, s);
+
+    // pass 1 (every wave): tiles and non-empty sequences
+    int64_t SB = 0;
+    int U = 0;
+    for (int c0 = 0; c0 < p.S; c0 += 64) {
+        const int nsb = (ctx_in(c0) + kTile - 1) / kTile;
+        SB += readlane_i32(wave_prefix_sum_i(nsb), 63);
+        U += __popcll(__ballot(nsb > 0));
+    }
+    if (U == 0) return;
+    const bool split = U <= NW;
+    // when split, SB <= NW * 2^15 and the arithmetic fits 32 bits
+    const uint32_t spare = split ? (uint32_t)(NW - U) : 0u, SB32 = split ? (uint32_t)SB : 1u;
+    auto pieces_of = [&](int nsb) -> int {
+        if (nsb == 0) return 0;
+        if (!split) return 1;
+        const uint32_t n = 1u + (uint32_t)nsb * spare / SB32;
+        return n < (uint32_t)nsb ? (int)n : nsb;
+    };
+
+    for (int64_t v = w; ; v += NW) {
+        // find piece v (every wave computes the same)
+        int s = -1, k = 0, n = 1, a = 0, b = 0, ctx = 0, P_u = 0;
+        int64_t base = 0;  // pieces of the sequences before window c0
+        for (int c0 = 0; c0 < p.S; c0 += 64) {
+            const int ctx_l = ctx_in(c0);
+            const int nsb_l = (ctx_l + kTile - 1) / kTile;
+            const int np_l = pieces_of(nsb_l);
+            const int incl = wave_prefix_sum_i(np_l);
+            const uint64_t past = __ballot(base + incl > v);
+            if (past) {
+                const int i = __builtin_ctzll(past);
+                n = readlane_i32(np_l, i);
+                const int nsb = readlane_i32(nsb_l, i);
+                const int64_t first = base + readlane_i32(incl, i) - n;
+                k = (int)(v - first);
+                s = c0 + i;
+                a = (int)((uint32_t)k * (uint32_t)nsb / (uint32_t)n);
+                b = (int)((uint32_t)(k + 1) * (uint32_t)nsb / (uint32_t)n);
+                P_u = (int)first;
+                ctx = readlane_i32(ctx_l, i);
+                if (s >= p.S || n < 1 || k >= n || (split && (int64_t)P_u + n > NW)) s = -1;
+                break;
+            }
+            base += readlane_i32(incl, 63);
+        }
+        if (s < 0) break;  // no piece left for this workgroup
+
+        uint32_t qreg[kHPW][kSlices];
+        mla_load_queries(p, s, qreg);
+        float m[kHPW], lsum[kHPW], acc[kHPW][8];
+        mla_reset(m, lsum, acc);
+        mla_attend(p, sm, s, a * kTile, min(b * kTile, ctx), qreg, m, lsum, acc);
+        mla_emit(p, s, n == 1, m, lsum, acc, p.part_out + (size_t)v * p.Hq * kDv, kDv,
+                 p.part_lse + (size_t)v * p.Hq, 1);
+        if (n > 1 && mla_count(p, s, n))
+            merge_mla_partials(p, s, p.part_out + (size_t)P_u * p.Hq * kDv, kDv,
+                               (size_t)p.Hq * kDv, (uint32_t)n * p.Hq * kDv,
+                               p.part_lse + (size_t)P_u * p.Hq, 1, p.Hq, n);
+        if (split) break;  // one piece per workgroup
+    }
 }
 
 }  // namespace
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream) {
+    if (p.balanced_workgroups > 0) {
+        // one wave of workgroups: as many as are resident together
+        static const int per_cu = [] {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, reinterpret_cast<const void *>(&mla_decode_balanced_kernel), 256, 0) !=
+                    hipSuccess || n < 1)
+                n = 1;
+            return n;
+        }();
+        const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
+        hipLaunchKernelGGL(mla_decode_balanced_kernel, dim3((unsigned)nw), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     const int64_t units = (int64_t)p.max_parts * p.S;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);

@@ -49,7 +49,7 @@ MLA_LENS = [1, 31, 32, 33, 0, 100, 257, 700]
 
 
 @pytest.mark.parametrize("Hq", [16, 3])
-@pytest.mark.parametrize("partition", [-1, 64, 0])
+@pytest.mark.parametrize("partition", [-1, 64, 0, -2])
 def test_mla_small(orc, Hq, partition):
     cases = W.mla_decode_cases("mla_small", 410 + Hq, S=len(MLA_LENS), lens_range=None,
                                lens=MLA_LENS, Hq=Hq, Dl=576, Dv=512, block_sizes=(1, 64, 5),
@@ -86,6 +86,32 @@ def test_mla_split_invariance():
     d = (o1.float() - o2.float()).abs().max().item()
     say(f"  mla split vs unsplit: {d:.3e}")
     assert d <= 1e-2 and (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_mla_balanced_matches_partitioned():
+    cases = W.mla_decode_cases("mla_bal", 423, S=12, lens_range=(100, 4000), Hq=16, Dl=576,
+                               Dv=512, block_sizes=(64,), scale=SCALE)
+    g = GpuMLA(cases[64])
+    o1, l1 = g.decode(partition_tokens=-2)
+    o2, l2 = g.decode(partition_tokens=256)
+    torch.cuda.synchronize()
+    d = (o1.float() - o2.float()).abs().max().item()
+    say(f"  mla balanced vs 256-token partitions: {d:.3e}")
+    assert d <= 1e-2 and (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_mla_balanced_more_sequences_than_workgroups(orc):
+    """1500 short sequences: more sequences than the balanced grid has
+    workgroups, so each is one piece and workgroups take several."""
+    rng = np.random.default_rng(424)
+    lens = rng.integers(0, 80, size=1500)
+    cases = W.mla_decode_cases("mla_many", 424, S=len(lens), lens_range=None, lens=lens.tolist(),
+                               Hq=4, Dl=576, Dv=512, block_sizes=(16,), scale=SCALE)
+    case = cases[16]
+    say("mla balanced 1500 sequences")
+    out, lse = GpuMLA(case).decode(partition_tokens=-2)
+    ref_out, ref_lse = oracle_mla(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what="mla balanced, sequences > workgroups")
 
 
 @pytest.mark.parametrize("B", [1, 64])
