@@ -47,6 +47,7 @@ constexpr int kSlices = kHalfDw / 16;     // 16-dword query slices per half (9)
 constexpr int kRowVec = kDl / 8;          // 16-byte vectors per latent row (72)
 constexpr int kLoadVec = kTile * kRowVec / 256;  // vectors each thread loads per tile (9)
 constexpr int kMaxPartition = 4096;       // tokens per partition, at most
+constexpr int kPVAhead = 2;               // P.V: tokens whose V rows are read ahead
 
 // context length limited to the host's bound and what the block table covers
 __device__ __forceinline__ int clamp_ctx(const MLAParams &p, int ctx) {
@@ -223,7 +224,6 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
             store_tile(next);
             const bool tok_ok = token_ok(t0);
             __syncthreads();
-            if (t0 + kTile < wend) load_tile(t0 + kTile, next);
 
             // QK: half f of the row of token tk against the wave's heads
             float za[kHPW], zb[kHPW];
@@ -259,11 +259,21 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
 #pragma unroll
                 for (int i = 0; i < 8; i++) acc[j][i] *= alpha;
             }
-            // PV: dims 8 lane .. 8 lane + 7 of every token of the tile
+            // the next tile's loads overlap P.V (issued after QK, so their
+            // registers are not live during QK)
+            if (t0 + kTile < wend) load_tile(t0 + kTile, next);
+            // PV: dims 8 lane .. 8 lane + 7 of every token of the tile; the
+            // LDS reads run kPVAhead tokens ahead of their use
             const uint4 *vr = reinterpret_cast<const uint4 *>(sm.tile) + lane;
+            uint4 vbuf[kPVAhead];
+            static_for<kPVAhead>([&](auto u_c) {
+                constexpr int u = decltype(u_c)::value;
+                vbuf[u] = vr[u * (kRowDw / 4)];
+            });
             static_for<kTile>([&](auto t_c) {
                 constexpr int t = decltype(t_c)::value;
-                const uint4 v = vr[t * (kRowDw / 4)];
+                const uint4 v = vbuf[t % kPVAhead];
+                if constexpr (t + kPVAhead < kTile) vbuf[t % kPVAhead] = vr[(t + kPVAhead) * (kRowDw / 4)];
                 const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
