@@ -169,30 +169,45 @@ __global__ __launch_bounds__(256, 2) void fa_kernel(FAParams p) {
     const uint16_t *vbase = reinterpret_cast<const uint16_t *>(p.v) + ((size_t)k0 * p.Hkv + g) * kD;
     const size_t kstride = (size_t)p.Hkv * kD;
 
-    for (int kt0 = 0; kt0 < nk_eff; kt0 += kBN) {
-        // K tile: 64 keys x 16 vectors, thread -> (key, vector), 16-byte LDS writes
+    // K and V of a tile go global -> registers -> LDS; the next tile's loads
+    // are issued right after the current tile is in LDS, so they overlap its
+    // math.  K: thread -> (key, vector) for 4 keys; V: thread -> (key pair,
+    // 8 dims) for 2 pairs (past the end: zeros, no memory access).
+    uint4 kreg[4], va[2], vb[2];
+    auto load_kv = [&](int kt0) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int idx = threadIdx.x + 256 * u, key = idx >> 4, c = idx & 15;
-            const uint4 v = kt0 + key < nk
-                                ? *reinterpret_cast<const uint4 *>(kbase + (size_t)(kt0 + key) * kstride + 8 * c)
-                                : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&sK[key * kKRow + 8 * c]) = v;
+            kreg[u] = kt0 + key < nk
+                          ? *reinterpret_cast<const uint4 *>(kbase + (size_t)(kt0 + key) * kstride + 8 * c)
+                          : make_uint4(0, 0, 0, 0);
         }
-        // V tile, transposed: thread -> (key pair, 8 dims); for each dim the
-        // pair's two values form one 4-byte LDS write
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int idx = threadIdx.x + 256 * u, pr = idx & 31, c = idx >> 5;
             const int key = 2 * pr;
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            const uint4 a = kt0 + key < nk
-                                ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(kt0 + key) * kstride + 8 * c)
-                                : z;
-            const uint4 b = kt0 + key + 1 < nk
-                                ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(kt0 + key + 1) * kstride + 8 * c)
-                                : z;
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+            va[u] = kt0 + key < nk
+                        ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(kt0 + key) * kstride + 8 * c)
+                        : make_uint4(0, 0, 0, 0);
+            vb[u] = kt0 + key + 1 < nk
+                        ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(kt0 + key + 1) * kstride + 8 * c)
+                        : make_uint4(0, 0, 0, 0);
+        }
+    };
+    // K rows as they are (16-byte LDS writes); V transposed: for each dim the
+    // key pair's two values form one 4-byte LDS write
+    auto store_kv = [&]() {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int idx = threadIdx.x + 256 * u, key = idx >> 4, c = idx & 15;
+            *reinterpret_cast<uint4 *>(&sK[key * kKRow + 8 * c]) = kreg[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int idx = threadIdx.x + 256 * u, pr = idx & 31, c = idx >> 5;
+            const int key = 2 * pr;
+            const uint32_t aw[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
+            const uint32_t bw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 const uint32_t lo = (aw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
@@ -200,7 +215,13 @@ __global__ __launch_bounds__(256, 2) void fa_kernel(FAParams p) {
                 *reinterpret_cast<uint32_t *>(&sVt[(8 * c + e) * kVRow + key]) = lo | (hi << 16);
             }
         }
+    };
+
+    load_kv(0);
+    for (int kt0 = 0; kt0 < nk_eff; kt0 += kBN) {
+        store_kv();
         __syncthreads();
+        load_kv(kt0 + kBN);
 
         // S^T = K Q^T for the two 32-key blocks of the tile
         f32x16_t s[2];
