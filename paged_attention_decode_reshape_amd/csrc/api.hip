@@ -363,18 +363,37 @@ pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
     return from_hip(launch_gather_chunk(gp, chunk_tokens, (hipStream_t)stream));
 }
 
+// Extend workspace: the group prefix [S + 1], the new tokens' V in 8-token
+// groups, and fp32 partials (output, LSE) for up to kExtendMaxPieces context
+// pieces of every (new token, q head).
+struct ExtendWorkspace {
+    size_t prefix, vsh, part_out, part_lse;
+    int32_t new_groups;
+    size_t total() const { return prefix + vsh + part_out + part_lse; }
+};
+
+static ExtendWorkspace extend_workspace(int32_t S, int32_t Tn, int32_t Hq, int32_t Hkv) {
+    ExtendWorkspace w;
+    w.new_groups = (Tn + 7) / 8 + S + 1;
+    w.prefix = align256((size_t)(S + 1) * sizeof(int32_t));
+    w.vsh = align256((size_t)Hkv * w.new_groups * 128 * 8 * 2);
+    w.part_out = align256((size_t)Tn * Hq * kExtendMaxPieces * 128 * sizeof(float));
+    w.part_lse = align256((size_t)Tn * Hq * kExtendMaxPieces * sizeof(float));
+    return w;
+}
+
 size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                 int32_t chunk_budget_tokens) {
     if (num_seqs < 1 || total_new_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
         head_dim < 1 || block_size < 1 || chunk_budget_tokens < 1)
         return 0;
-    const int64_t c = pa_extend_chunk_tokens(num_seqs, block_size, chunk_budget_tokens);
-    const size_t kv = align256((size_t)num_seqs * c * num_kv_heads * head_dim * 2);
-    const size_t run_o = align256((size_t)total_new_tokens * num_q_heads * head_dim * 4);
-    const size_t run_l = align256((size_t)total_new_tokens * num_q_heads * 4);
-    return 2 * kv + run_o + run_l;
+    return extend_workspace(num_seqs, total_new_tokens, num_q_heads, num_kv_heads).total();
 }
+
+// Pieces are sized so that the longest unit of work is about an eighth of
+// one workgroup slot's share of the whole call (2 workgroups per CU).
+constexpr int64_t kExtendPieceFraction = 8;
 
 pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const void *k_new,
                                  const void *v_new, const int32_t *query_start_loc,
@@ -396,86 +415,72 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
         !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lse, 4))
         return PA_ERR_INVALID_ARG;
-    if (head_dim != 128 || block_size % 8 != 0 || num_seqs > 65535 || num_q_heads > 65535)
+    if (head_dim != 128 || block_size % 16 != 0 || num_seqs > 65535 || num_q_heads > 65535)
         return PA_ERR_UNSUPPORTED;
-    // plan on the host copies: lengths, iterations, largest query / chunk extents
+    // plan on the host copies: lengths, the work per workgroup slot, pieces
     if (query_start_loc_host[0] != 0) return PA_ERR_INVALID_ARG;
-    int32_t max_new = 0, max_ctx = 0;
+    int32_t max_new = 0;
+    int64_t work = 0;  // 64-key tiles over all (request, q head, 128-row block)
     for (int32_t r = 0; r < num_seqs; r++) {
         const int32_t n = query_start_loc_host[r + 1] - query_start_loc_host[r];
         const int32_t c = context_lens_host[r];
         if (n < 0 || c < 0 || (int64_t)c > (int64_t)max_blocks_per_seq * block_size)
             return PA_ERR_INVALID_ARG;
+        if (c > kMaxContext) return PA_ERR_UNSUPPORTED;
         max_new = n > max_new ? n : max_new;
-        max_ctx = c > max_ctx ? c : max_ctx;
+        work += cdiv(n, 128) * num_q_heads * cdiv((int64_t)c + n, 64);
     }
     const int32_t total_new = query_start_loc_host[num_seqs];
-    const size_t need = pa_extend_workspace_size(num_seqs, total_new, num_q_heads, num_kv_heads,
-                                                 head_dim, block_size, chunk_budget_tokens);
-    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+    const ExtendWorkspace w = extend_workspace(num_seqs, total_new, num_q_heads, num_kv_heads);
+    if (!workspace || workspace_bytes < w.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
     if (total_new == 0) return PA_OK;
 
-    const int32_t c = pa_extend_chunk_tokens(num_seqs, block_size, chunk_budget_tokens);
-    const int32_t n_iter = (int32_t)cdiv(max_ctx, c);
-    char *ws = (char *)workspace;
-    const size_t kv = align256((size_t)num_seqs * c * num_kv_heads * head_dim * 2);
-    void *k_chunk = ws, *v_chunk = ws + kv;
-    float *run_o = (float *)(ws + 2 * kv);
-    float *run_l = (float *)(ws + 2 * kv + align256((size_t)total_new * num_q_heads * head_dim * 4));
-    hipStream_t st = (hipStream_t)stream;
-
-    FAParams f;
-    f.q = query;
-    f.q_start = query_start_loc;
-    f.context_lens = context_lens;
-    f.S = num_seqs;
-    f.Hq = num_q_heads;
-    f.Hkv = num_kv_heads;
-    f.scale = scale;
-    f.run_out = run_o;
-    f.run_lse = run_l;
-    f.out = out;
-    f.lse = lse;
-    // stage 1: causal attention of the new tokens over their own K / V
-    f.k = k_new;
-    f.v = v_new;
-    f.iteration = 0;
-    f.chunk = 0;
-    hipError_t e = launch_fa(f, max_new, true, 0, n_iter == 0, st);
-    if (e != hipSuccess) return PA_ERR_HIP;
-    // stage 2: context chunks, gathered to the standard layout, merged in
-    GatherParams gp;
-    gp.k_cache = k_cache;
-    gp.v_cache = v_cache;
-    gp.block_table = block_table;
-    gp.max_blocks = max_blocks_per_seq;
-    gp.context_lens = context_lens;
-    gp.S = num_seqs;
-    gp.Hkv = num_kv_heads;
-    gp.B = block_size;
-    gp.num_blocks = num_blocks;
-    gp.chunk = c;
-    gp.k_out = k_chunk;
-    gp.v_out = v_chunk;
-    f.k = k_chunk;
-    f.v = v_chunk;
-    f.chunk = c;
-    for (int32_t it = 0; it < n_iter; it++) {
-        int32_t max_len = 0;
-        for (int32_t r = 0; r < num_seqs; r++) {
-            const int64_t rest = (int64_t)context_lens_host[r] - (int64_t)it * c;
-            const int32_t len = rest <= 0 ? 0 : (rest < c ? (int32_t)rest : c);
-            max_len = len > max_len ? len : max_len;
-        }
-        gp.iteration = it;
-        if ((e = launch_gather_chunk(gp, max_len, st)) != hipSuccess) return PA_ERR_HIP;
-        f.iteration = it;
-        // stage 3 is the last iteration's merge, which writes the output
-        if ((e = launch_fa(f, max_new, false, 1, it == n_iter - 1, st)) != hipSuccess)
-            return PA_ERR_HIP;
+    int32_t c = pa_extend_chunk_tokens(num_seqs, block_size, chunk_budget_tokens);
+    if (c > kMaxContext) c = kMaxContext / block_size * block_size;
+    const int64_t slots = 2 * (int64_t)device_cus();
+    int64_t target = cdiv(cdiv(work, slots) * 64, kExtendPieceFraction);
+    target = cdiv(target < c ? c : target, c) * c;
+    if (target > kMaxContext) target = kMaxContext;
+    ExtendParams p;
+    p.chunk = c;
+    p.piece_target = (int32_t)target;
+    p.max_pieces = kExtendMaxPieces;
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
+    p.max_ctx = table_tokens < kMaxContext ? (int32_t)table_tokens : kMaxContext;
+    int64_t groups = 0;
+    for (int32_t r = 0; r < num_seqs; r++) {
+        int32_t len;
+        groups += (int64_t)extend_pieces(context_lens_host[r], p.piece_target, c, p.max_pieces,
+                                         &len) * num_kv_heads;
     }
-    return PA_OK;
+    char *ws = (char *)workspace;
+    p.q = query;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.group_prefix = (int32_t *)ws;
+    p.v_new_sh = ws + w.prefix;
+    p.new_groups = w.new_groups;
+    p.part_out = (float *)(ws + w.prefix + w.vsh);
+    p.part_lse = (float *)(ws + w.prefix + w.vsh + w.part_out);
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.q_start = query_start_loc;
+    p.context_lens = context_lens;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.B = block_size;
+    p.Tn = total_new;
+    p.q_blocks = (int32_t)cdiv(max_new, 128);
+    p.num_groups = (int32_t)groups;
+    p.scale = scale;
+    p.out = out;
+    p.lse = lse;
+    return from_hip(launch_extend(p, max_new, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,31 +1,42 @@
-// Chunked extend: context gather and MFMA tile attention with LSE merges.
+// Chunked extend: new query tokens attend to their request's cached context
+// (in the shuffled cache) and, causally, to themselves.
 //
-// The extend-path recipe of the "ROCm attention backends" blog: new query
-// tokens attend to their own new K/V (causal) and to the request's cached
-// context, which lives in the shuffled cache.  The context is processed in
-// chunks: each iteration gathers every request's next chunk from the
-// shuffled cache into the standard [tokens, kv_heads, head_dim] layout,
-// runs attention of the new queries over it without a mask, and merges the
-// result into the running one by log-sum-exp (merge_attn_states semantics).
+// The extend-path recipe of the "ROCm attention backends" blog processes
+// the context in chunks: each chunk's attention yields a partial output and
+// LSE, and merge_attn_states combines the partials and the new-token result.
+// The blog gathers each chunk out of the shuffled cache into the standard
+// [tokens, kv_heads, head_dim] layout first, because its attention kernel
+// cannot read the shuffled one.  On gfx950 the shuffled layout is already
+// the matrix-core operand layout (a K x-vector is 8 consecutive dims of one
+// token, a V x-vector 8 consecutive tokens of one dim), so here the
+// attention kernel reads the cache directly through the block table and the
+// gather (gather_chunk_kernel) remains a separate exported operation.
 //
-// gather_chunk_kernel  K vectors copy 16 bytes at a time; a V vector of the
-//   cache holds 8 tokens of one dim, so 8 of them (8 dims) are transposed
-//   in registers into 8 standard-layout vectors (8 dims of one token).
-// fa_kernel  flash attention on gfx950 MFMA (v_mfma_f32_32x32x16_bf16),
-//   head_dim 128, bf16 inputs, fp32 accumulation.  A workgroup takes 128
-//   query rows of one (request, q head), 32 per wave, and walks the keys 64
-//   at a time through LDS:
-//     S^T = K Q^T   (keys x queries): lane l owns query l % 32, so the
-//                   online softmax state of a query sits in one lane pair
-//                   (l, l + 32) and needs no shuffles beyond one swap;
+// extend_attn_kernel  flash attention on gfx950 MFMA
+//   (v_mfma_f32_32x32x16_bf16), head_dim 128, bf16 inputs, fp32
+//   accumulation.  A workgroup takes 128 query rows of one (request, q head)
+//   -- 32 per wave -- and one piece of the request's context: a run of whole
+//   chunks (pieces exist only to balance long contexts over the GPU).  The
+//   last piece also takes the request's new tokens with the causal mask.
+//   Keys go 64 at a time through double-buffered LDS tiles (the next tile is
+//   loaded into registers while the current one is used; one barrier per
+//   tile).  Per tile:
+//     S^T = K Q^T    (keys x queries): lane l owns query l % 32, so a
+//                    query's softmax state sits in one lane pair (l, l + 32);
 //     O^T += V^T P^T (dims x queries): P is split into bf16 hi + lo parts
-//                   (two MFMAs, ~2^-16 relative accuracy of the weights),
-//                   regrouped between the lane halves with v_permlane32_swap
-//                   into the MFMA operand layout; V^T is read from an LDS
-//                   tile that the workgroup writes transposed.
-//   The epilogue either writes the result, merges it into the running
-//   (output, LSE) state, or (last step) writes the bf16 output and LSE.
+//                    (two MFMAs, ~2^-16 relative accuracy of the weights),
+//                    regrouped between the lane halves with
+//                    v_permlane32_swap into the operand layout.
+//   The online softmax keeps a reference maximum that moves only when a
+//   score exceeds it by more than 8 (log2 units), so most tiles skip the
+//   rescale of the running sum and output.  A request with one piece writes
+//   its output and LSE directly; otherwise each piece writes an fp32 partial
+//   (output, LSE) and extend_merge_kernel combines them.
+// Workgroups are numbered so that the units sharing one (request, kv head,
+// piece) -- and so the same K/V tiles -- run together on one XCD (blocks
+// are dealt to the 8 XCDs round-robin) and share its L2.
 #include "common.h"
+#include "decode_common.h"
 #include "launch.h"
 
 namespace pa {
@@ -38,8 +49,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kD = 128;
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
-constexpr int kKRow = kD + 8;  // LDS K row stride in bf16 (272 bytes: conflict-free 16-byte reads)
-constexpr int kVRow = kBN + 8; // LDS V^T row stride in bf16 (144 bytes)
+constexpr int kKRow = 17;      // LDS K row stride in 16-byte vectors (272 bytes: conflict-free)
+constexpr int kXCDs = 8;
+constexpr float kLazyLog2 = 8.f;
 
 // Length of request r's context chunk in iteration `it` and its first row in
 // the gathered chunk (prefix over earlier requests); recomputed on the
@@ -116,35 +128,137 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// MODE 0: write the result as the running state; 1: merge it into the
-// running state; FINAL: write the bf16 output and LSE instead of the
-// running state.  HILO: P is split into bf16 hi + lo parts (two MFMAs per
-// step, ~2^-16 relative accuracy) for attention over few keys, where a
-// single bf16 rounding of a dominant weight would show in the output.
-template <bool CAUSAL, int MODE, bool FINAL, bool HILO>
-__global__ __launch_bounds__(256, 2) void fa_kernel(FAParams p) {
-    const int qb = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-    const int q0 = p.q_start[r];
-    const int nq = p.q_start[r + 1] - q0;
-    if (qb * kBM >= nq) return;
-    int k0, nk;
-    if (p.chunk > 0) {  // keys: this iteration's gathered context chunk
-        k0 = chunk_start(p.context_lens, r, p.iteration, p.chunk);
-        nk = chunk_len(p.context_lens, r, p.iteration, p.chunk);
-    } else {            // keys: the request's new tokens
-        k0 = q0;
-        nk = nq;
+// Raw buffer access: a descriptor of `bytes` bytes from `base`; a load past
+// the end returns zeros without touching memory (a 0-byte descriptor turns
+// every load into zeros).  0x00020000: gfx9 descriptor word 3, raw access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ext_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ext_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// The new tokens' V rearranged into the cache's 8-token groups:
+// v_new_sh[g][grp][d][0..8) holds dim d of request r's new tokens
+// 8 i .. 8 i + 7 at grp = q_start[r] / 8 + r + i (tokens past the request's
+// end are zero).  The groups of consecutive requests never overlap:
+// q_start[r + 1] / 8 + r + 1 >= q_start[r] / 8 + r + ceil(n_r / 8).
+// One workgroup per (8-token group, request); a thread transposes 8 tokens x
+// 8 dims of one kv head in registers.
+__global__ __launch_bounds__(256) void shuffle_new_v_kernel(ExtendParams p) {
+    const int r = blockIdx.y;
+    const int q0 = p.q_start[r], q1 = p.q_start[r + 1];
+    const int i8 = blockIdx.x * 8;
+    if (q0 < 0 || q1 > p.Tn || i8 >= q1 - q0) return;
+    const int nt = min(8, q1 - q0 - i8);
+    const int grp = q0 / 8 + r + (int)blockIdx.x;
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.v_new);
+    uint4 *dst = reinterpret_cast<uint4 *>(p.v_new_sh);
+    for (int it = threadIdx.x; it < p.Hkv * 16; it += blockDim.x) {
+        const int g = it >> 4, c = it & 15;
+        uint32_t w[8][4];  // w[t] = dims 8 c .. 8 c + 7 of token t, as bf16 pairs
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const uint4 v = t < nt ? src[((size_t)(q0 + i8 + t) * p.Hkv + g) * 16 + c]
+                                   : make_uint4(0, 0, 0, 0);
+            w[t][0] = v.x; w[t][1] = v.y; w[t][2] = v.z; w[t][3] = v.w;
+        }
+        uint4 *o = dst + ((size_t)g * p.new_groups + grp) * kD + 8 * c;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {  // dim 8 c + e: tokens 0..7 as 4 bf16 pairs
+            uint32_t d[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint32_t lo = (w[2 * k][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                const uint32_t hi = (w[2 * k + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                d[k] = lo | (hi << 16);
+            }
+            o[e] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
     }
-    const int g = h / (p.Hq / p.Hkv);
+}
+
+// Exclusive prefix over requests of pieces * Hkv (the workgroup groups of
+// each request), one workgroup, 256 requests per step.
+__global__ __launch_bounds__(256) void extend_plan_kernel(ExtendParams p) {
+    __shared__ int sc[256];
+    int carry = 0;
+    for (int base = 0; base < p.S; base += 256) {
+        const int r = base + threadIdx.x;
+        int v = 0;
+        if (r < p.S) {
+            int32_t len;
+            v = extend_pieces(min(p.context_lens[r], p.max_ctx), p.piece_target, p.chunk, p.max_pieces, &len) * p.Hkv;
+        }
+        sc[threadIdx.x] = v;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int add = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+            __syncthreads();
+            sc[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (r < p.S) p.group_prefix[r + 1] = carry + sc[threadIdx.x];
+        carry += sc[255];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) p.group_prefix[0] = 0;
+}
+
+// One 64-key tile staged in registers: wave w holds keys 16 w .. 16 w + 15
+// of the tile.  K: lane -> (key 16 w + lane % 16, x-vectors 4 u + lane / 16
+// for u = 0..3); V: lane -> (dim 64 (u % 2) + lane of the 8-token group
+// 2 w + u / 2).
+struct TileRegs {
+    uint4 k[4], v[4];
+};
+
+template <bool HILO>
+__global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
+    // workgroup -> (group j, unit u): the units of a group are consecutive
+    // blocks of one XCD
+    const int G = p.Hq / p.Hkv;
+    const int gs = G * p.q_blocks;
+    const int t = (int)(blockIdx.x / kXCDs);
+    const int j = (t / gs) * kXCDs + (int)(blockIdx.x % kXCDs);
+    if (j >= p.num_groups) return;
+    const int u = t % gs;
+    // request of group j: the last r with group_prefix[r] <= j
+    int lo = 0, hi = p.S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (__builtin_amdgcn_readfirstlane(p.group_prefix[mid]) <= j) lo = mid;
+        else hi = mid - 1;
+    }
+    const int r = lo;
+    const int local = j - __builtin_amdgcn_readfirstlane(p.group_prefix[r]);
+    const int piece = local / p.Hkv, g = local % p.Hkv;
+    const int qb = u / G, h = g * G + u % G;
+    const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[r]);
+    const int q1 = __builtin_amdgcn_readfirstlane(p.q_start[r + 1]);
+    const int nq = q1 - q0;
+    if (q0 < 0 || q1 > p.Tn || qb * kBM >= nq) return;
+    const int ctx = min(__builtin_amdgcn_readfirstlane(p.context_lens[r]), p.max_ctx);
+    int32_t plen;
+    const int npieces = extend_pieces(ctx, p.piece_target, p.chunk, p.max_pieces, &plen);
+    if (piece >= npieces) return;
+    // keys: context tokens [c0, c1), then (last piece) new tokens [0, nk_new)
+    const int c0 = piece * plen;
+    const int c1 = max(c0, min(ctx, c0 + plen));
+    const int n_ctx_tiles = (c1 - c0 + kBN - 1) / kBN;
+    const int nk_new = piece == npieces - 1 ? min(nq, (qb + 1) * kBM) : 0;
+    const int ntiles = n_ctx_tiles + (nk_new + kBN - 1) / kBN;
+
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int l32 = lane & 31, hl = lane >> 5;
+    const int l32 = lane & 31, hl = lane >> 5, l16 = lane & 15, l4 = lane >> 4;
     const int qi = qb * kBM + wave * 32 + l32;  // this lane's query, request-relative
     const bool q_ok = qi < nq;
     const size_t qrow = (size_t)q0 + (q_ok ? qi : 0);
 
-    __shared__ __align__(16) uint16_t sK[kBN * kKRow];
-    __shared__ __align__(16) uint16_t sVt[kD * kVRow];
+    __shared__ __align__(16) uint4 sK[2][kBN * kKRow];  // [key][x-vector], padded rows
+    __shared__ __align__(16) uint4 sV[2][8 * kD];    // [8-token group][dim]
 
     // Q^T operand for the 8 k-steps of head_dim: dims 16 ks + 8 hl .. + 7
     bf16x8_t qf[8];
@@ -163,130 +277,171 @@ __global__ __launch_bounds__(256, 2) void fa_kernel(FAParams p) {
     float m = kNegInf, lsum = 0.f;
     const float sl2 = p.scale * kLog2e;
 
-    // keys past the block's last query are never visible under the causal mask
-    const int nk_eff = CAUSAL ? min(nk, (qb + 1) * kBM + (nk - nq)) : nk;
-    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(p.k) + ((size_t)k0 * p.Hkv + g) * kD;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(p.v) + ((size_t)k0 * p.Hkv + g) * kD;
-    const size_t kstride = (size_t)p.Hkv * kD;
+    const int B = p.B;
+    const uint32_t k_ctx_off = (uint32_t)((l4 * B + l16) * 16);
+    const uint32_t k_new_off = (uint32_t)((l16 * p.Hkv * 16 + l4) * 16);
+    const uint32_t v_off = (uint32_t)(lane * 16);
+    const int gbase = q0 / 8 + r;        // first group of the request's new V
+    const int ngrp_r = (nq + 7) / 8;
 
-    // K and V of a tile go global -> registers -> LDS; the next tile's loads
-    // are issued right after the current tile is in LDS, so they overlap its
-    // math.  K: thread -> (key, vector) for 4 keys; V: thread -> (key pair,
-    // 8 dims) for 2 pairs (past the end: zeros, no memory access).
-    uint4 kreg[4], va[2], vb[2];
-    auto load_kv = [&](int kt0) {
+    TileRegs st;
+    auto load_tile = [&](int i) {
+        if (i < n_ctx_tiles) {
+            // context tokens tw .. tw + 15 lie in one cache block (B % 16 == 0)
+            const int tw = c0 + kBN * i + 16 * wave;
+            int blk = -1, o0 = 0;
+            if (tw < c1) {
+                const int bi = tw / B;
+                o0 = tw - bi * B;
+                blk = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)r * p.max_blocks + bi]);
+            }
+            const bool live = blk >= 0 && (int64_t)blk < p.num_blocks;
+            const size_t region = (size_t)(live ? blk : 0) * p.Hkv + g;  // (block, kv head)
+            const auto rk = ext_rsrc(reinterpret_cast<const char *>(p.k_cache) +
+                                         (region * 16 * B + o0) * 16,
+                                     live ? (uint32_t)((16 * B - o0) * 16) : 0u);
+            const auto rv = ext_rsrc(reinterpret_cast<const char *>(p.v_cache) +
+                                         (region * (B / 8) + o0 / 8) * (kD * 16),
+                                     live ? (uint32_t)(2 * kD * 16) : 0u);
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int idx = threadIdx.x + 256 * u, key = idx >> 4, c = idx & 15;
-            kreg[u] = kt0 + key < nk
-                          ? *reinterpret_cast<const uint4 *>(kbase + (size_t)(kt0 + key) * kstride + 8 * c)
-                          : make_uint4(0, 0, 0, 0);
-        }
+            for (int u4 = 0; u4 < 4; u4++) st.k[u4] = ext_load16(rk, k_ctx_off + u4 * 4 * B * 16);
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int idx = threadIdx.x + 256 * u, pr = idx & 31, c = idx >> 5;
-            const int key = 2 * pr;
-            va[u] = kt0 + key < nk
-                        ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(kt0 + key) * kstride + 8 * c)
-                        : make_uint4(0, 0, 0, 0);
-            vb[u] = kt0 + key + 1 < nk
-                        ? *reinterpret_cast<const uint4 *>(vbase + (size_t)(kt0 + key + 1) * kstride + 8 * c)
-                        : make_uint4(0, 0, 0, 0);
+            for (int u4 = 0; u4 < 4; u4++) st.v[u4] = ext_load16(rv, v_off + u4 * 64 * 16);
+        } else {
+            // new tokens tw .. tw + 15 (rows of k_new; groups of v_new_sh)
+            const int tw = kBN * (i - n_ctx_tiles) + 16 * wave;
+            const bool live = tw < nk_new;
+            const auto rk = ext_rsrc(reinterpret_cast<const char *>(p.k_new) +
+                                         ((size_t)(q0 + (live ? tw : 0)) * p.Hkv + g) * (kD * 2),
+                                     live ? (uint32_t)(((nq - tw - 1) * p.Hkv + 1) * kD * 2) : 0u);
+            const int gi = tw / 8;
+            const auto rv = ext_rsrc(reinterpret_cast<const char *>(p.v_new_sh) +
+                                         ((size_t)g * p.new_groups + gbase + (live ? gi : 0)) * (kD * 16),
+                                     live ? (uint32_t)(min(2, ngrp_r - gi) * kD * 16) : 0u);
+#pragma unroll
+            for (int u4 = 0; u4 < 4; u4++) st.k[u4] = ext_load16(rk, k_new_off + u4 * 64);
+#pragma unroll
+            for (int u4 = 0; u4 < 4; u4++) st.v[u4] = ext_load16(rv, v_off + u4 * 64 * 16);
         }
     };
-    // K rows as they are (16-byte LDS writes); V transposed: for each dim the
-    // key pair's two values form one 4-byte LDS write
-    auto store_kv = [&]() {
+    // registers -> LDS buffer b; context V past c1 (possibly uninitialised
+    // cache memory) is zeroed so that a zero weight cannot meet a NaN
+    auto store_tile = [&](int i, int b) {
+        if (i < n_ctx_tiles) {
+            const int tw = c0 + kBN * i + 16 * wave;
+            if (tw < c1 && tw + 16 > c1) {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int idx = threadIdx.x + 256 * u, key = idx >> 4, c = idx & 15;
-            *reinterpret_cast<uint4 *>(&sK[key * kKRow + 8 * c]) = kreg[u];
-        }
+                for (int u4 = 0; u4 < 4; u4++) {
+                    const int nv = c1 - (tw + 8 * (u4 >> 1));  // valid tokens of the group
+                    uint32_t w[4] = {st.v[u4].x, st.v[u4].y, st.v[u4].z, st.v[u4].w};
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int idx = threadIdx.x + 256 * u, pr = idx & 31, c = idx >> 5;
-            const int key = 2 * pr;
-            const uint32_t aw[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
-            const uint32_t bw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const uint32_t lo = (aw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                const uint32_t hi = (bw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                *reinterpret_cast<uint32_t *>(&sVt[(8 * c + e) * kVRow + key]) = lo | (hi << 16);
+                    for (int k2 = 0; k2 < 4; k2++)
+                        w[k2] &= (2 * k2 < nv ? 0xffffu : 0u) | (2 * k2 + 1 < nv ? 0xffff0000u : 0u);
+                    st.v[u4] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
             }
         }
+#pragma unroll
+        for (int u4 = 0; u4 < 4; u4++) sK[b][(16 * wave + l16) * kKRow + 4 * u4 + l4] = st.k[u4];
+#pragma unroll
+        for (int u4 = 0; u4 < 4; u4++) sV[b][wave * 256 + u4 * 64 + lane] = st.v[u4];
     };
 
-    load_kv(0);
-    for (int kt0 = 0; kt0 < nk_eff; kt0 += kBN) {
-        store_kv();
-        __syncthreads();
-        load_kv(kt0 + kBN);
-
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0, 0);
+        if (ntiles > 1) load_tile(1);
+    }
+    __syncthreads();
+    for (int i = 0; i < ntiles; i++) {
+        const int b = i & 1;
         // S^T = K Q^T for the two 32-key blocks of the tile
         f32x16_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
-            for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
-            const uint16_t *kr = &sK[(kb * 32 + l32) * kKRow + 8 * hl];
+            for (int e = 0; e < 16; e++) s[kb][e] = 0.f;
+            const uint4 *kr = &sK[b][(32 * kb + l32) * kKRow + hl];
 #pragma unroll
-            for (int ks = 0; ks < 8; ks++)
-                s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const uint4 *>(kr + 16 * ks)), qf[ks], s[kb]);
+            for (int ks = 0; ks < 8; ks++) s[kb] = mfma32(as_bf16x8(kr[2 * ks]), qf[ks], s[kb]);
         }
-        // s[kb][i]: key kt0 + 32 kb + 8 (i / 4) + 4 hl + i % 4 of query qi
+        // s[kb][e]: tile key 32 kb + 8 (e / 4) + 4 hl + e % 4 of query qi.
+        // Visible keys: tile keys below `lim` (context end; new tokens: the
+        // causal bound and the request's end).
+        int lim, wave_lim;
+        if (i < n_ctx_tiles) {
+            lim = wave_lim = c1 - (c0 + kBN * i);
+        } else {
+            const int kt0 = kBN * (i - n_ctx_tiles);
+            lim = min(qi + 1, nk_new) - kt0;
+            wave_lim = min(qb * kBM + wave * 32 + 1, nk_new) - kt0;  // the wave's first query
+        }
         float mx = kNegInf;
+        if (wave_lim >= kBN) {
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
+            for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int key = kt0 + 32 * kb + 8 * (i >> 2) + 4 * hl + (i & 3);
-                const bool vis = key < nk && (!CAUSAL || key <= qi + (nk - nq));
-                s[kb][i] = vis ? s[kb][i] * sl2 : kNegInf;
-                mx = fmax_nc(mx, s[kb][i]);
-            }
+                for (int e = 0; e < 16; e++) {
+                    s[kb][e] *= sl2;
+                    mx = fmax_nc(mx, s[kb][e]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int kl = 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
+                    s[kb][e] = kl < lim ? s[kb][e] * sl2 : kNegInf;
+                    mx = fmax_nc(mx, s[kb][e]);
+                }
+        }
         {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                              false, false);
             mx = fmax_nc(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        const float mn = fmax_nc(m, mx);
-        const float mref = mn == kNegInf ? 0.f : mn;
-        const float alpha = fast_exp2(m - mref);
-        m = mn;
-        lsum *= alpha;
+        // lazy reference maximum: moves only when a score passes it by more
+        // than 2^8, so weights stay <= 256
+        const bool grow = mx > m + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float mn = grow ? mx : m;
+            const float alpha = grow ? fast_exp2(m - mn) : 1.f;
+            m = mn;
+            lsum *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; db++)
+            for (int db = 0; db < 4; db++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) o[db][i] *= alpha;
-        // P^T as the B operand of O^T += V^T P^T: bf16 pairs (i, i + 1),
+                for (int e = 0; e < 16; e++) o[db][e] *= alpha;
+        }
+        const float mref = m == kNegInf ? 0.f : m;
+        // P^T as the B operand of O^T += V^T P^T: bf16 pairs (e, e + 1),
         // regrouped so that lane half 0 holds keys 0-7 and half 1 keys 8-15
         // of each 16-key step
         uint32_t pk[2][8], pl[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float a = fast_exp2(s[kb][2 * j] - mref), b = fast_exp2(s[kb][2 * j + 1] - mref);
-                pk[kb][j] = pack_bf16x2(a, b);
+            for (int jj = 0; jj < 8; jj++) {
+                const float a = fast_exp2(s[kb][2 * jj] - mref), c = fast_exp2(s[kb][2 * jj + 1] - mref);
+                pk[kb][jj] = pack_bf16x2(a, c);
                 if constexpr (HILO) {
-                    pl[kb][j] = pack_bf16x2(a - bf16_lo(pk[kb][j]), b - bf16_hi(pk[kb][j]));
-                    lsum += a + b;
+                    pl[kb][jj] = pack_bf16x2(a - bf16_lo(pk[kb][jj]), c - bf16_hi(pk[kb][jj]));
+                    lsum += a + c;
                 } else {
-                    lsum += bf16_lo(pk[kb][j]) + bf16_hi(pk[kb][j]);
+                    lsum += bf16_lo(pk[kb][jj]) + bf16_hi(pk[kb][jj]);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 8; j += 4) {
+            for (int jj = 0; jj < 8; jj += 4) {
 #pragma unroll
-                for (int jj = 0; jj < 2; jj++) {
-                    auto x = __builtin_amdgcn_permlane32_swap(pk[kb][j + jj], pk[kb][j + jj + 2], false, false);
-                    pk[kb][j + jj] = x[0];
-                    pk[kb][j + jj + 2] = x[1];
+                for (int j2 = 0; j2 < 2; j2++) {
+                    auto x = __builtin_amdgcn_permlane32_swap(pk[kb][jj + j2], pk[kb][jj + j2 + 2], false, false);
+                    pk[kb][jj + j2] = x[0];
+                    pk[kb][jj + j2 + 2] = x[1];
                     if constexpr (HILO) {
-                        auto y = __builtin_amdgcn_permlane32_swap(pl[kb][j + jj], pl[kb][j + jj + 2], false, false);
-                        pl[kb][j + jj] = y[0];
-                        pl[kb][j + jj + 2] = y[1];
+                        auto y = __builtin_amdgcn_permlane32_swap(pl[kb][jj + j2], pl[kb][jj + j2 + 2], false, false);
+                        pl[kb][jj + j2] = y[0];
+                        pl[kb][jj + j2 + 2] = y[1];
                     }
                 }
             }
@@ -294,22 +449,26 @@ __global__ __launch_bounds__(256, 2) void fa_kernel(FAParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-            for (int st = 0; st < 2; st++) {
-                const bf16x8_t pb = as_bf16x8(make_uint4(pk[kb][4 * st], pk[kb][4 * st + 1],
-                                                         pk[kb][4 * st + 2], pk[kb][4 * st + 3]));
+            for (int sp = 0; sp < 2; sp++) {
+                const bf16x8_t pb = as_bf16x8(make_uint4(pk[kb][4 * sp], pk[kb][4 * sp + 1],
+                                                         pk[kb][4 * sp + 2], pk[kb][4 * sp + 3]));
                 bf16x8_t pbl;
                 if constexpr (HILO)
-                    pbl = as_bf16x8(make_uint4(pl[kb][4 * st], pl[kb][4 * st + 1],
-                                               pl[kb][4 * st + 2], pl[kb][4 * st + 3]));
-                const int kk = 32 * kb + 16 * st + 8 * hl;
+                    pbl = as_bf16x8(make_uint4(pl[kb][4 * sp], pl[kb][4 * sp + 1],
+                                               pl[kb][4 * sp + 2], pl[kb][4 * sp + 3]));
+                // V^T operand: dims 32 db + l32, tokens of group 4 kb + 2 sp + hl
+                const uint4 *vr = &sV[b][(4 * kb + 2 * sp + hl) * kD + l32];
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
-                    const bf16x8_t va = as_bf16x8(
-                        *reinterpret_cast<const uint4 *>(&sVt[(32 * db + l32) * kVRow + kk]));
+                    const bf16x8_t va = as_bf16x8(vr[32 * db]);
                     o[db] = mfma32(va, pb, o[db]);
                     if constexpr (HILO) o[db] = mfma32(va, pbl, o[db]);
                 }
             }
+        if (i + 1 < ntiles) {
+            store_tile(i + 1, b ^ 1);
+            if (i + 2 < ntiles) load_tile(i + 2);
+        }
         __syncthreads();
     }
 
@@ -322,55 +481,50 @@ __global__ __launch_bounds__(256, 2) void fa_kernel(FAParams p) {
     const float L = lsum > 0.f ? (m + fast_log2(lsum)) * kLn2 : kNegInf;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (!q_ok) return;
-    // o[db][i]: dim 32 db + 8 (i / 4) + 4 hl + i % 4 of query qi
-    const size_t orow = qrow * p.Hq + h;
-    float *run_o = p.run_out + orow * kD;
-    float Lr = kNegInf, wr = 0.f, wn = 1.f, invd = inv;
-    if constexpr (MODE == 1) {
-        Lr = p.run_lse[orow];
-        const float M = fmax_nc(Lr, L);
-        const float Mr = M == kNegInf ? 0.f : M;
-        wr = fast_exp2((Lr - Mr) * kLog2e);
-        wn = fast_exp2((L - Mr) * kLog2e);
-        const float den = wr + wn;
-        const float id = den > 0.f ? 1.f / den : 0.f;
-        wr *= id;
-        wn *= id;
-        invd = inv * wn;
-        Lr = den > 0.f ? Mr + fast_log2(den) * kLn2 : kNegInf;
+    // o[db][e]: dim 32 db + 8 (e / 4) + 4 hl + e % 4 of query qi
+    const size_t row = qrow * p.Hq + h;
+    if (npieces == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const int d = 32 * db + 8 * (e >> 2) + 4 * hl;
+                uint2 w;
+                w.x = pack_bf16x2(o[db][e] * inv, o[db][e + 1] * inv);
+                w.y = pack_bf16x2(o[db][e + 2] * inv, o[db][e + 3] * inv);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + row * kD + d) = w;
+            }
+        if (hl == 0 && p.lse) p.lse[row] = L;
     } else {
-        Lr = L;
-    }
+        float *po = p.part_out + (row * p.max_pieces + piece) * kD;
 #pragma unroll
-    for (int db = 0; db < 4; db++)
+        for (int db = 0; db < 4; db++)
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            const int d = 32 * db + 8 * (i >> 2) + 4 * hl;
-            float4 v = make_float4(o[db][i] * invd, o[db][i + 1] * invd, o[db][i + 2] * invd,
-                                   o[db][i + 3] * invd);
-            if constexpr (MODE == 1) {
-                const float4 pr = *reinterpret_cast<const float4 *>(run_o + d);
-                v.x += wr * pr.x;
-                v.y += wr * pr.y;
-                v.z += wr * pr.z;
-                v.w += wr * pr.w;
+            for (int e = 0; e < 16; e += 4) {
+                const int d = 32 * db + 8 * (e >> 2) + 4 * hl;
+                *reinterpret_cast<float4 *>(po + d) =
+                    make_float4(o[db][e] * inv, o[db][e + 1] * inv, o[db][e + 2] * inv, o[db][e + 3] * inv);
             }
-            if constexpr (FINAL) {
-                uint2 b;
-                b.x = pack_bf16x2(v.x, v.y);
-                b.y = pack_bf16x2(v.z, v.w);
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + orow * kD + d) = b;
-            } else {
-                *reinterpret_cast<float4 *>(run_o + d) = v;
-            }
-        }
-    if (hl == 0) {
-        if constexpr (FINAL) {
-            if (p.lse) p.lse[orow] = Lr;
-        } else {
-            p.run_lse[orow] = Lr;
-        }
+        if (hl == 0) p.part_lse[row * p.max_pieces + piece] = L;
     }
+}
+
+// LSE merge of the pieces of split requests (merge_attn_states over n
+// parts): 8 (token, head) rows per workgroup, 4 dims per thread.
+__global__ __launch_bounds__(256) void extend_merge_kernel(ExtendParams p) {
+    const int r = blockIdx.y;
+    const int q0 = p.q_start[r], q1 = p.q_start[r + 1];
+    if (q0 < 0 || q1 > p.Tn || q1 <= q0) return;
+    int32_t plen;
+    const int npieces =
+        extend_pieces(min(p.context_lens[r], p.max_ctx), p.piece_target, p.chunk, p.max_pieces, &plen);
+    if (npieces < 2) return;
+    const int64_t rows = (int64_t)(q1 - q0) * p.Hq;
+    const int64_t first = (int64_t)blockIdx.x * 8;
+    if (first >= rows) return;
+    merge_partition_rows<kD, 4, kExtendMaxPieces>(
+        p.part_out, p.part_lse, p.max_pieces, reinterpret_cast<uint16_t *>(p.out), p.lse,
+        (size_t)q0 * p.Hq + first, (int)min<int64_t>(8, rows - first), npieces);
 }
 
 }  // namespace
@@ -382,22 +536,23 @@ hipError_t launch_gather_chunk(const GatherParams &p, int max_chunk_len, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_fa(const FAParams &p, int max_q_len, bool causal, int mode, bool final_,
-                     hipStream_t stream) {
-    if (max_q_len <= 0 || p.S <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((max_q_len + kBM - 1) / kBM), (unsigned)p.Hq, (unsigned)p.S);
-    // hi / lo weights everywhere: a single bf16 rounding of the weights
-    // misses the output tolerance when a few keys dominate (short contexts,
-    // the first causal rows, small chunks)
-#define PA_FA(C, M, F) hipLaunchKernelGGL((fa_kernel<C, M, F, true>), grid, dim3(256), 0, stream, p)
-    if (causal) {
-        if (mode == 0) { if (final_) PA_FA(true, 0, true); else PA_FA(true, 0, false); }
-        else { if (final_) PA_FA(true, 1, true); else PA_FA(true, 1, false); }
-    } else {
-        if (mode == 0) { if (final_) PA_FA(false, 0, true); else PA_FA(false, 0, false); }
-        else { if (final_) PA_FA(false, 1, true); else PA_FA(false, 1, false); }
-    }
-#undef PA_FA
+hipError_t launch_extend(const ExtendParams &p, int max_new, hipStream_t stream) {
+    if (max_new <= 0 || p.S <= 0 || p.num_groups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(extend_plan_kernel, dim3(1), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(shuffle_new_v_kernel, dim3((unsigned)((max_new + 7) / 8), (unsigned)p.S),
+                       dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t gs = (int64_t)(p.Hq / p.Hkv) * p.q_blocks;
+    const int64_t blocks = (int64_t)(p.num_groups + kXCDs - 1) / kXCDs * kXCDs * gs;
+    // hi / lo weights: a single bf16 rounding of the weights misses the
+    // output tolerance when a few keys dominate
+    hipLaunchKernelGGL(extend_attn_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t rows = (int64_t)max_new * p.Hq;
+    hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)((rows + 7) / 8), (unsigned)p.S),
+                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

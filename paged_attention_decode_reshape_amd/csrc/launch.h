@@ -81,24 +81,55 @@ struct GatherParams {
 
 hipError_t launch_gather_chunk(const GatherParams &p, int max_chunk_len, hipStream_t stream);
 
-struct FAParams {
+// Context pieces of one extend request: the context is cut into runs of
+// whole chunks, at most max_pieces runs of about `target` tokens each;
+// *piece_len receives the run length.  A request without context has one
+// empty piece, which carries its new tokens.  Host and device both call
+// this, so the grid and the kernels agree on the plan.  32-bit arithmetic:
+// callers keep ctx, target and chunk within [0, 2^20].
+__host__ __device__ inline int32_t extend_pieces(int32_t ctx, int32_t target, int32_t chunk,
+                                                 int32_t max_pieces, int32_t *piece_len) {
+    if (ctx <= 0) {
+        *piece_len = 0;
+        return 1;
+    }
+    int32_t n = (ctx + target - 1) / target;
+    n = n < 1 ? 1 : (n > max_pieces ? max_pieces : n);
+    int32_t len = (ctx + n - 1) / n;
+    len = (len + chunk - 1) / chunk * chunk;
+    *piece_len = len;
+    return (ctx + len - 1) / len;
+}
+
+constexpr int32_t kExtendMaxPieces = 4;
+
+struct ExtendParams {
     const void *q;             // bf16 [Tn, Hq, 128]
-    const void *k, *v;         // bf16 standard [rows, Hkv, 128]
-    const int32_t *q_start;    // [S + 1] query rows of request r
-    const int32_t *context_lens;  // chunk > 0: keys are the gathered chunk rows of request r
-    int32_t iteration, chunk;  // chunk == 0: keys are the request's new tokens (rows of q)
-    int32_t S, Hq, Hkv;
+    const void *k_new;         // bf16 [Tn, Hkv, 128]
+    const void *v_new;         // bf16 [Tn, Hkv, 128]
+    void *v_new_sh;            // bf16 [Hkv, new_groups, 128, 8]: new V in 8-token groups
+    int32_t new_groups;        // (Tn + 7) / 8 + S + 1; request r starts at group q_start[r] / 8 + r
+    const void *k_cache;       // shuffled [NB, Hkv, 16, B, 8]
+    const void *v_cache;       // shuffled [NB, Hkv, B / 8, 128, 8]
+    const int32_t *block_table;
+    int32_t max_blocks;
+    int64_t num_blocks;
+    const int32_t *q_start;    // [S + 1]
+    const int32_t *context_lens;  // [S]
+    int32_t *group_prefix;     // [S + 1]: workgroup groups before request r
+    int32_t S, Hq, Hkv, B, Tn;
+    int32_t chunk, piece_target, max_pieces;
+    int32_t max_ctx;           // context lengths are clamped to [0, max_ctx] (<= 2^20)
+    int32_t q_blocks;          // 128-row query blocks of the longest request
+    int32_t num_groups;        // sum over requests of pieces * Hkv
     float scale;
-    float *run_out;            // fp32 [Tn, Hq, 128] running output
-    float *run_lse;            // fp32 [Tn, Hq]
-    void *out;                 // bf16 [Tn, Hq, 128] (final step)
-    float *lse;                // fp32 [Tn, Hq] or null (final step)
+    float *part_out;           // f32 [Tn * Hq, max_pieces, 128] (split requests)
+    float *part_lse;           // f32 [Tn * Hq, max_pieces]
+    void *out;                 // bf16 [Tn, Hq, 128]
+    float *lse;                // f32 [Tn, Hq] or null
 };
 
-// mode 0: result -> running state; mode 1: merged into it.  final_: write
-// out / lse instead of the running state.
-hipError_t launch_fa(const FAParams &p, int max_q_len, bool causal, int mode, bool final_,
-                     hipStream_t stream);
+hipError_t launch_extend(const ExtendParams &p, int max_new, hipStream_t stream);
 
 hipError_t launch_merge_pair(void *out, float *out_lse, int out_f32, const void *a,
                              const float *a_lse, const void *b, const float *b_lse, int in_f32,
