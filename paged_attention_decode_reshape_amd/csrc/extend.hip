@@ -49,7 +49,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kD = 128;
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
-constexpr int kKRow = 17;      // LDS K row stride in 16-byte vectors (272 bytes: conflict-free)
 constexpr int kXCDs = 8;
 constexpr float kLazyLog2 = 8.f;
 
@@ -206,13 +205,27 @@ __global__ __launch_bounds__(256) void extend_plan_kernel(ExtendParams p) {
     if (threadIdx.x == 0) p.group_prefix[0] = 0;
 }
 
-// One 64-key tile staged in registers: wave w holds keys 16 w .. 16 w + 15
-// of the tile.  K: lane -> (key 16 w + lane % 16, x-vectors 4 u + lane / 16
-// for u = 0..3); V: lane -> (dim 64 (u % 2) + lane of the 8-token group
-// 2 w + u / 2).
-struct TileRegs {
-    uint4 k[4], v[4];
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4
+// ... lds): lane l's bytes land at lds + 16 l.  An instruction offset would
+// move the LDS address as well, so none is used.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, (int)voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt not waited for)
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS tiles of 64 keys, one per buffer (two buffers, distinct variables so
+// that the compiler can tell the tile being read from the one being loaded):
+//   K: [16-key run w][x-vector c][key w * 16 + o] (the cache block's own
+//      order), 16 bytes each; wave w loads run w.
+//   V: [8-token group][dim], 16 bytes (8 tokens of one dim) each; wave w
+//      loads groups 2 w, 2 w + 1.
+__shared__ __align__(16) uint4 ext_k0[kBN * 16];
+__shared__ __align__(16) uint4 ext_k1[kBN * 16];
+__shared__ __align__(16) uint4 ext_v0[8 * kD];
+__shared__ __align__(16) uint4 ext_v1[8 * kD];
 
 template <bool HILO>
 __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
@@ -257,16 +270,21 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
     const bool q_ok = qi < nq;
     const size_t qrow = (size_t)q0 + (q_ok ? qi : 0);
 
-    __shared__ __align__(16) uint4 sK[2][kBN * kKRow];  // [key][x-vector], padded rows
-    __shared__ __align__(16) uint4 sV[2][8 * kD];    // [8-token group][dim]
 
     // Q^T operand for the 8 k-steps of head_dim: dims 16 ks + 8 hl .. + 7
     bf16x8_t qf[8];
     {
         const uint4 *qp = reinterpret_cast<const uint4 *>(
             reinterpret_cast<const uint16_t *>(p.q) + (qrow * p.Hq + h) * kD) + hl;
+        // a negative scale is applied as -q with |scale| (exact), so that
+        // the softmax can take its maximum over raw scores
+        const uint32_t sign = p.scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-        for (int ks = 0; ks < 8; ks++) qf[ks] = as_bf16x8(q_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0));
+        for (int ks = 0; ks < 8; ks++) {
+            uint4 v = q_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0);
+            v.x ^= sign; v.y ^= sign; v.z ^= sign; v.w ^= sign;
+            qf[ks] = as_bf16x8(v);
+        }
     }
 
     f32x16_t o[4];
@@ -275,7 +293,9 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
 #pragma unroll
         for (int i = 0; i < 16; i++) o[db][i] = 0.f;
     float m = kNegInf, lsum = 0.f;
-    const float sl2 = p.scale * kLog2e;
+    // log2-domain scale, kept positive (a zero scale acts as 1e-30: the
+    // weights are then 1 to within 1e-25, the uniform average)
+    const float sl2 = fmaxf(fabsf(p.scale) * kLog2e, 1e-30f);
 
     const int B = p.B;
     const uint32_t k_ctx_off = (uint32_t)((l4 * B + l16) * 16);
@@ -284,17 +304,30 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
     const int gbase = q0 / 8 + r;        // first group of the request's new V
     const int ngrp_r = (nq + 7) / 8;
 
-    TileRegs st;
-    auto load_tile = [&](int i) {
+    // Block-table entries of the wave's context tokens, 64 tiles at a time:
+    // lane j of `win` holds the entry of tile win_base + j (-1: none).  The
+    // window is read only when no tile load is in flight, so waiting for it
+    // never waits for a tile, and the tile loop itself reads no table.
+    const int32_t *bt_row = p.block_table + (size_t)r * p.max_blocks;
+    int win = -1, win_base = 0;
+    auto fetch_window = [&](int base) {
+        const int ti = base + lane;
+        const int tw = c0 + kBN * ti + 16 * wave;
+        win = ti < n_ctx_tiles && tw < c1 ? bt_row[tw / B] : -1;
+        win_base = base;
+    };
+    auto tile_block = [&](int i) {
+        if (i - win_base >= 64) fetch_window(i);
+        return __builtin_amdgcn_readlane(win, i - win_base);
+    };
+    // tile i's K and V into LDS (kbuf, vbuf): lane l of load u fills vector
+    // slot 256 wave + 64 u + l of both
+    auto load_tile = [&](int i, int blk, uint4 *kbuf, uint4 *vbuf) {
+        uint4 *dk = kbuf + 256 * wave, *dv = vbuf + 256 * wave;
         if (i < n_ctx_tiles) {
             // context tokens tw .. tw + 15 lie in one cache block (B % 16 == 0)
             const int tw = c0 + kBN * i + 16 * wave;
-            int blk = -1, o0 = 0;
-            if (tw < c1) {
-                const int bi = tw / B;
-                o0 = tw - bi * B;
-                blk = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)r * p.max_blocks + bi]);
-            }
+            const int o0 = tw % B;
             const bool live = blk >= 0 && (int64_t)blk < p.num_blocks;
             const size_t region = (size_t)(live ? blk : 0) * p.Hkv + g;  // (block, kv head)
             const auto rk = ext_rsrc(reinterpret_cast<const char *>(p.k_cache) +
@@ -304,9 +337,9 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                                          (region * (B / 8) + o0 / 8) * (kD * 16),
                                      live ? (uint32_t)(2 * kD * 16) : 0u);
 #pragma unroll
-            for (int u4 = 0; u4 < 4; u4++) st.k[u4] = ext_load16(rk, k_ctx_off + u4 * 4 * B * 16);
+            for (int u4 = 0; u4 < 4; u4++) dma16(rk, dk + 64 * u4, k_ctx_off + u4 * 4 * B * 16);
 #pragma unroll
-            for (int u4 = 0; u4 < 4; u4++) st.v[u4] = ext_load16(rv, v_off + u4 * 64 * 16);
+            for (int u4 = 0; u4 < 4; u4++) dma16(rv, dv + 64 * u4, v_off + u4 * 64 * 16);
         } else {
             // new tokens tw .. tw + 15 (rows of k_new; groups of v_new_sh)
             const int tw = kBN * (i - n_ctx_tiles) + 16 * wave;
@@ -319,51 +352,52 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                                          ((size_t)g * p.new_groups + gbase + (live ? gi : 0)) * (kD * 16),
                                      live ? (uint32_t)(min(2, ngrp_r - gi) * kD * 16) : 0u);
 #pragma unroll
-            for (int u4 = 0; u4 < 4; u4++) st.k[u4] = ext_load16(rk, k_new_off + u4 * 64);
+            for (int u4 = 0; u4 < 4; u4++) dma16(rk, dk + 64 * u4, k_new_off + u4 * 64);
 #pragma unroll
-            for (int u4 = 0; u4 < 4; u4++) st.v[u4] = ext_load16(rv, v_off + u4 * 64 * 16);
+            for (int u4 = 0; u4 < 4; u4++) dma16(rv, dv + 64 * u4, v_off + u4 * 64 * 16);
         }
     };
-    // registers -> LDS buffer b; context V past c1 (possibly uninitialised
-    // cache memory) is zeroed so that a zero weight cannot meet a NaN
-    auto store_tile = [&](int i, int b) {
-        if (i < n_ctx_tiles) {
-            const int tw = c0 + kBN * i + 16 * wave;
-            if (tw < c1 && tw + 16 > c1) {
+    // once the wave's loads of tile i have landed: context V past c1
+    // (possibly uninitialised cache memory) is zeroed in the wave's own
+    // slots, so that a zero weight never meets a NaN
+    auto fix_tile = [&](int i, uint4 *vbuf) {
+        if (i >= n_ctx_tiles) return;
+        const int tw = c0 + kBN * i + 16 * wave;
+        if (tw >= c1 || tw + 16 <= c1) return;
 #pragma unroll
-                for (int u4 = 0; u4 < 4; u4++) {
-                    const int nv = c1 - (tw + 8 * (u4 >> 1));  // valid tokens of the group
-                    uint32_t w[4] = {st.v[u4].x, st.v[u4].y, st.v[u4].z, st.v[u4].w};
+        for (int u4 = 0; u4 < 4; u4++) {
+            const int nv = c1 - (tw + 8 * (u4 >> 1));  // valid tokens of the group
+            uint4 &slot = vbuf[256 * wave + 64 * u4 + lane];
+            uint4 v = slot;
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                    for (int k2 = 0; k2 < 4; k2++)
-                        w[k2] &= (2 * k2 < nv ? 0xffffu : 0u) | (2 * k2 + 1 < nv ? 0xffff0000u : 0u);
-                    st.v[u4] = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
+            for (int k2 = 0; k2 < 4; k2++)
+                w[k2] &= (2 * k2 < nv ? 0xffffu : 0u) | (2 * k2 + 1 < nv ? 0xffff0000u : 0u);
+            slot = make_uint4(w[0], w[1], w[2], w[3]);
         }
-#pragma unroll
-        for (int u4 = 0; u4 < 4; u4++) sK[b][(16 * wave + l16) * kKRow + 4 * u4 + l4] = st.k[u4];
-#pragma unroll
-        for (int u4 = 0; u4 < 4; u4++) sV[b][wave * 256 + u4 * 64 + lane] = st.v[u4];
     };
 
     if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0, 0);
-        if (ntiles > 1) load_tile(1);
+        fetch_window(0);
+        load_tile(0, tile_block(0), ext_k0, ext_v0);
+        wait_dma();
+        fix_tile(0, ext_v0);
     }
     __syncthreads();
-    for (int i = 0; i < ntiles; i++) {
-        const int b = i & 1;
+    // one tile: start loading tile i + 1 into the other buffers, attend to
+    // tile i, wait for tile i + 1 and meet at the barrier
+    auto step = [&](int i, const uint4 *sk, const uint4 *sv, uint4 *nk, uint4 *nv) {
+        if (i + 1 < ntiles) load_tile(i + 1, tile_block(i + 1), nk, nv);
         // S^T = K Q^T for the two 32-key blocks of the tile
         f32x16_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
             for (int e = 0; e < 16; e++) s[kb][e] = 0.f;
-            const uint4 *kr = &sK[b][(32 * kb + l32) * kKRow + hl];
+            // key 32 kb + l32 = run 2 kb + l32 / 16, position l32 % 16
+            const uint4 *kr = sk + (2 * kb + (l32 >> 4)) * 256 + 16 * hl + (l32 & 15);
 #pragma unroll
-            for (int ks = 0; ks < 8; ks++) s[kb] = mfma32(as_bf16x8(kr[2 * ks]), qf[ks], s[kb]);
+            for (int ks = 0; ks < 8; ks++) s[kb] = mfma32(as_bf16x8(kr[32 * ks]), qf[ks], s[kb]);
         }
         // s[kb][e]: tile key 32 kb + 8 (e / 4) + 4 hl + e % 4 of query qi.
         // Visible keys: tile keys below `lim` (context end; new tokens: the
@@ -376,22 +410,20 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
             lim = min(qi + 1, nk_new) - kt0;
             wave_lim = min(qb * kBM + wave * 32 + 1, nk_new) - kt0;  // the wave's first query
         }
+        // the maximum is taken over raw scores (sl2 > 0); hidden keys get -inf
         float mx = kNegInf;
         if (wave_lim >= kBN) {
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    s[kb][e] *= sl2;
-                    mx = fmax_nc(mx, s[kb][e]);
-                }
+                for (int e = 0; e < 16; e++) mx = fmax_nc(mx, s[kb][e]);
         } else {
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
                     const int kl = 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
-                    s[kb][e] = kl < lim ? s[kb][e] * sl2 : kNegInf;
+                    s[kb][e] = kl < lim ? s[kb][e] : kNegInf;
                     mx = fmax_nc(mx, s[kb][e]);
                 }
         }
@@ -399,6 +431,7 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                              false, false);
             mx = fmax_nc(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            mx = mx == kNegInf ? kNegInf : mx * sl2;
         }
         // lazy reference maximum: moves only when a score passes it by more
         // than 2^8, so weights stay <= 256
@@ -422,7 +455,8 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
         for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
             for (int jj = 0; jj < 8; jj++) {
-                const float a = fast_exp2(s[kb][2 * jj] - mref), c = fast_exp2(s[kb][2 * jj + 1] - mref);
+                const float a = fast_exp2(__builtin_fmaf(s[kb][2 * jj], sl2, -mref));
+                const float c = fast_exp2(__builtin_fmaf(s[kb][2 * jj + 1], sl2, -mref));
                 pk[kb][jj] = pack_bf16x2(a, c);
                 if constexpr (HILO) {
                     pl[kb][jj] = pack_bf16x2(a - bf16_lo(pk[kb][jj]), c - bf16_hi(pk[kb][jj]));
@@ -457,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                     pbl = as_bf16x8(make_uint4(pl[kb][4 * sp], pl[kb][4 * sp + 1],
                                                pl[kb][4 * sp + 2], pl[kb][4 * sp + 3]));
                 // V^T operand: dims 32 db + l32, tokens of group 4 kb + 2 sp + hl
-                const uint4 *vr = &sV[b][(4 * kb + 2 * sp + hl) * kD + l32];
+                const uint4 *vr = sv + (4 * kb + 2 * sp + hl) * kD + l32;
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
                     const bf16x8_t va = as_bf16x8(vr[32 * db]);
@@ -466,10 +500,14 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                 }
             }
         if (i + 1 < ntiles) {
-            store_tile(i + 1, b ^ 1);
-            if (i + 2 < ntiles) load_tile(i + 2);
+            wait_dma();
+            fix_tile(i + 1, nv);
         }
         __syncthreads();
+    };
+    for (int i = 0; i < ntiles; i += 2) {
+        step(i, ext_k0, ext_v0, ext_k1, ext_v1);
+        if (i + 1 < ntiles) step(i + 1, ext_k1, ext_v1, ext_k0, ext_v0);
     }
 
     // the lane pair (l, l + 32) holds the same query over different keys
