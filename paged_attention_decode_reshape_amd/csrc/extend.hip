@@ -23,10 +23,10 @@
 //   tile).  Per tile:
 //     S^T = K Q^T    (keys x queries): lane l owns query l % 32, so a
 //                    query's softmax state sits in one lane pair (l, l + 32);
+//                    the K rows are fed in a permuted order so that each
+//                    lane's scores are already in the P^T operand layout;
 //     O^T += V^T P^T (dims x queries): P is split into bf16 hi + lo parts
-//                    (two MFMAs, ~2^-16 relative accuracy of the weights),
-//                    regrouped between the lane halves with
-//                    v_permlane32_swap into the operand layout.
+//                    (two MFMAs, ~2^-16 relative accuracy of the weights).
 //   The online softmax keeps a reference maximum that moves only when a
 //   score exceeds it by more than 8 (log2 units), so most tiles skip the
 //   rescale of the running sum and output.  A request with one piece writes
@@ -394,12 +394,17 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
         for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
             for (int e = 0; e < 16; e++) s[kb][e] = 0.f;
-            // key 32 kb + l32 = run 2 kb + l32 / 16, position l32 % 16
-            const uint4 *kr = sk + (2 * kb + (l32 >> 4)) * 256 + 16 * hl + (l32 & 15);
+            // A-operand row l32 holds tile key 32 kb + pi(l32), pi swapping
+            // bits 2 and 3 (run 2 kb + l32 / 16 of the LDS tile); then the
+            // result rows a lane holds are 8 consecutive keys per 16-key
+            // step, the layout of the P^T operand, and no regrouping of P
+            // across lanes is needed
+            const int pr = (l32 & 3) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+            const uint4 *kr = sk + (2 * kb + (l32 >> 4)) * 256 + 16 * hl + pr;
 #pragma unroll
             for (int ks = 0; ks < 8; ks++) s[kb] = mfma32(as_bf16x8(kr[32 * ks]), qf[ks], s[kb]);
         }
-        // s[kb][e]: tile key 32 kb + 8 (e / 4) + 4 hl + e % 4 of query qi.
+        // s[kb][e]: tile key 32 kb + 16 (e / 8) + 8 hl + e % 8 of query qi.
         // Visible keys: tile keys below `lim` (context end; new tokens: the
         // causal bound and the request's end).
         int lim, wave_lim;
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
-                    const int kl = 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
+                    const int kl = 32 * kb + 16 * (e >> 3) + 8 * hl + (e & 7);
                     s[kb][e] = kl < lim ? s[kb][e] : kNegInf;
                     mx = fmax_nc(mx, s[kb][e]);
                 }
@@ -447,9 +452,8 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                 for (int e = 0; e < 16; e++) o[db][e] *= alpha;
         }
         const float mref = m == kNegInf ? 0.f : m;
-        // P^T as the B operand of O^T += V^T P^T: bf16 pairs (e, e + 1),
-        // regrouped so that lane half 0 holds keys 0-7 and half 1 keys 8-15
-        // of each 16-key step
+        // P^T as the B operand of O^T += V^T P^T: bf16 pairs (e, e + 1); lane
+        // half hl holds keys 8 hl .. 8 hl + 7 of each 16-key step
         uint32_t pk[2][8], pl[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
@@ -463,20 +467,6 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                     lsum += a + c;
                 } else {
                     lsum += bf16_lo(pk[kb][jj]) + bf16_hi(pk[kb][jj]);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < 8; jj += 4) {
-#pragma unroll
-                for (int j2 = 0; j2 < 2; j2++) {
-                    auto x = __builtin_amdgcn_permlane32_swap(pk[kb][jj + j2], pk[kb][jj + j2 + 2], false, false);
-                    pk[kb][jj + j2] = x[0];
-                    pk[kb][jj + j2 + 2] = x[1];
-                    if constexpr (HILO) {
-                        auto y = __builtin_amdgcn_permlane32_swap(pl[kb][jj + j2], pl[kb][jj + j2 + 2], false, false);
-                        pl[kb][jj + j2] = y[0];
-                        pl[kb][jj + j2 + 2] = y[1];
-                    }
                 }
             }
         }
