@@ -415,7 +415,8 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
     if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
         !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lse, 4))
         return PA_ERR_INVALID_ARG;
-    if (head_dim != 128 || block_size % 16 != 0 || num_seqs > 65535 || num_q_heads > 65535)
+    if (head_dim != 128 || (block_size != 16 && block_size != 32) || num_seqs > 65535 ||
+        num_q_heads > 65535)
         return PA_ERR_UNSUPPORTED;
     // plan on the host copies: lengths, the work per workgroup slot, pieces
     if (query_start_loc_host[0] != 0) return PA_ERR_INVALID_ARG;

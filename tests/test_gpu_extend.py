@@ -90,6 +90,22 @@ def test_extend_no_context(orc):
     assert_attn_close(out, lse, ref_out, ref_lse, what="extend without context")
 
 
+@pytest.mark.parametrize("block_size,budget", [(32, 256), (16, 1024), (32, 32768)])
+def test_extend_pieces_group3(orc, block_size, budget):
+    """12 q heads on 4 kv heads (group 3: 85 tokens x 3 heads per 256-row
+    workgroup, one row unused), contexts that are not multiples of the tile
+    or of 8, up to 4 context pieces per request merged by LSE, and a request
+    whose new tokens span three workgroups."""
+    case = W.extend_case("ext_g3", 606, ctx_lens=[5000, 17, 64, 1000, 0],
+                         new_tokens=[40, 3, 200, 1, 9], Hq=12, Hkv=4, D=128,
+                         block_size=block_size, chunk_budget_tokens=budget)
+    say(f"extend group 3, block {block_size}, budget {budget}")
+    g = GpuExtend(case)
+    out, lse = g.run()
+    ref_out, ref_lse = oracle_extend(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what=f"extend g3 B={block_size} budget {budget}")
+
+
 def test_extend_budget_invariance():
     case = W.extend_case("ext_inv", 604, ctx_lens=[1000, 3000], new_tokens=[64, 200], Hq=16,
                          Hkv=2, D=128, block_size=16)
