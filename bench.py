@@ -323,10 +323,13 @@ def bench_mla(args, case, label):
     dec_ms = time_launches(decode, min(args.steps, 200))
     algo = mla_algorithmic_bytes(case)
     flops = mla_algorithmic_flops(case)
+    # MLA picks its split like GQA decode with one unit per sequence
+    balanced = pa.decode_uses_balanced_split(case.S, 1, max_ctx, P)
     return {"value": case.S / (ms_per_step * 1e-3), "ms_per_step": ms_per_step,
             "decode_ms": dec_ms, "algo_bytes": algo, "algo_flops": flops,
             "hbm_gbps": algo / (dec_ms * 1e-3) / 1e9, "tflops": flops / (dec_ms * 1e-3) / 1e12,
-            "pools": pools}
+            "pools": pools,
+            "kernel": "mla_decode_balanced_kernel" if balanced else "mla_decode_kernel"}
 
 
 def cpu_baseline_mla(case, seconds):
@@ -404,8 +407,26 @@ def bench_extend(args, case, label):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ev_ms = time_launches(call, args.steps)
     flops = extend_algorithmic_flops(case)
+
+    # The context gather on its own (pa_gather_cache_chunk, the pages'
+    # cp_mha_gather_cache): one pass = every iteration of the chunk plan,
+    # each request's context copied out once (bytes read + written).
+    c = pa.extend_chunk_tokens(case.S, case.B, case.chunk_budget_tokens)
+    iters = -(-int(case.ctx_lens.max()) // c)
+    ko = torch.empty((case.S * c, case.Hkv, case.D), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+
+    def gather_pass(i):
+        for it in range(iters):
+            pa.gather_cache_chunk(kc, vc, bt, cl, it, c, k_out=ko, v_out=vo)
+
+    g_ms = time_launches(gather_pass, max(3, args.steps // 20))
+    g_bytes = int(case.ctx_lens.astype(np.int64).sum()) * case.Hkv * case.D * 2 * 2 * 2
     return {"value": Tn / (ms * 1e-3), "ms_per_step": ms, "call_ms": ev_ms, "algo_flops": flops,
-            "tflops": flops / (ev_ms * 1e-3) / 1e12}
+            "tflops": flops / (ev_ms * 1e-3) / 1e12,
+            "gather": {"kernel": "gather_chunk_kernel", "chunk_tokens": c, "iterations": iters,
+                       "ms_per_pass": g_ms, "algo_bytes_per_pass": g_bytes,
+                       "gbps": g_bytes / (g_ms * 1e-3) / 1e9}}
 
 
 def cpu_baseline_extend(case, seconds):
@@ -483,7 +504,7 @@ def main():
         line = base_line(args, r, workload)
         line["hbm_gbps"] = r["hbm_gbps"]
         line["pct_hbm_peak"] = 100.0 * r["hbm_gbps"] / HBM_PEAK_GBPS
-        line["roofline"] = {"bound": "alu", "kernel": "mla_decode_kernel", "achieved": r["tflops"],
+        line["roofline"] = {"bound": "alu", "kernel": r["kernel"], "achieved": r["tflops"],
                             "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": r["tflops"] / VALU_PEAK_TFLOPS, "traffic": None,
                             "algo_flops_per_launch": r["algo_flops"],
@@ -500,11 +521,12 @@ def main():
                     "q_heads": 64, "kv_heads": 4, "head_dim": 128, "block_size": 16,
                     "context_lens": "U[8192,40960]", "chunk_budget_tokens": case.chunk_budget_tokens}
         line = base_line(args, r, workload, unit="new tok/s")
-        line["roofline"] = {"bound": "mfma", "kernel": "fa_kernel (+ gather_chunk_kernel)",
+        line["roofline"] = {"bound": "mfma", "kernel": "extend_attn_kernel (+ plan, new-V shuffle, merge)",
                             "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS,
                             "traffic": None, "algo_flops_per_call": r["algo_flops"],
                             "avg_call_ms": r["call_ms"]}
+        line["gather_pass"] = r["gather"]
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_extend(case, args.cpu_seconds)
