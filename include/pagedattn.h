@@ -241,12 +241,14 @@ size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int3
  * query_start_loc[r] .. query_start_loc[r+1]; new token i attends to every
  * cached token and to new tokens 0..i.
  *
- * Stage 1: causal attention of the new tokens over k_new / v_new.
- * Stage 2: for each iteration, every request's next chunk of context
- *   (pa_extend_chunk_tokens tokens) is gathered from the shuffled cache to
- *   the standard [tokens, kv_heads, head_dim] layout in the workspace,
- *   attended without a mask, and merged into the running context result.
- * Stage 3: the context result is merged with the stage-1 result.
+ * The pages' three stages (new-token causal attention; per context chunk of
+ * pa_extend_chunk_tokens tokens, attention and a running LSE merge; a final
+ * merge) are computed as follows: the context is cut into at most 4 pieces
+ * of whole chunks; one pass per piece attends to the piece's chunks straight
+ * from the shuffled cache (no gather copy) and, for the last piece, then to
+ * the new tokens with the causal mask, all in one online softmax; a request
+ * with several pieces gets its pieces merged by LSE (merge_attn_states over
+ * n parts).  The result equals the three-stage recipe up to rounding order.
  *
  * out [total_new_tokens, num_q_heads, head_dim] bf16; lse
  *   [total_new_tokens, num_q_heads] f32 (nullable).
@@ -254,9 +256,15 @@ size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int3
  *   [total_new_tokens, num_kv_heads, head_dim] bf16.
  * query_start_loc [num_seqs + 1] int32 on the device and the same values in
  *   query_start_loc_host; context_lens [num_seqs] int32 on the device and
- *   the same values in context_lens_host (the host copies plan the chunk
- *   loop without a device read-back).
- * Supported: head_dim == 128, block_size in {16, 32}, group size 1..16.
+ *   the same values in context_lens_host (the host copies size the launch
+ *   without a device read-back; the kernels read the device copies and stay
+ *   in bounds if the two disagree).
+ * A block-table entry outside [0, num_blocks) reads as zero K and V.
+ * The workspace (pa_extend_workspace_size bytes, 256-byte aligned) holds the
+ *   plan, the new tokens' V regrouped into 8-token groups and the pieces'
+ *   fp32 partials; it needs no initialisation.
+ * Supported: head_dim == 128, block_size in {16, 32}, group size 1..16,
+ *   context lengths up to 2^20.
  */
 pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const void *k_new,
                                  const void *v_new, const int32_t *query_start_loc,

@@ -409,6 +409,7 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
         num_blocks < 1 || max_blocks_per_seq < 1 || chunk_budget_tokens < 1 || !isfinite(scale))
         return PA_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
     if (!out || !query || !k_new || !v_new || !query_start_loc || !query_start_loc_host ||
         !k_cache || !v_cache || !block_table || !context_lens || !context_lens_host)
         return PA_ERR_INVALID_ARG;
