@@ -6,12 +6,14 @@ One step is one decode step of the 64-request Qwen3-235B-shaped workload
 block_size 16, contexts U[1000,2000]):
   1. cache write of each request's new token into the shuffled KV cache,
   2. paged GQA decode attention over every request's whole context
-     (split-KV partitions + log-sum-exp merge).
-Steps rotate over several independent KV pools (like the layers of a
-model), together larger than the 256 MB Infinity Cache, so every step reads
-its KV from HBM.  The timed region replays a captured HIP graph of the
-steps; the decode kernels' own duration is measured with HIP events on the
-stream they are launched on.
+     (split-KV partitions + log-sum-exp merge),
+both in one launch (pa_paged_decode_attn_write; --separate-cache-write runs
+them as two launches).  Steps rotate over several independent KV pools
+(like the layers of a model), together larger than the 256 MB Infinity
+Cache, so every step reads its KV from HBM.  The timed region launches the
+steps eagerly (--graph-timing replays captured HIP graphs instead; a replay
+is also checked against the eager result); the decode kernel's own duration
+is measured with HIP events on the stream it is launched on.
 
 Prints one JSON line.  Other workloads: --config long_context | mla | extend.
 """
@@ -64,7 +66,12 @@ def parse():
     ap.add_argument("--pools", type=int, default=0, help="KV pool copies (0: enough to exceed the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph capture check")
+    ap.add_argument("--graph-timing", action="store_true",
+                    help="time GQA steps as HIP-graph replays instead of eager launches")
+    ap.add_argument("--separate-cache-write", action="store_true",
+                    help="GQA step as two launches (cache write, then decode) instead of the "
+                         "fused pa_paged_decode_attn_write")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="decode split (GQA and MLA): 0 auto, -2 balanced, > 0 fixed "
                          "partitions, -1 unsplit (default: the workload's own)")
@@ -82,14 +89,17 @@ def log(msg):
 # GQA decode workloads
 # ---------------------------------------------------------------------------
 
-def gqa_algorithmic_bytes(case) -> int:
+def gqa_algorithmic_bytes(case, with_write=False) -> int:
     """Bytes the method must move per decode launch: every context token's K
-    and V once, q, out, lse, the used block-table entries and lengths."""
+    and V once, q, out, lse, the used block-table entries and lengths (and,
+    with the fused cache write, each new token's K and V read and written
+    plus its slot)."""
     S, Hq, Hkv, D, B = case.S, case.Hq, case.Hkv, case.D, case.B
     n = case.context_lens.astype(np.int64)
     kv = int(n.sum()) * Hkv * D * 2 * 2
     blocks = int(((n + B - 1) // B).sum())
-    return kv + S * Hq * D * 2 * 2 + S * Hq * 4 + blocks * 4 + S * 4
+    write = S * Hkv * D * 2 * 2 * 2 + S * 8 if with_write else 0
+    return kv + S * Hq * D * 2 * 2 + S * Hq * 4 + blocks * 4 + S * 4 + write
 
 
 def gqa_algorithmic_flops(case) -> int:
@@ -149,14 +159,21 @@ def bench_gqa(args, case, label):
     lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    fused = not args.separate_cache_write
+
     def decode(i):
         kc, vc = caches[i % pools]
-        pa.paged_decode_attn(q, kc, vc, bt, cl, case.scale, max_ctx, partition_tokens=P,
-                             out=out, lse=lse, workspace=ws)
+        if fused:  # the new tokens' cache write inside the decode launch
+            pa.paged_decode_attn_write(q, new_k, new_v, new_slots, kc, vc, bt, cl, case.scale,
+                                       max_ctx, partition_tokens=P, out=out, lse=lse, workspace=ws)
+        else:
+            pa.paged_decode_attn(q, kc, vc, bt, cl, case.scale, max_ctx, partition_tokens=P,
+                                 out=out, lse=lse, workspace=ws)
 
     def step(i):
-        kc, vc = caches[i % pools]
-        pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots)
+        if not fused:
+            kc, vc = caches[i % pools]
+            pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots)
         decode(i)
 
     # eager reference for the graph check
@@ -179,8 +196,13 @@ def bench_gqa(args, case, label):
             graphs.append(g)
         torch.cuda.synchronize()
 
+    # A step is timed as eager launches unless asked otherwise: with the
+    # fused cache write the step is one launch, and a graph replay costs
+    # ~5 us more per step on this stack (25.0 vs 20.3 us measured).
+    replay = bool(graphs) and args.graph_timing
+
     def run(i):
-        if graphs:
+        if replay:
             graphs[i % pools].replay()
         else:
             step(i)
@@ -194,16 +216,18 @@ def bench_gqa(args, case, label):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # every replay recomputes pool 0's step output bit for bit
-    run(0 if not graphs else pools * 1000)
-    torch.cuda.synchronize()
-    graph_ok = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
+    # a graph replay recomputes pool 0's step output bit for bit
+    graph_ok = None
+    if graphs:
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        graph_ok = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
 
     # the decode kernel's own duration: HIP events on the launch stream around
     # back-to-back launches (rotating pools), averaged per launch
     dec_ms = time_launches(decode, min(args.steps, 400))
 
-    algo = gqa_algorithmic_bytes(case)
+    algo = gqa_algorithmic_bytes(case, with_write=fused)
     achieved = algo / (dec_ms * 1e-3) / 1e9
     tok_s = case.S / (ms_per_step * 1e-3)
     return {
@@ -216,6 +240,8 @@ def bench_gqa(args, case, label):
         "algo_bytes": algo,
         "algo_flops": gqa_algorithmic_flops(case),
         "pools": pools,
+        "cache_write": "fused" if fused else "separate launch",
+        "step_launch": "graph replay" if replay else "eager",
         "partition_tokens": ("balanced" if pa.decode_uses_balanced_split(case.S, case.Hkv, max_ctx, P)
                              else pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P)),
     }
@@ -486,14 +512,15 @@ def main():
         workload = {"workload": "qwen3_235b_tp8_decode_64req", "requests": 64, "q_heads": 8,
                     "kv_heads": 1, "head_dim": 128, "block_size": 16,
                     "context_lens": "U[1000,2000]", "kv_layout": "shuffled",
-                    "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"]}
+                    "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"],
+                    "cache_write": r["cache_write"], "step_launch": r["step_launch"]}
     elif args.config == "long_context":
         case = W.long_context_decode()
         r = bench_gqa(args, case, "long_context_decode")
         workload = {"workload": "long_context_gqa_decode_8req", "requests": 8, "q_heads": 64,
                     "kv_heads": 4, "head_dim": 128, "block_size": 16,
                     "context_lens": "U[32768,131072]", "kv_pool_copies": r["pools"],
-                    "partition_tokens": r["partition_tokens"]}
+                    "partition_tokens": r["partition_tokens"], "cache_write": r["cache_write"]}
     elif args.config in ("mla", "mla_bs1"):
         B = 1 if args.config == "mla_bs1" else 64
         case = W.deepseek_mla_decode(block_sizes=(B,))[B]
@@ -542,7 +569,8 @@ def main():
         "graph_replay_matches_eager": r["graph_replay_matches_eager"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel (partitions + fused merge)",
+            "kernel": ("paged_decode_kernel (partitions + fused merge"
+                       + (" + fused cache write)" if r["cache_write"] == "fused" else ")")),
             "achieved": r["hbm_gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

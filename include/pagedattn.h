@@ -152,6 +152,34 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
                                int64_t num_blocks, float scale, int32_t partition_tokens,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * A decode step in one launch: the cache write of each sequence's new token
+ * (reshape_and_cache; the blog's decode path writes the new token into the
+ * preshuffled cache, then attention reads the whole cache) fused into
+ * pa_paged_decode_attn.
+ *
+ * new_key, new_value [num_seqs, num_kv_heads, head_dim] bf16 (16-byte
+ *   aligned); slot_mapping [num_seqs] int64: sequence s's token goes to
+ *   slot slot_mapping[s] = block * block_size + offset, written exactly as
+ *   pa_reshape_and_cache writes it (bit for bit); a negative or out-of-pool
+ *   slot is skipped.  k_cache and v_cache are written.
+ * Every other argument, the workspace and the result are those of
+ *   pa_paged_decode_attn on the cache after the write, provided that
+ *   slot_mapping[s] is the slot of token context_lens[s] - 1 through the
+ *   block table (the usual decode step): the workgroup that reads that token
+ *   writes it first.  Another slot is written too, but a concurrent read of
+ *   it may see the old contents.
+ */
+pa_status pa_paged_decode_attn_write(void *out, float *lse, const void *query,
+                                     const void *new_key, const void *new_value,
+                                     const int64_t *slot_mapping, void *k_cache, void *v_cache,
+                                     const int32_t *block_table, int32_t max_blocks_per_seq,
+                                     const int32_t *context_lens, int32_t max_context_len,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                     float scale, int32_t partition_tokens, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace pa_mla_decode_attn needs (0 if no split is needed).
  * For partition_tokens 0 and -2 the size depends on the current device's
  * compute-unit count. */

@@ -22,5 +22,6 @@ from .ops import (  # noqa: F401
     mla_decode_attn,
     mla_workspace_size,
     paged_decode_attn,
+    paged_decode_attn_write,
     reshape_and_cache,
 )

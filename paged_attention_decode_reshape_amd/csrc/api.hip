@@ -172,13 +172,17 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
     return sp.total();
 }
 
-pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
-                               const void *v_cache, const int32_t *block_table,
-                               int32_t max_blocks_per_seq, const int32_t *context_lens,
-                               int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int64_t num_blocks, float scale, int32_t partition_tokens,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+// GQA decode, optionally with the fused cache write of each sequence's new
+// token (new_key / new_value / slot_mapping all null: no write).
+static pa_status decode_impl(void *out, float *lse, const void *query, const void *new_key,
+                             const void *new_value, const int64_t *slot_mapping,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float scale, int32_t partition_tokens, void *workspace,
+                             size_t workspace_bytes, void *stream) {
     if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
         num_blocks < 1 || max_context_len < 0 || partition_tokens < kRequestBalanced ||
         !isfinite(scale))
@@ -232,7 +236,41 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
     p.counters = split ? (int *)ws : nullptr;
     p.part_out = split ? (float *)(ws + sp.counter_bytes) : nullptr;
     p.part_lse = split ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
+    p.new_key = new_key;
+    p.new_value = new_value;
+    p.slot_mapping = slot_mapping;
     return from_hip(launch_paged_decode(p, (hipStream_t)stream));
+}
+
+pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float scale, int32_t partition_tokens,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_impl(out, lse, query, nullptr, nullptr, nullptr, k_cache, v_cache, block_table,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
+                       workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_decode_attn_write(void *out, float *lse, const void *query,
+                                     const void *new_key, const void *new_value,
+                                     const int64_t *slot_mapping, void *k_cache, void *v_cache,
+                                     const int32_t *block_table, int32_t max_blocks_per_seq,
+                                     const int32_t *context_lens, int32_t max_context_len,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                     float scale, int32_t partition_tokens, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (!new_key || !new_value || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!aligned(new_key, 16) || !aligned(new_value, 16) || !aligned(slot_mapping, 8))
+        return PA_ERR_INVALID_ARG;
+    return decode_impl(out, lse, query, new_key, new_value, slot_mapping, k_cache, v_cache,
+                       block_table, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                       partition_tokens, workspace, workspace_bytes, stream);
 }
 
 size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,

@@ -749,6 +749,40 @@ __device__ __forceinline__ bool count_finished(int *counter, int nparts) {
     return sm_last;
 }
 
+// Fused cache write (reshape_and_cache for one decode token, "ROCm
+// attention backends" blog, decode path: the new token is written into the
+// preshuffled cache before attention reads it): sequence s's key and value
+// for kv head g go to slot slot_mapping[s] = block * B + o, the key vector of
+// dims 8c..8c+7 to k_cache[block][g][c][o][0..8) and dim d of the value to
+// v_cache[block][g][o / 8][d][o % 8].  Threads 0..D/8-1 write the key,
+// D/8..2D/8-1 the value; the stores are complete and the workgroup has met at
+// a barrier before any wave reads the cache.  Called by every thread.
+template <int D, int B>
+__device__ __forceinline__ void write_new_token(const DecodeParams &p, int s, int g) {
+    constexpr int C = D / 8;
+    const int64_t slot = as_const<int64_t>(p.slot_mapping)[s];
+    if (slot >= 0 && slot < p.num_blocks * B && (int)threadIdx.x < 2 * C) {
+        const int t = threadIdx.x, c = t % C;
+        const int64_t blk = slot / B;
+        const int o = (int)(slot - blk * B);
+        const size_t row = ((size_t)s * p.Hkv + g) * C + c;
+        if (t < C) {
+            const uint4 kv = reinterpret_cast<const uint4 *>(p.new_key)[row];
+            uint4 *kc = reinterpret_cast<uint4 *>(const_cast<void *>(p.k_cache));
+            kc[(((size_t)blk * p.Hkv + g) * C + c) * B + o] = kv;
+        } else {
+            const uint4 vv = reinterpret_cast<const uint4 *>(p.new_value)[row];
+            uint16_t *vc = reinterpret_cast<uint16_t *>(const_cast<void *>(p.v_cache)) +
+                           ((((size_t)blk * p.Hkv + g) * (B / 8) + o / 8) * D + 8 * c) * 8 + o % 8;
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) vc[e * 8] = (uint16_t)(w[e / 2] >> ((e & 1) * 16));
+        }
+        wait_stores();
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ void write_empty(const DecodeParams &p, int s, int g, int Ga, int D) {
     uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
     for (int idx = threadIdx.x; idx < Ga * D; idx += blockDim.x) {
@@ -780,11 +814,16 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     load_queries<D, G>(p, s, g, Ga, qreg);
     const int ctx = clamp_ctx<B>(p, ctx_raw);
     if (start >= ctx) {
-        if (ctx == 0 && part == 0) write_empty(p, s, g, Ga, D);
+        if (ctx == 0 && part == 0) {
+            if (p.slot_mapping) write_new_token<D, B>(p, s, g);
+            write_empty(p, s, g, Ga, D);
+        }
         return;
     }
     const int end = min(start + P, ctx);
     const int nparts = (ctx + P - 1) / P;
+    // the partition holding the last token writes the new token first
+    if (p.slot_mapping && end == ctx) write_new_token<D, B>(p, s, g);
     float m[G], lsum[G], acc[G][DV];
     reset_state<G, DV>(m, lsum, acc);
     attend_range<D, B, G, SUBS, true>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
@@ -906,7 +945,10 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
     // empty sequences: workgroup s % NW writes out = 0, lse = -inf
     for (int s = w; s < p.S; s += NW)
         if (readlane_i32(ctx_in(s & ~63), s & 63) == 0)
-            for (int g = 0; g < Hkv; g++) write_empty(p, s, g, Ga, D);
+            for (int g = 0; g < Hkv; g++) {
+                if (p.slot_mapping) write_new_token<D, B>(p, s, g);
+                write_empty(p, s, g, Ga, D);
+            }
 
     // pass 1 (every wave): sub-blocks and non-empty sequences
     int64_t SBs = 0;
@@ -964,6 +1006,8 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
         if (v != w) __syncthreads();  // the LDS of the previous piece has been read
 
         const int tb = a * kSub, te = min(b * kSub, ctx);
+        // the piece holding the last token writes the new token first
+        if (p.slot_mapping && te == ctx) write_new_token<D, B>(p, s, g);
         const int bt_first = bt_entry<B, 1, true>(p, s, tb);
         uint32_t qreg[G];
         load_queries<D, G>(p, s, g, Ga, qreg);

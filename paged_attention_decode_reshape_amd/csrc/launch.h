@@ -39,6 +39,12 @@ struct DecodeParams {
     int *counters;             // [S, Hkv] pieces finished; zero between calls
     int32_t balanced_workgroups;  // > 0: balanced split over at most this many workgroups
     int32_t num_cus;              // compute units of the device (balanced split)
+    // Fused cache write (null slot_mapping: none): new_key / new_value
+    // [S, Hkv, D] bf16, sequence s's token goes to slot slot_mapping[s]
+    // (< 0: skipped) of the shuffled caches, written by the workgroup that
+    // reads the sequence's last token before it reads it.
+    const void *new_key, *new_value;
+    const int64_t *slot_mapping;
 };
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);

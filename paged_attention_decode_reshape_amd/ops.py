@@ -44,6 +44,9 @@ _SIGS = {
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_paged_decode_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                               _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
+    "pa_paged_decode_attn_write": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                    _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
+                                    _sz, _vp], _i32),
     "pa_mla_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
     "pa_mla_decode_attn": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                             _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
@@ -208,6 +211,52 @@ def paged_decode_attn(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                   NB, float(scale), int(partition_tokens), _ptr(ws), nbytes,
                                   _stream(query))
     _check("paged_decode_attn", st)
+    return out, lse
+
+
+def paged_decode_attn_write(query: torch.Tensor, new_key: torch.Tensor, new_value: torch.Tensor,
+                            slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_table: torch.Tensor,
+                            context_lens: torch.Tensor, scale: float, max_context_len: int,
+                            partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                            workspace: Optional[torch.Tensor] = None
+                            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One decode step in one launch: each sequence's new token (new_key,
+    new_value [S, Hkv, D] bf16 at slot_mapping [S] int64) is written into the
+    shuffled caches, then GQA paged decode runs over them."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("new_key", new_key, torch.bfloat16, 3)
+    _gpu("new_value", new_value, torch.bfloat16, 3)
+    _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    _gpu("k_cache", k_cache, torch.bfloat16, 5)
+    _gpu("v_cache", v_cache, torch.bfloat16, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, D = query.shape
+    NB, Hkv, _, B, _ = k_cache.shape
+    if tuple(new_key.shape) != (S, Hkv, D) or tuple(new_value.shape) != (S, Hkv, D):
+        raise ValueError("new_key / new_value must be [num_seqs, num_kv_heads, head_dim]")
+    if slot_mapping.numel() != S:
+        raise ValueError("slot_mapping must hold one slot per sequence")
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_paged_decode_attn_write(out.data_ptr(), _ptr(lse), query.data_ptr(),
+                                        new_key.data_ptr(), new_value.data_ptr(),
+                                        slot_mapping.data_ptr(), k_cache.data_ptr(),
+                                        v_cache.data_ptr(), block_table.data_ptr(),
+                                        block_table.shape[1], context_lens.data_ptr(),
+                                        int(max_context_len), S, Hq, Hkv, D, B, NB, float(scale),
+                                        int(partition_tokens), _ptr(ws), nbytes, _stream(query))
+    _check("paged_decode_attn_write", st)
     return out, lse
 
 

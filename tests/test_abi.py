@@ -106,6 +106,19 @@ def test_decode_workspace_sizes():
     assert pa.decode_workspace_size(4, 4, 1, 128, 511, 128) == want
 
 
+def test_fused_decode_validation():
+    f = pa.library().pa_paged_decode_attn_write
+    args = lambda nk, nv, sl: (FAKE, None, FAKE, nk, nv, sl, FAKE, FAKE, FAKE, 8, FAKE, 100, 4, 8, 1,
+                               128, 16, 64, 0.1, -1, None, 0, None)
+    assert f(*args(None, FAKE, FAKE)) == INVALID          # no new key
+    assert f(*args(FAKE, FAKE, None)) == INVALID          # no slot mapping
+    assert f(*args(FAKE + 8, FAKE, FAKE)) == INVALID      # new key not 16-byte aligned
+    assert f(*args(FAKE, FAKE, FAKE + 4)) == INVALID      # slots not 8-byte aligned
+    bad = list(args(FAKE, FAKE, FAKE))
+    bad[15] = 96                                          # head_dim
+    assert f(*bad) == UNSUPPORTED
+
+
 def test_cache_write_validation():
     lib = pa.library()
     f = lib.pa_reshape_and_cache

@@ -66,6 +66,66 @@ def test_cache_write_decode_step_overwrite(orc):
     assert np.array_equal(_bits(g.kc), kc) and np.array_equal(_bits(g.vc), vc)
 
 
+def _fused_vs_separate(case, partition, skip=None):
+    """Overwrite every sequence's newest token in the caches with other
+    values, then run (a) the fused write + decode and (b) the cache write
+    followed by decode on a copy: outputs, LSEs and caches must agree bit for
+    bit.  `skip`: sequences whose slot is -1 in both (nothing written)."""
+    dev = device()
+    g = GpuGQA(case)
+    rows = torch.from_numpy(case.new_token_rows())
+    nk = case.key[rows].to(dev).contiguous()
+    nv = case.value[rows].to(dev).contiguous()
+    real_slots = g.slots[rows.to(dev)].contiguous()
+    gen = torch.Generator("cpu").manual_seed(77)
+    junk = torch.randn((2,) + tuple(nk.shape), generator=gen).to(torch.bfloat16).to(dev)
+    pa.reshape_and_cache(junk[0].contiguous(), junk[1].contiguous(), g.kc, g.vc, real_slots)
+    slots = real_slots.clone()
+    if skip is not None:
+        slots[skip] = -1
+    kc2, vc2 = g.kc.clone(), g.vc.clone()
+    o1, l1 = pa.paged_decode_attn_write(g.q, nk, nv, slots, g.kc, g.vc, g.bt, g.cl, case.scale,
+                                        g.max_ctx, partition_tokens=partition)
+    pa.reshape_and_cache(nk, nv, kc2, vc2, slots)
+    o2, l2 = pa.paged_decode_attn(g.q, kc2, vc2, g.bt, g.cl, case.scale, g.max_ctx,
+                                  partition_tokens=partition)
+    torch.cuda.synchronize()
+    assert torch.equal(_t(o1), _t(o2)) and torch.equal(l1, l2), "output differs"
+    assert torch.equal(_t(g.kc), _t(kc2)) and torch.equal(_t(g.vc), _t(vc2)), "cache differs"
+    return g, o1, l1
+
+
+@pytest.mark.parametrize("mk,partition", [
+    (lambda: W.tiny_gqa(), -1),
+    (lambda: W.tiny_gqa(), 128),
+    (lambda: W.gqa_decode_case("fw", 205, [1, 16, 17, 64, 65, 300], Hq=8, Hkv=2, D=128,
+                               block_size=16), 64),
+    (lambda: W.gqa_decode_case("fw32", 206, [1, 31, 32, 33, 200], Hq=8, Hkv=4, D=64,
+                               block_size=32), 0),
+    (lambda: W.qwen3_decode(S=16), -2),
+    (lambda: W.qwen3_decode(S=16), 256),
+], ids=["tiny_unsplit", "tiny_p128", "edges_p64", "d64b32_auto", "qwen16_balanced",
+        "qwen16_p256"])
+def test_decode_fused_cache_write(orc, mk, partition):
+    """A decode step in one launch equals the cache write followed by decode
+    (bits), leaves the caches equal to the oracle's, and matches the oracle's
+    attention."""
+    case = mk()
+    say(f"fused cache write + decode {case.name} partition {partition}")
+    g, out, lse = _fused_vs_separate(case, partition)
+    kc, vc = oracle_pins.oracle_cache(orc, case)
+    assert np.array_equal(_bits(g.kc), kc) and np.array_equal(_bits(g.vc), vc)
+    ref_out, ref_lse = oracle_gqa(orc, case)
+    assert_attn_close(out, lse, ref_out, ref_lse, what=f"fused {case.name}")
+
+
+@pytest.mark.parametrize("partition", [-1, 64, -2])
+def test_decode_fused_cache_write_skipped_slot(partition):
+    """A negative slot writes nothing, exactly like the separate cache write."""
+    case = W.gqa_decode_case("fwskip", 207, [40, 3, 129], Hq=4, Hkv=1, D=128, block_size=16)
+    _fused_vs_separate(case, partition, skip=1)
+
+
 def test_latent_cache_write_bitexact(orc):
     cases = W.mla_decode_cases("lat", 204, S=3, lens_range=None, lens=[1, 70, 129], Hq=2, Dl=576,
                                Dv=512, block_sizes=(1, 64, 5), scale=0.1)
