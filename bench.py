@@ -38,7 +38,7 @@ METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 
 # kernel sources it was measured on: (sha256 prefix of those sources, bytes).
 DECODE_SOURCES = ("paged_attention_decode_reshape_amd/csrc/decode_gqa.hip",
                   "paged_attention_decode_reshape_amd/csrc/decode_common.h")
-MEASURED_TRAFFIC = {"qwen3": ("9aca12e1009fbc00", 52.19e6)}
+MEASURED_TRAFFIC = {"qwen3": ("9cc962a88549de36", 52.39e6)}
 
 
 def measured_traffic(config):
