@@ -18,9 +18,10 @@
 //   -- 32 per wave -- and one piece of the request's context: a run of whole
 //   chunks (pieces exist only to balance long contexts over the GPU).  The
 //   last piece also takes the request's new tokens with the causal mask.
-//   Keys go 64 at a time through double-buffered LDS tiles (the next tile is
-//   loaded into registers while the current one is used; one barrier per
-//   tile).  Per tile:
+//   Keys go 64 at a time through double-buffered LDS tiles: the next tile is
+//   loaded straight into the other buffer (buffer_load_dwordx4 ... lds, in
+//   the cache's own order) while the current one is used; one barrier per
+//   tile.  Per tile:
 //     S^T = K Q^T    (keys x queries): lane l owns query l % 32, so a
 //                    query's softmax state sits in one lane pair (l, l + 32);
 //                    the K rows are fed in a permuted order so that each
@@ -132,10 +133,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
 // every load into zeros).  0x00020000: gfx9 descriptor word 3, raw access.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ext_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ext_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // The new tokens' V rearranged into the cache's 8-token groups:
