@@ -18,8 +18,10 @@
 //   QK  lane (half f, token t): the 288 latent dims of half f of token t's
 //       row, against query dwords broadcast by DPP from registers that stay
 //       resident (9 per head); one permlane swap adds the halves.
-//   PV  lane l: output dims 8l .. 8l + 7; per token one 16-byte LDS read,
-//       the weight taken from the token's lane with v_readlane, fp32 FMAs.
+//   PV  lane l: output dims 8l .. 8l + 7; per token one 16-byte LDS read of
+//       its latent and one of its 4 heads' weights (which the token's lane
+//       wrote to LDS: a broadcast read, so the FMAs take plain registers),
+//       fp32 FMAs.
 // Two ways to split the sequences over workgroups: fixed-length partitions
 // (one workgroup per (partition, sequence)) or the balanced split (a grid of
 // the resident workgroups, each sequence cut into pieces proportional to its
@@ -152,6 +154,9 @@ struct MLASmem {
     // an out-of-range block id), resolved once per window so that the tile
     // loop issues no dependent block-table reads
     int32_t row[kMaxPartition];
+    // P.V weights of each wave's 4 heads for the tile's tokens (written and
+    // read by the same wave only)
+    float4 w[kWaves][kTile];
 };
 
 // Query registers of the wave's heads (past num_q_heads: repeats of real
@@ -265,6 +270,13 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
             // PV: dims 8 lane .. 8 lane + 7 of every token of the tile; the
             // LDS reads run kPVAhead tokens ahead of their use
             const uint4 *vr = reinterpret_cast<const uint4 *>(sm.tile) + lane;
+            // token lane t publishes its weights; every lane reads them back
+            if (lane < kTile) sm.w[wave][lane] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+            float4 wbuf[kPVAhead];
+            static_for<kPVAhead>([&](auto u_c) {
+                constexpr int u = decltype(u_c)::value;
+                wbuf[u] = sm.w[wave][u];
+            });
             uint4 vbuf[kPVAhead];
             static_for<kPVAhead>([&](auto u_c) {
                 constexpr int u = decltype(u_c)::value;
@@ -273,12 +285,17 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
             static_for<kTile>([&](auto t_c) {
                 constexpr int t = decltype(t_c)::value;
                 const uint4 v = vbuf[t % kPVAhead];
-                if constexpr (t + kPVAhead < kTile) vbuf[t % kPVAhead] = vr[(t + kPVAhead) * (kRowDw / 4)];
+                const float4 wt = wbuf[t % kPVAhead];
+                if constexpr (t + kPVAhead < kTile) {
+                    vbuf[t % kPVAhead] = vr[(t + kPVAhead) * (kRowDw / 4)];
+                    wbuf[t % kPVAhead] = sm.w[wave][t + kPVAhead];
+                }
+                const float wts[4] = {wt.x, wt.y, wt.z, wt.w};
                 const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
                 for (int j = 0; j < kHPW; j++) {
-                    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[j]), t));
+                    const float w = wts[j];
 #pragma unroll
                     for (int i = 0; i < 8; i++) acc[j][i] = __builtin_fmaf(w, vf[i], acc[j][i]);
                 }
