@@ -50,6 +50,7 @@ constexpr int kRowVec = kDl / 8;          // 16-byte vectors per latent row (72)
 constexpr int kLoadVec = kTile * kRowVec / 256;  // vectors each thread loads per tile (9)
 constexpr int kMaxPartition = 4096;       // tokens per partition, at most
 constexpr int kPVAhead = 2;               // P.V: tokens whose V rows are read ahead
+constexpr float kLazyLog2 = 8.f;          // softmax reference lag (log2 units)
 
 // context length limited to the host's bound and what the block table covers
 __device__ __forceinline__ int clamp_ctx(const MLAParams &p, int ctx) {
@@ -243,7 +244,9 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
             }
             dpp_result_fence<kHPW>(za);
             dpp_result_fence<kHPW>(zb);
-            // softmax: exact max of the tile, one rescale of the running state
+            // softmax: the tile's exact max; the reference maximum m moves only
+            // when the tile's passes it by more than 8 (log2 units), so weights
+            // stay <= 2^8 and most tiles skip the rescale of the running state
             float pw[kHPW];
 #pragma unroll
             for (int j = 0; j < kHPW; j++) {
@@ -255,14 +258,16 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
                 const auto mm = __builtin_amdgcn_permlane16_swap(__float_as_uint(rm),
                                                                  __float_as_uint(rm), false, false);
                 const float mx = uniform_f(fmax_nc(__uint_as_float(mm[0]), __uint_as_float(mm[1])));
-                const float mn = fmax_nc(m[j], mx);
-                const float mref = mn == kNegInf ? 0.f : mn;
-                const float alpha = fast_exp2(m[j] - mref);
-                m[j] = mn;
-                pw[j] = fast_exp2(sc - mref);
-                lsum[j] = lsum[j] * alpha + pw[j];
+                if (mx > m[j] + kLazyLog2) {  // uniform
+                    const float alpha = fast_exp2(m[j] - mx);
+                    m[j] = mx;
+                    lsum[j] *= alpha;
 #pragma unroll
-                for (int i = 0; i < 8; i++) acc[j][i] *= alpha;
+                    for (int i = 0; i < 8; i++) acc[j][i] *= alpha;
+                }
+                const float mref = m[j] == kNegInf ? 0.f : m[j];
+                pw[j] = fast_exp2(sc - mref);
+                lsum[j] += pw[j];
             }
             // the next tile's loads overlap P.V (issued after QK, so their
             // registers are not live during QK)
