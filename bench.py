@@ -287,11 +287,16 @@ VALU_PEAK_TFLOPS = 157.3  # fp32 vector (bf16 dot2 issues at the same rate)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def mla_algorithmic_bytes(case) -> int:
+def mla_algorithmic_bytes(case, with_write=False) -> int:
+    """Every context latent row once, q, out, lse, used table entries and
+    lengths (and, with the fused cache write, each new latent read and
+    written plus its slot)."""
     n = case.context_lens.astype(np.int64)
     lat = int(n.sum()) * case.Dl * 2
     blocks = int(((n + case.B - 1) // case.B).sum())
-    return lat + case.S * case.Hq * (case.Dl + case.Dv) * 2 + case.S * case.Hq * 4 + blocks * 4 + case.S * 4
+    write = case.S * case.Dl * 2 * 2 + case.S * 8 if with_write else 0
+    return (lat + case.S * case.Hq * (case.Dl + case.Dv) * 2 + case.S * case.Hq * 4 + blocks * 4 +
+            case.S * 4 + write)
 
 
 def mla_algorithmic_flops(case) -> int:
@@ -329,13 +334,21 @@ def bench_mla(args, case, label):
     out = torch.empty((case.S, case.Hq, case.Dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
 
+    fused = not args.separate_cache_write
+
     def decode(i):
-        pa.mla_decode_attn(q, caches[i % pools], bt, cl, case.scale, max_ctx, v_dim=case.Dv,
-                           partition_tokens=P, out=out, lse=lse, workspace=ws)
+        if fused:  # the new latents' cache write inside the decode launch
+            pa.mla_decode_attn_write(q, new_lat, new_slots, caches[i % pools], bt, cl, case.scale,
+                                     max_ctx, v_dim=case.Dv, partition_tokens=P, out=out, lse=lse,
+                                     workspace=ws)
+        else:
+            pa.mla_decode_attn(q, caches[i % pools], bt, cl, case.scale, max_ctx, v_dim=case.Dv,
+                               partition_tokens=P, out=out, lse=lse, workspace=ws)
 
     def step(i):
-        pa.reshape_and_cache(new_lat, None, caches[i % pools], None, new_slots,
-                             layout=pa.LAYOUT_MLA_LATENT)
+        if not fused:
+            pa.reshape_and_cache(new_lat, None, caches[i % pools], None, new_slots,
+                                 layout=pa.LAYOUT_MLA_LATENT)
         decode(i)
 
     for i in range(args.warmup):
@@ -347,14 +360,14 @@ def bench_mla(args, case, label):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     dec_ms = time_launches(decode, min(args.steps, 200))
-    algo = mla_algorithmic_bytes(case)
+    algo = mla_algorithmic_bytes(case, with_write=fused)
     flops = mla_algorithmic_flops(case)
     # MLA picks its split like GQA decode with one unit per sequence
     balanced = pa.decode_uses_balanced_split(case.S, 1, max_ctx, P)
     return {"value": case.S / (ms_per_step * 1e-3), "ms_per_step": ms_per_step,
             "decode_ms": dec_ms, "algo_bytes": algo, "algo_flops": flops,
             "hbm_gbps": algo / (dec_ms * 1e-3) / 1e9, "tflops": flops / (dec_ms * 1e-3) / 1e12,
-            "pools": pools,
+            "pools": pools, "cache_write": "fused" if fused else "separate launch",
             "kernel": "mla_decode_balanced_kernel" if balanced else "mla_decode_kernel"}
 
 
@@ -527,7 +540,8 @@ def main():
         r = bench_mla(args, case, f"deepseek_mla_decode_bs{B}")
         workload = {"workload": f"deepseek_r1_tp8_mla_decode_64req_bs{B}", "requests": 64,
                     "q_heads": 16, "latent_dim": 576, "v_dim": 512, "block_size": B,
-                    "context_lens": "U[1024,4096]", "kv_pool_copies": r["pools"]}
+                    "context_lens": "U[1024,4096]", "kv_pool_copies": r["pools"],
+                    "cache_write": r["cache_write"]}
         line = base_line(args, r, workload)
         line["hbm_gbps"] = r["hbm_gbps"]
         line["pct_hbm_peak"] = 100.0 * r["hbm_gbps"] / HBM_PEAK_GBPS

@@ -211,6 +211,26 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
                              void *stream);
 
 /*
+ * An MLA decode step in one launch: the cache write of each sequence's new
+ * latent (reshape_and_cache, MLA layout) fused into pa_mla_decode_attn.
+ * new_latent [num_seqs, latent_dim] bf16 (16-byte aligned); slot_mapping
+ * [num_seqs] int64: sequence s's latent goes to slot slot_mapping[s]
+ * exactly as pa_reshape_and_cache writes it; a negative or out-of-pool slot
+ * is skipped.  kv_cache is written.  Everything else is as for
+ * pa_mla_decode_attn on the cache after the write, provided that
+ * slot_mapping[s] is the slot of token context_lens[s] - 1 through the block
+ * table (the workgroup that reads that token writes it first).
+ */
+pa_status pa_mla_decode_attn_write(void *out, float *lse, const void *query,
+                                   const void *new_latent, const int64_t *slot_mapping,
+                                   void *kv_cache, const int32_t *block_table,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t latent_dim, int32_t v_dim, int32_t block_size,
+                                   int64_t num_blocks, float scale, int32_t partition_tokens,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Log-sum-exp merge of two partial attention results (merge_attn_states;
  * extend-path pseudocode): with M = max(Lp, Ls), wp = exp(Lp - M),
  * ws = exp(Ls - M): out = (wp * Op + ws * Os) / (wp + ws),

@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     library,
     merge_attn_states,
     mla_decode_attn,
+    mla_decode_attn_write,
     mla_workspace_size,
     paged_decode_attn,
     paged_decode_attn_write,

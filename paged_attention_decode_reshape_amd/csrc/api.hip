@@ -284,13 +284,16 @@ size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_di
     return sp.total();
 }
 
-pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const void *kv_cache,
-                             const int32_t *block_table, int32_t max_blocks_per_seq,
-                             const int32_t *context_lens, int32_t max_context_len,
-                             int32_t num_seqs, int32_t num_q_heads, int32_t latent_dim,
-                             int32_t v_dim, int32_t block_size, int64_t num_blocks, float scale,
-                             int32_t partition_tokens, void *workspace, size_t workspace_bytes,
-                             void *stream) {
+// MLA decode, optionally with the fused cache write of each sequence's new
+// latent (new_latent / slot_mapping null: no write).
+static pa_status mla_impl(void *out, float *lse, const void *query, const void *new_latent,
+                          const int64_t *slot_mapping, const void *kv_cache,
+                          const int32_t *block_table, int32_t max_blocks_per_seq,
+                          const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t latent_dim, int32_t v_dim,
+                          int32_t block_size, int64_t num_blocks, float scale,
+                          int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                          void *stream) {
     if (num_seqs < 0 || num_q_heads < 1 || block_size < 1 || num_blocks < 1 ||
         max_blocks_per_seq < 1 || max_context_len < 0 || partition_tokens < kRequestBalanced ||
         !isfinite(scale))
@@ -338,7 +341,38 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
     p.counters = split ? (int *)ws : nullptr;
     p.part_out = split ? (float *)(ws + sp.counter_bytes) : nullptr;
     p.part_lse = split ? (float *)(ws + sp.counter_bytes + sp.out_bytes) : nullptr;
+    p.new_latent = new_latent;
+    p.slot_mapping = slot_mapping;
     return from_hip(launch_mla_decode(p, (hipStream_t)stream));
+}
+
+pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const void *kv_cache,
+                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t latent_dim,
+                             int32_t v_dim, int32_t block_size, int64_t num_blocks, float scale,
+                             int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    return mla_impl(out, lse, query, nullptr, nullptr, kv_cache, block_table, max_blocks_per_seq,
+                    context_lens, max_context_len, num_seqs, num_q_heads, latent_dim, v_dim,
+                    block_size, num_blocks, scale, partition_tokens, workspace, workspace_bytes,
+                    stream);
+}
+
+pa_status pa_mla_decode_attn_write(void *out, float *lse, const void *query,
+                                   const void *new_latent, const int64_t *slot_mapping,
+                                   void *kv_cache, const int32_t *block_table,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t latent_dim, int32_t v_dim, int32_t block_size,
+                                   int64_t num_blocks, float scale, int32_t partition_tokens,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    if (!new_latent || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!aligned(new_latent, 16) || !aligned(slot_mapping, 8)) return PA_ERR_INVALID_ARG;
+    return mla_impl(out, lse, query, new_latent, slot_mapping, kv_cache, block_table,
+                    max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                    latent_dim, v_dim, block_size, num_blocks, scale, partition_tokens, workspace,
+                    workspace_bytes, stream);
 }
 
 pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,

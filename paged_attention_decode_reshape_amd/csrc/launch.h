@@ -68,6 +68,12 @@ struct MLAParams {
     int *counters;             // [S] pieces finished; zero between calls
     int32_t balanced_workgroups;  // > 0: balanced split over at most this many workgroups
     int32_t num_cus;              // compute units of the device (balanced split)
+    // Fused cache write (null slot_mapping: none): sequence s's new latent
+    // new_latent[s] ([S, Dl] bf16) goes to slot slot_mapping[s] (< 0:
+    // skipped), written by the workgroup that reads the sequence's last
+    // token before it reads it.
+    const void *new_latent;
+    const int64_t *slot_mapping;
 };
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);

@@ -149,6 +149,21 @@ __device__ __forceinline__ void merge_mla_partials(const MLAParams &p, int s, co
     if (c == 0 && p.lse) p.lse[row] = den > 0.f ? M + fast_log2(den) * kLn2 : kNegInf;
 }
 
+// Fused cache write of one decode token's latent (reshape_and_cache, MLA
+// layout: the row of slot = block * B + o is kv_cache[block][o][0..576)),
+// by the workgroup that reads the sequence's last token: threads 0..71 copy
+// the 72 16-byte vectors, the stores complete and the workgroup meets at a
+// barrier before any wave reads the cache.  Called by every thread.
+__device__ __forceinline__ void mla_write_new_token(const MLAParams &p, int s) {
+    const int64_t slot = as_const<int64_t>(p.slot_mapping)[s];
+    if (slot >= 0 && slot < p.num_blocks * p.B && (int)threadIdx.x < kRowVec) {
+        const uint4 v = reinterpret_cast<const uint4 *>(p.new_latent)[(size_t)s * kRowVec + threadIdx.x];
+        reinterpret_cast<uint4 *>(const_cast<void *>(p.kv_cache))[(size_t)slot * kRowVec + threadIdx.x] = v;
+        wait_stores();
+    }
+    __syncthreads();
+}
+
 struct MLASmem {
     __align__(16) uint32_t tile[kTile * kRowDw];
     // latent row of every token of the current window (-1: past the end or
@@ -398,11 +413,16 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
 
     const int ctx = clamp_ctx(p, as_const<int32_t>(p.context_lens)[s]);
     if (start >= ctx) {
-        if (ctx == 0 && part == 0) mla_write_empty(p, s);
+        if (ctx == 0 && part == 0) {
+            if (p.slot_mapping) mla_write_new_token(p, s);
+            mla_write_empty(p, s);
+        }
         return;
     }
     const int end = min(start + P, ctx);
     const int nparts = (ctx + P - 1) / P;
+    // the partition holding the last token writes the new token first
+    if (p.slot_mapping && end == ctx) mla_write_new_token(p, s);
     uint32_t qreg[kHPW][kSlices];
     mla_load_queries(p, s, qreg);
     float m[kHPW], lsum[kHPW], acc[kHPW][8];
@@ -448,7 +468,10 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
     auto ctx_in = [&](int c0) { return c0 == 0 ? ctx_w0 : ctx_of(c0 + lane); };
 
     for (int s = w; s < p.S; s += NW)
-        if (readlane_i32(ctx_in(s & ~63), s & 63) == 0) mla_write_empty(p, s);
+        if (readlane_i32(ctx_in(s & ~63), s & 63) == 0) {
+            if (p.slot_mapping) mla_write_new_token(p, s);
+            mla_write_empty(p, s);
+        }
 
     // pass 1 (every wave): tiles and non-empty sequences
     int64_t SB = 0;
@@ -501,6 +524,8 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
         mla_load_queries(p, s, qreg);
         float m[kHPW], lsum[kHPW], acc[kHPW][8];
         mla_reset(m, lsum, acc);
+        // the piece holding the last token writes the new token first
+        if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token(p, s);
         mla_attend(p, sm, s, a * kTile, min(b * kTile, ctx), qreg, m, lsum, acc);
         mla_emit(p, s, n == 1, m, lsum, acc, p.part_out + (size_t)v * p.Hq * kDv, kDv,
                  p.part_lse + (size_t)v * p.Hq, 1);

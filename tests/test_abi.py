@@ -119,6 +119,18 @@ def test_fused_decode_validation():
     assert f(*bad) == UNSUPPORTED
 
 
+def test_fused_mla_validation():
+    f = pa.library().pa_mla_decode_attn_write
+    args = lambda nl, sl: (FAKE, None, FAKE, nl, sl, FAKE, FAKE, 8, FAKE, 100, 4, 16, 576, 512, 64,
+                           64, 0.1, -1, None, 0, None)
+    assert f(*args(None, FAKE)) == INVALID                # no new latent
+    assert f(*args(FAKE, None)) == INVALID                # no slot mapping
+    assert f(*args(FAKE + 8, FAKE)) == INVALID            # latent not 16-byte aligned
+    bad = list(args(FAKE, FAKE))
+    bad[12] = 512                                         # latent_dim
+    assert f(*bad) == UNSUPPORTED
+
+
 def test_cache_write_validation():
     lib = pa.library()
     f = lib.pa_reshape_and_cache

@@ -141,3 +141,34 @@ def test_mla_rejects_unsupported():
     with pytest.raises(pa.PagedAttnError) as e:
         pa.mla_decode_attn(g.q, g.kv, g.bt, g.cl, float("inf"), g.max_ctx)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("partition", [-1, 64, 0, -2])
+def test_mla_fused_cache_write(orc, partition):
+    """An MLA decode step in one launch equals the latent cache write
+    followed by decode (output, LSE and cache bits), and matches the oracle,
+    at block sizes 1, 64 and 5."""
+    lens = [1, 31, 32, 33, 100, 257, 700]
+    cases = W.mla_decode_cases("mla_fw", 420, S=len(lens), lens_range=None, lens=lens, Hq=16,
+                               Dl=576, Dv=512, block_sizes=(1, 64, 5), scale=SCALE)
+    dev = device()
+    for B, case in cases.items():
+        say(f"mla fused cache write B={B} P={partition}")
+        g = GpuMLA(case)
+        rows = case.new_token_rows()
+        nl = case.latent[torch.from_numpy(rows)].to(dev).contiguous()
+        slots = torch.from_numpy(case.paging.slot_mapping[rows]).to(dev).contiguous()
+        gen = torch.Generator("cpu").manual_seed(79)
+        junk = torch.randn(tuple(nl.shape), generator=gen).to(torch.bfloat16).to(dev)
+        pa.reshape_and_cache(junk, None, g.kv, None, slots, layout=pa.LAYOUT_MLA_LATENT)
+        kv2 = g.kv.clone()
+        o1, l1 = pa.mla_decode_attn_write(g.q, nl, slots, g.kv, g.bt, g.cl, case.scale, g.max_ctx,
+                                          v_dim=case.Dv, partition_tokens=partition)
+        pa.reshape_and_cache(nl, None, kv2, None, slots, layout=pa.LAYOUT_MLA_LATENT)
+        o2, l2 = pa.mla_decode_attn(g.q, kv2, g.bt, g.cl, case.scale, g.max_ctx, v_dim=case.Dv,
+                                    partition_tokens=partition)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+        assert torch.equal(g.kv.view(torch.int16), kv2.view(torch.int16))
+        ref_out, ref_lse = oracle_mla(orc, case)
+        assert_attn_close(o1, l1, ref_out, ref_lse, what=f"mla fused B={B} P={partition}")
