@@ -33,12 +33,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 reqs"
 
-# HBM traffic per decode launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
-# plain copy of known size (summary and commands in profiles/), valid only for the
-# kernel sources it was measured on: (sha256 prefix of those sources, bytes).
-DECODE_SOURCES = ("paged_attention_decode_reshape_amd/csrc/decode_gqa.hip",
-                  "paged_attention_decode_reshape_amd/csrc/decode_common.h")
-MEASURED_TRAFFIC = {"qwen3": ("9cc962a88549de36", 52.39e6)}
+# HBM traffic per launch of each workload's dominant kernel from rocprofv3 FETCH_SIZE +
+# WRITE_SIZE, scaled by a plain copy of known size (summaries and commands in profiles/),
+# valid only for the kernel sources it was measured on:
+# workload -> (sources, sha256 prefix of those sources, bytes per launch).
+_CSRC = "paged_attention_decode_reshape_amd/csrc/"
+MEASURED_TRAFFIC = {
+    "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "9cc962a88549de36", 52.39e6),
+    "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "25a9444b960aeec7", 237.19e6),
+    "extend": ((_CSRC + "extend.hip", _CSRC + "decode_common.h"), "17bb752e1679d13e", 1294.56e6),
+}
 
 
 def measured_traffic(config):
@@ -46,12 +50,14 @@ def measured_traffic(config):
     import hashlib
     if config not in MEASURED_TRAFFIC:
         return None
+    sources, sha, nbytes = MEASURED_TRAFFIC[config]
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    sha, nbytes = MEASURED_TRAFFIC[config]
     return nbytes if h.hexdigest()[:16] == sha else None
+
+
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -518,6 +524,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     from paged_attention_decode_reshape_amd import workloads as W
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
 
     if args.config == "qwen3":
         case = W.qwen3_decode()
@@ -547,7 +555,8 @@ def main():
         line["pct_hbm_peak"] = 100.0 * r["hbm_gbps"] / HBM_PEAK_GBPS
         line["roofline"] = {"bound": "alu", "kernel": r["kernel"], "achieved": r["tflops"],
                             "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": r["tflops"] / VALU_PEAK_TFLOPS, "traffic": None,
+                            "frac": r["tflops"] / VALU_PEAK_TFLOPS,
+                            "traffic": measured_traffic(args.config),
                             "algo_flops_per_launch": r["algo_flops"],
                             "algo_bytes_per_launch": r["algo_bytes"], "avg_launch_ms": r["decode_ms"]}
         if not args.no_cpu_baseline:
@@ -565,7 +574,9 @@ def main():
         line["roofline"] = {"bound": "mfma", "kernel": "extend_attn_kernel (+ plan, new-V shuffle, merge)",
                             "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS,
-                            "traffic": None, "algo_flops_per_call": r["algo_flops"],
+                            "traffic": measured_traffic(args.config),
+                            "traffic_kernel": "extend_attn_kernel",
+                            "algo_flops_per_call": r["algo_flops"],
                             "avg_call_ms": r["call_ms"]}
         line["gather_pass"] = r["gather"]
         if not args.no_cpu_baseline:
@@ -574,8 +585,6 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
-    if args.copy_calibration_mb:
-        copy_calibration(args.copy_calibration_mb)
     line = base_line(args, r, workload)
     line.update({
         "hbm_gbps": r["hbm_gbps"],
