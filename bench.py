@@ -15,6 +15,10 @@ steps eagerly (--graph-timing replays captured HIP graphs instead; a replay
 is also checked against the eager result); the decode kernel's own duration
 is measured with HIP events on the stream it is launched on.
 
+The decode lines also carry hbm_read_ceiling: the time of a plain
+streaming read (pa_stream_read) of the same number of bytes on the same GPU,
+i.e. what the memory system delivers at this transfer size.
+
 Prints one JSON line.  Other workloads: --config long_context | mla | extend.
 """
 from __future__ import annotations
@@ -73,6 +77,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph capture check")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip timing a plain streaming read of the decode's algorithmic bytes")
     ap.add_argument("--graph-timing", action="store_true",
                     help="time GQA steps as HIP-graph replays instead of eager launches")
     ap.add_argument("--separate-cache-write", action="store_true",
@@ -126,6 +132,31 @@ def time_launches(launch, n):
     e1.record(cur)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def read_ceiling(nbytes, grids=(1024, 2048, 4096, 8192), n=200):
+    """What a plain streaming read of `nbytes` achieves on this GPU: the
+    library's pa_stream_read over enough rotated copies to defeat the
+    Infinity Cache, best workgroup count, HIP events around n back-to-back
+    launches."""
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+
+    nbytes = max(16, nbytes // 16 * 16)
+    copies = max(2, math.ceil(2 * MALL_BYTES / nbytes))
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.empty(max(grids), dtype=torch.int32, device="cuda")
+    best = None
+    for g in grids:
+        ms = time_launches(lambda i: pa.stream_read(bufs[i % copies], g, sink, verify=False), n)
+        if best is None or ms < best[1]:
+            best = (g, ms)
+    del bufs
+    torch.cuda.empty_cache()
+    gbps = nbytes / (best[1] * 1e-3) / 1e9
+    return {"kernel": "stream_read_kernel (pa_stream_read)", "bytes": nbytes,
+            "workgroups": best[0], "avg_launch_ms": best[1], "gbps": gbps,
+            "frac_of_peak": gbps / HBM_PEAK_GBPS}
 
 
 def bench_gqa(args, case, label):
@@ -553,6 +584,10 @@ def main():
         line = base_line(args, r, workload)
         line["hbm_gbps"] = r["hbm_gbps"]
         line["pct_hbm_peak"] = 100.0 * r["hbm_gbps"] / HBM_PEAK_GBPS
+        if not args.no_read_ceiling:
+            rc = read_ceiling(r["algo_bytes"])
+            rc["decode_frac_of_ceiling"] = r["hbm_gbps"] / rc["gbps"]
+            line["hbm_read_ceiling"] = rc
         line["roofline"] = {"bound": "alu", "kernel": r["kernel"], "achieved": r["tflops"],
                             "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": r["tflops"] / VALU_PEAK_TFLOPS,
@@ -603,6 +638,10 @@ def main():
             "avg_launch_ms": r["decode_ms"],
         },
     })
+    if not args.no_read_ceiling:
+        rc = read_ceiling(r["algo_bytes"])
+        rc["decode_frac_of_ceiling"] = r["hbm_gbps"] / rc["gbps"]
+        line["hbm_read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds)

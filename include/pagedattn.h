@@ -325,6 +325,24 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
                                  int32_t chunk_budget_tokens, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/*
+ * Streaming read (a measurement aid, not a step of the method): reads the
+ * `bytes` bytes at src once, in 16-byte vectors, with `workgroups`
+ * workgroups of 256 threads walking the buffer grid-stride, and stores one
+ * xor word per workgroup in sink[0 .. workgroups) when verify is nonzero
+ * (with verify 0 nothing is reduced and a lane stores its own word only if
+ * it is all ones, so that a timed read adds no reduction or store drain; the
+ * sink contents are then meaningless).  Its time at a given size
+ * is the yardstick for the decode kernels' achieved bandwidth: the paged
+ * decode's claim is to be memory-bound, and this is what plain reading of
+ * the same number of bytes achieves on the same GPU.
+ * src: device, 16-byte aligned, bytes a multiple of 16.  sink: device,
+ * `workgroups` uint32 words.  workgroups in [1, 65536].
+ * Errors: PA_ERR_INVALID_ARG (nothing launched), PA_ERR_HIP.
+ */
+pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups,
+                         int32_t verify, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,4 +25,5 @@ from .ops import (  # noqa: F401
     paged_decode_attn,
     paged_decode_attn_write,
     reshape_and_cache,
+    stream_read,
 )

@@ -61,6 +61,7 @@ _SIGS = {
     "pa_chunked_extend_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                 _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp],
                                _i32),
+    "pa_stream_read": ([_vp, _sz, _vp, _i32, _i32, _vp], _i32),
 }
 
 _lib = None
@@ -471,3 +472,22 @@ def chunked_extend_attn(query: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
                                     _stream(query))
     _check("chunked_extend_attn", st)
     return out, lse
+
+
+def stream_read(src: torch.Tensor, workgroups: int, sink: Optional[torch.Tensor] = None,
+                verify: bool = True) -> torch.Tensor:
+    """Read every byte of `src` once with the library's plain streaming-read
+    kernel (a bandwidth yardstick, not part of attention); with `verify` the
+    per-workgroup xor words are stored in the returned sink (otherwise a word
+    is stored only if it is all ones, for timing)."""
+    lib = library()
+    _gpu("src", src)
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=src.device)
+    _gpu("sink", sink, torch.int32, 1)
+    if sink.numel() < workgroups:
+        raise ValueError("sink needs one word per workgroup")
+    _check("stream_read", lib.pa_stream_read(src.data_ptr(), nbytes, sink.data_ptr(),
+                                             int(workgroups), int(bool(verify)), _stream(src)))
+    return sink

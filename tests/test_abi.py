@@ -157,3 +157,15 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pa.paged_decode_attn(q, q, q, q, q, 0.1, 1)
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, 100, FAKE, 8),        # bytes not a multiple of 16
+    (FAKE + 4, 64, FAKE, 8),     # source not 16-byte aligned
+    (FAKE, 64, FAKE, 0),         # no workgroups
+    (FAKE, 64, FAKE, 65537),     # too many workgroups
+    (None, 64, FAKE, 8),
+    (FAKE, 64, None, 8),
+])
+def test_stream_read_validation(args):
+    assert pa.library().pa_stream_read(*args, 1, None) == INVALID
