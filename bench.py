@@ -72,7 +72,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="qwen3",
-                    choices=["qwen3", "long_context", "mla", "mla_bs1", "extend"])
+                    choices=["qwen3", "qwen3_10k", "long_context", "mla", "mla_bs1", "extend"])
+    ap.add_argument("--kv-layout", default="shuffled", choices=["shuffled", "standard"],
+                    help="GQA decode cache layout: the pages' shuffled one, or the standard "
+                         "[num_blocks, block_size, kv_heads, head_dim] it replaces (same "
+                         "kernel, V transposed through LDS) to measure the difference")
     ap.add_argument("--pools", type=int, default=0, help="KV pool copies (0: enough to exceed the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -165,6 +169,8 @@ def bench_gqa(args, case, label):
 
     dev = torch.device("cuda:0")
     pg = case.paging
+    std = args.kv_layout == "standard"
+    layout = pa.LAYOUT_STANDARD_KV if std else pa.LAYOUT_SHUFFLED_KV
     pool_bytes = pg.num_blocks * case.Hkv * case.D * case.B * 2 * 2
     pools = args.pools or max(1, math.ceil(2 * MALL_BYTES / pool_bytes))
     log(f"[bench] {label}: S={case.S} Hq={case.Hq} Hkv={case.Hkv} D={case.D} B={case.B} "
@@ -174,11 +180,16 @@ def bench_gqa(args, case, label):
     slots_all = torch.from_numpy(pg.slot_mapping).to(dev)
     caches = []
     for _ in range(pools):
-        kc = torch.zeros((pg.num_blocks, case.Hkv, case.D // 8, case.B, 8), dtype=torch.bfloat16,
-                         device=dev)
-        vc = torch.zeros((pg.num_blocks, case.Hkv, case.B // 8, case.D, 8), dtype=torch.bfloat16,
-                         device=dev)
-        pa.reshape_and_cache(key, value, kc, vc, slots_all)
+        if std:
+            kc = torch.zeros((pg.num_blocks, case.B, case.Hkv, case.D), dtype=torch.bfloat16,
+                             device=dev)
+            vc = torch.zeros_like(kc)
+        else:
+            kc = torch.zeros((pg.num_blocks, case.Hkv, case.D // 8, case.B, 8),
+                             dtype=torch.bfloat16, device=dev)
+            vc = torch.zeros((pg.num_blocks, case.Hkv, case.B // 8, case.D, 8),
+                             dtype=torch.bfloat16, device=dev)
+        pa.reshape_and_cache(key, value, kc, vc, slots_all, layout=layout)
         caches.append((kc, vc))
     rows = torch.from_numpy(case.new_token_rows()).to(dev)
     new_k = key[rows].contiguous()
@@ -200,7 +211,13 @@ def bench_gqa(args, case, label):
 
     def decode(i):
         kc, vc = caches[i % pools]
-        if fused:  # the new tokens' cache write inside the decode launch
+        if std:  # same kernel over the standard layout
+            pa.paged_decode_attn_layout(layout, q, kc, vc, bt, cl, case.scale, max_ctx,
+                                        partition_tokens=P, new_key=new_k if fused else None,
+                                        new_value=new_v if fused else None,
+                                        slot_mapping=new_slots if fused else None, out=out,
+                                        lse=lse, workspace=ws)
+        elif fused:  # the new tokens' cache write inside the decode launch
             pa.paged_decode_attn_write(q, new_k, new_v, new_slots, kc, vc, bt, cl, case.scale,
                                        max_ctx, partition_tokens=P, out=out, lse=lse, workspace=ws)
         else:
@@ -210,7 +227,7 @@ def bench_gqa(args, case, label):
     def step(i):
         if not fused:
             kc, vc = caches[i % pools]
-            pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots)
+            pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots, layout=layout)
         decode(i)
 
     # eager reference for the graph check
@@ -278,6 +295,7 @@ def bench_gqa(args, case, label):
         "algo_flops": gqa_algorithmic_flops(case),
         "pools": pools,
         "cache_write": "fused" if fused else "separate launch",
+        "kv_layout": args.kv_layout,
         "step_launch": "graph replay" if replay else "eager",
         "partition_tokens": ("balanced" if pa.decode_uses_balanced_split(case.S, case.Hkv, max_ctx, P)
                              else pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P)),
@@ -563,7 +581,15 @@ def main():
         r = bench_gqa(args, case, "qwen3_decode_64req")
         workload = {"workload": "qwen3_235b_tp8_decode_64req", "requests": 64, "q_heads": 8,
                     "kv_heads": 1, "head_dim": 128, "block_size": 16,
-                    "context_lens": "U[1000,2000]", "kv_layout": "shuffled",
+                    "context_lens": "U[1000,2000]", "kv_layout": r["kv_layout"],
+                    "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"],
+                    "cache_write": r["cache_write"], "step_launch": r["step_launch"]}
+    elif args.config == "qwen3_10k":
+        case = W.qwen3_decode(lens_range=(10000, 11000))
+        r = bench_gqa(args, case, "qwen3_decode_64req_10k")
+        workload = {"workload": "qwen3_235b_tp8_decode_64req_10k", "requests": 64, "q_heads": 8,
+                    "kv_heads": 1, "head_dim": 128, "block_size": 16,
+                    "context_lens": "U[10000,11000]", "kv_layout": r["kv_layout"],
                     "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"],
                     "cache_write": r["cache_write"], "step_launch": r["step_launch"]}
     elif args.config == "long_context":
@@ -571,7 +597,8 @@ def main():
         r = bench_gqa(args, case, "long_context_decode")
         workload = {"workload": "long_context_gqa_decode_8req", "requests": 8, "q_heads": 64,
                     "kv_heads": 4, "head_dim": 128, "block_size": 16,
-                    "context_lens": "U[32768,131072]", "kv_pool_copies": r["pools"],
+                    "context_lens": "U[32768,131072]", "kv_layout": r["kv_layout"],
+                    "kv_pool_copies": r["pools"],
                     "partition_tokens": r["partition_tokens"], "cache_write": r["cache_write"]}
     elif args.config in ("mla", "mla_bs1"):
         B = 1 if args.config == "mla_bs1" else 64
@@ -627,13 +654,17 @@ def main():
         "graph_replay_matches_eager": r["graph_replay_matches_eager"],
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_decode_kernel (partitions + fused merge"
-                       + (" + fused cache write)" if r["cache_write"] == "fused" else ")")),
+            "kernel": (("paged_decode_balanced_kernel (balanced split"
+                        if r["partition_tokens"] == "balanced" else
+                        "paged_decode_kernel (partitions")
+                       + " + fused merge"
+                       + (" + fused cache write" if r["cache_write"] == "fused" else "")
+                       + (", standard layout)" if r["kv_layout"] == "standard" else ")")),
             "achieved": r["hbm_gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(args.config),
+            "traffic": measured_traffic(args.config) if r["kv_layout"] == "shuffled" else None,
             "algo_bytes_per_launch": r["algo_bytes"],
             "avg_launch_ms": r["decode_ms"],
         },

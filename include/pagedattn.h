@@ -63,7 +63,10 @@ enum {
 };
 
 enum { PA_BF16 = 0, PA_F32 = 1 };                           /* element types for merge */
-enum { PA_LAYOUT_SHUFFLED_KV = 0, PA_LAYOUT_MLA_LATENT = 1 }; /* cache layouts */
+/* cache layouts; PA_LAYOUT_STANDARD_KV is the unshuffled
+ * [num_blocks, block_size, num_kv_heads, head_dim] cache, kept only so that
+ * the shuffled layout can be compared against it */
+enum { PA_LAYOUT_SHUFFLED_KV = 0, PA_LAYOUT_MLA_LATENT = 1, PA_LAYOUT_STANDARD_KV = 2 };
 
 /* Human-readable name of a status code (static storage). */
 const char *pa_status_string(pa_status s);
@@ -74,14 +77,16 @@ const char *pa_status_string(pa_status s);
  *
  * PA_LAYOUT_SHUFFLED_KV: key, value [num_tokens, num_kv_heads, head_dim]
  *   bf16 are scattered into k_cache / v_cache in the shuffled layout.
+ * PA_LAYOUT_STANDARD_KV: the same key and value rows are copied to
+ *   k_cache / v_cache [num_blocks, block_size, num_kv_heads, head_dim].
  * PA_LAYOUT_MLA_LATENT: key is the latent [num_tokens, head_dim] bf16
  *   (head_dim = latent width, e.g. 576); value and v_cache must be NULL,
  *   num_kv_heads must be 1; k_cache is the latent cache.
  * slot_mapping [num_tokens] int64: destination slot of each token.  A
  *   negative slot, or one >= num_blocks * block_size, is skipped.
  * Supported: shuffled layout needs head_dim in {64, 128} and block_size in
- *   {16, 32}; the latent layout needs head_dim % 8 == 0 and any
- *   block_size >= 1.  num_tokens == 0 is a no-op.
+ *   {16, 32}; the standard and latent layouts need head_dim % 8 == 0 and
+ *   any block_size >= 1.  num_tokens == 0 is a no-op.
  */
 pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *value,
                                void *k_cache, void *v_cache, const int64_t *slot_mapping,
@@ -179,6 +184,36 @@ pa_status pa_paged_decode_attn_write(void *out, float *lse, const void *query,
                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                      float scale, int32_t partition_tokens, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/*
+ * Paged GQA decode over a cache in either layout, with or without the fused
+ * cache write: the blog credits the preshuffled layout with 15-20% more
+ * decode throughput than the standard KV cache layout (ROCM_AITER_FA
+ * section, hardware-optimised KV cache layout); this entry runs the same
+ * kernel over both so the difference can be measured.
+ * layout: PA_LAYOUT_SHUFFLED_KV (as pa_paged_decode_attn /
+ *   pa_paged_decode_attn_write) or PA_LAYOUT_STANDARD_KV: k_cache and
+ *   v_cache [num_blocks, block_size, num_kv_heads, head_dim] bf16.  In the
+ *   standard layout K is read as in the shuffled one (a lane's 16-byte
+ *   vectors are 8 dims of one token) and V is transposed through LDS into
+ *   the registers the shuffled V vectors fill, so both layouts give
+ *   bit-identical results.
+ * new_key, new_value, slot_mapping: all NULL (no cache write, as
+ *   pa_paged_decode_attn) or all given (as pa_paged_decode_attn_write, the
+ *   rows written in `layout`).  Everything else as pa_paged_decode_attn;
+ *   the workspace size is the same for both layouts.
+ * Errors: PA_ERR_INVALID_ARG for another layout or a partial write triple,
+ *   otherwise as pa_paged_decode_attn.
+ */
+pa_status pa_paged_decode_attn_layout(int32_t layout, void *out, float *lse, const void *query,
+                                      const void *new_key, const void *new_value,
+                                      const int64_t *slot_mapping, void *k_cache, void *v_cache,
+                                      const int32_t *block_table, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t max_context_len,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int64_t num_blocks, float scale, int32_t partition_tokens,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace pa_mla_decode_attn needs (0 if no split is needed).
  * For partition_tokens 0 and -2 the size depends on the current device's

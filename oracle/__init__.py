@@ -111,6 +111,49 @@ class Oracle:
         self.lib.oracle_cache_write_shuffled(key, value, _i64a(slot_mapping), T, Hkv, D, B, x, nb,
                                              k_cache, v_cache)
 
+    # The standard layout [num_blocks, block_size, kv_heads, head_dim] is the
+    # one the shuffled layout replaces ("ROCm attention backends" blog,
+    # ROCM_AITER_FA section, hardware-optimised KV cache layout: the decode
+    # gain is stated against the standard KV cache layout); token o of block
+    # p keeps its [kv_heads, head_dim] rows as they are.
+    @staticmethod
+    def empty_standard_cache(num_blocks: int, B: int, Hkv: int, D: int, fill: int = 0x7FC0):
+        k = np.full((num_blocks, B, Hkv, D), fill, dtype=np.uint16)
+        return k, k.copy()
+
+    @staticmethod
+    def cache_write_standard(key, value, slot_mapping, k_cache, v_cache):
+        """Token i goes to block slot // B, offset slot % B; slots outside the
+        pool are skipped (the same rule as the shuffled write)."""
+        key, value = _u16(key), _u16(value)
+        nb, B = k_cache.shape[0], k_cache.shape[1]
+        for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+            if 0 <= slot < nb * B:
+                k_cache[slot // B, slot % B] = key[i]
+                v_cache[slot // B, slot % B] = value[i]
+
+    @staticmethod
+    def standard_to_shuffled(k_std, v_std, x: int = 8):
+        """The shuffle of the pages' cache shapes applied to a standard cache:
+        k_cache[p][g][d div x][o][d mod x] = K[p][o][g][d] and
+        v_cache[p][g][o div x][d][o mod x] = V[p][o][g][d]."""
+        nb, B, Hkv, D = k_std.shape
+        k = np.empty((nb, Hkv, D // x, B, x), dtype=np.uint16)
+        v = np.empty((nb, Hkv, B // x, D, x), dtype=np.uint16)
+        for o in range(B):
+            for d in range(D):
+                k[:, :, d // x, o, d % x] = k_std[:, o, :, d]
+                v[:, :, o // x, d, o % x] = v_std[:, o, :, d]
+        return k, v
+
+    def paged_decode_gqa_standard(self, q, k_std, v_std, block_table, context_lens,
+                                  scale: float, row_mask=None):
+        """Decode over a standard-layout cache: the same tokens, so the same
+        attention as over their shuffled copy."""
+        k, v = self.standard_to_shuffled(k_std, v_std)
+        return self.paged_decode_gqa(q, k, v, block_table, context_lens, k_std.shape[1], scale,
+                                     row_mask=row_mask)
+
     def cache_write_latent(self, latent, slot_mapping, kv_cache, B: int):
         latent = _u16(latent)
         T, Dl = latent.shape

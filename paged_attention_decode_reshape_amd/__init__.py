@@ -9,6 +9,7 @@ not on a GPU.
 from .ops import (  # noqa: F401
     LAYOUT_MLA_LATENT,
     LAYOUT_SHUFFLED_KV,
+    LAYOUT_STANDARD_KV,
     PagedAttnError,
     chunked_extend_attn,
     decode_partition_tokens,
@@ -23,6 +24,7 @@ from .ops import (  # noqa: F401
     mla_decode_attn_write,
     mla_workspace_size,
     paged_decode_attn,
+    paged_decode_attn_layout,
     paged_decode_attn_write,
     reshape_and_cache,
     stream_read,

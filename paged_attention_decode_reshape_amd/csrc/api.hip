@@ -138,6 +138,15 @@ pa_status pa_reshape_and_cache(int32_t layout, const void *key, const void *valu
                                                     num_tokens, num_kv_heads, head_dim, block_size,
                                                     num_blocks, st));
     }
+    if (layout == PA_LAYOUT_STANDARD_KV) {
+        if (!value || !v_cache || !aligned(value, 16) || !aligned(v_cache, 16))
+            return PA_ERR_INVALID_ARG;
+        if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;
+        if (num_tokens == 0) return PA_OK;
+        return from_hip(launch_cache_write_standard(key, value, k_cache, v_cache, slot_mapping,
+                                                    num_tokens, num_kv_heads, head_dim,
+                                                    block_size, num_blocks, st));
+    }
     if (layout == PA_LAYOUT_MLA_LATENT) {
         if (value || v_cache || num_kv_heads != 1) return PA_ERR_INVALID_ARG;
         if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;
@@ -174,7 +183,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 // GQA decode, optionally with the fused cache write of each sequence's new
 // token (new_key / new_value / slot_mapping all null: no write).
-static pa_status decode_impl(void *out, float *lse, const void *query, const void *new_key,
+static pa_status decode_impl(bool std_layout, void *out, float *lse, const void *query,
+                             const void *new_key,
                              const void *new_value, const int64_t *slot_mapping,
                              const void *k_cache, const void *v_cache,
                              const int32_t *block_table, int32_t max_blocks_per_seq,
@@ -239,6 +249,7 @@ static pa_status decode_impl(void *out, float *lse, const void *query, const voi
     p.new_key = new_key;
     p.new_value = new_value;
     p.slot_mapping = slot_mapping;
+    p.std_layout = std_layout ? 1 : 0;
     return from_hip(launch_paged_decode(p, (hipStream_t)stream));
 }
 
@@ -249,7 +260,8 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int64_t num_blocks, float scale, int32_t partition_tokens,
                                void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_impl(out, lse, query, nullptr, nullptr, nullptr, k_cache, v_cache, block_table,
+    return decode_impl(false, out, lse, query, nullptr, nullptr, nullptr, k_cache, v_cache,
+                       block_table,
                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
                        workspace, workspace_bytes, stream);
@@ -267,10 +279,33 @@ pa_status pa_paged_decode_attn_write(void *out, float *lse, const void *query,
     if (!new_key || !new_value || !slot_mapping) return PA_ERR_INVALID_ARG;
     if (!aligned(new_key, 16) || !aligned(new_value, 16) || !aligned(slot_mapping, 8))
         return PA_ERR_INVALID_ARG;
-    return decode_impl(out, lse, query, new_key, new_value, slot_mapping, k_cache, v_cache,
-                       block_table, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                       partition_tokens, workspace, workspace_bytes, stream);
+    return decode_impl(false, out, lse, query, new_key, new_value, slot_mapping, k_cache,
+                       v_cache, block_table, max_blocks_per_seq, context_lens, max_context_len,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_decode_attn_layout(int32_t layout, void *out, float *lse, const void *query,
+                                      const void *new_key, const void *new_value,
+                                      const int64_t *slot_mapping, void *k_cache, void *v_cache,
+                                      const int32_t *block_table, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t max_context_len,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int64_t num_blocks, float scale, int32_t partition_tokens,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (layout != PA_LAYOUT_SHUFFLED_KV && layout != PA_LAYOUT_STANDARD_KV)
+        return PA_ERR_INVALID_ARG;
+    const int given = (new_key != nullptr) + (new_value != nullptr) + (slot_mapping != nullptr);
+    if (given != 0 && given != 3) return PA_ERR_INVALID_ARG;
+    if (given == 3 && (!aligned(new_key, 16) || !aligned(new_value, 16) ||
+                       !aligned(slot_mapping, 8)))
+        return PA_ERR_INVALID_ARG;
+    return decode_impl(layout == PA_LAYOUT_STANDARD_KV, out, lse, query, new_key, new_value,
+                       slot_mapping, k_cache, v_cache, block_table, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, partition_tokens, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,

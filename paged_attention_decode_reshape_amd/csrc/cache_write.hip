@@ -50,6 +50,23 @@ __global__ __launch_bounds__(256) void cache_write_shuffled_kernel(
     }
 }
 
+// Standard layout [num_blocks, block_size, kv_heads, head_dim] (the layout the
+// shuffled one replaces; kept so the two can be compared): a token's head row
+// is contiguous in source and cache, one 16-byte K and V vector per thread.
+__global__ __launch_bounds__(256) void cache_write_standard_kernel(
+    const uint4 *__restrict__ key, const uint4 *__restrict__ value, uint4 *__restrict__ k_cache,
+    uint4 *__restrict__ v_cache, const int64_t *__restrict__ slot_mapping, int64_t num_tokens,
+    int row_vecs, int B, int64_t num_blocks) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= num_tokens * row_vecs) return;
+    const int64_t i = idx / row_vecs;
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * B) return;
+    const int64_t dst = slot * row_vecs + (idx - i * row_vecs);  // (slot, head g, vector c)
+    k_cache[dst] = key[idx];
+    v_cache[dst] = value[idx];
+}
+
 // Latent rows are contiguous in both source and cache: one 16-byte vector per thread.
 __global__ __launch_bounds__(256) void cache_write_latent_kernel(
     const uint4 *__restrict__ latent, uint4 *__restrict__ kv_cache,
@@ -79,6 +96,19 @@ hipError_t launch_cache_write_shuffled(const void *key, const void *value, void 
         hipLaunchKernelGGL(cache_write_shuffled_kernel<64>, dim3((unsigned)grid), dim3(256), 0,
                            stream, (const uint4 *)key, (const uint4 *)value, (uint16_t *)k_cache,
                            (uint16_t *)v_cache, slot_mapping, num_tokens, Hkv, B, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_write_standard(const void *key, const void *value, void *k_cache,
+                                       void *v_cache, const int64_t *slot_mapping,
+                                       int64_t num_tokens, int Hkv, int D, int B,
+                                       int64_t num_blocks, hipStream_t stream) {
+    const int row_vecs = Hkv * (D / 8);
+    const int64_t grid = (num_tokens * row_vecs + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cache_write_standard_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4 *)key, (const uint4 *)value, (uint4 *)k_cache,
+                       (uint4 *)v_cache, slot_mapping, num_tokens, row_vecs, B, num_blocks);
     return hipGetLastError();
 }
 

@@ -439,6 +439,71 @@ __device__ __forceinline__ void load_v_sub(const char *v_cache, size_t tile, int
         for (int jj = 0; jj < DV; jj++) vv[tg][jj] = buf_load16(r, lane_off + (tg * D + 64 * jj) * 16);
 }
 
+// Standard layout [num_blocks, block_size, kv_heads, head_dim] (the layout
+// the shuffled one replaces, kept for comparing the two): token o of block
+// b, head g, is the row of head_dim bf16 at ((b * B + o) * Hkv + g) * D.
+// K and V are both read like the shuffled K: lane (row, col) loads token
+// `col`'s vectors row * CQ .. row * CQ + CQ - 1 (CQ = D / 32), so K lands in
+// the same registers as from the shuffled cache.  `first` is the
+// sub-block's first row ((b * B + 16 half) * Hkv + g).
+template <int D>
+__device__ __forceinline__ void load_rows_std(const char *cache, size_t first, int Hkv, bool live,
+                                              uint32_t lane_off, uint4 (&kq)[D / 32]) {
+    constexpr int CQ = D / 32;
+    const char *base = cache + first * (size_t)D * 2;
+    const auto r = tile_rsrc(base, live ? (uint32_t)((15 * Hkv + 1) * D * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < CQ; i++) kq[i] = buf_load16(r, lane_off + i * 16);
+}
+// byte offset of lane (row, col) inside a standard-layout sub-block
+template <int D>
+__device__ __forceinline__ uint32_t std_lane_off(int row, int col, int Hkv) {
+    return (uint32_t)((col * Hkv * D + row * (D / 32) * 8) * 2);
+}
+
+// V from the standard layout, transposed through the wave's LDS region into
+// the shuffled V registers: raw[i] (token col's dims 8 (row CQ + i) ..
+// + 7) is scattered as 2-byte values to slot (token group col / 8, dim),
+// 16 bytes of 8 tokens each; lane l then reads slot (tg, l + 64 jj) into
+// vv[tg][jj], exactly what load_v_sub returns from the shuffled cache.
+// Slots are padded every 32 dims and per token group so that a row's 16
+// lanes and the 4 rows fall into different LDS banks.
+template <int D>
+struct StdVLayout {
+    static constexpr int kGroupBytes = D * 16 + (D / 32) * 16 + 64;  // one 8-token group
+    static constexpr int kWaveBytes = 2 * kGroupBytes;
+    static __device__ __forceinline__ uint32_t slot(int tg, int dim) {
+        return (uint32_t)(tg * kGroupBytes + dim * 16 + (dim / 32) * 16);
+    }
+};
+template <int D>
+__device__ __forceinline__ void transpose_v_std(char *region, const uint4 (&raw)[D / 32],
+                                                uint4 (&vv)[2][D / 64]) {
+    constexpr int CQ = D / 32, DV = D / 64;
+    using L = StdVLayout<D>;
+    const int lane = threadIdx.x & 63, row = lane >> 4, col = lane & 15;
+    const uint32_t tok = (uint32_t)(col % 8) * 2;
+#pragma unroll
+    for (int i = 0; i < CQ; i++) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int dim = (row * CQ + i) * 8 + e;
+            *reinterpret_cast<uint16_t *>(region + L::slot(col / 8, dim) + tok) =
+                (uint16_t)(w[e / 2] >> ((e & 1) * 16));
+        }
+    }
+    // the wave's own lanes wrote the slots: LDS operations of a wave are
+    // performed in order, so only the compiler must not move reads up
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int tg = 0; tg < 2; tg++)
+#pragma unroll
+        for (int jj = 0; jj < DV; jj++)
+            vv[tg][jj] = *reinterpret_cast<const uint4 *>(region + L::slot(tg, lane + 64 * jj));
+    asm volatile("" ::: "memory");
+}
+
 // Token offset, from `start`, of a wave's sub-block k.  SHARED: the 4 waves
 // of the workgroup take SUBS-sub-block chunks of the range round-robin
 // (sub-block k of a wave is sub-block k % SUBS of its chunk k / SUBS);
@@ -470,7 +535,7 @@ __device__ __forceinline__ int bt_entry(const DecodeParams &p, int s, int start)
 // tracks the block ids of 64 sub-blocks at a time, so longer ranges are
 // taken in windows; bt_first is bt_entry() of the first window, loaded
 // early by the caller.
-template <int D, int B, int G, int SUBS, bool SHARED>
+template <int D, int B, int G, int SUBS, bool SHARED, bool STD>
 __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g, int range_start,
                                              int range_end, int bt_first, const uint32_t (&qreg)[G],
                                              float (&m)[G], float (&lsum)[G],
@@ -486,7 +551,13 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
     const float sl2 = p.scale * kLog2e;
     const char *kc = reinterpret_cast<const char *>(p.k_cache);
     const char *vc = reinterpret_cast<const char *>(p.v_cache);
-    const uint32_t k_off = k_lane_off<D, B>(row, col), v_off = (uint32_t)lane * 16;
+    const uint32_t k_off = STD ? std_lane_off<D>(row, col, p.Hkv) : k_lane_off<D, B>(row, col);
+    const uint32_t v_off = STD ? k_off : (uint32_t)lane * 16;
+    char *vt_region = nullptr;
+    if constexpr (STD) {
+        __shared__ __align__(16) char vt_lds[kWaves][StdVLayout<D>::kWaveBytes];
+        vt_region = vt_lds[wave];
+    }
 
     int bt_raw = bt_first;
     for (int start = range_start; start < range_end; start += kWindow) {
@@ -509,17 +580,31 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
             tile = (size_t)(b < 0 ? 0 : b) * p.Hkv + g;
             half = (t0 % B) / kSub;
         };
+        // standard layout: the sub-block's first row (block, 16-token half, head g)
+        auto std_first = [&](int k) -> size_t {
+            k = min(k, 63);
+            const int b = readlane_i32(bid, k);
+            const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
+            return ((size_t)(b < 0 ? 0 : b) * B + (t0 % B) / kSub * kSub) * p.Hkv + g;
+        };
         auto load_k = [&](int k, uint4 (&kq)[CQ]) {
             size_t tile;
             int half;
             locate(k, tile, half);
-            load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
+            if constexpr (STD)
+                load_rows_std<D>(kc, std_first(k), p.Hkv, k < nmine, k_off, kq);
+            else
+                load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
         };
         auto load_v = [&](int k, uint4 (&vv)[2][DV]) {
             size_t tile;
             int half;
             locate(k, tile, half);
-            load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
+            if constexpr (STD)
+                load_rows_std<D>(vc, std_first(k), p.Hkv, k < nmine,
+                                 v_off, reinterpret_cast<uint4(&)[CQ]>(vv));
+            else
+                load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
         };
 
         // One sub-block: QK, a lazy softmax update, PV (skipped, by uniform
@@ -601,13 +686,17 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
                 // PV: the V of tokens past the end is zeroed (weight 0, data may
                 // be anything); the buffers themselves are only read
                 wait_vm_loads<LK + LV>();
+                uint4 vt[2][DV];
+                if constexpr (STD)
+                    transpose_v_std<D>(vt_region, reinterpret_cast<const uint4(&)[CQ]>(vv), vt);
+                const uint4 (&vsrc)[2][DV] = STD ? vt : vv;
 #pragma unroll
                 for (int tg = 0; tg < 2; tg++) {
                     const int nv = nvalid - 8 * tg;
                     float vf[DV][8];
 #pragma unroll
                     for (int jj = 0; jj < DV; jj++) {
-                        uint4 v = vv[tg][jj];
+                        uint4 v = vsrc[tg][jj];
                         if (nvalid < kSub) {
                             v.x = mask_pair(v.x, 0, nv);
                             v.y = mask_pair(v.y, 2, nv);
@@ -757,7 +846,7 @@ __device__ __forceinline__ bool count_finished(int *counter, int nparts) {
 // v_cache[block][g][o / 8][d][o % 8].  Threads 0..D/8-1 write the key,
 // D/8..2D/8-1 the value; the stores are complete and the workgroup has met at
 // a barrier before any wave reads the cache.  Called by every thread.
-template <int D, int B>
+template <int D, int B, bool STD>
 __device__ __forceinline__ void write_new_token(const DecodeParams &p, int s, int g) {
     constexpr int C = D / 8;
     const int64_t slot = as_const<int64_t>(p.slot_mapping)[s];
@@ -766,7 +855,12 @@ __device__ __forceinline__ void write_new_token(const DecodeParams &p, int s, in
         const int64_t blk = slot / B;
         const int o = (int)(slot - blk * B);
         const size_t row = ((size_t)s * p.Hkv + g) * C + c;
-        if (t < C) {
+        if (STD) {  // both rows are copied whole: ((blk * B + o) * Hkv + g) * C + c
+            const void *src = t < C ? p.new_key : p.new_value;
+            void *dst = const_cast<void *>(t < C ? p.k_cache : p.v_cache);
+            reinterpret_cast<uint4 *>(dst)[((size_t)slot * p.Hkv + g) * C + c] =
+                reinterpret_cast<const uint4 *>(src)[row];
+        } else if (t < C) {
             const uint4 kv = reinterpret_cast<const uint4 *>(p.new_key)[row];
             uint4 *kc = reinterpret_cast<uint4 *>(const_cast<void *>(p.k_cache));
             kc[(((size_t)blk * p.Hkv + g) * C + c) * B + o] = kv;
@@ -794,7 +888,7 @@ __device__ __forceinline__ void write_empty(const DecodeParams &p, int s, int g,
 
 // Explicit partitions: one workgroup per (partition, kv head, sequence),
 // partition-major grid; partials in [S, Hq, max_parts, D].
-template <int D, int B, int G, int SUBS>
+template <int D, int B, int G, int SUBS, bool STD>
 __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     constexpr int DV = D / 64;
     const int units = p.S * p.Hkv;
@@ -815,7 +909,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     const int ctx = clamp_ctx<B>(p, ctx_raw);
     if (start >= ctx) {
         if (ctx == 0 && part == 0) {
-            if (p.slot_mapping) write_new_token<D, B>(p, s, g);
+            if (p.slot_mapping) write_new_token<D, B, STD>(p, s, g);
             write_empty(p, s, g, Ga, D);
         }
         return;
@@ -823,10 +917,10 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     const int end = min(start + P, ctx);
     const int nparts = (ctx + P - 1) / P;
     // the partition holding the last token writes the new token first
-    if (p.slot_mapping && end == ctx) write_new_token<D, B>(p, s, g);
+    if (p.slot_mapping && end == ctx) write_new_token<D, B, STD>(p, s, g);
     float m[G], lsum[G], acc[G][DV];
     reset_state<G, DV>(m, lsum, acc);
-    attend_range<D, B, G, SUBS, true>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
+    attend_range<D, B, G, SUBS, true, STD>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
 
     __shared__ WaveMergeLDS<D, G> sm;
     const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
@@ -930,7 +1024,7 @@ __device__ __forceinline__ void merge_unit_partials(const DecodeParams &p, size_
     }
 }
 
-template <int D, int B, int G>
+template <int D, int B, int G, bool STD>
 __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
     constexpr int DV = D / 64;
     const int NW = gridDim.x, w = blockIdx.x;
@@ -946,7 +1040,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
     for (int s = w; s < p.S; s += NW)
         if (readlane_i32(ctx_in(s & ~63), s & 63) == 0)
             for (int g = 0; g < Hkv; g++) {
-                if (p.slot_mapping) write_new_token<D, B>(p, s, g);
+                if (p.slot_mapping) write_new_token<D, B, STD>(p, s, g);
                 write_empty(p, s, g, Ga, D);
             }
 
@@ -1007,13 +1101,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
 
         const int tb = a * kSub, te = min(b * kSub, ctx);
         // the piece holding the last token writes the new token first
-        if (p.slot_mapping && te == ctx) write_new_token<D, B>(p, s, g);
+        if (p.slot_mapping && te == ctx) write_new_token<D, B, STD>(p, s, g);
         const int bt_first = bt_entry<B, 1, true>(p, s, tb);
         uint32_t qreg[G];
         load_queries<D, G>(p, s, g, Ga, qreg);
         float m[G], lsum[G], acc[G][DV];
         reset_state<G, DV>(m, lsum, acc);
-        attend_range<D, B, G, 1, true>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
+        attend_range<D, B, G, 1, true, STD>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
 
         const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
         const auto prs = coherent_rsrc(p.part_out + (size_t)v * Ga * D, (uint32_t)Ga * D * 4);
@@ -1032,7 +1126,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
     }
 }
 
-template <int D, int B, int G>
+template <int D, int B, int G, bool STD>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
     constexpr int kSubs = 1;  // waves take single sub-blocks in turn
     if (p.balanced_workgroups > 0) {
@@ -1040,39 +1134,45 @@ hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
         static const int per_cu = [] {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(&paged_decode_balanced_kernel<D, B, G>),
+                    &n, reinterpret_cast<const void *>(&paged_decode_balanced_kernel<D, B, G, STD>),
                     256, 0) != hipSuccess || n < 1)
                 n = 1;
             return n;
         }();
         const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G>), dim3((unsigned)nw),
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G, STD>), dim3((unsigned)nw),
                            dim3(256), 0, stream, p);
         return hipGetLastError();
     }
     const int64_t units = (int64_t)p.max_parts * p.S * p.Hkv;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((paged_decode_kernel<D, B, G, kSubs>), dim3((unsigned)units), dim3(256), 0,
+    hipLaunchKernelGGL((paged_decode_kernel<D, B, G, kSubs, STD>), dim3((unsigned)units), dim3(256), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-template <int D, int B>
+template <int D, int B, bool STD>
 hipError_t dispatch_group(const DecodeParams &p, hipStream_t stream) {
     const int Ga = p.Hq / p.Hkv;
-    if (Ga <= 1) return launch_partition<D, B, 1>(p, stream);
-    if (Ga <= 2) return launch_partition<D, B, 2>(p, stream);
-    if (Ga <= 4) return launch_partition<D, B, 4>(p, stream);
-    if (Ga <= 8) return launch_partition<D, B, 8>(p, stream);
-    return launch_partition<D, B, 16>(p, stream);
+    if (Ga <= 1) return launch_partition<D, B, 1, STD>(p, stream);
+    if (Ga <= 2) return launch_partition<D, B, 2, STD>(p, stream);
+    if (Ga <= 4) return launch_partition<D, B, 4, STD>(p, stream);
+    if (Ga <= 8) return launch_partition<D, B, 8, STD>(p, stream);
+    return launch_partition<D, B, 16, STD>(p, stream);
+}
+
+template <bool STD>
+hipError_t dispatch_layout(const DecodeParams &p, hipStream_t stream) {
+    if (p.D == 128)
+        return p.B == 16 ? dispatch_group<128, 16, STD>(p, stream)
+                         : dispatch_group<128, 32, STD>(p, stream);
+    return p.B == 16 ? dispatch_group<64, 16, STD>(p, stream) : dispatch_group<64, 32, STD>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
-    if (p.D == 128)
-        return p.B == 16 ? dispatch_group<128, 16>(p, stream) : dispatch_group<128, 32>(p, stream);
-    return p.B == 16 ? dispatch_group<64, 16>(p, stream) : dispatch_group<64, 32>(p, stream);
+    return p.std_layout ? dispatch_layout<true>(p, stream) : dispatch_layout<false>(p, stream);
 }
 
 }  // namespace pa

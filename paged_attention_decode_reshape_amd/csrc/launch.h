@@ -14,6 +14,10 @@ hipError_t launch_cache_write_shuffled(const void *key, const void *value, void 
                                        int64_t num_tokens, int Hkv, int D, int B,
                                        int64_t num_blocks, hipStream_t stream);
 
+hipError_t launch_cache_write_standard(const void *key, const void *value, void *k_cache,
+                                       void *v_cache, const int64_t *slot_mapping,
+                                       int64_t num_tokens, int Hkv, int D, int B,
+                                       int64_t num_blocks, hipStream_t stream);
 hipError_t launch_cache_write_latent(const void *latent, void *kv_cache,
                                      const int64_t *slot_mapping, int64_t num_tokens, int Dl,
                                      int B, int64_t num_blocks, hipStream_t stream);
@@ -22,8 +26,8 @@ struct DecodeParams {
     void *out;                 // bf16 [S, Hq, D]
     float *lse;                // f32 [S, Hq] or null
     const void *query;         // bf16 [S, Hq, D]
-    const void *k_cache;       // shuffled
-    const void *v_cache;       // shuffled
+    const void *k_cache;       // shuffled (or standard: std_layout)
+    const void *v_cache;       // shuffled (or standard: std_layout)
     const int32_t *block_table;
     int32_t max_blocks;
     const int32_t *context_lens;
@@ -41,10 +45,13 @@ struct DecodeParams {
     int32_t num_cus;              // compute units of the device (balanced split)
     // Fused cache write (null slot_mapping: none): new_key / new_value
     // [S, Hkv, D] bf16, sequence s's token goes to slot slot_mapping[s]
-    // (< 0: skipped) of the shuffled caches, written by the workgroup that
+    // (< 0: skipped) of the caches, written by the workgroup that
     // reads the sequence's last token before it reads it.
     const void *new_key, *new_value;
     const int64_t *slot_mapping;
+    // nonzero: k_cache / v_cache are in the standard layout
+    // [num_blocks, block_size, kv_heads, head_dim] instead of the shuffled one
+    int32_t std_layout;
 };
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);

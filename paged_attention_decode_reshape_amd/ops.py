@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
 
 LAYOUT_SHUFFLED_KV = 0
 LAYOUT_MLA_LATENT = 1
+LAYOUT_STANDARD_KV = 2
 _BF16, _F32 = 0, 1
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
@@ -47,6 +48,9 @@ _SIGS = {
     "pa_paged_decode_attn_write": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                     _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
                                     _sz, _vp], _i32),
+    "pa_paged_decode_attn_layout": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                     _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32,
+                                     _vp, _sz, _vp], _i32),
     "pa_mla_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
     "pa_mla_decode_attn": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                             _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
@@ -132,7 +136,8 @@ def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], k_cache:
     """Write new tokens into the paged cache.
 
     Shuffled: key/value [T, Hkv, D] bf16, k_cache [NB, Hkv, D/8, B, 8],
-    v_cache [NB, Hkv, B/8, D, 8].  MLA latent: key [T, Dl], value None,
+    v_cache [NB, Hkv, B/8, D, 8].  Standard (kept for comparison): k_cache,
+    v_cache [NB, B, Hkv, D].  MLA latent: key [T, Dl], value None,
     k_cache [NB, B, Dl], v_cache None.  slot_mapping [T] int64.
     """
     lib = library()
@@ -146,6 +151,17 @@ def reshape_and_cache(key: torch.Tensor, value: Optional[torch.Tensor], k_cache:
         NB, B = k_cache.shape[0], k_cache.shape[3]
         if (value.shape != key.shape or tuple(k_cache.shape) != (NB, Hkv, D // 8, B, 8)
                 or tuple(v_cache.shape) != (NB, Hkv, B // 8, D, 8)):
+            raise ValueError("cache shapes do not match key/value")
+        vptr, vcptr = value.data_ptr(), v_cache.data_ptr()
+    elif layout == LAYOUT_STANDARD_KV:
+        _gpu("key", key, torch.bfloat16, 3)
+        _gpu("value", value, torch.bfloat16, 3)
+        _gpu("k_cache", k_cache, torch.bfloat16, 4)
+        _gpu("v_cache", v_cache, torch.bfloat16, 4)
+        T, Hkv, D = key.shape
+        NB, B = k_cache.shape[0], k_cache.shape[1]
+        if (value.shape != key.shape or tuple(k_cache.shape) != (NB, B, Hkv, D)
+                or tuple(v_cache.shape) != (NB, B, Hkv, D)):
             raise ValueError("cache shapes do not match key/value")
         vptr, vcptr = value.data_ptr(), v_cache.data_ptr()
     elif layout == LAYOUT_MLA_LATENT:
@@ -260,6 +276,66 @@ def paged_decode_attn_write(query: torch.Tensor, new_key: torch.Tensor, new_valu
                                         int(max_context_len), S, Hq, Hkv, D, B, NB, float(scale),
                                         int(partition_tokens), _ptr(ws), nbytes, _stream(query))
     _check("paged_decode_attn_write", st)
+    return out, lse
+
+
+def paged_decode_attn_layout(layout: int, query: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, block_table: torch.Tensor,
+                             context_lens: torch.Tensor, scale: float, max_context_len: int,
+                             partition_tokens: int = 0, new_key: Optional[torch.Tensor] = None,
+                             new_value: Optional[torch.Tensor] = None,
+                             slot_mapping: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                             return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """GQA paged decode over caches in `layout` (LAYOUT_SHUFFLED_KV or
+    LAYOUT_STANDARD_KV [NB, B, Hkv, D]), with the fused write of each
+    sequence's new token when new_key / new_value / slot_mapping are given."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, D = query.shape
+    if layout == LAYOUT_STANDARD_KV:
+        _gpu("k_cache", k_cache, torch.bfloat16, 4)
+        _gpu("v_cache", v_cache, torch.bfloat16, 4)
+        NB, B, Hkv, _ = k_cache.shape
+        if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != D:
+            raise ValueError("standard caches must both be [NB, B, Hkv, head_dim]")
+    elif layout == LAYOUT_SHUFFLED_KV:
+        _gpu("k_cache", k_cache, torch.bfloat16, 5)
+        _gpu("v_cache", v_cache, torch.bfloat16, 5)
+        NB, Hkv, _, B, _ = k_cache.shape
+    else:
+        raise ValueError(f"unsupported layout {layout}")
+    given = [t is not None for t in (new_key, new_value, slot_mapping)]
+    if any(given) and not all(given):
+        raise ValueError("new_key, new_value and slot_mapping go together")
+    if all(given):
+        _gpu("new_key", new_key, torch.bfloat16, 3)
+        _gpu("new_value", new_value, torch.bfloat16, 3)
+        _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+        if tuple(new_key.shape) != (S, Hkv, D) or tuple(new_value.shape) != (S, Hkv, D):
+            raise ValueError("new_key / new_value must be [num_seqs, num_kv_heads, head_dim]")
+        if slot_mapping.numel() != S:
+            raise ValueError("slot_mapping must hold one slot per sequence")
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_paged_decode_attn_layout(int(layout), out.data_ptr(), _ptr(lse), query.data_ptr(),
+                                         _ptr(new_key), _ptr(new_value), _ptr(slot_mapping),
+                                         k_cache.data_ptr(), v_cache.data_ptr(),
+                                         block_table.data_ptr(), block_table.shape[1],
+                                         context_lens.data_ptr(), int(max_context_len), S, Hq,
+                                         Hkv, D, B, NB, float(scale), int(partition_tokens),
+                                         _ptr(ws), nbytes, _stream(query))
+    _check("paged_decode_attn_layout", st)
     return out, lse
 
 

@@ -137,6 +137,38 @@ def pin_gather_roundtrip(orc):
         assert np.array_equal(ko[cu[s]:cu[s + 1]], kk[st + tb[s]:st + te[s]])
 
 
+def pin_standard_layout(orc):
+    """The standard-layout write puts (token, head, dim) at [slot // B][slot % B]
+    [head][dim], element by element, leaves every other element alone and
+    skips the slots the shuffled write skips; shuffling the standard cache
+    gives exactly what the shuffled write produces from the same tokens."""
+    for (Hkv, D, B, nb, T) in [(2, 64, 16, 7, 70), (1, 128, 32, 5, 100), (3, 128, 16, 4, 40)]:
+        rng = np.random.default_rng(Hkv * 77 + D + B)
+        slots = rng.choice(nb * B, size=T, replace=False).astype(np.int64)
+        slots[::9] = -1
+        slots[5] = nb * B + 3
+        key = _distinct_tokens(T, Hkv, D, 5)
+        val = _distinct_tokens(T, Hkv, D, 6)
+        ks, vs = orc.empty_standard_cache(nb, B, Hkv, D, fill=0x7FC0)
+        orc.cache_write_standard(key, val, slots, ks, vs)
+        written = np.zeros((nb, B), dtype=bool)
+        for i in range(T):
+            sl = int(slots[i])
+            if sl < 0 or sl >= nb * B:
+                continue
+            written[sl // B, sl % B] = True
+            for g in range(Hkv):
+                for d in range(0, D, 7):
+                    assert ks[sl // B, sl % B, g, d] == key[i, g, d]
+                    assert vs[sl // B, sl % B, g, d] == val[i, g, d]
+        assert np.all(ks[~written] == 0x7FC0) and np.all(vs[~written] == 0x7FC0)
+        assert written.sum() == np.sum((slots >= 0) & (slots < nb * B))
+        kc, vc = orc.empty_shuffled_cache(nb, Hkv, D, B, fill=0x7FC0)
+        orc.cache_write_shuffled(key, val, slots, kc, vc, B)
+        k2, v2 = orc.standard_to_shuffled(ks, vs)
+        assert np.array_equal(k2, kc) and np.array_equal(v2, vc)
+
+
 def pin_latent_write(orc):
     B, nb, Dl, T = 4, 9, 576, 20
     rng = np.random.default_rng(5)
@@ -366,6 +398,7 @@ ALL_PINS = [
     pin_shuffle_layout,
     pin_cache_write_skips,
     pin_gather_roundtrip,
+    pin_standard_layout,
     pin_latent_write,
     pin_decode_vs_numpy,
     pin_decode_closed_forms,

@@ -169,3 +169,39 @@ def test_binding_refuses_cpu_tensors():
 ])
 def test_stream_read_validation(args):
     assert pa.library().pa_stream_read(*args, 1, None) == INVALID
+
+
+def _decode_layout(lib, layout=0, nk=None, nv=None, sm=None, **kw):
+    a = dict(out=FAKE, lse=None, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxb=8, cl=FAKE, maxctx=100,
+             S=4, Hq=8, Hkv=1, D=128, B=16, NB=64, scale=0.1, P=-1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pa_paged_decode_attn_layout(layout, a["out"], a["lse"], a["query"], nk, nv, sm,
+                                           a["k"], a["v"], a["bt"], a["maxb"], a["cl"],
+                                           a["maxctx"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                                           a["NB"], a["scale"], a["P"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=1), INVALID),                            # latent layout is not GQA
+    (dict(layout=3), INVALID),
+    (dict(nk=FAKE), INVALID),                             # write triple incomplete
+    (dict(nk=FAKE, nv=FAKE), INVALID),
+    (dict(nk=FAKE + 4, nv=FAKE, sm=FAKE), INVALID),       # misaligned new key
+    (dict(layout=2, D=96), UNSUPPORTED),
+    (dict(layout=2, B=8), UNSUPPORTED),
+    (dict(layout=2, out=None), INVALID),
+    (dict(layout=2, P=-2), WS_SMALL),
+])
+def test_decode_layout_validation(kw, status):
+    assert _decode_layout(pa.library(), **kw) == status
+
+
+def test_standard_cache_write_validation():
+    lib = pa.library()
+    # value missing, misaligned cache, head_dim not a multiple of 8
+    assert lib.pa_reshape_and_cache(2, FAKE, None, FAKE, FAKE, FAKE, 4, 1, 128, 16, 8, None) == INVALID
+    assert lib.pa_reshape_and_cache(2, FAKE, FAKE, FAKE + 8, FAKE + 8, FAKE, 4, 1, 128, 16, 8,
+                                    None) == INVALID
+    assert lib.pa_reshape_and_cache(2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 100, 16, 8,
+                                    None) == UNSUPPORTED
+    assert lib.pa_reshape_and_cache(2, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 128, 16, 8, None) == OK
