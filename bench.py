@@ -72,7 +72,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="qwen3",
-                    choices=["qwen3", "qwen3_10k", "long_context", "mla", "mla_bs1", "extend"])
+                    choices=["qwen3", "qwen3_10k", "long_context", "mla", "mla_bs1", "extend",
+                             "mixed"])
     ap.add_argument("--kv-layout", default="shuffled", choices=["shuffled", "standard"],
                     help="GQA decode cache layout: the pages' shuffled one, or the standard "
                          "[num_blocks, block_size, kv_heads, head_dim] it replaces (same "
@@ -460,6 +461,77 @@ def extend_algorithmic_flops(case) -> int:
     return pairs * case.Hq * case.D * 4
 
 
+def mixed_case():
+    """One serving-shaped mixed batch: 60 decode requests (contexts
+    U[1000,2000]), 3 extend requests (256 new tokens over ~4000 cached) and
+    1 prefill of 512 tokens, interleaved; 8 q heads on 1 kv head."""
+    from paged_attention_decode_reshape_amd import workloads as W
+    rng = np.random.default_rng(1006)
+    ctx = list(rng.integers(1000, 2001, size=60)) + [4000, 4100, 3900, 0]
+    new = [1] * 60 + [256, 256, 256, 512]
+    perm = rng.permutation(len(ctx))
+    return W.extend_case("mixed_batch", 1006, ctx_lens=[ctx[i] for i in perm],
+                         new_tokens=[new[i] for i in perm], Hq=8, Hkv=1, D=128, block_size=16)
+
+
+def bench_mixed(args):
+    """The routed call (pa_mixed_batch_attn: cache write, decode, extend and
+    prefill paths) on one reordered mixed batch, eager launches."""
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+
+    dev = torch.device("cuda:0")
+    case = mixed_case()
+    pg = case.paging
+    new_rows = case.new_rows()
+    is_new = np.zeros(pg.total_tokens, dtype=bool)
+    is_new[new_rows] = True
+    cached = np.nonzero(~is_new)[0]
+    kc = torch.zeros((pg.num_blocks, case.Hkv, case.D // 8, case.B, 8), dtype=torch.bfloat16,
+                     device=dev)
+    vc = torch.zeros((pg.num_blocks, case.Hkv, case.B // 8, case.D, 8), dtype=torch.bfloat16,
+                     device=dev)
+    pa.reshape_and_cache(case.key[cached].to(dev), case.value[cached].to(dev), kc, vc,
+                         torch.from_numpy(pg.slot_mapping[cached]).to(dev))
+    qsl = case.query_start_loc
+    order, counts = pa.mixed_batch_plan(qsl, case.ctx_lens)
+    starts = np.cumsum(np.concatenate([[0], case.new_lens]))
+    q_rows = np.concatenate([np.arange(qsl[r], qsl[r + 1]) for r in order])
+    n_rows = np.concatenate([new_rows[starts[r]:starts[r + 1]] for r in order])
+    new_qsl = np.concatenate([[0], np.cumsum(case.new_lens[order])]).astype(np.int32)
+    ctx = case.ctx_lens[order].astype(np.int32)
+    q = case.query[torch.from_numpy(q_rows)].to(dev).contiguous()
+    k = case.key[torch.from_numpy(n_rows)].to(dev).contiguous()
+    v = case.value[torch.from_numpy(n_rows)].to(dev).contiguous()
+    slots = torch.from_numpy(pg.slot_mapping[n_rows]).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(pg.block_table[order])).to(dev)
+    qsl_d = torch.from_numpy(new_qsl).to(dev)
+    ctx_d = torch.from_numpy(ctx).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], case.Hq), dtype=torch.float32, device=dev)
+    nbytes = int(pa.library().pa_mixed_batch_workspace_size(
+        len(ctx), new_qsl.ctypes.data, ctx.ctypes.data, case.Hq, case.Hkv, case.D, case.B,
+        case.chunk_budget_tokens))
+    ws = torch.zeros(max(1, nbytes), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        pa.mixed_batch_attn(q, k, v, slots, qsl_d, ctx_d, kc, vc, bt, case.scale, new_qsl, ctx,
+                            chunk_budget_tokens=case.chunk_budget_tokens, out=out, lse=lse,
+                            workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    tokens = int(new_qsl[-1])
+    return {"value": tokens / (ms * 1e-3), "ms_per_step": ms, "counts": [int(c) for c in counts],
+            "new_tokens": tokens, "cached_tokens": int(ctx.sum())}
+
+
 def bench_extend(args, case, label):
     import torch
     import paged_attention_decode_reshape_amd as pa
@@ -624,6 +696,16 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+        return
+    elif args.config == "mixed":
+        r = bench_mixed(args)
+        workload = {"workload": "mixed_batch_60dec_3ext_1pre", "requests": 64,
+                    "decode_extend_prefill": r["counts"], "q_heads": 8, "kv_heads": 1,
+                    "head_dim": 128, "block_size": 16, "new_tokens": r["new_tokens"],
+                    "cached_tokens": r["cached_tokens"],
+                    "step": "pa_mixed_batch_attn: cache write + decode + extend + prefill paths"}
+        line = base_line(args, r, workload, unit="new tok/s")
         print(json.dumps(line), flush=True)
         return
     else:  # extend

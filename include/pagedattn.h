@@ -361,6 +361,67 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * Three-path routing of one mixed batch (the blog's ROCM_AITER_FA section:
+ * decode, extend and prefill requests go to separate kernels, after the model
+ * runner has reordered the batch as [decode : extend : prefill] with a
+ * reorder threshold of one token).
+ *
+ * A request r has query_start_loc[r + 1] - query_start_loc[r] >= 1 new
+ * tokens and context_lens[r] cached tokens before them.  It is decode when
+ * it has one new token (it attends to its cached tokens and itself),
+ * prefill when it has more and nothing is cached, extend otherwise.
+ *
+ * pa_mixed_batch_plan (host only): order_host[0 .. num_reqs) receives the
+ *   request indices in [decode : extend : prefill] order, stable within each
+ *   path; counts_host[0..3) the number of decode, extend and prefill
+ *   requests.  PA_ERR_INVALID_ARG if a request has no new token, a negative
+ *   context, or query_start_loc_host[0] != 0.
+ */
+pa_status pa_mixed_batch_plan(int32_t num_reqs, const int32_t *query_start_loc_host,
+                              const int32_t *context_lens_host, int32_t *order_host,
+                              int32_t *counts_host);
+
+/* Bytes of workspace pa_mixed_batch_attn needs for this batch (0 on invalid
+ * arguments). */
+size_t pa_mixed_batch_workspace_size(int32_t num_reqs, const int32_t *query_start_loc_host,
+                                     const int32_t *context_lens_host, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t chunk_budget_tokens);
+
+/*
+ * Attention of one mixed batch already in [decode : extend : prefill] order
+ * (PA_ERR_INVALID_ARG otherwise), on one stream: the cache write of every
+ * new token (pa_reshape_and_cache, shuffled layout), then
+ * pa_paged_decode_attn over the decode requests (context length cached + 1)
+ * and one pa_chunked_extend_attn over the extend and prefill requests, which
+ * the order leaves adjacent (the extend kernel takes a request with nothing
+ * cached as a causal prefill).
+ * out [T, num_q_heads, head_dim] bf16 and lse [T, num_q_heads] f32
+ *   (nullable) for the T = query_start_loc_host[num_reqs] new tokens, in
+ *   batch order; query [T, num_q_heads, head_dim], key / value
+ *   [T, num_kv_heads, head_dim] bf16 of the new tokens; slot_mapping [T]
+ *   int64 their cache slots (token i of request r at position
+ *   context_lens[r] + i through block_table row r).
+ * query_start_loc [num_reqs + 1], context_lens [num_reqs] int32 on the
+ *   device, with the same values in the _host copies (read during the call).
+ * k_cache, v_cache: the shuffled caches; block_table [num_reqs,
+ *   max_blocks_per_seq].  The workspace (pa_mixed_batch_workspace_size
+ *   bytes, 256-byte aligned) needs no initialisation.
+ * Supported: what the three paths support (head_dim 128 when an extend or
+ *   prefill request is present).  Errors of a path are returned as they are;
+ *   paths launched before it have run.
+ */
+pa_status pa_mixed_batch_attn(void *out, float *lse, const void *query, const void *key,
+                              const void *value, const int64_t *slot_mapping,
+                              const int32_t *query_start_loc, const int32_t *query_start_loc_host,
+                              const int32_t *context_lens, const int32_t *context_lens_host,
+                              void *k_cache, void *v_cache, const int32_t *block_table,
+                              int32_t max_blocks_per_seq, int32_t num_reqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, float scale, int32_t chunk_budget_tokens,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Streaming read (a measurement aid, not a step of the method): reads the
  * `bytes` bytes at src once, in 16-byte vectors, with `workgroups`
  * workgroups of 256 threads walking the buffer grid-stride, and stores one

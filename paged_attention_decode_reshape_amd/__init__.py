@@ -22,6 +22,8 @@ from .ops import (  # noqa: F401
     merge_attn_states,
     mla_decode_attn,
     mla_decode_attn_write,
+    mixed_batch_attn,
+    mixed_batch_plan,
     mla_workspace_size,
     paged_decode_attn,
     paged_decode_attn_layout,

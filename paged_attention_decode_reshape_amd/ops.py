@@ -11,6 +11,7 @@ import math
 import os
 from typing import Optional, Tuple
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +67,11 @@ _SIGS = {
                                 _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp],
                                _i32),
     "pa_stream_read": ([_vp, _sz, _vp, _i32, _i32, _vp], _i32),
+    "pa_mixed_batch_plan": ([_i32, _vp, _vp, _vp, _vp], _i32),
+    "pa_mixed_batch_workspace_size": ([_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pa_mixed_batch_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz,
+                             _vp], _i32),
 }
 
 _lib = None
@@ -567,3 +573,70 @@ def stream_read(src: torch.Tensor, workgroups: int, sink: Optional[torch.Tensor]
     _check("stream_read", lib.pa_stream_read(src.data_ptr(), nbytes, sink.data_ptr(),
                                              int(workgroups), int(bool(verify)), _stream(src)))
     return sink
+
+
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def mixed_batch_plan(query_start_loc_host, context_lens_host) -> Tuple[np.ndarray, np.ndarray]:
+    """Host routing of a mixed batch: (order, counts) with order the request
+    indices in [decode : extend : prefill] order and counts the three sizes."""
+    qsl = _host_i32(query_start_loc_host)
+    ctx = _host_i32(context_lens_host)
+    R = ctx.shape[0]
+    if qsl.shape[0] != R + 1:
+        raise ValueError("query_start_loc needs num_reqs + 1 entries")
+    order = np.zeros(R, dtype=np.int32)
+    counts = np.zeros(3, dtype=np.int32)
+    _check("mixed_batch_plan", library().pa_mixed_batch_plan(
+        R, qsl.ctypes.data, ctx.ctypes.data, order.ctypes.data, counts.ctypes.data))
+    return order, counts
+
+
+def mixed_batch_attn(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                     slot_mapping: torch.Tensor, query_start_loc: torch.Tensor,
+                     context_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     block_table: torch.Tensor, scale: float, query_start_loc_host,
+                     context_lens_host, chunk_budget_tokens: int = 32768,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of a mixed batch in [decode : extend : prefill] order: the
+    new tokens' cache write, then the decode, extend and prefill paths."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("key", key, torch.bfloat16, 3)
+    _gpu("value", value, torch.bfloat16, 3)
+    _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    _gpu("query_start_loc", query_start_loc, torch.int32, 1)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    _gpu("k_cache", k_cache, torch.bfloat16, 5)
+    _gpu("v_cache", v_cache, torch.bfloat16, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    qsl_h = _host_i32(query_start_loc_host)
+    ctx_h = _host_i32(context_lens_host)
+    R = ctx_h.shape[0]
+    T, Hq, D = query.shape
+    NB, Hkv, _, B, _ = k_cache.shape
+    if qsl_h.shape[0] != R + 1 or int(qsl_h[-1]) != T or block_table.shape[0] != R:
+        raise ValueError("batch arrays disagree")
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = int(lib.pa_mixed_batch_workspace_size(R, qsl_h.ctypes.data, ctx_h.ctypes.data, Hq,
+                                                   Hkv, D, B, int(chunk_budget_tokens)))
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_mixed_batch_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), key.data_ptr(),
+                                 value.data_ptr(), slot_mapping.data_ptr(),
+                                 query_start_loc.data_ptr(), qsl_h.ctypes.data,
+                                 context_lens.data_ptr(), ctx_h.ctypes.data, k_cache.data_ptr(),
+                                 v_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+                                 R, Hq, Hkv, D, B, NB, float(scale), int(chunk_budget_tokens),
+                                 _ptr(ws), nbytes, _stream(query))
+    _check("mixed_batch_attn", st)
+    return out, lse

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import paged_attention_decode_reshape_amd as pa
@@ -205,3 +206,52 @@ def test_standard_cache_write_validation():
     assert lib.pa_reshape_and_cache(2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, 100, 16, 8,
                                     None) == UNSUPPORTED
     assert lib.pa_reshape_and_cache(2, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 128, 16, 8, None) == OK
+
+
+def _classify(n, c):
+    return 0 if n <= 1 else (2 if c == 0 else 1)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_mixed_batch_plan(seed):
+    """The plan is the stable [decode : extend : prefill] order of a plain
+    classification (one new token: decode; nothing cached: prefill)."""
+    rng = np.random.default_rng(seed)
+    R = int(rng.integers(1, 40))
+    n = rng.choice([1, 1, 1, 2, 5, 300], size=R)
+    c = rng.choice([0, 0, 1, 17, 4000], size=R)
+    qsl = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    order, counts = pa.mixed_batch_plan(qsl, c)
+    kinds = [_classify(int(n[r]), int(c[r])) for r in range(R)]
+    want = sorted(range(R), key=lambda r: (kinds[r], r))
+    assert list(order) == want
+    assert list(counts) == [kinds.count(0), kinds.count(1), kinds.count(2)]
+
+
+def test_mixed_batch_plan_rejects():
+    with pytest.raises(pa.PagedAttnError):
+        pa.mixed_batch_plan([0, 1, 1], [3, 4])          # a request without new tokens
+    with pytest.raises(pa.PagedAttnError):
+        pa.mixed_batch_plan([1, 2], [3])                # offsets not starting at 0
+    with pytest.raises(pa.PagedAttnError):
+        pa.mixed_batch_plan([0, 1], [-1])               # negative context
+
+
+def test_mixed_batch_attn_validation():
+    """Unordered batches and short workspaces are refused before any launch."""
+    lib = pa.library()
+    i32 = lambda a: np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+    def call(qsl, ctx, ws=FAKE, wsb=1 << 30):
+        qsl, ctx = i32(qsl), i32(ctx)
+        R = ctx.shape[0]
+        return lib.pa_mixed_batch_attn(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, qsl.ctypes.data,
+                                       FAKE, ctx.ctypes.data, FAKE, FAKE, FAKE, 8, R, 8, 1, 128,
+                                       16, 64, 0.1, 32768, ws, wsb, None)
+
+    assert call([0, 5, 6], [10, 3]) == INVALID            # extend before decode
+    assert call([0, 4, 5], [0, 3]) == INVALID             # prefill before decode
+    assert call([0, 4, 10], [0, 3]) == INVALID            # prefill before extend
+    assert call([0, 1, 5], [3, 3], ws=FAKE + 8) == INVALID  # misaligned workspace
+    assert call([0, 1, 5], [3, 3], wsb=16) == WS_SMALL
+    assert call([0, 1, 1], [3, 3]) == INVALID             # request without a token
