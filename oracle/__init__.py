@@ -6,7 +6,9 @@ never imports, links or calls it, and it imports nothing from the GPU
 library: the two share only the seeded input generators.
 
 The arithmetic lives in ``oracle.c`` (plain C, double precision); this file
-builds it with gcc, loads it with ctypes and adapts numpy arrays.  The
+builds it with gcc, loads it with ctypes and adapts numpy arrays.  The FP8
+(E4M3) cache -- codes, quantisation, its write, the gather with
+dequantisation and decode over it -- is plain numpy in ``oracle/fp8.py``.  The
 extend "recipe" (new-token attention, then a loop of gather -> attention ->
 merge over context chunks, then a final merge; "ROCm attention backends"
 blog, extend-path pseudocode) is composed here from the C primitives.

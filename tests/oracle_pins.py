@@ -169,6 +169,121 @@ def pin_standard_layout(orc):
         assert np.array_equal(k2, kc) and np.array_equal(v2, vc)
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache
+# ---------------------------------------------------------------------------
+
+def pin_fp8_codes(orc):
+    """E4M3 values from its definition: hand-listed codes, symmetry,
+    monotonicity; encode inverts decode on every finite code, sends every
+    midpoint between neighbours to the even code and anything just off a
+    midpoint to the nearer one, and saturates at 448."""
+    from oracle import fp8
+    t = fp8.decode_table()
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2 ** -6,
+            0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x48: 4.0, 0x77: 240.0,
+            0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in hand.items():
+        assert t[c] == v, (hex(c), t[c], v)
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.signbit(t[0x80]) and t[0x80] == 0
+    assert np.all(np.diff(t[:0x7F]) > 0)
+    assert np.array_equal(t[0x80:0xFF], -t[:0x7F])
+    finite = np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+    assert np.array_equal(fp8.encode(t[finite].astype(np.float32)), finite)
+    for c in range(0, 0x7E):
+        lo, hi = np.float32(t[c]), np.float32(t[c + 1])
+        mid = np.float32((t[c] + t[c + 1]) / 2)  # exact in float32
+        even = c if c % 2 == 0 else c + 1
+        assert fp8.encode(mid) == even, hex(c)
+        assert fp8.encode(np.nextafter(mid, hi)) == c + 1
+        assert fp8.encode(np.nextafter(mid, lo)) == c
+        assert fp8.encode(-mid) == (even | 0x80)
+    for big in (448.0, 449.0, 464.0, 480.0, 1e30):
+        assert fp8.encode(np.float32(big)) == 0x7E and fp8.encode(np.float32(-big)) == 0xFE
+
+
+def pin_fp8_quantize_and_bf16(orc):
+    """Quantisation error within half a code step times the scale (inside the
+    range), exact for values on the grid; bf16 rounding of known values."""
+    from oracle import fp8
+    rng = np.random.default_rng(81)
+    x = rng.standard_normal(20000).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16
+    xb = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for scale in (2.0 ** -5, 0.0137, 0.5):
+        codes = fp8.quantize_bf16(bits, scale)
+        got = fp8.dequant_f64(codes, scale)
+        y = np.abs(xb) / scale
+        # code spacing at |y|: 2^(floor(log2 y) - 3) above 2^-6, 2^-9 below
+        e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+        step = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+        inside = y < 440
+        assert np.all(np.abs(got - xb)[inside] <= 0.5 * step[inside] * scale * (1 + 1e-6) + 1e-12)
+        assert np.all(np.abs(got[~inside]) == 448 * float(np.float32(scale)))
+    grid = fp8.decode_table()[[0x01, 0x08, 0x38, 0x3F, 0x77]] * 2.0 ** -5
+    gb = fp8.bf16_rne(grid.astype(np.float32))
+    assert np.array_equal(fp8.quantize_bf16(gb, 2.0 ** -5), np.array([0x01, 0x08, 0x38, 0x3F, 0x77]))
+    vals = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -9, 1 + 2.0 ** -7 + 2.0 ** -8, -2.5],
+                    dtype=np.float32)
+    assert list(fp8.bf16_rne(vals)) == [0x3F80, 0x3F80, 0x3F81, 0x3F82, 0xC020]
+
+
+def pin_fp8_cache_layout(orc):
+    """FP8 codes land at [p][g][d div 16][o][d mod 16] and [p][g][o div 16][d][o mod 16],
+    nothing else changes, bad slots are skipped."""
+    from oracle import fp8
+    for (Hkv, D, B, nb, T) in [(2, 64, 16, 5, 40), (1, 128, 32, 3, 60)]:
+        rng = np.random.default_rng(D + B)
+        slots = rng.choice(nb * B, size=T, replace=False).astype(np.int64)
+        slots[::6] = -1
+        key = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+        val = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+        kb = (key.view(np.uint32) >> 16).astype(np.uint16)
+        vb = (val.view(np.uint32) >> 16).astype(np.uint16)
+        kc, vc = fp8.empty_cache(nb, Hkv, D, B)
+        fp8.cache_write(kb, vb, slots, kc, vc, 0.05, 0.07)
+        kq, vq = fp8.quantize_bf16(kb, 0.05), fp8.quantize_bf16(vb, 0.07)
+        seen_k = np.zeros(kc.shape, dtype=bool)
+        seen_v = np.zeros(vc.shape, dtype=bool)
+        for i in range(T):
+            if slots[i] < 0:
+                continue
+            p, o = int(slots[i]) // B, int(slots[i]) % B
+            for g in range(Hkv):
+                for d in range(D):
+                    assert kc[p, g, d // 16, o, d % 16] == kq[i, g, d]
+                    assert vc[p, g, o // 16, d, o % 16] == vq[i, g, d]
+                    seen_k[p, g, d // 16, o, d % 16] = True
+                    seen_v[p, g, o // 16, d, o % 16] = True
+        assert np.all(kc[~seen_k] == 0x7F) and np.all(vc[~seen_v] == 0x7F)
+
+
+def pin_fp8_decode_matches_bf16(orc):
+    """With power-of-two scales every dequantised value is a bf16, so FP8
+    decode equals the C oracle's bf16 decode over caches holding those values."""
+    from oracle import fp8
+    case = W.gqa_decode_case("fp8pin", 82, [1, 17, 100, 300], Hq=8, Hkv=2, D=64, block_size=16)
+    pg = case.paging
+    ks, vs = 2.0 ** -5, 2.0 ** -4
+    kc8, vc8 = fp8.empty_cache(pg.num_blocks, case.Hkv, case.D, case.B)
+    fp8.cache_write(W.bf16_bits(case.key), W.bf16_bits(case.value), pg.slot_mapping, kc8, vc8,
+                    ks, vs)
+    out8, lse8 = fp8.paged_decode_gqa(W.bf16_bits(case.query), kc8, vc8, pg.block_table,
+                                      case.context_lens, case.scale, ks, vs)
+    kdq = fp8.bf16_rne(fp8.dequant_f64(fp8.quantize_bf16(W.bf16_bits(case.key), ks), ks)
+                       .astype(np.float32))
+    vdq = fp8.bf16_rne(fp8.dequant_f64(fp8.quantize_bf16(W.bf16_bits(case.value), vs), vs)
+                       .astype(np.float32))
+    assert np.array_equal(fp8.dequant_f64(fp8.quantize_bf16(W.bf16_bits(case.key), ks), ks),
+                          (kdq.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    kc, vc = orc.empty_shuffled_cache(pg.num_blocks, case.Hkv, case.D, case.B)
+    orc.cache_write_shuffled(kdq, vdq, pg.slot_mapping, kc, vc, case.B)
+    out, lse = orc.paged_decode_gqa(W.bf16_bits(case.query), kc, vc, pg.block_table,
+                                    case.context_lens, case.B, case.scale)
+    _close(out8, out, what="fp8 out")
+    _close(lse8, lse, what="fp8 lse")
+
+
 def pin_latent_write(orc):
     B, nb, Dl, T = 4, 9, 576, 20
     rng = np.random.default_rng(5)
@@ -399,6 +514,10 @@ ALL_PINS = [
     pin_cache_write_skips,
     pin_gather_roundtrip,
     pin_standard_layout,
+    pin_fp8_codes,
+    pin_fp8_quantize_and_bf16,
+    pin_fp8_cache_layout,
+    pin_fp8_decode_matches_bf16,
     pin_latent_write,
     pin_decode_vs_numpy,
     pin_decode_closed_forms,
