@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--config", default="qwen3",
                     choices=["qwen3", "qwen3_10k", "long_context", "mla", "mla_bs1", "extend",
                              "mixed"])
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="GQA decode cache element type: bf16, or FP8 E4M3 codes with "
+                         "per-tensor scales (amax / 448), shuffled layout with x = 16")
     ap.add_argument("--kv-layout", default="shuffled", choices=["shuffled", "standard"],
                     help="GQA decode cache layout: the pages' shuffled one, or the standard "
                          "[num_blocks, block_size, kv_heads, head_dim] it replaces (same "
@@ -106,16 +109,17 @@ def log(msg):
 # GQA decode workloads
 # ---------------------------------------------------------------------------
 
-def gqa_algorithmic_bytes(case, with_write=False) -> int:
+def gqa_algorithmic_bytes(case, with_write=False, kv_bytes=2) -> int:
     """Bytes the method must move per decode launch: every context token's K
-    and V once, q, out, lse, the used block-table entries and lengths (and,
-    with the fused cache write, each new token's K and V read and written
-    plus its slot)."""
+    and V once (kv_bytes per element: 2 bf16, 1 FP8), q, out, lse, the used
+    block-table entries and lengths (and, with the fused cache write, each
+    new token's bf16 K and V read and its cache elements written, plus its
+    slot)."""
     S, Hq, Hkv, D, B = case.S, case.Hq, case.Hkv, case.D, case.B
     n = case.context_lens.astype(np.int64)
-    kv = int(n.sum()) * Hkv * D * 2 * 2
+    kv = int(n.sum()) * Hkv * D * 2 * kv_bytes
     blocks = int(((n + B - 1) // B).sum())
-    write = S * Hkv * D * 2 * 2 * 2 + S * 8 if with_write else 0
+    write = S * Hkv * D * 2 * (2 + kv_bytes) + S * 8 if with_write else 0
     return kv + S * Hq * D * 2 * 2 + S * Hq * 4 + blocks * 4 + S * 4 + write
 
 
@@ -171,8 +175,15 @@ def bench_gqa(args, case, label):
     dev = torch.device("cuda:0")
     pg = case.paging
     std = args.kv_layout == "standard"
+    f8 = args.kv_dtype == "fp8"
+    if std and f8:
+        raise SystemExit("--kv-dtype fp8 uses the shuffled layout only")
     layout = pa.LAYOUT_STANDARD_KV if std else pa.LAYOUT_SHUFFLED_KV
-    pool_bytes = pg.num_blocks * case.Hkv * case.D * case.B * 2 * 2
+    kv_bytes = 1 if f8 else 2
+    pool_bytes = pg.num_blocks * case.Hkv * case.D * case.B * 2 * kv_bytes
+    if f8:  # per-tensor scales from the data's largest magnitude
+        k_scale = float(case.key.abs().max()) / 448.0
+        v_scale = float(case.value.abs().max()) / 448.0
     pools = args.pools or max(1, math.ceil(2 * MALL_BYTES / pool_bytes))
     log(f"[bench] {label}: S={case.S} Hq={case.Hq} Hkv={case.Hkv} D={case.D} B={case.B} "
         f"tokens={pg.total_tokens} pool={pool_bytes / 1e6:.1f} MB x {pools} copies")
@@ -181,6 +192,14 @@ def bench_gqa(args, case, label):
     slots_all = torch.from_numpy(pg.slot_mapping).to(dev)
     caches = []
     for _ in range(pools):
+        if f8:
+            kc = torch.zeros((pg.num_blocks, case.Hkv, case.D // 16, case.B, 16),
+                             dtype=torch.uint8, device=dev)
+            vc = torch.zeros((pg.num_blocks, case.Hkv, case.B // 16, case.D, 16),
+                             dtype=torch.uint8, device=dev)
+            pa.reshape_and_cache_fp8(key, value, kc, vc, slots_all, k_scale, v_scale)
+            caches.append((kc, vc))
+            continue
         if std:
             kc = torch.zeros((pg.num_blocks, case.B, case.Hkv, case.D), dtype=torch.bfloat16,
                              device=dev)
@@ -212,7 +231,13 @@ def bench_gqa(args, case, label):
 
     def decode(i):
         kc, vc = caches[i % pools]
-        if std:  # same kernel over the standard layout
+        if f8:
+            pa.paged_decode_attn_fp8(q, kc, vc, bt, cl, case.scale, max_ctx, k_scale, v_scale,
+                                     partition_tokens=P, new_key=new_k if fused else None,
+                                     new_value=new_v if fused else None,
+                                     slot_mapping=new_slots if fused else None, out=out, lse=lse,
+                                     workspace=ws)
+        elif std:  # same kernel over the standard layout
             pa.paged_decode_attn_layout(layout, q, kc, vc, bt, cl, case.scale, max_ctx,
                                         partition_tokens=P, new_key=new_k if fused else None,
                                         new_value=new_v if fused else None,
@@ -228,7 +253,10 @@ def bench_gqa(args, case, label):
     def step(i):
         if not fused:
             kc, vc = caches[i % pools]
-            pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots, layout=layout)
+            if f8:
+                pa.reshape_and_cache_fp8(new_k, new_v, kc, vc, new_slots, k_scale, v_scale)
+            else:
+                pa.reshape_and_cache(new_k, new_v, kc, vc, new_slots, layout=layout)
         decode(i)
 
     # eager reference for the graph check
@@ -282,7 +310,7 @@ def bench_gqa(args, case, label):
     # back-to-back launches (rotating pools), averaged per launch
     dec_ms = time_launches(decode, min(args.steps, 400))
 
-    algo = gqa_algorithmic_bytes(case, with_write=fused)
+    algo = gqa_algorithmic_bytes(case, with_write=fused, kv_bytes=kv_bytes)
     achieved = algo / (dec_ms * 1e-3) / 1e9
     tok_s = case.S / (ms_per_step * 1e-3)
     return {
@@ -297,6 +325,7 @@ def bench_gqa(args, case, label):
         "pools": pools,
         "cache_write": "fused" if fused else "separate launch",
         "kv_layout": args.kv_layout,
+        "kv_dtype": args.kv_dtype,
         "step_launch": "graph replay" if replay else "eager",
         "partition_tokens": ("balanced" if pa.decode_uses_balanced_split(case.S, case.Hkv, max_ctx, P)
                              else pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P)),
@@ -653,7 +682,7 @@ def main():
         r = bench_gqa(args, case, "qwen3_decode_64req")
         workload = {"workload": "qwen3_235b_tp8_decode_64req", "requests": 64, "q_heads": 8,
                     "kv_heads": 1, "head_dim": 128, "block_size": 16,
-                    "context_lens": "U[1000,2000]", "kv_layout": r["kv_layout"],
+                    "context_lens": "U[1000,2000]", "kv_layout": r["kv_layout"], "kv_dtype": r["kv_dtype"],
                     "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"],
                     "cache_write": r["cache_write"], "step_launch": r["step_launch"]}
     elif args.config == "qwen3_10k":
@@ -661,7 +690,7 @@ def main():
         r = bench_gqa(args, case, "qwen3_decode_64req_10k")
         workload = {"workload": "qwen3_235b_tp8_decode_64req_10k", "requests": 64, "q_heads": 8,
                     "kv_heads": 1, "head_dim": 128, "block_size": 16,
-                    "context_lens": "U[10000,11000]", "kv_layout": r["kv_layout"],
+                    "context_lens": "U[10000,11000]", "kv_layout": r["kv_layout"], "kv_dtype": r["kv_dtype"],
                     "kv_pool_copies": r["pools"], "partition_tokens": r["partition_tokens"],
                     "cache_write": r["cache_write"], "step_launch": r["step_launch"]}
     elif args.config == "long_context":
@@ -669,7 +698,7 @@ def main():
         r = bench_gqa(args, case, "long_context_decode")
         workload = {"workload": "long_context_gqa_decode_8req", "requests": 8, "q_heads": 64,
                     "kv_heads": 4, "head_dim": 128, "block_size": 16,
-                    "context_lens": "U[32768,131072]", "kv_layout": r["kv_layout"],
+                    "context_lens": "U[32768,131072]", "kv_layout": r["kv_layout"], "kv_dtype": r["kv_dtype"],
                     "kv_pool_copies": r["pools"],
                     "partition_tokens": r["partition_tokens"], "cache_write": r["cache_write"]}
     elif args.config in ("mla", "mla_bs1"):
@@ -741,12 +770,14 @@ def main():
                         "paged_decode_kernel (partitions")
                        + " + fused merge"
                        + (" + fused cache write" if r["cache_write"] == "fused" else "")
-                       + (", standard layout)" if r["kv_layout"] == "standard" else ")")),
+                       + (", standard layout" if r["kv_layout"] == "standard" else "")
+                       + (", FP8 cache)" if r["kv_dtype"] == "fp8" else ")")),
             "achieved": r["hbm_gbps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(args.config) if r["kv_layout"] == "shuffled" else None,
+            "traffic": (measured_traffic(args.config)
+                        if r["kv_layout"] == "shuffled" and r["kv_dtype"] == "bf16" else None),
             "algo_bytes_per_launch": r["algo_bytes"],
             "avg_launch_ms": r["decode_ms"],
         },

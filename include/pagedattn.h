@@ -215,6 +215,65 @@ pa_status pa_paged_decode_attn_layout(int32_t layout, void *out, float *lse, con
                                       int64_t num_blocks, float scale, int32_t partition_tokens,
                                       void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * FP8 KV cache.  The pages' MLA extend path gathers the context and
+ * dequantises it when the cache is quantised (the blog's AITER MLA section,
+ * extend pseudocode); they fix no format.  This library reads it as OCP
+ * 8-bit E4M3 ("fn": no infinities, largest finite 448) with one float32
+ * scale per tensor:
+ *   value(code) = E4M3(code) * scale,
+ *   code(x)     = nearest E4M3 value to float32(x) * float32(1 / scale),
+ *                 ties to the even code, saturating at +-448.
+ * Caches hold codes (uint8) in the shuffled layout with x = 16 codes per
+ * 16-byte vector:
+ *   k_cache [num_blocks, num_kv_heads, head_dim / 16, block_size, 16]
+ *   v_cache [num_blocks, num_kv_heads, block_size / 16, head_dim, 16].
+ *
+ * pa_reshape_and_cache_fp8: key, value [num_tokens, num_kv_heads, head_dim]
+ *   bf16 quantised with k_scale / v_scale into the caches at slot_mapping
+ *   (as pa_reshape_and_cache: negative or out-of-pool slots are skipped).
+ * Supported: head_dim in {64, 128}, block_size in {16, 32}; scales finite and
+ * positive (PA_ERR_INVALID_ARG otherwise).
+ */
+pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, void *k_cache,
+                                   void *v_cache, const int64_t *slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, float k_scale, float v_scale, void *stream);
+
+/*
+ * GQA paged decode over FP8 caches: pa_paged_decode_attn (or, with new_key,
+ * new_value and slot_mapping all given, pa_paged_decode_attn_write, the new
+ * token quantised as pa_reshape_and_cache_fp8 does) with K and V the
+ * dequantised values code * k_scale and code * v_scale.  The codes are
+ * converted exactly (every E4M3 value is a bf16); k_scale folds into the
+ * softmax scale and v_scale into the output.  Workspace as for
+ * pa_paged_decode_attn.  Supported: head_dim in {64, 128}, block_size in
+ * {16, 32}, group size 1..16.
+ */
+pa_status pa_paged_decode_attn_fp8(void *out, float *lse, const void *query, const void *new_key,
+                                   const void *new_value, const int64_t *slot_mapping,
+                                   void *k_cache, void *v_cache, const int32_t *block_table,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, float scale, float k_scale, float v_scale,
+                                   int32_t partition_tokens, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
+ * The gather with dequantisation: pa_gather_cache_chunk over FP8 caches,
+ * writing bf16(float(E4M3(code)) * scale) (float32 product, rounded to
+ * nearest even) into the standard [rows, num_kv_heads, head_dim] outputs.
+ * Supported: head_dim 128, block_size a multiple of 16.
+ */
+pa_status pa_gather_cache_chunk_fp8(void *k_out, void *v_out, const void *k_cache,
+                                    const void *v_cache, const int32_t *block_table,
+                                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, int32_t iteration,
+                                    int32_t chunk_tokens, float k_scale, float v_scale,
+                                    void *stream);
+
 /* Bytes of workspace pa_mla_decode_attn needs (0 if no split is needed).
  * For partition_tokens 0 and -2 the size depends on the current device's
  * compute-unit count. */

@@ -103,10 +103,9 @@ def cache_write(key_bits, value_bits, slot_mapping, k_cache, v_cache, k_scale, v
         if not 0 <= slot < nb * B:
             continue
         p, o = int(slot) // B, int(slot) % B
-        for g in range(Hkv):
-            for d in range(D):
-                k_cache[p, g, d // X, o, d % X] = kq[i, g, d]
-                v_cache[p, g, o // X, d, o % X] = vq[i, g, d]
+        # dim d = 16 c + j of token o: K at [p][g][c][o][j], V at [p][g][o div 16][d][o mod 16]
+        k_cache[p, :, :, o, :] = kq[i].reshape(Hkv, D // X, X)
+        v_cache[p, :, o // X, :, o % X] = vq[i]
 
 
 def gather_codes(k_cache, v_cache, block_table, seq, tokens):
@@ -117,9 +116,8 @@ def gather_codes(k_cache, v_cache, block_table, seq, tokens):
     V = np.empty_like(K)
     for j, t in enumerate(tokens):
         p, o = int(block_table[seq][t // B]), t % B
-        for d in range(D):
-            K[j, :, d] = k_cache[p, :, d // X, o, d % X]
-            V[j, :, d] = v_cache[p, :, o // X, d, o % X]
+        K[j] = k_cache[p, :, :, o, :].reshape(Hkv, D)
+        V[j] = v_cache[p, :, o // X, :, o % X]
     return K, V
 
 

@@ -18,6 +18,7 @@ from .ops import (  # noqa: F401
     extend_chunk_tokens,
     extend_workspace_size,
     gather_cache_chunk,
+    gather_cache_chunk_fp8,
     library,
     merge_attn_states,
     mla_decode_attn,
@@ -26,8 +27,10 @@ from .ops import (  # noqa: F401
     mixed_batch_plan,
     mla_workspace_size,
     paged_decode_attn,
+    paged_decode_attn_fp8,
     paged_decode_attn_layout,
     paged_decode_attn_write,
     reshape_and_cache,
+    reshape_and_cache_fp8,
     stream_read,
 )

@@ -183,8 +183,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 // GQA decode, optionally with the fused cache write of each sequence's new
 // token (new_key / new_value / slot_mapping all null: no write).
-static pa_status decode_impl(bool std_layout, void *out, float *lse, const void *query,
-                             const void *new_key,
+// layout: 0 shuffled bf16, 1 standard bf16, 2 shuffled FP8 (k_scale,
+// v_scale used only there)
+static pa_status decode_impl(int layout, float k_scale, float v_scale, void *out, float *lse,
+                             const void *query, const void *new_key,
                              const void *new_value, const int64_t *slot_mapping,
                              const void *k_cache, const void *v_cache,
                              const int32_t *block_table, int32_t max_blocks_per_seq,
@@ -249,7 +251,11 @@ static pa_status decode_impl(bool std_layout, void *out, float *lse, const void 
     p.new_key = new_key;
     p.new_value = new_value;
     p.slot_mapping = slot_mapping;
-    p.std_layout = std_layout ? 1 : 0;
+    p.layout = layout;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.k_inv = 1.0f / k_scale;
+    p.v_inv = 1.0f / v_scale;
     return from_hip(launch_paged_decode(p, (hipStream_t)stream));
 }
 
@@ -260,7 +266,7 @@ pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const v
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int64_t num_blocks, float scale, int32_t partition_tokens,
                                void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_impl(false, out, lse, query, nullptr, nullptr, nullptr, k_cache, v_cache,
+    return decode_impl(0, 1.f, 1.f, out, lse, query, nullptr, nullptr, nullptr, k_cache, v_cache,
                        block_table,
                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
@@ -279,7 +285,7 @@ pa_status pa_paged_decode_attn_write(void *out, float *lse, const void *query,
     if (!new_key || !new_value || !slot_mapping) return PA_ERR_INVALID_ARG;
     if (!aligned(new_key, 16) || !aligned(new_value, 16) || !aligned(slot_mapping, 8))
         return PA_ERR_INVALID_ARG;
-    return decode_impl(false, out, lse, query, new_key, new_value, slot_mapping, k_cache,
+    return decode_impl(0, 1.f, 1.f, out, lse, query, new_key, new_value, slot_mapping, k_cache,
                        v_cache, block_table, max_blocks_per_seq, context_lens, max_context_len,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        scale, partition_tokens, workspace, workspace_bytes, stream);
@@ -301,11 +307,54 @@ pa_status pa_paged_decode_attn_layout(int32_t layout, void *out, float *lse, con
     if (given == 3 && (!aligned(new_key, 16) || !aligned(new_value, 16) ||
                        !aligned(slot_mapping, 8)))
         return PA_ERR_INVALID_ARG;
-    return decode_impl(layout == PA_LAYOUT_STANDARD_KV, out, lse, query, new_key, new_value,
+    return decode_impl(layout == PA_LAYOUT_STANDARD_KV ? 1 : 0, 1.f, 1.f, out, lse, query,
+                       new_key, new_value,
                        slot_mapping, k_cache, v_cache, block_table, max_blocks_per_seq,
                        context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
                        head_dim, block_size, num_blocks, scale, partition_tokens, workspace,
                        workspace_bytes, stream);
+}
+
+static bool valid_scale(float s) { return isfinite(s) && s > 0.f && isfinite(1.0f / s); }
+
+pa_status pa_paged_decode_attn_fp8(void *out, float *lse, const void *query, const void *new_key,
+                                   const void *new_value, const int64_t *slot_mapping,
+                                   void *k_cache, void *v_cache, const int32_t *block_table,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, float scale, float k_scale, float v_scale,
+                                   int32_t partition_tokens, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_INVALID_ARG;
+    const int given = (new_key != nullptr) + (new_value != nullptr) + (slot_mapping != nullptr);
+    if (given != 0 && given != 3) return PA_ERR_INVALID_ARG;
+    if (given == 3 && (!aligned(new_key, 16) || !aligned(new_value, 16) ||
+                       !aligned(slot_mapping, 8)))
+        return PA_ERR_INVALID_ARG;
+    return decode_impl(2, k_scale, v_scale, out, lse, query, new_key, new_value, slot_mapping,
+                       k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, void *k_cache,
+                                   void *v_cache, const int64_t *slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, float k_scale, float v_scale,
+                                   void *stream) {
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+        return PA_ERR_INVALID_ARG;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return PA_ERR_INVALID_ARG;
+    if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    return from_hip(launch_cache_write_fp8(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                           num_kv_heads, head_dim, block_size, num_blocks,
+                                           1.0f / k_scale, 1.0f / v_scale, (hipStream_t)stream));
 }
 
 size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_dim,
@@ -435,12 +484,12 @@ int32_t pa_extend_chunk_tokens(int32_t num_seqs, int32_t block_size, int32_t chu
     return c < block_size ? block_size : c;
 }
 
-pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
-                                const void *v_cache, const int32_t *block_table,
-                                int32_t max_blocks_per_seq, const int32_t *context_lens,
-                                int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t block_size, int64_t num_blocks, int32_t iteration,
-                                int32_t chunk_tokens, void *stream) {
+static pa_status gather_impl(bool fp8, float k_scale, float v_scale, void *k_out, void *v_out,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             int32_t iteration, int32_t chunk_tokens, void *stream) {
     if (num_seqs < 0 || num_kv_heads < 1 || block_size < 1 || num_blocks < 1 ||
         max_blocks_per_seq < 1 || iteration < 0 || chunk_tokens < 1)
         return PA_ERR_INVALID_ARG;
@@ -449,7 +498,7 @@ pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
     if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(k_cache, 16) ||
         !aligned(v_cache, 16))
         return PA_ERR_INVALID_ARG;
-    if (head_dim != 128 || block_size % 8 != 0 || chunk_tokens % block_size != 0 ||
+    if (head_dim != 128 || block_size % (fp8 ? 16 : 8) != 0 || chunk_tokens % block_size != 0 ||
         num_seqs > 65535 || (int64_t)iteration * chunk_tokens > kMaxContext)
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
@@ -467,7 +516,34 @@ pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
     gp.chunk = chunk_tokens;
     gp.k_out = k_out;
     gp.v_out = v_out;
+    gp.fp8 = fp8 ? 1 : 0;
+    gp.k_scale = k_scale;
+    gp.v_scale = v_scale;
     return from_hip(launch_gather_chunk(gp, chunk_tokens, (hipStream_t)stream));
+}
+
+pa_status pa_gather_cache_chunk(void *k_out, void *v_out, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table,
+                                int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, int32_t iteration,
+                                int32_t chunk_tokens, void *stream) {
+    return gather_impl(false, 1.f, 1.f, k_out, v_out, k_cache, v_cache, block_table,
+                       max_blocks_per_seq, context_lens, num_seqs, num_kv_heads, head_dim,
+                       block_size, num_blocks, iteration, chunk_tokens, stream);
+}
+
+pa_status pa_gather_cache_chunk_fp8(void *k_out, void *v_out, const void *k_cache,
+                                    const void *v_cache, const int32_t *block_table,
+                                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, int32_t iteration,
+                                    int32_t chunk_tokens, float k_scale, float v_scale,
+                                    void *stream) {
+    if (!isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_INVALID_ARG;
+    return gather_impl(true, k_scale, v_scale, k_out, v_out, k_cache, v_cache, block_table,
+                       max_blocks_per_seq, context_lens, num_seqs, num_kv_heads, head_dim,
+                       block_size, num_blocks, iteration, chunk_tokens, stream);
 }
 
 // Extend workspace: the group prefix [S + 1], the new tokens' V in 8-token

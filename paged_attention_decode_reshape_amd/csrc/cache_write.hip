@@ -15,6 +15,7 @@
 // 8 dims of one token and issues 8 two-byte stores; neighbouring threads hit
 // neighbouring 16-byte vectors, which L2 write-combines.
 #include "common.h"
+#include "fp8.h"
 #include "launch.h"
 
 namespace pa {
@@ -67,6 +68,34 @@ __global__ __launch_bounds__(256) void cache_write_standard_kernel(
     v_cache[dst] = value[idx];
 }
 
+// FP8 shuffled layout (x = 16 codes): thread (token, kv head, 16-dim group
+// c) quantises 16 dims of K into one 16-byte vector,
+// k_cache[p][g][c][o][0..16), and 16 dims of V into 16 single bytes,
+// v_cache[p][g][o / 16][16 c + j][o % 16].
+__global__ __launch_bounds__(256) void cache_write_fp8_kernel(
+    const uint4 *__restrict__ key, const uint4 *__restrict__ value, uint4 *__restrict__ k_cache,
+    uint8_t *__restrict__ v_cache, const int64_t *__restrict__ slot_mapping, int64_t num_tokens,
+    int Hkv, int D, int B, int64_t num_blocks, float k_inv, float v_inv) {
+    const int C16 = D / kFp8X;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= num_tokens * Hkv * C16) return;
+    const int c = (int)(idx % C16);
+    const int g = (int)((idx / C16) % Hkv);
+    const int64_t i = idx / ((int64_t)C16 * Hkv);
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * B) return;
+    const int64_t p = slot / B;
+    const int o = (int)(slot % B);
+    const size_t src = (size_t)idx * 2;  // two bf16 vectors per 16 dims
+    k_cache[((p * Hkv + g) * C16 + c) * B + o] = quantize16(key[src], key[src + 1], k_inv);
+    const uint4 vq = quantize16(value[src], value[src + 1], v_inv);
+    const uint32_t w[4] = {vq.x, vq.y, vq.z, vq.w};
+    uint8_t *vdst = v_cache + (((p * Hkv + g) * (B / kFp8X) + o / kFp8X) * D + c * kFp8X) * kFp8X +
+                    o % kFp8X;
+#pragma unroll
+    for (int j = 0; j < 16; j++) vdst[j * kFp8X] = (uint8_t)(w[j / 4] >> ((j % 4) * 8));
+}
+
 // Latent rows are contiguous in both source and cache: one 16-byte vector per thread.
 __global__ __launch_bounds__(256) void cache_write_latent_kernel(
     const uint4 *__restrict__ latent, uint4 *__restrict__ kv_cache,
@@ -109,6 +138,19 @@ hipError_t launch_cache_write_standard(const void *key, const void *value, void 
     hipLaunchKernelGGL(cache_write_standard_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                        (const uint4 *)key, (const uint4 *)value, (uint4 *)k_cache,
                        (uint4 *)v_cache, slot_mapping, num_tokens, row_vecs, B, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_write_fp8(const void *key, const void *value, void *k_cache, void *v_cache,
+                                  const int64_t *slot_mapping, int64_t num_tokens, int Hkv, int D,
+                                  int B, int64_t num_blocks, float k_inv, float v_inv,
+                                  hipStream_t stream) {
+    const int64_t grid = (num_tokens * Hkv * (D / kFp8X) + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cache_write_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4 *)key, (const uint4 *)value, (uint4 *)k_cache,
+                       (uint8_t *)v_cache, slot_mapping, num_tokens, Hkv, D, B, num_blocks, k_inv,
+                       v_inv);
     return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@
 
 #include "common.h"
 #include "decode_common.h"
+#include "fp8.h"
 #include "launch.h"
 
 namespace pa {
@@ -45,6 +46,8 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
+// cache layouts the kernels are built for (DecodeParams::layout)
+constexpr int kLayShuffled = 0, kLayStd = 1, kLayFp8 = 2;
 constexpr int kStep = 64;  // tokens per wave step
 
 // context length limited to the host's bound and what the block table covers
@@ -461,6 +464,41 @@ __device__ __forceinline__ uint32_t std_lane_off(int row, int col, int Hkv) {
     return (uint32_t)((col * Hkv * D + row * (D / 32) * 8) * 2);
 }
 
+// FP8 shuffled layout (x = 16): lane (row, col) loads token `col`'s K vectors
+// row * CQ8 .. row * CQ8 + CQ8 - 1 (CQ8 = D / 64; 16 dims each) from
+// k_cache[tile][c][o][0..16), and lane l the V vector of dim l + 64 jj
+// (the sub-block's 16 tokens) from v_cache[tile][o / 16][d][0..16).
+template <int D, int B>
+__device__ __forceinline__ void load_k_sub8(const char *k_cache, size_t tile, int half, bool live,
+                                            uint32_t lane_off, uint4 (&kq)[D / 32]) {
+    constexpr int CQ8 = D / 64;
+    const char *base = k_cache + tile * (size_t)(D * B) + half * kSub * kFp8X;
+    const auto r = tile_rsrc(base, live ? (uint32_t)(D * B - half * kSub * kFp8X) : 0u);
+#pragma unroll
+    for (int i = 0; i < CQ8; i++) kq[i] = buf_load16(r, lane_off + i * B * 16);
+}
+template <int D, int B>
+__device__ __forceinline__ void load_v_sub8(const char *v_cache, size_t tile, int half, bool live,
+                                            uint32_t lane_off, uint4 (&vv)[2][D / 64]) {
+    constexpr int DV = D / 64;
+    const char *base = v_cache + ((tile * (B / kFp8X) + half) * (size_t)D) * kFp8X;
+    const auto r = tile_rsrc(base, live ? (uint32_t)(D * kFp8X) : 0u);
+#pragma unroll
+    for (int jj = 0; jj < DV; jj++) vv[0][jj] = buf_load16(r, lane_off + 64 * jj * 16);
+}
+// 16 FP8 K codes per vector -> the bf16 pairs the QK blocks read (exact)
+template <int D>
+__device__ __forceinline__ void k_fp8_to_bf16(const uint4 (&raw)[D / 32], uint4 (&kb)[D / 32]) {
+    constexpr int CQ8 = D / 64;
+#pragma unroll
+    for (int i = 0; i < CQ8; i++) {
+        fp8x4_to_bf16x2(raw[i].x, kb[2 * i].x, kb[2 * i].y);
+        fp8x4_to_bf16x2(raw[i].y, kb[2 * i].z, kb[2 * i].w);
+        fp8x4_to_bf16x2(raw[i].z, kb[2 * i + 1].x, kb[2 * i + 1].y);
+        fp8x4_to_bf16x2(raw[i].w, kb[2 * i + 1].z, kb[2 * i + 1].w);
+    }
+}
+
 // V from the standard layout, transposed through the wave's LDS region into
 // the shuffled V registers: raw[i] (token col's dims 8 (row CQ + i) ..
 // + 7) is scattered as 2-byte values to slot (token group col / 8, dim),
@@ -535,7 +573,7 @@ __device__ __forceinline__ int bt_entry(const DecodeParams &p, int s, int start)
 // tracks the block ids of 64 sub-blocks at a time, so longer ranges are
 // taken in windows; bt_first is bt_entry() of the first window, loaded
 // early by the caller.
-template <int D, int B, int G, int SUBS, bool SHARED, bool STD>
+template <int D, int B, int G, int SUBS, bool SHARED, int LAY>
 __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g, int range_start,
                                              int range_end, int bt_first, const uint32_t (&qreg)[G],
                                              float (&m)[G], float (&lsum)[G],
@@ -545,13 +583,16 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
     constexpr bool kPairs = G >= 2;
     constexpr int HS = kPairs ? 2 : 1;
     constexpr int kWindow = (SHARED ? kWaves : 1) * 64 * kSub;  // tokens per window
+    constexpr bool STD = LAY == kLayStd, FP8 = LAY == kLayFp8;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int row = lane >> 4, col = lane & 15;
-    const float sl2 = p.scale * kLog2e;
+    const float sl2 = p.scale * kLog2e * (FP8 ? p.k_scale : 1.f);
     const char *kc = reinterpret_cast<const char *>(p.k_cache);
     const char *vc = reinterpret_cast<const char *>(p.v_cache);
-    const uint32_t k_off = STD ? std_lane_off<D>(row, col, p.Hkv) : k_lane_off<D, B>(row, col);
+    const uint32_t k_off = STD ? std_lane_off<D>(row, col, p.Hkv)
+                               : FP8 ? (uint32_t)((row * (D / 64) * B + col) * 16)
+                                     : k_lane_off<D, B>(row, col);
     const uint32_t v_off = STD ? k_off : (uint32_t)lane * 16;
     char *vt_region = nullptr;
     if constexpr (STD) {
@@ -593,6 +634,8 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
             locate(k, tile, half);
             if constexpr (STD)
                 load_rows_std<D>(kc, std_first(k), p.Hkv, k < nmine, k_off, kq);
+            else if constexpr (FP8)
+                load_k_sub8<D, B>(kc, tile, half, k < nmine, k_off, kq);
             else
                 load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
         };
@@ -603,6 +646,8 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
             if constexpr (STD)
                 load_rows_std<D>(vc, std_first(k), p.Hkv, k < nmine,
                                  v_off, reinterpret_cast<uint4(&)[CQ]>(vv));
+            else if constexpr (FP8)
+                load_v_sub8<D, B>(vc, tile, half, k < nmine, v_off, vv);
             else
                 load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
         };
@@ -612,14 +657,18 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
         // When it starts, the loads in flight are, oldest first: this
         // sub-block's K and V, then the other buffer's K and V; the explicit
         // waits say exactly that to the compiler.
-        constexpr int LK = CQ, LV = 2 * DV;  // load instructions per sub-block
-        auto compute_sub = [&](int k, const uint4 (&kq)[CQ], const uint4 (&vv)[2][DV]) {
+        // load instructions per sub-block
+        constexpr int LK = FP8 ? D / 64 : CQ, LV = FP8 ? DV : 2 * DV;
+        auto compute_sub = [&](int k, const uint4 (&kin)[CQ], const uint4 (&vv)[2][DV]) {
             const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
             const int nvalid =
                 k < nmine && readlane_i32(bid, min(k, 63)) >= 0 ? min(kSub, end - t0) : 0;
             float z[G];
             if (nvalid > 0) {
                 wait_vm_loads<LV + LK + LV>();
+                uint4 kconv[CQ];
+                if constexpr (FP8) k_fp8_to_bf16<D>(kin, kconv);
+                const uint4 (&kq)[CQ] = FP8 ? kconv : kin;
                 // QK: each lane sums a quarter of the dims; the rows are then
                 // summed, leaving every row with the 16 scores of the sub-block
                 float a[G][2];
@@ -696,14 +745,25 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
                     float vf[DV][8];
 #pragma unroll
                     for (int jj = 0; jj < DV; jj++) {
-                        uint4 v = vsrc[tg][jj];
-                        if (nvalid < kSub) {
-                            v.x = mask_pair(v.x, 0, nv);
-                            v.y = mask_pair(v.y, 2, nv);
-                            v.z = mask_pair(v.z, 4, nv);
-                            v.w = mask_pair(v.w, 6, nv);
+                        if constexpr (FP8) {  // tokens 8 tg .. 8 tg + 7 of the 16-code vector
+                            const uint4 raw = vv[0][jj];
+                            fp8x4_to_f32(tg ? raw.z : raw.x, vf[jj]);
+                            fp8x4_to_f32(tg ? raw.w : raw.y, vf[jj] + 4);
+                            if (nvalid < kSub) {
+#pragma unroll
+                                for (int e = 0; e < 8; e++)
+                                    if (e >= nv) vf[jj][e] = 0.f;
+                            }
+                        } else {
+                            uint4 v = vsrc[tg][jj];
+                            if (nvalid < kSub) {
+                                v.x = mask_pair(v.x, 0, nv);
+                                v.y = mask_pair(v.y, 2, nv);
+                                v.z = mask_pair(v.z, 4, nv);
+                                v.w = mask_pair(v.w, 6, nv);
+                            }
+                            widen8(v, vf[jj]);
                         }
-                        widen8(v, vf[jj]);
                     }
 #pragma unroll
                     for (int h = 0; h < G; h += HS) {
@@ -732,6 +792,12 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
             load_v(k + 2, vA);
             compute_sub(k + 1, kB, vB);
         }
+    }
+    if constexpr (FP8) {  // V codes were summed unscaled
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int jj = 0; jj < DV; jj++) acc[h][jj] *= p.v_scale;
     }
 }
 
@@ -846,10 +912,39 @@ __device__ __forceinline__ bool count_finished(int *counter, int nparts) {
 // v_cache[block][g][o / 8][d][o % 8].  Threads 0..D/8-1 write the key,
 // D/8..2D/8-1 the value; the stores are complete and the workgroup has met at
 // a barrier before any wave reads the cache.  Called by every thread.
-template <int D, int B, bool STD>
+template <int D, int B, int LAY>
 __device__ __forceinline__ void write_new_token(const DecodeParams &p, int s, int g) {
     constexpr int C = D / 8;
+    constexpr bool STD = LAY == kLayStd;
     const int64_t slot = as_const<int64_t>(p.slot_mapping)[s];
+    if constexpr (LAY == kLayFp8) {
+        // thread t < D / 16: K codes of dims 16 t .. 16 t + 15 (one vector);
+        // D / 16 <= t < D / 8: V codes of the same dims (16 single bytes)
+        constexpr int C16 = D / kFp8X;
+        if (slot >= 0 && slot < p.num_blocks * B && (int)threadIdx.x < 2 * C16) {
+            const int t = threadIdx.x, j = t % C16;
+            const int64_t blk = slot / B;
+            const int o = (int)(slot - blk * B);
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(t < C16 ? p.new_key : p.new_value) +
+                ((size_t)s * p.Hkv + g) * C + 2 * j;
+            if (t < C16) {
+                uint4 *kc = reinterpret_cast<uint4 *>(const_cast<void *>(p.k_cache));
+                kc[(((size_t)blk * p.Hkv + g) * C16 + j) * B + o] = quantize16(src[0], src[1], p.k_inv);
+            } else {
+                const uint4 vq = quantize16(src[0], src[1], p.v_inv);
+                const uint32_t w[4] = {vq.x, vq.y, vq.z, vq.w};
+                uint8_t *vc = reinterpret_cast<uint8_t *>(const_cast<void *>(p.v_cache)) +
+                              ((((size_t)blk * p.Hkv + g) * (B / kFp8X) + o / kFp8X) * D +
+                               j * kFp8X) * kFp8X + o % kFp8X;
+#pragma unroll
+                for (int e = 0; e < 16; e++) vc[e * kFp8X] = (uint8_t)(w[e / 4] >> ((e % 4) * 8));
+            }
+            wait_stores();
+        }
+        __syncthreads();
+        return;
+    }
     if (slot >= 0 && slot < p.num_blocks * B && (int)threadIdx.x < 2 * C) {
         const int t = threadIdx.x, c = t % C;
         const int64_t blk = slot / B;
@@ -888,7 +983,7 @@ __device__ __forceinline__ void write_empty(const DecodeParams &p, int s, int g,
 
 // Explicit partitions: one workgroup per (partition, kv head, sequence),
 // partition-major grid; partials in [S, Hq, max_parts, D].
-template <int D, int B, int G, int SUBS, bool STD>
+template <int D, int B, int G, int SUBS, int LAY>
 __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     constexpr int DV = D / 64;
     const int units = p.S * p.Hkv;
@@ -909,7 +1004,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     const int ctx = clamp_ctx<B>(p, ctx_raw);
     if (start >= ctx) {
         if (ctx == 0 && part == 0) {
-            if (p.slot_mapping) write_new_token<D, B, STD>(p, s, g);
+            if (p.slot_mapping) write_new_token<D, B, LAY>(p, s, g);
             write_empty(p, s, g, Ga, D);
         }
         return;
@@ -917,10 +1012,10 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     const int end = min(start + P, ctx);
     const int nparts = (ctx + P - 1) / P;
     // the partition holding the last token writes the new token first
-    if (p.slot_mapping && end == ctx) write_new_token<D, B, STD>(p, s, g);
+    if (p.slot_mapping && end == ctx) write_new_token<D, B, LAY>(p, s, g);
     float m[G], lsum[G], acc[G][DV];
     reset_state<G, DV>(m, lsum, acc);
-    attend_range<D, B, G, SUBS, true, STD>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
+    attend_range<D, B, G, SUBS, true, LAY>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
 
     __shared__ WaveMergeLDS<D, G> sm;
     const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
@@ -1024,7 +1119,7 @@ __device__ __forceinline__ void merge_unit_partials(const DecodeParams &p, size_
     }
 }
 
-template <int D, int B, int G, bool STD>
+template <int D, int B, int G, int LAY>
 __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
     constexpr int DV = D / 64;
     const int NW = gridDim.x, w = blockIdx.x;
@@ -1040,7 +1135,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
     for (int s = w; s < p.S; s += NW)
         if (readlane_i32(ctx_in(s & ~63), s & 63) == 0)
             for (int g = 0; g < Hkv; g++) {
-                if (p.slot_mapping) write_new_token<D, B, STD>(p, s, g);
+                if (p.slot_mapping) write_new_token<D, B, LAY>(p, s, g);
                 write_empty(p, s, g, Ga, D);
             }
 
@@ -1101,13 +1196,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
 
         const int tb = a * kSub, te = min(b * kSub, ctx);
         // the piece holding the last token writes the new token first
-        if (p.slot_mapping && te == ctx) write_new_token<D, B, STD>(p, s, g);
+        if (p.slot_mapping && te == ctx) write_new_token<D, B, LAY>(p, s, g);
         const int bt_first = bt_entry<B, 1, true>(p, s, tb);
         uint32_t qreg[G];
         load_queries<D, G>(p, s, g, Ga, qreg);
         float m[G], lsum[G], acc[G][DV];
         reset_state<G, DV>(m, lsum, acc);
-        attend_range<D, B, G, 1, true, STD>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
+        attend_range<D, B, G, 1, true, LAY>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
 
         const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
         const auto prs = coherent_rsrc(p.part_out + (size_t)v * Ga * D, (uint32_t)Ga * D * 4);
@@ -1126,7 +1221,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
     }
 }
 
-template <int D, int B, int G, bool STD>
+template <int D, int B, int G, int LAY>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
     constexpr int kSubs = 1;  // waves take single sub-blocks in turn
     if (p.balanced_workgroups > 0) {
@@ -1134,45 +1229,47 @@ hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
         static const int per_cu = [] {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(&paged_decode_balanced_kernel<D, B, G, STD>),
+                    &n, reinterpret_cast<const void *>(&paged_decode_balanced_kernel<D, B, G, LAY>),
                     256, 0) != hipSuccess || n < 1)
                 n = 1;
             return n;
         }();
         const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G, STD>), dim3((unsigned)nw),
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G, LAY>), dim3((unsigned)nw),
                            dim3(256), 0, stream, p);
         return hipGetLastError();
     }
     const int64_t units = (int64_t)p.max_parts * p.S * p.Hkv;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((paged_decode_kernel<D, B, G, kSubs, STD>), dim3((unsigned)units), dim3(256), 0,
+    hipLaunchKernelGGL((paged_decode_kernel<D, B, G, kSubs, LAY>), dim3((unsigned)units), dim3(256), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-template <int D, int B, bool STD>
+template <int D, int B, int LAY>
 hipError_t dispatch_group(const DecodeParams &p, hipStream_t stream) {
     const int Ga = p.Hq / p.Hkv;
-    if (Ga <= 1) return launch_partition<D, B, 1, STD>(p, stream);
-    if (Ga <= 2) return launch_partition<D, B, 2, STD>(p, stream);
-    if (Ga <= 4) return launch_partition<D, B, 4, STD>(p, stream);
-    if (Ga <= 8) return launch_partition<D, B, 8, STD>(p, stream);
-    return launch_partition<D, B, 16, STD>(p, stream);
+    if (Ga <= 1) return launch_partition<D, B, 1, LAY>(p, stream);
+    if (Ga <= 2) return launch_partition<D, B, 2, LAY>(p, stream);
+    if (Ga <= 4) return launch_partition<D, B, 4, LAY>(p, stream);
+    if (Ga <= 8) return launch_partition<D, B, 8, LAY>(p, stream);
+    return launch_partition<D, B, 16, LAY>(p, stream);
 }
 
-template <bool STD>
+template <int LAY>
 hipError_t dispatch_layout(const DecodeParams &p, hipStream_t stream) {
     if (p.D == 128)
-        return p.B == 16 ? dispatch_group<128, 16, STD>(p, stream)
-                         : dispatch_group<128, 32, STD>(p, stream);
-    return p.B == 16 ? dispatch_group<64, 16, STD>(p, stream) : dispatch_group<64, 32, STD>(p, stream);
+        return p.B == 16 ? dispatch_group<128, 16, LAY>(p, stream)
+                         : dispatch_group<128, 32, LAY>(p, stream);
+    return p.B == 16 ? dispatch_group<64, 16, LAY>(p, stream) : dispatch_group<64, 32, LAY>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
-    return p.std_layout ? dispatch_layout<true>(p, stream) : dispatch_layout<false>(p, stream);
+    if (p.layout == kLayStd) return dispatch_layout<kLayStd>(p, stream);
+    if (p.layout == kLayFp8) return dispatch_layout<kLayFp8>(p, stream);
+    return dispatch_layout<kLayShuffled>(p, stream);
 }
 
 }  // namespace pa

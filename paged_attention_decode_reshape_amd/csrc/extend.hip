@@ -38,6 +38,7 @@
 // are dealt to the 8 XCDs round-robin) and share its L2.
 #include "common.h"
 #include "decode_common.h"
+#include "fp8.h"
 #include "launch.h"
 
 namespace pa {
@@ -118,6 +119,56 @@ __global__ __launch_bounds__(256) void gather_chunk_kernel(GatherParams p) {
             vo[((size_t)(row0 + t) * p.Hkv + g) * C + d8 / 8] = make_uint4(d[0], d[1], d[2], d[3]);
         }
     }
+}
+
+// FP8 cache: thread (token, kv head, 8-dim group) writes 8 dequantised bf16
+// values of K and of V: bf16(float(code) * scale), round to nearest even.
+// K's 8 codes are half of one 16-byte vector; V's are one byte of each of 8
+// dims' token vectors.
+__global__ __launch_bounds__(256) void gather_chunk_fp8_kernel(GatherParams p) {
+    const int r = blockIdx.y;
+    const int it = p.iteration;
+    const int len = chunk_len(p.context_lens, r, it, p.chunk);
+    const int C8 = kD / 8, C16 = kD / kFp8X;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int t = (int)(idx / (p.Hkv * C8));
+    if (t >= len) return;
+    const int g = (int)(idx / C8 % p.Hkv), c8 = (int)(idx % C8);
+    const int row = chunk_start(p.context_lens, r, it, p.chunk) + t;
+    const int pos = it * p.chunk + t;
+    const int bi = pos / p.B, o = pos % p.B;
+    const int b = bi < p.max_blocks ? p.block_table[(size_t)r * p.max_blocks + bi] : -1;
+    const bool ok = b >= 0 && (int64_t)b < p.num_blocks;
+    const uint8_t *kc = reinterpret_cast<const uint8_t *>(p.k_cache);
+    const uint8_t *vc = reinterpret_cast<const uint8_t *>(p.v_cache);
+    uint32_t kw[2] = {0, 0}, vw[2] = {0, 0};
+    if (ok) {
+        const uint2 k2 = *reinterpret_cast<const uint2 *>(
+            kc + ((((size_t)b * p.Hkv + g) * C16 + c8 / 2) * p.B + o) * kFp8X + (c8 % 2) * 8);
+        kw[0] = k2.x;
+        kw[1] = k2.y;
+        const uint8_t *vs =
+            vc + ((((size_t)b * p.Hkv + g) * (p.B / kFp8X) + o / kFp8X) * kD + c8 * 8) * kFp8X +
+            o % kFp8X;
+#pragma unroll
+        for (int e = 0; e < 8; e++) vw[e / 4] |= (uint32_t)vs[e * kFp8X] << ((e % 4) * 8);
+    }
+    float kf[8], vf[8];
+    fp8x4_to_f32(kw[0], kf);
+    fp8x4_to_f32(kw[1], kf + 4);
+    fp8x4_to_f32(vw[0], vf);
+    fp8x4_to_f32(vw[1], vf + 4);
+    uint32_t ko[4], vo[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        ko[e] = f32_to_bf16_rne(kf[2 * e] * p.k_scale) |
+                (f32_to_bf16_rne(kf[2 * e + 1] * p.k_scale) << 16);
+        vo[e] = f32_to_bf16_rne(vf[2 * e] * p.v_scale) |
+                (f32_to_bf16_rne(vf[2 * e + 1] * p.v_scale) << 16);
+    }
+    const size_t dst = ((size_t)row * p.Hkv + g) * C8 + c8;
+    reinterpret_cast<uint4 *>(p.k_out)[dst] = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+    reinterpret_cast<uint4 *>(p.v_out)[dst] = make_uint4(vo[0], vo[1], vo[2], vo[3]);
 }
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t &a, const bf16x8_t &b, const f32x16_t &c) {
@@ -556,6 +607,12 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(ExtendParams p) {
 
 hipError_t launch_gather_chunk(const GatherParams &p, int max_chunk_len, hipStream_t stream) {
     if (max_chunk_len <= 0 || p.S <= 0) return hipSuccess;
+    if (p.fp8) {
+        const int64_t threads = (int64_t)max_chunk_len * p.Hkv * (kD / 8);
+        hipLaunchKernelGGL(gather_chunk_fp8_kernel, dim3((unsigned)((threads + 255) / 256), (unsigned)p.S),
+                           dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     const unsigned gx = (unsigned)((max_chunk_len + 7) / 8);
     hipLaunchKernelGGL(gather_chunk_kernel, dim3(gx, (unsigned)p.S), dim3(256), 0, stream, p);
     return hipGetLastError();

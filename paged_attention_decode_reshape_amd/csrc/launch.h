@@ -18,6 +18,10 @@ hipError_t launch_cache_write_standard(const void *key, const void *value, void 
                                        void *v_cache, const int64_t *slot_mapping,
                                        int64_t num_tokens, int Hkv, int D, int B,
                                        int64_t num_blocks, hipStream_t stream);
+hipError_t launch_cache_write_fp8(const void *key, const void *value, void *k_cache, void *v_cache,
+                                  const int64_t *slot_mapping, int64_t num_tokens, int Hkv, int D,
+                                  int B, int64_t num_blocks, float k_inv, float v_inv,
+                                  hipStream_t stream);
 hipError_t launch_cache_write_latent(const void *latent, void *kv_cache,
                                      const int64_t *slot_mapping, int64_t num_tokens, int Dl,
                                      int B, int64_t num_blocks, hipStream_t stream);
@@ -49,9 +53,12 @@ struct DecodeParams {
     // reads the sequence's last token before it reads it.
     const void *new_key, *new_value;
     const int64_t *slot_mapping;
-    // nonzero: k_cache / v_cache are in the standard layout
-    // [num_blocks, block_size, kv_heads, head_dim] instead of the shuffled one
-    int32_t std_layout;
+    // cache layout: 0 shuffled bf16; 1 standard bf16 [num_blocks, block_size,
+    // kv_heads, head_dim]; 2 shuffled FP8 E4M3 codes (x = 16) with per-tensor
+    // scales (value = code * scale; the fused write quantises with the
+    // float32 reciprocals k_inv, v_inv)
+    int32_t layout;
+    float k_scale, v_scale, k_inv, v_inv;
 };
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
@@ -96,6 +103,10 @@ struct GatherParams {
     int64_t num_blocks;
     int32_t iteration, chunk;  // gathers context tokens [iteration * chunk, +chunk)
     void *k_out, *v_out;       // standard [rows, Hkv, D] bf16, request-major
+    // nonzero: the caches hold FP8 codes (x = 16 layout) and the gather
+    // writes bf16(code value * scale)
+    int32_t fp8;
+    float k_scale, v_scale;
 };
 
 hipError_t launch_gather_chunk(const GatherParams &p, int max_chunk_len, hipStream_t stream);

@@ -67,6 +67,13 @@ _SIGS = {
                                 _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp],
                                _i32),
     "pa_stream_read": ([_vp, _sz, _vp, _i32, _i32, _vp], _i32),
+    "pa_reshape_and_cache_fp8": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _f32,
+                                  _f32, _vp], _i32),
+    "pa_paged_decode_attn_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _f32, _i32,
+                                  _vp, _sz, _vp], _i32),
+    "pa_gather_cache_chunk_fp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                   _i64, _i32, _i32, _f32, _f32, _vp], _i32),
     "pa_mixed_batch_plan": ([_i32, _vp, _vp, _vp, _vp], _i32),
     "pa_mixed_batch_workspace_size": ([_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_mixed_batch_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -640,3 +647,106 @@ def mixed_batch_attn(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor
                                  _ptr(ws), nbytes, _stream(query))
     _check("mixed_batch_attn", st)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache: uint8 codes, x = 16 shuffled layout, per-tensor scales
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                          v_scale: float) -> None:
+    """Quantise key/value [T, Hkv, D] bf16 into k_cache [NB, Hkv, D/16, B, 16] and
+    v_cache [NB, Hkv, B/16, D, 16] (uint8 E4M3 codes)."""
+    lib = library()
+    _gpu("key", key, torch.bfloat16, 3)
+    _gpu("value", value, torch.bfloat16, 3)
+    _gpu("k_cache", k_cache, torch.uint8, 5)
+    _gpu("v_cache", v_cache, torch.uint8, 5)
+    _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    T, Hkv, D = key.shape
+    NB, B = k_cache.shape[0], k_cache.shape[3]
+    if (value.shape != key.shape or tuple(k_cache.shape) != (NB, Hkv, D // 16, B, 16)
+            or tuple(v_cache.shape) != (NB, Hkv, B // 16, D, 16) or slot_mapping.numel() != T):
+        raise ValueError("fp8 cache shapes do not match key/value")
+    _check("reshape_and_cache_fp8", lib.pa_reshape_and_cache_fp8(
+        key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, Hkv, D, B, NB, float(k_scale), float(v_scale), _stream(key)))
+
+
+def paged_decode_attn_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                          max_context_len: int, k_scale: float, v_scale: float,
+                          partition_tokens: int = 0, new_key: Optional[torch.Tensor] = None,
+                          new_value: Optional[torch.Tensor] = None,
+                          slot_mapping: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """GQA paged decode over FP8 caches (K = code * k_scale, V = code * v_scale),
+    with the fused quantised write when new_key / new_value / slot_mapping are given."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("k_cache", k_cache, torch.uint8, 5)
+    _gpu("v_cache", v_cache, torch.uint8, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, D = query.shape
+    NB, Hkv, _, B, _ = k_cache.shape
+    given = [t is not None for t in (new_key, new_value, slot_mapping)]
+    if any(given) and not all(given):
+        raise ValueError("new_key, new_value and slot_mapping go together")
+    if all(given):
+        _gpu("new_key", new_key, torch.bfloat16, 3)
+        _gpu("new_value", new_value, torch.bfloat16, 3)
+        _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_paged_decode_attn_fp8(out.data_ptr(), _ptr(lse), query.data_ptr(), _ptr(new_key),
+                                      _ptr(new_value), _ptr(slot_mapping), k_cache.data_ptr(),
+                                      v_cache.data_ptr(), block_table.data_ptr(),
+                                      block_table.shape[1], context_lens.data_ptr(),
+                                      int(max_context_len), S, Hq, Hkv, D, B, NB, float(scale),
+                                      float(k_scale), float(v_scale), int(partition_tokens),
+                                      _ptr(ws), nbytes, _stream(query))
+    _check("paged_decode_attn_fp8", st)
+    return out, lse
+
+
+def gather_cache_chunk_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_table: torch.Tensor, context_lens: torch.Tensor, iteration: int,
+                           chunk_tokens: int, k_scale: float, v_scale: float,
+                           k_out: Optional[torch.Tensor] = None,
+                           v_out: Optional[torch.Tensor] = None
+                           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gather_cache_chunk over FP8 caches: dequantised bf16 [rows, Hkv, D] outputs."""
+    lib = library()
+    _gpu("k_cache", k_cache, torch.uint8, 5)
+    _gpu("v_cache", v_cache, torch.uint8, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    NB, Hkv, C, B, x = k_cache.shape
+    D = C * x
+    S = context_lens.shape[0]
+    rows = S * chunk_tokens
+    if k_out is None:
+        k_out = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=k_cache.device)
+    _gpu("k_out", k_out, torch.bfloat16, 3)
+    _gpu("v_out", v_out, torch.bfloat16, 3)
+    if k_out.shape[0] < rows or v_out.shape[0] < rows:
+        raise ValueError("output tensors need num_seqs * chunk_tokens rows")
+    st = lib.pa_gather_cache_chunk_fp8(k_out.data_ptr(), v_out.data_ptr(), k_cache.data_ptr(),
+                                       v_cache.data_ptr(), block_table.data_ptr(),
+                                       block_table.shape[1], context_lens.data_ptr(), S, Hkv, D,
+                                       B, NB, int(iteration), int(chunk_tokens), float(k_scale),
+                                       float(v_scale), _stream(k_cache))
+    _check("gather_cache_chunk_fp8", st)
+    return k_out, v_out

@@ -255,3 +255,28 @@ def test_mixed_batch_attn_validation():
     assert call([0, 1, 5], [3, 3], ws=FAKE + 8) == INVALID  # misaligned workspace
     assert call([0, 1, 5], [3, 3], wsb=16) == WS_SMALL
     assert call([0, 1, 1], [3, 3]) == INVALID             # request without a token
+
+
+def test_fp8_entry_validation():
+    """FP8 entries refuse bad scales, shapes and partial write triples before any launch."""
+    lib = pa.library()
+    nan = float("nan")
+    # cache write: bad scale, misaligned, unsupported head_dim / block size
+    w = lambda **k: lib.pa_reshape_and_cache_fp8(
+        k.get("key", FAKE), FAKE, k.get("kc", FAKE), FAKE, FAKE, 4, 1, k.get("D", 128),
+        k.get("B", 16), 8, k.get("ks", 0.1), k.get("vs", 0.1), None)
+    assert w(ks=0.0) == INVALID and w(vs=-1.0) == INVALID and w(ks=nan) == INVALID
+    assert w(ks=1e-45) == INVALID                      # 1 / scale overflows
+    assert w(kc=FAKE + 4) == INVALID
+    assert w(D=96) == UNSUPPORTED and w(B=8) == UNSUPPORTED
+    # decode: partial triple, bad scales, unsupported shapes
+    d = lambda nk=None, nv=None, sm=None, ks=0.1, vs=0.1, D=128, B=16, P=-1: \
+        lib.pa_paged_decode_attn_fp8(FAKE, None, FAKE, nk, nv, sm, FAKE, FAKE, FAKE, 8, FAKE, 100,
+                                     4, 8, 1, D, B, 64, 0.1, ks, vs, P, None, 0, None)
+    assert d(nk=FAKE) == INVALID and d(ks=0.0) == INVALID and d(vs=float("inf")) == INVALID
+    assert d(D=96) == UNSUPPORTED and d(B=8) == UNSUPPORTED
+    assert d(P=-2) == WS_SMALL
+    # gather: block size must be a multiple of 16
+    g = lambda B=16, ks=0.1: lib.pa_gather_cache_chunk_fp8(
+        FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 1, 128, B, 64, 0, 64, ks, 0.1, None)
+    assert g(B=8) == UNSUPPORTED and g(ks=nan) == INVALID
