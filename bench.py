@@ -43,9 +43,9 @@ METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 
 # workload -> (sources, sha256 prefix of those sources, bytes per launch).
 _CSRC = "paged_attention_decode_reshape_amd/csrc/"
 MEASURED_TRAFFIC = {
-    "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "1f63770bc2456ce4", 52.39e6),
+    "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "c7875b7c37b66cf0", 52.39e6),
     "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "25a9444b960aeec7", 237.19e6),
-    "extend": ((_CSRC + "extend.hip", _CSRC + "decode_common.h"), "17bb752e1679d13e", 1294.56e6),
+    "extend": ((_CSRC + "extend.hip", _CSRC + "decode_common.h"), "74420352bf28f086", 1294.40e6),
 }
 
 
