@@ -326,42 +326,106 @@ def bench_gqa(args, case, label):
         "cache_write": "fused" if fused else "separate launch",
         "kv_layout": args.kv_layout,
         "kv_dtype": args.kv_dtype,
+        "kv_scales": (k_scale, v_scale) if f8 else None,
         "step_launch": "graph replay" if replay else "eager",
         "partition_tokens": ("balanced" if pa.decode_uses_balanced_split(case.S, case.Hkv, max_ctx, P)
                              else pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P)),
     }
 
 
-def cpu_baseline_gqa(case, seconds):
+def cpu_baseline_gqa(case, seconds, kv_layout="shuffled", kv_scales=None):
     """The oracle as it stands on this host: decode steps (cache write of the
     new tokens + exact attention through the block table), repeated for
-    about `seconds`."""
+    about `seconds`.  The oracle of the step's own cache: the shuffled bf16
+    cache (C, fp64), the standard-layout one (shuffled on the fly, then the
+    same C decode) or the FP8 one (numpy, fp64 over the dequantised values;
+    every step covers a sample of the requests)."""
+    import oracle
+    from oracle import fp8 as OF
+    from paged_attention_decode_reshape_amd import workloads as W
+
+    orc = oracle.get()
+    pg = case.paging
+    rows = case.new_token_rows()
+    kb, vb = W.bf16_bits(case.key), W.bf16_bits(case.value)
+    nk, nv, ns = kb[rows], vb[rows], pg.slot_mapping[rows]
+    qb = W.bf16_bits(case.query)
+    seqs = list(range(case.S))
+    if kv_scales is not None:
+        ks, vs = kv_scales
+        kc, vc = OF.empty_cache(pg.num_blocks, case.Hkv, case.D, case.B)
+        OF.cache_write(kb, vb, pg.slot_mapping, kc, vc, ks, vs)
+        seqs = seqs[::8]  # the numpy decode takes ~20 ms per request
+
+        def step():
+            OF.cache_write(nk, nv, ns, kc, vc, ks, vs)
+            OF.paged_decode_gqa(qb, kc, vc, pg.block_table, case.context_lens, case.scale, ks,
+                                vs, seqs=seqs)
+    elif kv_layout == "standard":
+        kc, vc = orc.empty_standard_cache(pg.num_blocks, case.B, case.Hkv, case.D)
+        orc.cache_write_standard(kb, vb, pg.slot_mapping, kc, vc)
+
+        def step():
+            orc.cache_write_standard(nk, nv, ns, kc, vc)
+            orc.paged_decode_gqa_standard(qb, kc, vc, pg.block_table, case.context_lens,
+                                          case.scale)
+    else:
+        kc, vc = orc.empty_shuffled_cache(pg.num_blocks, case.Hkv, case.D, case.B)
+        orc.cache_write_shuffled(kb, vb, pg.slot_mapping, kc, vc, case.B)
+
+        def step():
+            orc.cache_write_shuffled(nk, nv, ns, kc, vc, case.B)
+            orc.paged_decode_gqa(qb, kc, vc, pg.block_table, case.context_lens, case.B,
+                                 case.scale)
+    from threadpoolctl import threadpool_limits
+    reps = 0
+    t0 = time.perf_counter()
+    # numpy's BLAS on one thread, so the FP8 oracle's `cores` is exact (the C
+    # oracle's OpenMP threads are not limited)
+    with threadpool_limits(1, user_api="blas"):
+        while True:
+            step()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    what = ("FP8 numpy oracle, every 8th request" if kv_scales is not None else
+            "standard-layout cache, shuffled on the fly" if kv_layout == "standard" else
+            "shuffled bf16 cache")
+    return {"value": len(seqs) * reps / el, "unit": "tok/s",
+            "cores": orc.max_threads() if kv_scales is None else 1, "kind": "oracle",
+            "sample": f"{reps} decode steps of the same workload ({len(seqs)} of {case.S} "
+                      f"requests per step, {what}) in {el:.1f} s, fp64"}
+
+
+def cpu_baseline_mixed(case, seconds):
+    """The oracle's extend definition over the whole mixed batch (decode,
+    extend and prefill requests alike), repeated for about `seconds`."""
     import oracle
     from paged_attention_decode_reshape_amd import workloads as W
 
     orc = oracle.get()
-    kc, vc = orc.empty_shuffled_cache(case.paging.num_blocks, case.Hkv, case.D, case.B)
-    orc.cache_write_shuffled(W.bf16_bits(case.key), W.bf16_bits(case.value),
-                             case.paging.slot_mapping, kc, vc, case.B)
-    rows = case.new_token_rows()
-    nk = W.bf16_bits(case.key)[rows]
-    nv = W.bf16_bits(case.value)[rows]
-    ns = case.paging.slot_mapping[rows]
+    pg = case.paging
+    kb, vb = W.bf16_bits(case.key), W.bf16_bits(case.value)
+    kc, vc = orc.empty_shuffled_cache(pg.num_blocks, case.Hkv, case.D, case.B)
+    orc.cache_write_shuffled(kb, vb, pg.slot_mapping, kc, vc, case.B)
+    rows = case.new_rows()
+    kn, vn = kb[rows], vb[rows]
     qb = W.bf16_bits(case.query)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        orc.cache_write_shuffled(nk, nv, ns, kc, vc, case.B)
-        orc.paged_decode_gqa(qb, kc, vc, case.paging.block_table, case.context_lens, case.B,
-                             case.scale)
+        orc.extend(qb, kn, vn, case.query_start_loc, kc, vc, case.paging.block_table,
+                   case.ctx_lens, case.B, case.scale)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": case.S * reps / el, "unit": "tok/s", "cores": orc.max_threads(),
+    tokens = int(case.query_start_loc[-1])
+    return {"value": tokens * reps / el, "unit": "new tok/s", "cores": orc.max_threads(),
             "kind": "oracle",
-            "sample": f"{reps} full decode steps of the same workload ({case.S} requests) "
-                      f"in {el:.1f} s, fp64"}
+            "sample": f"{reps} passes over the whole mixed batch ({tokens} new tokens) in "
+                      f"{el:.1f} s, fp64"}
 
 
 # ---------------------------------------------------------------------------
@@ -735,6 +799,9 @@ def main():
                     "cached_tokens": r["cached_tokens"],
                     "step": "pa_mixed_batch_attn: cache write + decode + extend + prefill paths"}
         line = base_line(args, r, workload, unit="new tok/s")
+        if not args.no_cpu_baseline:
+            log("[bench] timing the oracle on the host cores")
+            line["cpu_baseline"] = cpu_baseline_mixed(mixed_case(), args.cpu_seconds)
         print(json.dumps(line), flush=True)
         return
     else:  # extend
@@ -788,7 +855,8 @@ def main():
         line["hbm_read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
-        line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds, r["kv_layout"],
+                                                r["kv_scales"])
     print(json.dumps(line), flush=True)
 
 
