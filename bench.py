@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="qwen3",
                     choices=["qwen3", "qwen3_10k", "long_context", "mla", "mla_bs1", "extend",
-                             "mixed"])
+                             "mixed", "merge"])
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="GQA decode cache element type: bf16, or FP8 E4M3 codes with "
                          "per-tensor scales (amax / 448), shuffled layout with x = 16")
@@ -625,6 +625,40 @@ def bench_mixed(args):
             "new_tokens": tokens, "cached_tokens": int(ctx.sum())}
 
 
+def bench_merge(args):
+    """The standalone merge_attn_states at the chunked-extend shape: two fp32
+    partial results [4096, 64, 128] with their LSEs -> bf16 output and LSE
+    (one context-chunk merge of the pages' extend loop), over rotated copies
+    larger than the Infinity Cache; HIP events over back-to-back launches."""
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+
+    T, H, D = 4096, 64, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(1007)
+    per = 2 * T * H * D * 4 + 2 * T * H * 4
+    copies = max(2, math.ceil(2 * MALL_BYTES / per))
+    sets = []
+    for _ in range(copies):
+        po = torch.randn((T, H, D), generator=g).to(dev)
+        so = torch.randn((T, H, D), generator=g).to(dev)
+        pl = (torch.randn((T, H), generator=g) * 3).to(dev)
+        sl = (torch.randn((T, H), generator=g) * 3).to(dev)
+        sets.append((po, pl, so, sl))
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        po, pl, so, sl = sets[i % copies]
+        pa.merge_attn_states(po, pl, so, sl, out=out, out_lse=lse)
+
+    ms = time_launches(launch, min(args.steps, 400))
+    nbytes = per + T * H * D * 2 + T * H * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"value": T / (ms * 1e-3), "ms_per_step": ms, "algo_bytes": nbytes, "gbps": gbps,
+            "copies": copies}
+
+
 def bench_extend(args, case, label):
     import torch
     import paged_attention_decode_reshape_amd as pa
@@ -789,6 +823,24 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+        return
+    elif args.config == "merge":
+        r = bench_merge(args)
+        workload = {"workload": "merge_attn_states_4096x64x128", "tokens": 4096, "heads": 64,
+                    "head_dim": 128, "inputs": "two fp32 partials + LSEs", "output": "bf16 + LSE",
+                    "copies": r["copies"]}
+        line = base_line(args, r, workload, unit="rows/s")
+        line["dtype"] = "f32"
+        line["roofline"] = {"bound": "hbm", "kernel": "merge_pair_kernel", "achieved": r["gbps"],
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                            "algo_bytes_per_launch": r["algo_bytes"],
+                            "avg_launch_ms": r["ms_per_step"]}
+        if not args.no_read_ceiling:
+            rc = read_ceiling(r["algo_bytes"])
+            rc["decode_frac_of_ceiling"] = r["gbps"] / rc["gbps"]
+            line["hbm_read_ceiling"] = rc
         print(json.dumps(line), flush=True)
         return
     elif args.config == "mixed":
