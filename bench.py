@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="qwen3",
                     choices=["qwen3", "qwen3_10k", "long_context", "mla", "mla_bs1", "extend",
-                             "mixed", "merge"])
+                             "mixed", "merge", "cache_write"])
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="GQA decode cache element type: bf16, or FP8 E4M3 codes with "
                          "per-tensor scales (amax / 448), shuffled layout with x = 16")
@@ -625,6 +625,39 @@ def bench_mixed(args):
             "new_tokens": tokens, "cached_tokens": int(ctx.sum())}
 
 
+def bench_cache_write(args):
+    """Bulk reshape_and_cache: every token of the 64-request workload (93.5 K
+    tokens, one kv head, head_dim 128) written into the shuffled cache in one
+    launch, over rotated pools larger than the Infinity Cache."""
+    import torch
+    import paged_attention_decode_reshape_amd as pa
+    from paged_attention_decode_reshape_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    case = W.qwen3_decode()
+    pg = case.paging
+    pool_bytes = pg.num_blocks * case.Hkv * case.D * case.B * 2 * 2
+    pools = max(2, math.ceil(2 * MALL_BYTES / pool_bytes))
+    key, value = case.key.to(dev), case.value.to(dev)
+    slots = torch.from_numpy(pg.slot_mapping).to(dev)
+    caches = [(torch.zeros((pg.num_blocks, 1, 16, 16, 8), dtype=torch.bfloat16, device=dev),
+               torch.zeros((pg.num_blocks, 1, 2, 128, 8), dtype=torch.bfloat16, device=dev))
+              for _ in range(pools)]
+    srcs = [(key.clone(), value.clone()) for _ in range(pools)]
+
+    def launch(i):
+        kc, vc = caches[i % pools]
+        k, v = srcs[i % pools]
+        pa.reshape_and_cache(k, v, kc, vc, slots)
+
+    ms = time_launches(launch, min(args.steps, 400))
+    T = pg.total_tokens
+    nbytes = T * case.Hkv * case.D * 2 * 2 * 2 + T * 8
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"value": T / (ms * 1e-3), "ms_per_step": ms, "algo_bytes": nbytes, "gbps": gbps,
+            "tokens": T, "pools": pools}
+
+
 def bench_merge(args):
     """The standalone merge_attn_states at the chunked-extend shape: two fp32
     partial results [4096, 64, 128] with their LSEs -> bf16 output and LSE
@@ -823,6 +856,19 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+        return
+    elif args.config == "cache_write":
+        r = bench_cache_write(args)
+        workload = {"workload": "reshape_and_cache_bulk_93k_tokens", "tokens": r["tokens"],
+                    "kv_heads": 1, "head_dim": 128, "block_size": 16, "layout": "shuffled",
+                    "pools": r["pools"]}
+        line = base_line(args, r, workload, unit="tokens/s")
+        line["roofline"] = {"bound": "hbm", "kernel": "cache_write_shuffled_kernel",
+                            "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                            "algo_bytes_per_launch": r["algo_bytes"],
+                            "avg_launch_ms": r["ms_per_step"]}
         print(json.dumps(line), flush=True)
         return
     elif args.config == "merge":

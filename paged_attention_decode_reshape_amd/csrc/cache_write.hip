@@ -20,18 +20,30 @@
 
 namespace pa {
 
+// Lanes are laid out so that 8 neighbouring lanes take 8 consecutive tokens
+// of the same 8 dims (lane = 8 * (chunk % 8) + token % 8): when those tokens
+// go to consecutive slots (a prefill or a bulk fill), the 2-byte V values of
+// one store instruction sit next to each other in memory and are written
+// together, and K's vectors are contiguous too.  (Transposing whole 8-token
+// groups through LDS to store full V vectors gained nothing on a bulk fill
+// whose sequences start at arbitrary token offsets.)
 template <int D>
 __global__ __launch_bounds__(256) void cache_write_shuffled_kernel(
     const uint4 *__restrict__ key, const uint4 *__restrict__ value, uint16_t *__restrict__ k_cache,
     uint16_t *__restrict__ v_cache, const int64_t *__restrict__ slot_mapping, int64_t num_tokens,
     int Hkv, int B, int64_t num_blocks) {
-    constexpr int C = D / 8;  // 16-byte vectors per head row
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = num_tokens * Hkv * C;
-    if (idx >= total) return;
-    const int c = (int)(idx % C);
-    const int g = (int)((idx / C) % Hkv);
-    const int64_t i = idx / ((int64_t)C * Hkv);
+    constexpr int C = D / 8;  // 16-byte vectors per head row (a multiple of 8)
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // t = ((group of 8 tokens * Hkv + g) * C / 8 + chunk block) * 64 + 8 * (chunk % 8) + token % 8
+    const int lane = (int)(t & 63);
+    const int64_t wv = t >> 6;
+    const int cq = (int)(wv % (C / 8));
+    const int g = (int)((wv / (C / 8)) % Hkv);
+    const int64_t i8 = wv / ((int64_t)(C / 8) * Hkv);
+    const int64_t i = i8 * 8 + (lane & 7);
+    const int c = cq * 8 + (lane >> 3);
+    if (i >= num_tokens) return;
+    const int64_t idx = (i * Hkv + g) * C + c;  // source vector
     const int64_t slot = slot_mapping[i];
     if (slot < 0 || slot >= num_blocks * B) return;
     const int64_t p = slot / B;
@@ -114,7 +126,7 @@ hipError_t launch_cache_write_shuffled(const void *key, const void *value, void 
                                        void *v_cache, const int64_t *slot_mapping,
                                        int64_t num_tokens, int Hkv, int D, int B,
                                        int64_t num_blocks, hipStream_t stream) {
-    const int64_t total = num_tokens * Hkv * (D / 8);
+    const int64_t total = (num_tokens + 7) / 8 * 8 * Hkv * (D / 8);  // whole groups of 8 tokens
     const int64_t grid = (total + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (D == 128)
