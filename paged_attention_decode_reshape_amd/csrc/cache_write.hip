@@ -83,22 +83,29 @@ __global__ __launch_bounds__(256) void cache_write_standard_kernel(
 // FP8 shuffled layout (x = 16 codes): thread (token, kv head, 16-dim group
 // c) quantises 16 dims of K into one 16-byte vector,
 // k_cache[p][g][c][o][0..16), and 16 dims of V into 16 single bytes,
-// v_cache[p][g][o / 16][16 c + j][o % 16].
+// v_cache[p][g][o / 16][16 c + j][o % 16].  As for bf16, 16 neighbouring
+// lanes take 16 consecutive tokens of the same dims (lane = 16 * (c % 4) +
+// token % 16), so V's byte stores of consecutive slots sit side by side.
 __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
     const uint4 *__restrict__ key, const uint4 *__restrict__ value, uint4 *__restrict__ k_cache,
     uint8_t *__restrict__ v_cache, const int64_t *__restrict__ slot_mapping, int64_t num_tokens,
     int Hkv, int D, int B, int64_t num_blocks, float k_inv, float v_inv) {
-    const int C16 = D / kFp8X;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= num_tokens * Hkv * C16) return;
-    const int c = (int)(idx % C16);
-    const int g = (int)((idx / C16) % Hkv);
-    const int64_t i = idx / ((int64_t)C16 * Hkv);
+    const int C16 = D / kFp8X;  // a multiple of 4
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // t = ((group of 16 tokens * Hkv + g) * C16 / 4 + chunk block) * 64 + 16 * (c % 4) + token % 16
+    const int lane = (int)(t & 63);
+    const int64_t wv = t >> 6;
+    const int cq = (int)(wv % (C16 / 4));
+    const int g = (int)((wv / (C16 / 4)) % Hkv);
+    const int64_t i16 = wv / ((int64_t)(C16 / 4) * Hkv);
+    const int64_t i = i16 * 16 + (lane & 15);
+    const int c = cq * 4 + (lane >> 4);
+    if (i >= num_tokens) return;
     const int64_t slot = slot_mapping[i];
     if (slot < 0 || slot >= num_blocks * B) return;
     const int64_t p = slot / B;
     const int o = (int)(slot % B);
-    const size_t src = (size_t)idx * 2;  // two bf16 vectors per 16 dims
+    const size_t src = ((size_t)(i * Hkv + g) * C16 + c) * 2;  // two bf16 vectors per 16 dims
     k_cache[((p * Hkv + g) * C16 + c) * B + o] = quantize16(key[src], key[src + 1], k_inv);
     const uint4 vq = quantize16(value[src], value[src + 1], v_inv);
     const uint32_t w[4] = {vq.x, vq.y, vq.z, vq.w};
@@ -157,7 +164,8 @@ hipError_t launch_cache_write_fp8(const void *key, const void *value, void *k_ca
                                   const int64_t *slot_mapping, int64_t num_tokens, int Hkv, int D,
                                   int B, int64_t num_blocks, float k_inv, float v_inv,
                                   hipStream_t stream) {
-    const int64_t grid = (num_tokens * Hkv * (D / kFp8X) + 255) / 256;
+    const int64_t threads = (num_tokens + 15) / 16 * 16 * Hkv * (D / kFp8X);  // groups of 16
+    const int64_t grid = (threads + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(cache_write_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                        (const uint4 *)key, (const uint4 *)value, (uint4 *)k_cache,
