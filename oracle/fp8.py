@@ -170,3 +170,44 @@ def paged_decode_gqa(q_bits, k_cache, v_cache, block_table, context_lens, scale,
             out[s, h] = (w @ Vf[:, g, :]) / lsum
             lse[s, h] = m + np.log(lsum)
     return out, lse
+
+
+# ---- MLA latent cache in FP8 -------------------------------------------------
+# The latent row of a token (576 values: keys are the whole row, values its
+# first 512) is one tensor with one scale; the cache is [num_blocks,
+# block_size, 576] codes, rows as they are (no shuffle, as for bf16).
+
+def cache_write_latent(latent_bits, slot_mapping, kv_cache, scale):
+    """Token i's row of codes goes to kv_cache[slot // B][slot % B]; slots
+    outside the pool are skipped."""
+    nb, B, _ = kv_cache.shape
+    codes = quantize_bf16(latent_bits, scale)
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if 0 <= slot < nb * B:
+            kv_cache[int(slot) // B, int(slot) % B] = codes[i]
+
+
+def paged_decode_mla(q_bits, kv_cache, block_table, context_lens, Dv, scale, kv_scale,
+                     seqs=None):
+    """Exact attention in float64 of each head's query over the dequantised
+    latent rows (K = row, V = row[:Dv]); returns (out [S, Hq, Dv], lse [S, Hq])."""
+    q = (np.asarray(q_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    q = q.astype(np.float64)
+    S, Hq, Dl = q.shape
+    B = kv_cache.shape[1]
+    out = np.zeros((S, Hq, Dv))
+    lse = np.full((S, Hq), -np.inf)
+    for s in (range(S) if seqs is None else seqs):
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        rows = kv_cache[np.asarray(block_table[s])[t // B], t % B]  # [n, Dl] codes
+        K = dequant_f64(rows, kv_scale)
+        z = float(np.float32(scale)) * (K @ q[s].T)  # [n, Hq]
+        m = z.max(axis=0)
+        w = np.exp(z - m)
+        lsum = w.sum(axis=0)
+        out[s] = (w.T @ K[:, :Dv]) / lsum[:, None]
+        lse[s] = m + np.log(lsum)
+    return out, lse

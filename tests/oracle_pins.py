@@ -284,6 +284,36 @@ def pin_fp8_decode_matches_bf16(orc):
     _close(lse8, lse, what="fp8 lse")
 
 
+def pin_fp8_mla_matches_bf16(orc):
+    """FP8 latent cache: codes land at [slot // B][slot % B] (bad slots skipped),
+    and with a power-of-two scale the FP8 MLA decode equals the C oracle's
+    bf16 MLA decode over the dequantised latents."""
+    from oracle import fp8
+    case = W.mla_decode_cases("fp8mla", 83, S=3, lens_range=None, lens=[1, 70, 300], Hq=4,
+                              Dl=576, Dv=512, block_sizes=(16,), scale=1 / 192 ** 0.5)[16]
+    pg = case.paging
+    s8 = 2.0 ** -5
+    kv8 = np.full((pg.num_blocks, case.B, 576), 0x7F, dtype=np.uint8)
+    slots = pg.slot_mapping.copy()
+    lat = W.bf16_bits(case.latent)
+    fp8.cache_write_latent(lat, slots, kv8, s8)
+    codes = fp8.quantize_bf16(lat, s8)
+    for i in range(0, len(slots), 7):
+        assert np.array_equal(kv8[slots[i] // case.B, slots[i] % case.B], codes[i])
+    k0 = kv8.copy()
+    fp8.cache_write_latent(lat[:2], np.array([-1, pg.num_blocks * case.B]), kv8, s8)
+    assert np.array_equal(kv8, k0)
+    out8, lse8 = fp8.paged_decode_mla(W.bf16_bits(case.query), kv8, pg.block_table,
+                                      case.context_lens, 512, case.scale, s8)
+    deq = fp8.bf16_rne(fp8.dequant_f64(codes, s8).astype(np.float32))
+    kv = np.full((pg.num_blocks, case.B, 576), 0x7FC0, dtype=np.uint16)
+    orc.cache_write_latent(deq, slots, kv, case.B)
+    out, lse = orc.paged_decode_mla(W.bf16_bits(case.query), kv, pg.block_table,
+                                    case.context_lens, case.B, 512, case.scale)
+    _close(out8, out, what="fp8 mla out")
+    _close(lse8, lse, what="fp8 mla lse")
+
+
 def pin_latent_write(orc):
     B, nb, Dl, T = 4, 9, 576, 20
     rng = np.random.default_rng(5)
@@ -518,6 +548,7 @@ ALL_PINS = [
     pin_fp8_quantize_and_bf16,
     pin_fp8_cache_layout,
     pin_fp8_decode_matches_bf16,
+    pin_fp8_mla_matches_bf16,
     pin_latent_write,
     pin_decode_vs_numpy,
     pin_decode_closed_forms,
