@@ -44,7 +44,9 @@ METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 
 _CSRC = "paged_attention_decode_reshape_amd/csrc/"
 MEASURED_TRAFFIC = {
     "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "c7875b7c37b66cf0", 52.39e6),
-    "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "25a9444b960aeec7", 237.19e6),
+    "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77", 237.19e6),
+    "mla_fp8": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77",
+                139.27e6),
     "extend": ((_CSRC + "extend.hip", _CSRC + "decode_common.h"), "74420352bf28f086", 1294.40e6),
 }
 
@@ -436,14 +438,15 @@ VALU_PEAK_TFLOPS = 157.3  # fp32 vector (bf16 dot2 issues at the same rate)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def mla_algorithmic_bytes(case, with_write=False) -> int:
-    """Every context latent row once, q, out, lse, used table entries and
-    lengths (and, with the fused cache write, each new latent read and
-    written plus its slot)."""
+def mla_algorithmic_bytes(case, with_write=False, kv_bytes=2) -> int:
+    """Every context latent row once (kv_bytes per value: 2 bf16, 1 FP8),
+    q, out, lse, used table entries and lengths (and, with the fused cache
+    write, each new bf16 latent read and its cache row written, plus its
+    slot)."""
     n = case.context_lens.astype(np.int64)
-    lat = int(n.sum()) * case.Dl * 2
+    lat = int(n.sum()) * case.Dl * kv_bytes
     blocks = int(((n + case.B - 1) // case.B).sum())
-    write = case.S * case.Dl * 2 * 2 + case.S * 8 if with_write else 0
+    write = case.S * case.Dl * (2 + kv_bytes) + case.S * 8 if with_write else 0
     return (lat + case.S * case.Hq * (case.Dl + case.Dv) * 2 + case.S * case.Hq * 4 + blocks * 4 +
             case.S * 4 + write)
 
@@ -458,16 +461,24 @@ def bench_mla(args, case, label):
 
     dev = torch.device("cuda:0")
     pg = case.paging
-    pool_bytes = pg.num_blocks * case.B * case.Dl * 2
+    f8 = args.kv_dtype == "fp8"
+    kv_bytes = 1 if f8 else 2
+    pool_bytes = pg.num_blocks * case.B * case.Dl * kv_bytes
     pools = args.pools or max(1, math.ceil(2 * MALL_BYTES / pool_bytes))
     log(f"[bench] {label}: S={case.S} Hq={case.Hq} B={case.B} tokens={pg.total_tokens} "
-        f"pool={pool_bytes / 1e6:.1f} MB x {pools} copies")
+        f"pool={pool_bytes / 1e6:.1f} MB x {pools} copies, {args.kv_dtype} cache")
     lat = case.latent.to(dev)
+    # FP8: one scale for the cache, the latents' amax over the largest code
+    kvs = float(np.float32(lat.float().abs().max().item() / 448.0)) if f8 else 1.0
     slots_all = torch.from_numpy(pg.slot_mapping).to(dev)
     caches = []
     for _ in range(pools):
-        kv = torch.zeros((pg.num_blocks, case.B, case.Dl), dtype=torch.bfloat16, device=dev)
-        pa.reshape_and_cache(lat, None, kv, None, slots_all, layout=pa.LAYOUT_MLA_LATENT)
+        if f8:
+            kv = torch.zeros((pg.num_blocks, case.B, case.Dl), dtype=torch.uint8, device=dev)
+            pa.reshape_and_cache_mla_fp8(lat, kv, slots_all, kvs)
+        else:
+            kv = torch.zeros((pg.num_blocks, case.B, case.Dl), dtype=torch.bfloat16, device=dev)
+            pa.reshape_and_cache(lat, None, kv, None, slots_all, layout=pa.LAYOUT_MLA_LATENT)
         caches.append(kv)
     rows = torch.from_numpy(case.new_token_rows()).to(dev)
     new_lat = lat[rows].contiguous()
@@ -486,7 +497,13 @@ def bench_mla(args, case, label):
     fused = not args.separate_cache_write
 
     def decode(i):
-        if fused:  # the new latents' cache write inside the decode launch
+        if f8:
+            pa.mla_decode_attn_fp8(q, caches[i % pools], bt, cl, case.scale, max_ctx, kvs,
+                                   v_dim=case.Dv, partition_tokens=P,
+                                   new_latent=new_lat if fused else None,
+                                   slot_mapping=new_slots if fused else None, out=out, lse=lse,
+                                   workspace=ws)
+        elif fused:  # the new latents' cache write inside the decode launch
             pa.mla_decode_attn_write(q, new_lat, new_slots, caches[i % pools], bt, cl, case.scale,
                                      max_ctx, v_dim=case.Dv, partition_tokens=P, out=out, lse=lse,
                                      workspace=ws)
@@ -495,7 +512,9 @@ def bench_mla(args, case, label):
                                partition_tokens=P, out=out, lse=lse, workspace=ws)
 
     def step(i):
-        if not fused:
+        if not fused and f8:
+            pa.reshape_and_cache_mla_fp8(new_lat, caches[i % pools], new_slots, kvs)
+        elif not fused:
             pa.reshape_and_cache(new_lat, None, caches[i % pools], None, new_slots,
                                  layout=pa.LAYOUT_MLA_LATENT)
         decode(i)
@@ -509,7 +528,7 @@ def bench_mla(args, case, label):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     dec_ms = time_launches(decode, min(args.steps, 200))
-    algo = mla_algorithmic_bytes(case, with_write=fused)
+    algo = mla_algorithmic_bytes(case, with_write=fused, kv_bytes=kv_bytes)
     flops = mla_algorithmic_flops(case)
     # MLA picks its split like GQA decode with one unit per sequence
     balanced = pa.decode_uses_balanced_split(case.S, 1, max_ctx, P)
@@ -517,29 +536,47 @@ def bench_mla(args, case, label):
             "decode_ms": dec_ms, "algo_bytes": algo, "algo_flops": flops,
             "hbm_gbps": algo / (dec_ms * 1e-3) / 1e9, "tflops": flops / (dec_ms * 1e-3) / 1e12,
             "pools": pools, "cache_write": "fused" if fused else "separate launch",
+            "kv_scale": kvs if f8 else None,
             "kernel": "mla_decode_balanced_kernel" if balanced else "mla_decode_kernel"}
 
 
-def cpu_baseline_mla(case, seconds):
+def cpu_baseline_mla(case, seconds, kv_scale=None):
+    """The oracle's MLA decode over the whole batch, repeated for about
+    `seconds`; with kv_scale, the FP8 numpy oracle on one BLAS thread."""
     import oracle
+    from oracle import fp8 as OF
     from paged_attention_decode_reshape_amd import workloads as W
 
     orc = oracle.get()
-    kv = np.zeros((case.paging.num_blocks, case.B, case.Dl), dtype=np.uint16)
-    orc.cache_write_latent(W.bf16_bits(case.latent), case.paging.slot_mapping, kv, case.B)
     qb = W.bf16_bits(case.query)
+    if kv_scale is None:
+        kv = np.zeros((case.paging.num_blocks, case.B, case.Dl), dtype=np.uint16)
+        orc.cache_write_latent(W.bf16_bits(case.latent), case.paging.slot_mapping, kv, case.B)
+
+        def step():
+            orc.paged_decode_mla(qb, kv, case.paging.block_table, case.context_lens, case.B,
+                                 case.Dv, case.scale)
+    else:
+        kv = np.zeros((case.paging.num_blocks, case.B, case.Dl), dtype=np.uint8)
+        OF.cache_write_latent(W.bf16_bits(case.latent), case.paging.slot_mapping, kv, kv_scale)
+
+        def step():
+            OF.paged_decode_mla(qb, kv, case.paging.block_table, case.context_lens, case.Dv,
+                                case.scale, kv_scale)
+    from threadpoolctl import threadpool_limits
     reps = 0
     t0 = time.perf_counter()
-    while True:
-        orc.paged_decode_mla(qb, kv, case.paging.block_table, case.context_lens, case.B, case.Dv,
-                             case.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": case.S * reps / el, "unit": "tok/s", "cores": orc.max_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} full MLA decode steps of the same workload ({case.S} requests) "
+    with threadpool_limits(1, user_api="blas"):
+        while True:
+            step()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": case.S * reps / el, "unit": "tok/s",
+            "cores": orc.max_threads() if kv_scale is None else 1, "kind": "oracle",
+            "sample": f"{reps} full MLA decode steps of the same workload ({case.S} requests"
+                      f"{', FP8 numpy oracle' if kv_scale is not None else ''}) "
                       f"in {el:.1f} s, fp64"}
 
 
@@ -839,7 +876,9 @@ def main():
         workload = {"workload": f"deepseek_r1_tp8_mla_decode_64req_bs{B}", "requests": 64,
                     "q_heads": 16, "latent_dim": 576, "v_dim": 512, "block_size": B,
                     "context_lens": "U[1024,4096]", "kv_pool_copies": r["pools"],
-                    "cache_write": r["cache_write"]}
+                    "cache_write": r["cache_write"], "kv_dtype": args.kv_dtype}
+        if r["kv_scale"] is not None:
+            workload["kv_scale"] = r["kv_scale"]
         line = base_line(args, r, workload)
         line["hbm_gbps"] = r["hbm_gbps"]
         line["pct_hbm_peak"] = 100.0 * r["hbm_gbps"] / HBM_PEAK_GBPS
@@ -850,12 +889,13 @@ def main():
         line["roofline"] = {"bound": "alu", "kernel": r["kernel"], "achieved": r["tflops"],
                             "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": r["tflops"] / VALU_PEAK_TFLOPS,
-                            "traffic": measured_traffic(args.config),
+                            "traffic": measured_traffic(
+                                args.config + ("_fp8" if args.kv_dtype == "fp8" else "")),
                             "algo_flops_per_launch": r["algo_flops"],
                             "algo_bytes_per_launch": r["algo_bytes"], "avg_launch_ms": r["decode_ms"]}
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
-            line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds)
+            line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds, r["kv_scale"])
         print(json.dumps(line), flush=True)
         return
     elif args.config == "cache_write":

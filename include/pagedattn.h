@@ -325,6 +325,40 @@ pa_status pa_mla_decode_attn_write(void *out, float *lse, const void *query,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * FP8 latent cache (the MLA extend pseudocode of the "vLLM ROCm attention
+ * backends" blog gathers the latent cache and may dequantise it; the code
+ * format is that of pa_reshape_and_cache_fp8, with one scale for the whole
+ * cache): kv_cache [num_blocks, block_size, latent_dim] E4M3 codes, value =
+ * E4M3(code) * kv_scale.
+ *
+ * pa_reshape_and_cache_mla_fp8: latent [num_tokens, latent_dim] bf16
+ *   quantised (nearest-even code of float32(x) * float32(1 / kv_scale),
+ *   saturating at +-448) into the row of slot slot_mapping[i]; negative or
+ *   out-of-pool slots are skipped.  Supported: latent_dim % 16 == 0.
+ *
+ * pa_mla_decode_attn_fp8: pa_mla_decode_attn over such a cache, keys and
+ *   values the dequantised rows (the codes are converted exactly; kv_scale
+ *   folds into the softmax scale and the output).  new_latent and
+ *   slot_mapping: both NULL (no write) or both given (the fused write of
+ *   pa_mla_decode_attn_write, quantised as above).  Workspace, support and
+ *   errors as for pa_mla_decode_attn; kv_scale finite and positive
+ *   (PA_ERR_INVALID_ARG otherwise).
+ */
+pa_status pa_reshape_and_cache_mla_fp8(const void *latent, void *kv_cache,
+                                       const int64_t *slot_mapping, int64_t num_tokens,
+                                       int32_t latent_dim, int32_t block_size, int64_t num_blocks,
+                                       float kv_scale, void *stream);
+
+pa_status pa_mla_decode_attn_fp8(void *out, float *lse, const void *query, const void *new_latent,
+                                 const int64_t *slot_mapping, void *kv_cache,
+                                 const int32_t *block_table, int32_t max_blocks_per_seq,
+                                 const int32_t *context_lens, int32_t max_context_len,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t latent_dim,
+                                 int32_t v_dim, int32_t block_size, int64_t num_blocks,
+                                 float scale, float kv_scale, int32_t partition_tokens,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Log-sum-exp merge of two partial attention results (merge_attn_states;
  * extend-path pseudocode): with M = max(Lp, Ls), wp = exp(Lp - M),
  * ws = exp(Ls - M): out = (wp * Op + ws * Os) / (wp + ws),

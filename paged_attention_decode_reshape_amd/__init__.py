@@ -28,9 +28,11 @@ from .ops import (  # noqa: F401
     mla_workspace_size,
     paged_decode_attn,
     paged_decode_attn_fp8,
+    mla_decode_attn_fp8,
     paged_decode_attn_layout,
     paged_decode_attn_write,
     reshape_and_cache,
     reshape_and_cache_fp8,
+    reshape_and_cache_mla_fp8,
     stream_read,
 )

@@ -129,6 +129,20 @@ __global__ __launch_bounds__(256) void cache_write_latent_kernel(
     kv_cache[slot * C + c] = latent[idx];
 }
 
+// FP8 latent rows: thread per 16-value vector, two bf16 vectors in, one code vector out.
+__global__ __launch_bounds__(256) void cache_write_latent_fp8_kernel(
+    const uint4 *__restrict__ latent, uint4 *__restrict__ kv_cache,
+    const int64_t *__restrict__ slot_mapping, int64_t num_tokens, int C16, int B,
+    int64_t num_blocks, float inv) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= num_tokens * C16) return;
+    const int64_t i = idx / C16;
+    const int c = (int)(idx % C16);
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * B) return;
+    kv_cache[slot * C16 + c] = quantize16(latent[2 * idx], latent[2 * idx + 1], inv);
+}
+
 hipError_t launch_cache_write_shuffled(const void *key, const void *value, void *k_cache,
                                        void *v_cache, const int64_t *slot_mapping,
                                        int64_t num_tokens, int Hkv, int D, int B,
@@ -183,6 +197,19 @@ hipError_t launch_cache_write_latent(const void *latent, void *kv_cache,
     hipLaunchKernelGGL(cache_write_latent_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                        (const uint4 *)latent, (uint4 *)kv_cache, slot_mapping, num_tokens, C, B,
                        num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_write_latent_fp8(const void *latent, void *kv_cache,
+                                         const int64_t *slot_mapping, int64_t num_tokens, int Dl,
+                                         int B, int64_t num_blocks, float inv,
+                                         hipStream_t stream) {
+    const int C16 = Dl / kFp8X;
+    const int64_t grid = (num_tokens * C16 + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cache_write_latent_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4 *)latent, (uint4 *)kv_cache, slot_mapping, num_tokens, C16, B,
+                       num_blocks, inv);
     return hipGetLastError();
 }
 

@@ -25,6 +25,9 @@ hipError_t launch_cache_write_fp8(const void *key, const void *value, void *k_ca
 hipError_t launch_cache_write_latent(const void *latent, void *kv_cache,
                                      const int64_t *slot_mapping, int64_t num_tokens, int Dl,
                                      int B, int64_t num_blocks, hipStream_t stream);
+hipError_t launch_cache_write_latent_fp8(const void *latent, void *kv_cache,
+                                         const int64_t *slot_mapping, int64_t num_tokens, int Dl,
+                                         int B, int64_t num_blocks, float inv, hipStream_t stream);
 
 struct DecodeParams {
     void *out;                 // bf16 [S, Hq, D]
@@ -88,6 +91,10 @@ struct MLAParams {
     // token before it reads it.
     const void *new_latent;
     const int64_t *slot_mapping;
+    // nonzero: kv_cache holds FP8 E4M3 codes [NB, B, Dl] with one scale
+    // (value = code * kv_scale; the fused write quantises with kv_inv)
+    int32_t fp8;
+    float kv_scale, kv_inv;
 };
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);

@@ -32,6 +32,7 @@
 
 #include "common.h"
 #include "decode_common.h"
+#include "fp8.h"
 #include "launch.h"
 
 namespace pa {
@@ -154,8 +155,23 @@ __device__ __forceinline__ void merge_mla_partials(const MLAParams &p, int s, co
 // by the workgroup that reads the sequence's last token: threads 0..71 copy
 // the 72 16-byte vectors, the stores complete and the workgroup meets at a
 // barrier before any wave reads the cache.  Called by every thread.
+// FP8 cache: threads 0..35 quantise 16 values each into one vector of codes.
+template <bool F8>
 __device__ __forceinline__ void mla_write_new_token(const MLAParams &p, int s) {
     const int64_t slot = as_const<int64_t>(p.slot_mapping)[s];
+    if constexpr (F8) {
+        constexpr int kRowVec8 = kDl / kFp8X;  // 36
+        if (slot >= 0 && slot < p.num_blocks * p.B && (int)threadIdx.x < kRowVec8) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(p.new_latent) +
+                               (size_t)s * kRowVec + 2 * threadIdx.x;
+            reinterpret_cast<uint4 *>(const_cast<void *>(p.kv_cache))[(size_t)slot * kRowVec8 +
+                                                                      threadIdx.x] =
+                quantize16(src[0], src[1], p.kv_inv);
+            wait_stores();
+        }
+        __syncthreads();
+        return;
+    }
     if (slot >= 0 && slot < p.num_blocks * p.B && (int)threadIdx.x < kRowVec) {
         const uint4 v = reinterpret_cast<const uint4 *>(p.new_latent)[(size_t)s * kRowVec + threadIdx.x];
         reinterpret_cast<uint4 *>(const_cast<void *>(p.kv_cache))[(size_t)slot * kRowVec + threadIdx.x] = v;
@@ -195,6 +211,7 @@ __device__ __forceinline__ void mla_load_queries(const MLAParams &p, int s,
 // Attention of the wave's heads over tokens [start, end) of sequence s,
 // accumulated into (m, lsum, acc): windows of at most kMaxPartition tokens
 // whose latent rows are resolved into LDS, then 32-token tiles.
+template <bool F8>
 __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int s, int start,
                                            int end, const uint32_t (&qreg)[kHPW][kSlices],
                                            float (&m)[kHPW], float (&lsum)[kHPW],
@@ -203,8 +220,9 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;  // QK: half of the latent row
     const int tk = lane & 31;  // QK: token of the tile
-    const float sl2 = p.scale * kLog2e;
+    const float sl2 = p.scale * kLog2e * (F8 ? p.kv_scale : 1.f);
     const uint4 *kv = reinterpret_cast<const uint4 *>(p.kv_cache);
+    const uint2 *kv8 = reinterpret_cast<const uint2 *>(p.kv_cache);  // FP8: 8 codes per uint2
     const int ld_tok = 8 * wave + (lane >> 3), ld_vec = lane & 7;
 
     for (int w0 = start; w0 < end; w0 += kMaxPartition) {
@@ -218,13 +236,25 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
         // Tile loader: thread (wave w, lane) moves vectors (lane & 7) + 8 i of
         // the latent row of tile token 8 w + (lane >> 3); tokens past the end
         // (or with an out-of-range block id) become zero rows.
+        // FP8: the same 16-byte bf16 vectors come from 8 codes each (half a
+        // 16-code vector), converted exactly on the way to LDS.
         auto load_tile = [&](int t0, uint4 (&r)[kLoadVec]) {
             const int t = t0 + ld_tok;
             const int rowi = t < wend ? sm.row[t - w0] : -1;
-            const uint4 *src = kv + (size_t)(rowi < 0 ? 0 : rowi) * kRowVec + ld_vec;
+            if constexpr (F8) {
+                const uint2 *src = kv8 + (size_t)(rowi < 0 ? 0 : rowi) * (kDl / 8) + ld_vec;
 #pragma unroll
-            for (int i = 0; i < kLoadVec; i++)
-                r[i] = rowi < 0 ? make_uint4(0, 0, 0, 0) : src[8 * i];
+                for (int i = 0; i < kLoadVec; i++) {
+                    const uint2 c = rowi < 0 ? make_uint2(0, 0) : src[8 * i];
+                    fp8x4_to_bf16x2(c.x, r[i].x, r[i].y);
+                    fp8x4_to_bf16x2(c.y, r[i].z, r[i].w);
+                }
+            } else {
+                const uint4 *src = kv + (size_t)(rowi < 0 ? 0 : rowi) * kRowVec + ld_vec;
+#pragma unroll
+                for (int i = 0; i < kLoadVec; i++)
+                    r[i] = rowi < 0 ? make_uint4(0, 0, 0, 0) : src[8 * i];
+            }
         };
         auto store_tile = [&](const uint4 (&r)[kLoadVec]) {
             uint4 *dst = reinterpret_cast<uint4 *>(&sm.tile[ld_tok * kRowDw]) + ld_vec;
@@ -322,6 +352,12 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
             });
         }
     }
+    if constexpr (F8) {  // the value rows were summed as unscaled codes
+#pragma unroll
+        for (int j = 0; j < kHPW; j++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[j][i] *= p.kv_scale;
+    }
 }
 
 // Normalise the wave's heads and write them: as output rows (whole = true)
@@ -404,6 +440,7 @@ __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW],
 }
 
 // Fixed partitions: one workgroup per (partition, sequence).
+template <bool F8>
 __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int part = blockIdx.x / p.S;
     const int s = blockIdx.x - part * p.S;
@@ -414,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int ctx = clamp_ctx(p, as_const<int32_t>(p.context_lens)[s]);
     if (start >= ctx) {
         if (ctx == 0 && part == 0) {
-            if (p.slot_mapping) mla_write_new_token(p, s);
+            if (p.slot_mapping) mla_write_new_token<F8>(p, s);
             mla_write_empty(p, s);
         }
         return;
@@ -422,12 +459,12 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int end = min(start + P, ctx);
     const int nparts = (ctx + P - 1) / P;
     // the partition holding the last token writes the new token first
-    if (p.slot_mapping && end == ctx) mla_write_new_token(p, s);
+    if (p.slot_mapping && end == ctx) mla_write_new_token<F8>(p, s);
     uint32_t qreg[kHPW][kSlices];
     mla_load_queries(p, s, qreg);
     float m[kHPW], lsum[kHPW], acc[kHPW][8];
     mla_reset(m, lsum, acc);
-    mla_attend(p, sm, s, start, end, qreg, m, lsum, acc);
+    mla_attend<F8>(p, sm, s, start, end, qreg, m, lsum, acc);
     // partials [S, Hq, max_parts, Dv] and [S, Hq, max_parts]
     float *po = p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
     float *pl = p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
@@ -459,6 +496,7 @@ __device__ __forceinline__ int wave_prefix_sum_i(int v) {
 // else one, numbered sequence-major; workgroup w takes piece w (+ NW, ...).
 // Pieces P_u .. P_u + n - 1 of a sequence leave partials in those slots of
 // [NW, Hq, Dv] and [NW, Hq]; the last to finish merges them in order.
+template <bool F8>
 __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p) {
     const int NW = gridDim.x, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -469,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
 
     for (int s = w; s < p.S; s += NW)
         if (readlane_i32(ctx_in(s & ~63), s & 63) == 0) {
-            if (p.slot_mapping) mla_write_new_token(p, s);
+            if (p.slot_mapping) mla_write_new_token<F8>(p, s);
             mla_write_empty(p, s);
         }
 
@@ -525,8 +563,8 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
         float m[kHPW], lsum[kHPW], acc[kHPW][8];
         mla_reset(m, lsum, acc);
         // the piece holding the last token writes the new token first
-        if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token(p, s);
-        mla_attend(p, sm, s, a * kTile, min(b * kTile, ctx), qreg, m, lsum, acc);
+        if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token<F8>(p, s);
+        mla_attend<F8>(p, sm, s, a * kTile, min(b * kTile, ctx), qreg, m, lsum, acc);
         mla_emit(p, s, n == 1, m, lsum, acc, p.part_out + (size_t)v * p.Hq * kDv, kDv,
                  p.part_lse + (size_t)v * p.Hq, 1);
         if (n > 1 && mla_count(p, s, n))
@@ -539,25 +577,35 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
 
 }  // namespace
 
-hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream) {
+namespace {
+
+template <bool F8>
+hipError_t launch_mla(const MLAParams &p, hipStream_t stream) {
     if (p.balanced_workgroups > 0) {
         // one wave of workgroups: as many as are resident together
         static const int per_cu = [] {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(&mla_decode_balanced_kernel), 256, 0) !=
+                    &n, reinterpret_cast<const void *>(&mla_decode_balanced_kernel<F8>), 256, 0) !=
                     hipSuccess || n < 1)
                 n = 1;
             return n;
         }();
         const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
-        hipLaunchKernelGGL(mla_decode_balanced_kernel, dim3((unsigned)nw), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(mla_decode_balanced_kernel<F8>, dim3((unsigned)nw), dim3(256), 0,
+                           stream, p);
         return hipGetLastError();
     }
     const int64_t units = (int64_t)p.max_parts * p.S;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)units), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mla_decode_kernel<F8>, dim3((unsigned)units), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream) {
+    return p.fp8 ? launch_mla<true>(p, stream) : launch_mla<false>(p, stream);
 }
 
 }  // namespace pa

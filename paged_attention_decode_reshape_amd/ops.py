@@ -74,6 +74,9 @@ _SIGS = {
                                   _vp, _sz, _vp], _i32),
     "pa_gather_cache_chunk_fp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                    _i64, _i32, _i32, _f32, _f32, _vp], _i32),
+    "pa_reshape_and_cache_mla_fp8": ([_vp, _vp, _vp, _i64, _i32, _i32, _i64, _f32, _vp], _i32),
+    "pa_mla_decode_attn_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _i64, _f32, _f32, _i32, _vp, _sz, _vp], _i32),
     "pa_mixed_batch_plan": ([_i32, _vp, _vp, _vp, _vp], _i32),
     "pa_mixed_batch_workspace_size": ([_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_mixed_batch_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -750,3 +753,64 @@ def gather_cache_chunk_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
                                        float(v_scale), _stream(k_cache))
     _check("gather_cache_chunk_fp8", st)
     return k_out, v_out
+
+
+def reshape_and_cache_mla_fp8(latent: torch.Tensor, kv_cache: torch.Tensor,
+                              slot_mapping: torch.Tensor, kv_scale: float) -> None:
+    """Quantise latent [T, Dl] bf16 into kv_cache [NB, B, Dl] (uint8 E4M3 codes)."""
+    lib = library()
+    _gpu("latent", latent, torch.bfloat16, 2)
+    _gpu("kv_cache", kv_cache, torch.uint8, 3)
+    _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    T, Dl = latent.shape
+    NB, B, Dl2 = kv_cache.shape
+    if Dl2 != Dl or slot_mapping.numel() != T:
+        raise ValueError("latent cache shape does not match the latent rows")
+    _check("reshape_and_cache_mla_fp8", lib.pa_reshape_and_cache_mla_fp8(
+        latent.data_ptr(), kv_cache.data_ptr(), slot_mapping.data_ptr(), T, Dl, B, NB,
+        float(kv_scale), _stream(latent)))
+
+
+def mla_decode_attn_fp8(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_context_len: int,
+                        kv_scale: float, v_dim: int = 512, partition_tokens: int = 0,
+                        new_latent: Optional[torch.Tensor] = None,
+                        slot_mapping: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Absorbed MLA decode over an FP8 latent cache (rows = code * kv_scale), with
+    the fused quantised write when new_latent and slot_mapping are given."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("kv_cache", kv_cache, torch.uint8, 3)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, Dl = query.shape
+    NB, B, Dl2 = kv_cache.shape
+    if Dl2 != Dl:
+        raise ValueError("kv_cache latent width differs from the query's")
+    if (new_latent is None) != (slot_mapping is None):
+        raise ValueError("new_latent and slot_mapping go together")
+    if new_latent is not None:
+        _gpu("new_latent", new_latent, torch.bfloat16, 2)
+        _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+        if tuple(new_latent.shape) != (S, Dl) or slot_mapping.numel() != S:
+            raise ValueError("new_latent [num_seqs, latent_dim] and one slot per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_mla_decode_attn_fp8(out.data_ptr(), _ptr(lse), query.data_ptr(), _ptr(new_latent),
+                                    _ptr(slot_mapping), kv_cache.data_ptr(),
+                                    block_table.data_ptr(), block_table.shape[1],
+                                    context_lens.data_ptr(), int(max_context_len), S, Hq, Dl,
+                                    v_dim, B, NB, float(scale), float(kv_scale),
+                                    int(partition_tokens), _ptr(ws), nbytes, _stream(query))
+    _check("mla_decode_attn_fp8", st)
+    return out, lse

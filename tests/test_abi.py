@@ -280,3 +280,22 @@ def test_fp8_entry_validation():
     g = lambda B=16, ks=0.1: lib.pa_gather_cache_chunk_fp8(
         FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 1, 128, B, 64, 0, 64, ks, 0.1, None)
     assert g(B=8) == UNSUPPORTED and g(ks=nan) == INVALID
+
+
+def test_mla_fp8_entry_validation():
+    """FP8 latent write and MLA FP8 decode refuse bad scales, half-given
+    write pairs and unsupported widths before any launch."""
+    lib = pa.library()
+    w = lambda Dl=576, ks=0.01, lat=FAKE: lib.pa_reshape_and_cache_mla_fp8(
+        lat, FAKE, FAKE, 4, Dl, 16, 8, ks, None)
+    assert w(ks=0.0) == INVALID and w(ks=float("nan")) == INVALID and w(ks=1e-45) == INVALID
+    assert w(lat=None) == INVALID and w(lat=FAKE + 8) == INVALID
+    assert w(Dl=520) == UNSUPPORTED
+    assert lib.pa_reshape_and_cache_mla_fp8(FAKE, FAKE, FAKE, 0, 576, 16, 8, 0.01, None) == OK
+    d = lambda nl=None, sm=None, ks=0.01, Dv=512, P=-1: lib.pa_mla_decode_attn_fp8(
+        FAKE, None, FAKE, nl, sm, FAKE, FAKE, 8, FAKE, 100, 4, 16, 576, Dv, 16, 64, 0.07, ks, P,
+        None, 0, None)
+    assert d(nl=FAKE) == INVALID and d(sm=FAKE) == INVALID
+    assert d(ks=-1.0) == INVALID and d(ks=float("inf")) == INVALID
+    assert d(Dv=448) == UNSUPPORTED
+    assert d(P=-2) == WS_SMALL
