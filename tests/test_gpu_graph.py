@@ -135,6 +135,39 @@ def test_graph_mla_step():
     check_graph(step, [out, lse])
 
 
+def test_graph_mla_fp8_step():
+    """The fused MLA decode step over an FP8 latent cache (the quantised
+    write of the new latents included), captured and replayed."""
+    case = W.deepseek_mla_decode(S=16, block_sizes=(64,))[64]
+    say("graph: fused MLA decode step, FP8 cache")
+    dev = device()
+    pg = case.paging
+    kvs = float(np.float32(case.latent.float().abs().max().item() / 448.0))
+    kv = torch.zeros((pg.num_blocks, 64, 576), dtype=torch.uint8, device=dev)
+    slots_all = torch.from_numpy(pg.slot_mapping).to(dev)
+    pa.reshape_and_cache_mla_fp8(case.latent.to(dev), kv, slots_all, kvs)
+    rows = torch.from_numpy(case.new_token_rows())
+    nl = case.latent[rows].to(dev).contiguous()
+    slots = slots_all[rows.to(dev)].contiguous()
+    q = case.query.to(dev)
+    bt = torch.from_numpy(pg.block_table).to(dev)
+    cl = torch.from_numpy(pg.lens).to(dev)
+    mc = int(pg.lens.max())
+    out = torch.empty((case.S, case.Hq, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(1, pa.mla_workspace_size(case.S, case.Hq, 512, mc, 0)),
+                     dtype=torch.uint8, device=dev)
+
+    kv_exp = kv.clone()  # the cache after the step's write (the same every replay)
+    pa.reshape_and_cache_mla_fp8(nl, kv_exp, slots, kvs)
+
+    def step():
+        pa.mla_decode_attn_fp8(q, kv, bt, cl, case.scale, mc, kvs, new_latent=nl,
+                               slot_mapping=slots, out=out, lse=lse, workspace=ws)
+    check_graph(step, [out, lse])
+    assert torch.equal(kv, kv_exp)
+
+
 def test_graph_extend_and_routed_batch():
     case = W.extend_case("graph_ext", 801, ctx_lens=[300, 0, 1000, 64], new_tokens=[37, 100, 1, 2],
                          Hq=8, Hkv=2, D=128, block_size=16, chunk_budget_tokens=512)
