@@ -44,6 +44,8 @@ METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 
 _CSRC = "paged_attention_decode_reshape_amd/csrc/"
 MEASURED_TRAFFIC = {
     "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "c7875b7c37b66cf0", 52.39e6),
+    "qwen3_fp8": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
+                  "9ce2920c1d3b0562", 28.39e6),
     "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77", 237.19e6),
     "mla_fp8": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77",
                 139.27e6),
@@ -981,8 +983,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-            "traffic": (measured_traffic(args.config)
-                        if r["kv_layout"] == "shuffled" and r["kv_dtype"] == "bf16" else None),
+            "traffic": (measured_traffic(args.config + ("_fp8" if r["kv_dtype"] == "fp8" else ""))
+                        if r["kv_layout"] == "shuffled" else None),
             "algo_bytes_per_launch": r["algo_bytes"],
             "avg_launch_ms": r["decode_ms"],
         },
