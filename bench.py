@@ -46,6 +46,8 @@ MEASURED_TRAFFIC = {
     "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "c7875b7c37b66cf0", 52.39e6),
     "qwen3_fp8": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
                   "9ce2920c1d3b0562", 28.39e6),
+    "merge": ((_CSRC + "merge.hip",), "5767d743027acd19", 340.74e6),
+    "cache_write": ((_CSRC + "cache_write.hip", _CSRC + "fp8.h"), "409d000f5c585fba", 107.43e6),
     "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77", 237.19e6),
     "mla_fp8": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77",
                 139.27e6),
@@ -908,7 +910,7 @@ def main():
         line = base_line(args, r, workload, unit="tokens/s")
         line["roofline"] = {"bound": "hbm", "kernel": "cache_write_shuffled_kernel",
                             "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
                             "algo_bytes_per_launch": r["algo_bytes"],
                             "avg_launch_ms": r["ms_per_step"]}
         print(json.dumps(line), flush=True)
@@ -922,7 +924,7 @@ def main():
         line["dtype"] = "f32"
         line["roofline"] = {"bound": "hbm", "kernel": "merge_pair_kernel", "achieved": r["gbps"],
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
                             "algo_bytes_per_launch": r["algo_bytes"],
                             "avg_launch_ms": r["ms_per_step"]}
         if not args.no_read_ceiling:
