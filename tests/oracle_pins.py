@@ -314,6 +314,96 @@ def pin_fp8_mla_matches_bf16(orc):
     _close(lse8, lse, what="fp8 mla lse")
 
 
+def _e4m3_value(code: int) -> float:
+    """E4M3 value from its bit fields (sign, 4 exponent bits, bias 7, 3
+    mantissa bits; exponent field 0 is subnormal), written out separately
+    from the oracle's table."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0:
+        return sign * math.ldexp(m / 8.0, -6)
+    return sign * math.ldexp(1.0 + m / 8.0, e - 7)
+
+
+def _bf16_bits_torch(f32: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns by torch's own round-to-nearest-even."""
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_fp8_gather_dequant(orc):
+    """The chunk gather with dequantisation (the MLA extend path's gather
+    "and maybe dequant", "ROCm attention backends" blog, AITER MLA extend
+    pseudocode): iteration `it` of chunk length c yields, request after
+    request, tokens [it c, min((it + 1) c, n)) as bf16(float32(value(code))
+    * float32(scale)), K under k_scale and V under v_scale.  Expected rows
+    come from the logical token codes (scattered by hand into the pages'
+    shapes), a bit-field decode and torch's bf16 rounding."""
+    from oracle import fp8
+    X = 16
+    rng = np.random.default_rng(77)
+    Hkv, D, B = 2, 32, 16
+    lens = [0, 5, 37, 70, 16]  # an empty request, a partial block, whole blocks
+    k_scale = np.float32(0.0371)   # distinct, not powers of two
+    v_scale = np.float32(1.7)
+    nblk = [(n + B - 1) // B for n in lens]
+    nb = sum(nblk) + 3
+    perm = rng.permutation(nb)
+    maxb = max(nblk)
+    table = np.zeros((len(lens), maxb), dtype=np.int32)
+    k_cache = np.full((nb, Hkv, D // X, B, X), 0x7F, dtype=np.uint8)
+    v_cache = np.full((nb, Hkv, B // X, D, X), 0x7F, dtype=np.uint8)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    kcodes, vcodes = [], []  # logical [n, Hkv, D] codes per request
+    nxt = 0
+    for s, n in enumerate(lens):
+        for j in range(nblk[s]):
+            table[s, j] = perm[nxt]
+            nxt += 1
+        kq = rng.choice(finite, size=(n, Hkv, D))
+        vq = rng.choice(finite, size=(n, Hkv, D))
+        for t in range(n):
+            p, o = int(table[s, t // B]), t % B
+            for g in range(Hkv):
+                for d in range(D):
+                    k_cache[p, g, d // X, o, d % X] = kq[t, g, d]
+                    v_cache[p, g, o // X, d, o % X] = vq[t, g, d]
+        kcodes.append(kq)
+        vcodes.append(vq)
+    # the constructed double-rounding case: code 0x3A is 1.25 and
+    # 1.25 * v_scale2 = 1 + 2^-8 + 2^-25 exactly; float32 rounds that to the
+    # tie 1 + 2^-8, which goes to the even bf16 0x3F80, while rounding the
+    # exact product straight to bf16 would give 0x3F81
+    v_scale2 = np.float32(13474202 * 2.0 ** -24)
+    assert 1.25 * float(v_scale2) == 1 + 2 ** -8 + 2 ** -25
+    vcodes[3][0, 0, 0] = 0x3A
+    p0 = int(table[3, 0])
+    v_cache[p0, 0, 0, 0, 0] = 0x3A
+    dec = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+    for chunk in (16, 32):
+        for vs in (v_scale, v_scale2):
+            for it in range(-(-max(lens) // chunk) + 1):  # one iteration past every end
+                ek, ev = [], []
+                for s, n in enumerate(lens):
+                    t0, t1 = it * chunk, min((it + 1) * chunk, n)
+                    if t1 > t0:
+                        ek.append(_bf16_bits_torch(
+                            dec[kcodes[s][t0:t1]].astype(np.float32) * k_scale))
+                        ev.append(_bf16_bits_torch(
+                            dec[vcodes[s][t0:t1]].astype(np.float32) * vs))
+                gk, gv = fp8.gather_dequant(k_cache, v_cache, table, np.array(lens), it, chunk,
+                                            float(k_scale), float(vs))
+                if not ek:
+                    assert gk.size == 0 and gv.size == 0, (chunk, it)
+                    continue
+                assert np.array_equal(gk, np.concatenate(ek)), ("fp8 gather K", chunk, it)
+                assert np.array_equal(gv, np.concatenate(ev)), ("fp8 gather V", chunk, it)
+    gk, gv = fp8.gather_dequant(k_cache, v_cache, table, np.array(lens), 0, 16,
+                                float(k_scale), float(v_scale2))
+    row = sum(min(16, n) for n in lens[:3])  # request 3's first token
+    assert gv[row, 0, 0] == 0x3F80, hex(gv[row, 0, 0])
+
+
 def pin_latent_write(orc):
     B, nb, Dl, T = 4, 9, 576, 20
     rng = np.random.default_rng(5)
@@ -549,6 +639,7 @@ ALL_PINS = [
     pin_fp8_cache_layout,
     pin_fp8_decode_matches_bf16,
     pin_fp8_mla_matches_bf16,
+    pin_fp8_gather_dequant,
     pin_latent_write,
     pin_decode_vs_numpy,
     pin_decode_closed_forms,

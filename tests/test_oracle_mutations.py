@@ -1,8 +1,9 @@
-"""Plant plausible mistakes in a copy of oracle.c and check that a pin fails.
+"""Plant plausible mistakes in a copy of the oracle and check that a pin fails.
 
 Each mutation is a (snippet, replacement) text edit: a dropped term, a wrong
-index, a transposed operand, an off-by-one.  The edited copy is compiled to a
-temporary library on the CPU and every pin in oracle_pins runs against it;
+index, a transposed operand, an off-by-one.  An edited copy of oracle.c is
+compiled to a temporary library on the CPU, an edited copy of fp8.py is
+loaded in place of ``oracle.fp8``, and every pin in oracle_pins runs against it;
 the mutation must make at least one of them fail.  This shows the pins are
 strong enough to catch that class of error in the oracle.  Each mutant runs
 in a child process, since a planted index error may also crash it (which
@@ -48,6 +49,34 @@ MUTATIONS = {
 }
 
 
+# mistakes in the FP8 oracle (oracle/fp8.py)
+FP8_MUTATIONS = {
+    "gather_scales_swapped": ("kf = _TABLE[K].astype(np.float32) * np.float32(k_scale)",
+                              "kf = _TABLE[K].astype(np.float32) * np.float32(v_scale)"),
+    "gather_range_one_too_long": ("t0, t1 = iteration * chunk, min((iteration + 1) * chunk, int(n))",
+                                  "t0, t1 = iteration * chunk, min((iteration + 1) * chunk + 1, int(n))"),
+    "gather_range_starts_late": ("t0, t1 = iteration * chunk, min((iteration + 1) * chunk, int(n))",
+                                 "t0, t1 = iteration * chunk + 1, min((iteration + 1) * chunk, int(n))"),
+    "gather_v_token_dim_transposed": ("V[j] = v_cache[p, :, o // X, :, o % X]",
+                                      "V[j] = v_cache[p, :, o % X, :, o // X]"),
+    "gather_product_rounded_from_f64": (
+        "vs.append(bf16_rne(vf))",
+        "vs.append(_bf16_direct(_TABLE[V] * float(np.float32(v_scale))))"),
+}
+_BF16_DIRECT = '''
+
+def _bf16_direct(x):
+    """float64 -> bf16 by rounding the float64 itself to nearest even."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    for i, v in np.ndenumerate(x):
+        m, e = np.frexp(v)
+        q = np.round(m * 256.0)  # numpy rounds halves to even
+        out[i] = (np.float32(np.ldexp(q, e - 8)).view(np.uint32) >> 16).astype(np.uint16)
+    return out
+'''
+
+
 def _run_all_pins(orc):
     """Names of the pins that fail against ``orc``."""
     failed = []
@@ -80,6 +109,31 @@ def test_mutation_is_caught(name, tmp_path):
             "failed = T._run_all_pins(oracle.Oracle(%r))\n"
             "print('FAILED_PINS', failed)\n"
             "sys.exit(3 if failed else 0)\n") % (os.path.dirname(here), here, lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutation {name} passed every pin: {r.stdout[-500:]}"
+    if r.returncode == 3:
+        assert "FAILED_PINS" in r.stdout
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
+def test_fp8_mutation_is_caught(name, tmp_path):
+    src_path = os.path.join(os.path.dirname(oracle.SRC), "fp8.py")
+    with open(src_path) as f:
+        src = f.read()
+    old, new = FP8_MUTATIONS[name]
+    assert src.count(old) >= 1, f"mutation site for {name} no longer in fp8.py"
+    mutated = tmp_path / "fp8_mut.py"
+    mutated.write_text(src.replace(old, new, 1) + _BF16_DIRECT)
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys; sys.path[:0] = [%r, %r]\n"
+            "import importlib.util, oracle\n"
+            "spec = importlib.util.spec_from_file_location('oracle.fp8', %r)\n"
+            "mod = importlib.util.module_from_spec(spec); spec.loader.exec_module(mod)\n"
+            "sys.modules['oracle.fp8'] = mod; oracle.fp8 = mod\n"
+            "import test_oracle_mutations as T\n"
+            "failed = T._run_all_pins(oracle.get())\n"
+            "print('FAILED_PINS', failed)\n"
+            "sys.exit(3 if failed else 0)\n") % (os.path.dirname(here), here, str(mutated))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutation {name} passed every pin: {r.stdout[-500:]}"
     if r.returncode == 3:
