@@ -546,10 +546,10 @@ __device__ __forceinline__ void transpose_v_std(char *region, const uint4 (&raw)
 // of the workgroup take SUBS-sub-block chunks of the range round-robin
 // (sub-block k of a wave is sub-block k % SUBS of its chunk k / SUBS);
 // otherwise the wave owns the range and its sub-blocks are consecutive.
-template <int SUBS, bool SHARED>
+template <int SUBS, bool SHARED, int NWV = kWaves>
 __device__ __forceinline__ int sub_t0(int k, int wave) {
     if constexpr (SHARED)
-        return (kWaves * (k / SUBS) + wave) * (kSub * SUBS) + kSub * (k % SUBS);
+        return (NWV * (k / SUBS) + wave) * (kSub * SUBS) + kSub * (k % SUBS);
     else
         return kSub * k;
 }
@@ -557,11 +557,11 @@ __device__ __forceinline__ int sub_t0(int k, int wave) {
 // Raw block-table entry of the wave's sub-block `lane` in the window that
 // starts at token `start` (index clamped into the table; the caller decides
 // validity).
-template <int B, int SUBS, bool SHARED>
+template <int B, int SUBS, bool SHARED, int NWV = kWaves>
 __device__ __forceinline__ int bt_entry(const DecodeParams &p, int s, int start) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int t0 = start + sub_t0<SUBS, SHARED>(lane, wave);
+    const int t0 = start + sub_t0<SUBS, SHARED, NWV>(lane, wave);
     return p.block_table[(size_t)s * p.max_blocks + min(t0 / B, p.max_blocks - 1)];
 }
 
@@ -573,7 +573,7 @@ __device__ __forceinline__ int bt_entry(const DecodeParams &p, int s, int start)
 // tracks the block ids of 64 sub-blocks at a time, so longer ranges are
 // taken in windows; bt_first is bt_entry() of the first window, loaded
 // early by the caller.
-template <int D, int B, int G, int SUBS, bool SHARED, int LAY>
+template <int D, int B, int G, int SUBS, bool SHARED, int LAY, int NBUF = 2, int NWV = kWaves>
 __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g, int range_start,
                                              int range_end, int bt_first, const uint32_t (&qreg)[G],
                                              float (&m)[G], float (&lsum)[G],
@@ -582,7 +582,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
     constexpr int DV = D / 64;        // output dims per lane
     constexpr bool kPairs = G >= 2;
     constexpr int HS = kPairs ? 2 : 1;
-    constexpr int kWindow = (SHARED ? kWaves : 1) * 64 * kSub;  // tokens per window
+    constexpr int kWindow = (SHARED ? NWV : 1) * 64 * kSub;  // tokens per window
     constexpr bool STD = LAY == kLayStd, FP8 = LAY == kLayFp8;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -596,18 +596,18 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
     const uint32_t v_off = STD ? k_off : (uint32_t)lane * 16;
     char *vt_region = nullptr;
     if constexpr (STD) {
-        __shared__ __align__(16) char vt_lds[kWaves][StdVLayout<D>::kWaveBytes];
+        __shared__ __align__(16) char vt_lds[NWV][StdVLayout<D>::kWaveBytes];
         vt_region = vt_lds[wave];
     }
 
     int bt_raw = bt_first;
     for (int start = range_start; start < range_end; start += kWindow) {
         const int end = min(start + kWindow, range_end);
-        if (start != range_start) bt_raw = bt_entry<B, SUBS, SHARED>(p, s, start);
+        if (start != range_start) bt_raw = bt_entry<B, SUBS, SHARED, NWV>(p, s, start);
         // lane k: physical block of this wave's sub-block k, -1 past the end or
         // out of range.  Validity is monotone in k, so the sub-blocks in range
         // are 0 .. nmine - 1.
-        const int t0_lane = start + sub_t0<SUBS, SHARED>(lane, wave);
+        const int t0_lane = start + sub_t0<SUBS, SHARED, NWV>(lane, wave);
         const bool lane_ok = t0_lane < end;
         const int bid = lane_ok && bt_raw >= 0 && (int64_t)bt_raw < p.num_blocks ? bt_raw : -1;
         const int nmine = __popcll(__ballot(lane_ok));
@@ -617,7 +617,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
         auto locate = [&](int k, size_t &tile, int &half) {
             k = min(k, 63);
             const int b = readlane_i32(bid, k);
-            const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
+            const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
             tile = (size_t)(b < 0 ? 0 : b) * p.Hkv + g;
             half = (t0 % B) / kSub;
         };
@@ -625,7 +625,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
         auto std_first = [&](int k) -> size_t {
             k = min(k, 63);
             const int b = readlane_i32(bid, k);
-            const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
+            const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
             return ((size_t)(b < 0 ? 0 : b) * B + (t0 % B) / kSub * kSub) * p.Hkv + g;
         };
         auto load_k = [&](int k, uint4 (&kq)[CQ]) {
@@ -659,13 +659,17 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
         // waits say exactly that to the compiler.
         // load instructions per sub-block
         constexpr int LK = FP8 ? D / 64 : CQ, LV = FP8 ? DV : 2 * DV;
+        // loads issued after sub-block k's, still in flight when k starts
+        constexpr int kAhead = (NBUF - 1) * (LK + LV);
+        static_assert(NBUF == 2 || NBUF == 4, "ring of 2 or 4 sub-blocks");
+        static_assert(LV + kAhead < 64, "vmcnt range");
         auto compute_sub = [&](int k, const uint4 (&kin)[CQ], const uint4 (&vv)[2][DV]) {
-            const int t0 = start + sub_t0<SUBS, SHARED>(k, wave);
+            const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
             const int nvalid =
                 k < nmine && readlane_i32(bid, min(k, 63)) >= 0 ? min(kSub, end - t0) : 0;
             float z[G];
             if (nvalid > 0) {
-                wait_vm_loads<LV + LK + LV>();
+                wait_vm_loads<LV + kAhead>();
                 uint4 kconv[CQ];
                 if constexpr (FP8) k_fp8_to_bf16<D>(kin, kconv);
                 const uint4 (&kq)[CQ] = FP8 ? kconv : kin;
@@ -734,7 +738,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
                 }
                 // PV: the V of tokens past the end is zeroed (weight 0, data may
                 // be anything); the buffers themselves are only read
-                wait_vm_loads<LK + LV>();
+                wait_vm_loads<kAhead>();
                 uint4 vt[2][DV];
                 if constexpr (STD)
                     transpose_v_std<D>(vt_region, reinterpret_cast<const uint4(&)[CQ]>(vv), vt);
@@ -781,16 +785,42 @@ __device__ __forceinline__ void attend_range(const DecodeParams &p, int s, int g
         // overlaps the stream (loads complete in issue order).  Every load is
         // issued on every path (a load past the end touches no memory), so
         // the buffers are plain loop-carried registers.
-        uint4 kA[CQ], vA[2][DV], kB[CQ], vB[2][DV];
-        load_k(0, kA);
-        load_v(0, vA);
-        for (int k = 0; k < nmine; k += 2) {
-            load_k(k + 1, kB);
-            load_v(k + 1, vB);
-            compute_sub(k, kA, vA);
-            load_k(k + 2, kA);
-            load_v(k + 2, vA);
-            compute_sub(k + 1, kB, vB);
+        if constexpr (NBUF == 2) {
+            uint4 kA[CQ], vA[2][DV], kB[CQ], vB[2][DV];
+            load_k(0, kA);
+            load_v(0, vA);
+            for (int k = 0; k < nmine; k += 2) {
+                load_k(k + 1, kB);
+                load_v(k + 1, vB);
+                compute_sub(k, kA, vA);
+                load_k(k + 2, kA);
+                load_v(k + 2, vA);
+                compute_sub(k + 1, kB, vB);
+            }
+        } else {
+            // four sub-blocks in flight: a wave's whole share of a short
+            // piece is requested before its first sub-block is computed
+            uint4 kA[CQ], vA[2][DV], kB[CQ], vB[2][DV], kC[CQ], vC[2][DV], kD[CQ], vD[2][DV];
+            load_k(0, kA);
+            load_v(0, vA);
+            load_k(1, kB);
+            load_v(1, vB);
+            load_k(2, kC);
+            load_v(2, vC);
+            for (int k = 0; k < nmine; k += 4) {
+                load_k(k + 3, kD);
+                load_v(k + 3, vD);
+                compute_sub(k, kA, vA);
+                load_k(k + 4, kA);
+                load_v(k + 4, vA);
+                compute_sub(k + 1, kB, vB);
+                load_k(k + 5, kB);
+                load_v(k + 5, vB);
+                compute_sub(k + 2, kC, vC);
+                load_k(k + 6, kC);
+                load_v(k + 6, vC);
+                compute_sub(k + 3, kD, vD);
+            }
         }
     }
     if constexpr (FP8) {  // V codes were summed unscaled
@@ -825,10 +855,10 @@ __device__ __forceinline__ void reset_state(float (&m)[G], float (&lsum)[G], flo
     }
 }
 
-template <int D, int G>
+template <int D, int G, int NWV = kWaves>
 struct WaveMergeLDS {
-    float m[kWaves][G], l[kWaves][G];
-    __align__(16) float acc[kWaves][G][D];
+    float m[NWV][G], l[NWV][G];
+    __align__(16) float acc[NWV][G][D];
 };
 
 // Merge the 4 waves' states in LDS; thread (head h, dims d .. d + 3) then
@@ -836,8 +866,8 @@ struct WaveMergeLDS {
 // (natural log).  Every row holds the same token weights, so a wave's sum
 // of weights is 4 x the row sum.  Ends with the workgroup synchronised only
 // before the emits: callers that reuse the LDS must synchronise again.
-template <int D, int G, typename Emit>
-__device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G> &sm, int Ga, const float (&m)[G],
+template <int D, int G, int NWV, typename Emit>
+__device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G, NWV> &sm, int Ga, const float (&m)[G],
                                             const float (&lsum)[G], const float (&acc)[G][D / 64],
                                             Emit emit) {
     constexpr int DV = D / 64;
@@ -858,11 +888,11 @@ __device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G> &sm, int Ga, cons
         const int h = idx / (D / 4), d = 4 * (idx % (D / 4));
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
+        for (int w = 0; w < NWV; w++) M = fmax_nc(M, sm.m[w][h]);
         const float Mr = M == kNegInf ? 0.f : M;
         float o[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) {
+        for (int w = 0; w < NWV; w++) {
             const float wt = fast_exp2(sm.m[w][h] - Mr);
             const float4 a = *reinterpret_cast<const float4 *>(&sm.acc[w][h][d]);
             o[0] += wt * a.x;
@@ -876,6 +906,409 @@ __device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G> &sm, int Ga, cons
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] *= inv;
         emit(h, d, o, L);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-per-head softmax with gathered weights (bf16 caches, 4, 8 or 16 query
+// heads per kv head).  QK is computed as above (lane (row r, column n): token
+// n, the r-th quarter of head_dim), but the four rows' partial dot products
+// of four heads are summed with two-register permlane swaps, after which row
+// r holds head r's 16 scores: 3 swaps and 3 adds per 4 heads instead of 8 and
+// 8, and each softmax weight is computed once, not once per row.  The
+// weights of token pairs are split into bf16 hi + lo parts and gathered so
+// that every row holds every head's (3 permlane swaps per register); P.V then
+// runs in the V cache's own layout (lane l: dims l and l + 64) as v_dot2c over
+// the bf16 pairs of a V vector, so V is neither widened nor loaded twice.
+//
+// Wait states the compiler cannot see inside the asm blocks (gfx950):
+//  - a VALU write of a VGPR followed by a DPP read of it needs 2 wait
+//    states: every block that reads an operand through DPP starts with
+//    s_nop 1 (the compiler may place the producer right before it);
+//  - a v_dot2c result read by any other VALU instruction, or by a dot as its
+//    A or B operand, needs 3 wait states; read by the same dot opcode as its
+//    accumulator it needs none.  Blocks whose results plain code reads next
+//    end with s_nop 4 (5 wait states), or the caller fences them
+//    (dpp_result_fence).
+// ---------------------------------------------------------------------------
+
+// 4 heads, one accumulator each, over the lane's 16 (D = 128) or 8 (D = 64)
+// K dwords; dword n of the row slice comes from lane n of each head's query
+// register.
+#define PA_QK4_N(kd, n) \
+    PA_DOT2_BC("%0", "%4", kd, n) PA_DOT2_BC("%1", "%5", kd, n) \
+    PA_DOT2_BC("%2", "%6", kd, n) PA_DOT2_BC("%3", "%7", kd, n)
+#define PA_QK4_D128                                                                         \
+    "s_nop 1\n\t"                                                                           \
+    PA_QK4_N("%8", "0") PA_QK4_N("%9", "1") PA_QK4_N("%10", "2") PA_QK4_N("%11", "3")       \
+    PA_QK4_N("%12", "4") PA_QK4_N("%13", "5") PA_QK4_N("%14", "6") PA_QK4_N("%15", "7")     \
+    PA_QK4_N("%16", "8") PA_QK4_N("%17", "9") PA_QK4_N("%18", "10") PA_QK4_N("%19", "11")   \
+    PA_QK4_N("%20", "12") PA_QK4_N("%21", "13") PA_QK4_N("%22", "14") PA_QK4_N("%23", "15") \
+    "s_nop 4\n\t"
+#define PA_QK4_D64                                                                          \
+    "s_nop 1\n\t"                                                                           \
+    PA_QK4_N("%8", "0") PA_QK4_N("%9", "1") PA_QK4_N("%10", "2") PA_QK4_N("%11", "3")       \
+    PA_QK4_N("%12", "4") PA_QK4_N("%13", "5") PA_QK4_N("%14", "6") PA_QK4_N("%15", "7")     \
+    "s_nop 4\n\t"
+
+template <int D>
+__device__ __forceinline__ void qk_4h(float (&a)[4], const uint32_t *q, const uint4 (&k)[D / 32]) {
+    if constexpr (D == 128)
+        asm volatile(PA_QK4_D128
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+                     : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(k[0].x), "v"(k[0].y),
+                       "v"(k[0].z), "v"(k[0].w), "v"(k[1].x), "v"(k[1].y), "v"(k[1].z),
+                       "v"(k[1].w), "v"(k[2].x), "v"(k[2].y), "v"(k[2].z), "v"(k[2].w),
+                       "v"(k[3].x), "v"(k[3].y), "v"(k[3].z), "v"(k[3].w));
+    else
+        asm volatile(PA_QK4_D64
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+                     : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(k[0].x), "v"(k[0].y),
+                       "v"(k[0].z), "v"(k[0].w), "v"(k[1].x), "v"(k[1].y), "v"(k[1].z),
+                       "v"(k[1].w));
+}
+
+// Sum over the 4 rows of 4 heads' partial dots: row r of the result holds
+// head r's totals (column n: token n).  A permlane16 swap of two registers
+// exchanges the odd rows of the first with the even rows of the second, a
+// permlane32 swap the upper half of the first with the lower half of the
+// second.
+__device__ __forceinline__ float rows_to_heads(float a0, float a1, float a2, float a3) {
+    auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+    const float s01 = __uint_as_float(x[0]) + __uint_as_float(x[1]);  // h0 r01, h1 r01, h0 r23, h1 r23
+    auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a2), __float_as_uint(a3), false, false);
+    const float s23 = __uint_as_float(y[0]) + __uint_as_float(y[1]);  // h2 r01, h3 r01, h2 r23, h3 r23
+    auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    return __uint_as_float(z[0]) + __uint_as_float(z[1]);             // h0, h1, h2, h3
+}
+
+// P.V in the V cache's own layout once every row holds every head's weights
+// (gather_rows below): lane l owns dims l and l + 64 of all heads, a V
+// vector is 8 tokens of one dim as 4 bf16 pairs, and the weights of token
+// pair w of token group tg come from lane 8 tg + 2 w of the row, in bf16 hi
+// and lo parts.  One block: two heads (a, b), both token groups.
+//   D = 128: %0 %1 a (dims l, l + 64), %2 %3 b; %4 %5 a hi / lo, %6 %7 b hi /
+//   lo; %8..%11 V of (tg 0, dim l), %12..%15 (tg 0, l + 64), %16..%19
+//   (tg 1, l), %20..%23 (tg 1, l + 64).
+#define PA_PVG2_W128(L, va0, va1)                                                           \
+    PA_DOT2_BC("%0", "%4", va0, L) PA_DOT2_BC("%1", "%4", va1, L)                           \
+    PA_DOT2_BC("%2", "%6", va0, L) PA_DOT2_BC("%3", "%6", va1, L)                           \
+    PA_DOT2_BC("%0", "%5", va0, L) PA_DOT2_BC("%1", "%5", va1, L)                           \
+    PA_DOT2_BC("%2", "%7", va0, L) PA_DOT2_BC("%3", "%7", va1, L)
+#define PA_PVG2_D128                                                                        \
+    "s_nop 1\n\t"                                                                           \
+    PA_PVG2_W128("0", "%8", "%12") PA_PVG2_W128("2", "%9", "%13")                           \
+    PA_PVG2_W128("4", "%10", "%14") PA_PVG2_W128("6", "%11", "%15")                         \
+    PA_PVG2_W128("8", "%16", "%20") PA_PVG2_W128("10", "%17", "%21")                        \
+    PA_PVG2_W128("12", "%18", "%22") PA_PVG2_W128("14", "%19", "%23")
+//   D = 64: %0 a, %1 b (dim l); %2 %3 a hi / lo, %4 %5 b hi / lo; %6..%9 V of
+//   (tg 0, dim l), %10..%13 (tg 1, dim l).
+#define PA_PVG2_W64(L, va)                                                                  \
+    PA_DOT2_BC("%0", "%2", va, L) PA_DOT2_BC("%1", "%4", va, L)                             \
+    PA_DOT2_BC("%0", "%3", va, L) PA_DOT2_BC("%1", "%5", va, L)
+#define PA_PVG2_D64                                                                         \
+    "s_nop 1\n\t"                                                                           \
+    PA_PVG2_W64("0", "%6") PA_PVG2_W64("2", "%7") PA_PVG2_W64("4", "%8") PA_PVG2_W64("6", "%9") \
+    PA_PVG2_W64("8", "%10") PA_PVG2_W64("10", "%11") PA_PVG2_W64("12", "%12")              \
+    PA_PVG2_W64("14", "%13")
+
+template <int D>
+__device__ __forceinline__ void pv_2h(float (&a)[D / 64], float (&b)[D / 64], uint32_t ah,
+                                      uint32_t al, uint32_t bh, uint32_t bl,
+                                      const uint4 (&v)[2][D / 64]) {
+    if constexpr (D == 128)
+        asm volatile(PA_PVG2_D128
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1])
+                     : "v"(ah), "v"(al), "v"(bh), "v"(bl), "v"(v[0][0].x), "v"(v[0][0].y),
+                       "v"(v[0][0].z), "v"(v[0][0].w), "v"(v[0][1].x), "v"(v[0][1].y),
+                       "v"(v[0][1].z), "v"(v[0][1].w), "v"(v[1][0].x), "v"(v[1][0].y),
+                       "v"(v[1][0].z), "v"(v[1][0].w), "v"(v[1][1].x), "v"(v[1][1].y),
+                       "v"(v[1][1].z), "v"(v[1][1].w));
+    else
+        asm volatile(PA_PVG2_D64
+                     : "+v"(a[0]), "+v"(b[0])
+                     : "v"(ah), "v"(al), "v"(bh), "v"(bl), "v"(v[0][0].x), "v"(v[0][0].y),
+                       "v"(v[0][0].z), "v"(v[0][0].w), "v"(v[1][0].x), "v"(v[1][0].y),
+                       "v"(v[1][0].z), "v"(v[1][0].w));
+}
+
+// bf16 hi and lo parts of the weights of token pairs: lane 2w of a row gets
+// (p[2w], p[2w + 1]) (its own weight and its right neighbour's), so that
+// p = hi + lo to 16 significant bits.
+__device__ __forceinline__ void split_pairs(float p, uint32_t &ph, uint32_t &pl) {
+    const float pn = dpp_f<kQuadXor1>(p);
+    ph = pack_bf16x2(p, pn);
+    pl = pack_bf16x2(p - bf16_lo(ph), pn - bf16_hi(ph));
+}
+
+// Every row gets every row's values: out[r] holds row r of v in all four
+// rows (one permlane32 swap and two permlane16 swaps).
+__device__ __forceinline__ void gather_rows(uint32_t v, uint32_t (&out)[4]) {
+    auto x = __builtin_amdgcn_permlane32_swap(v, v, false, false);        // r0 r1 r0 r1 | r2 r3 r2 r3
+    auto y = __builtin_amdgcn_permlane16_swap(x[0], x[0], false, false);  // r0 x4 | r1 x4
+    auto z = __builtin_amdgcn_permlane16_swap(x[1], x[1], false, false);  // r2 x4 | r3 x4
+    out[0] = y[0];
+    out[1] = y[1];
+    out[2] = z[0];
+    out[3] = z[1];
+}
+
+// Sum over the 16 lanes of each row (every lane gets its row's sum).
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp_f<kQuadXor1>(v);
+    v += dpp_f<kQuadXor2>(v);
+    v += dpp_f<kRowRor4>(v);
+    v += dpp_f<kRowRor8>(v);
+    return v;
+}
+
+// The gathered-weight counterpart of attend_range (bf16 caches, G a multiple
+// of 4).  State per lane: for the NR = G / 4 heads 4 i + r of its row r, the
+// reference maximum m[i] (log2 units, the same in every lane of the row) and
+// the lane's share of the weight sum lsum[i] (summed over the row at the
+// end); acc[h][jj] for every head h and dims l + 64 jj, as in attend_range.
+template <int D, int B, int G, int SUBS, bool SHARED, int LAY, int NWV = kWaves>
+__device__ __forceinline__ void attend_range_rh(const DecodeParams &p, int s, int g,
+                                                int range_start, int range_end, int bt_first,
+                                                const uint32_t (&qreg)[G], float (&m)[G / 4],
+                                                float (&lsum)[G / 4], float (&acc)[G][D / 64]) {
+    constexpr int CQ = D / 32;        // K vectors per lane per sub-block
+    constexpr int DV = D / 64;        // output dims per lane
+    constexpr int NR = G / 4;         // heads per row
+    constexpr int kWindow = (SHARED ? NWV : 1) * 64 * kSub;  // tokens per window
+    constexpr bool STD = LAY == kLayStd;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int row = lane >> 4, col = lane & 15;
+    const float sl2 = p.scale * kLog2e;
+    const char *kc = reinterpret_cast<const char *>(p.k_cache);
+    const char *vc = reinterpret_cast<const char *>(p.v_cache);
+    const uint32_t k_off = STD ? std_lane_off<D>(row, col, p.Hkv) : k_lane_off<D, B>(row, col);
+    const uint32_t v_off = STD ? k_off : (uint32_t)lane * 16;
+    char *vt_region = nullptr;
+    if constexpr (STD) {
+        __shared__ __align__(16) char vt_lds[NWV][StdVLayout<D>::kWaveBytes];
+        vt_region = vt_lds[wave];
+    }
+
+    int bt_raw = bt_first;
+    for (int start = range_start; start < range_end; start += kWindow) {
+        const int end = min(start + kWindow, range_end);
+        if (start != range_start) bt_raw = bt_entry<B, SUBS, SHARED, NWV>(p, s, start);
+        const int t0_lane = start + sub_t0<SUBS, SHARED, NWV>(lane, wave);
+        const bool lane_ok = t0_lane < end;
+        const int bid = lane_ok && bt_raw >= 0 && (int64_t)bt_raw < p.num_blocks ? bt_raw : -1;
+        const int nmine = __popcll(__ballot(lane_ok));
+
+        auto locate = [&](int k, size_t &tile, int &half) {
+            k = min(k, 63);
+            const int b = readlane_i32(bid, k);
+            const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
+            tile = (size_t)(b < 0 ? 0 : b) * p.Hkv + g;
+            half = (t0 % B) / kSub;
+        };
+        // standard layout: the sub-block's first row (block, 16-token half, head g)
+        auto std_first = [&](int k) -> size_t {
+            k = min(k, 63);
+            const int b = readlane_i32(bid, k);
+            const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
+            return ((size_t)(b < 0 ? 0 : b) * B + (t0 % B) / kSub * kSub) * p.Hkv + g;
+        };
+        auto load_kv = [&](int k, uint4 (&kq)[CQ], uint4 (&vv)[2][DV]) {
+            if constexpr (STD) {
+                const size_t first = std_first(k);
+                load_rows_std<D>(kc, first, p.Hkv, k < nmine, k_off, kq);
+                load_rows_std<D>(vc, first, p.Hkv, k < nmine, v_off,
+                                 reinterpret_cast<uint4(&)[CQ]>(vv));
+            } else {
+                size_t tile;
+                int half;
+                locate(k, tile, half);
+                load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
+                load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
+            }
+        };
+        constexpr int LK = CQ, LV = 2 * DV;
+
+        auto compute_sub = [&](int k, const uint4 (&kq)[CQ], const uint4 (&vin)[2][DV]) {
+            const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
+            const int nvalid =
+                k < nmine && readlane_i32(bid, min(k, 63)) >= 0 ? min(kSub, end - t0) : 0;
+            if (nvalid <= 0) return;
+            // in flight: this sub-block's K and V, then the next one's
+            wait_vm_loads<LV + LK + LV>();
+            float z[NR];
+#pragma unroll
+            for (int i = 0; i < NR; i++) {
+                float a[4] = {0.f, 0.f, 0.f, 0.f};
+                qk_4h<D>(a, &qreg[4 * i], kq);
+                z[i] = rows_to_heads(a[0], a[1], a[2], a[3]) * sl2;
+            }
+            if (nvalid < kSub) {
+#pragma unroll
+                for (int i = 0; i < NR; i++) z[i] = col < nvalid ? z[i] : kNegInf;
+            }
+            // lazy softmax: a row's reference moves only when one of its
+            // scores passes it by more than kLazyLog2
+            uint64_t over = 0;
+#pragma unroll
+            for (int i = 0; i < NR; i++) over |= __ballot(z[i] > m[i] + kLazyLog2);
+            if (over) {
+                dpp_result_fence<G * DV>(&acc[0][0]);
+#pragma unroll
+                for (int i = 0; i < NR; i++) {
+                    const float mx = row_max16(z[i]);
+                    float alpha = 1.f;
+                    if (mx > m[i] + kLazyLog2) {
+                        alpha = fast_exp2(m[i] - mx);  // 0 from -inf
+                        m[i] = mx;
+                    }
+                    lsum[i] *= alpha;
+                    uint32_t al[4];
+                    gather_rows(__float_as_uint(alpha), al);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+#pragma unroll
+                        for (int jj = 0; jj < DV; jj++) acc[4 * i + r][jj] *= __uint_as_float(al[r]);
+                }
+            }
+            uint32_t ph[G], pl[G];
+#pragma unroll
+            for (int i = 0; i < NR; i++) {
+                const float pr = fast_exp2(z[i] - m[i]);  // m[i] is finite here
+                lsum[i] += pr;
+                uint32_t h, l;
+                split_pairs(pr, h, l);
+                gather_rows(h, reinterpret_cast<uint32_t(&)[4]>(ph[4 * i]));
+                gather_rows(l, reinterpret_cast<uint32_t(&)[4]>(pl[4 * i]));
+            }
+            // in flight: this sub-block's V, then the next sub-block's K and V
+            wait_vm_loads<LK + LV>();
+            uint4 vv[2][DV];
+            if constexpr (STD) {
+                transpose_v_std<D>(vt_region, reinterpret_cast<const uint4(&)[CQ]>(vin), vv);
+            } else {
+#pragma unroll
+                for (int tg = 0; tg < 2; tg++)
+#pragma unroll
+                    for (int jj = 0; jj < DV; jj++) vv[tg][jj] = vin[tg][jj];
+            }
+            if (nvalid < kSub) {
+                // tokens past the end carry weight 0 and V may hold anything
+                // (NaN included): zero their V
+#pragma unroll
+                for (int tg = 0; tg < 2; tg++) {
+                    const int nv = nvalid - 8 * tg;
+#pragma unroll
+                    for (int jj = 0; jj < DV; jj++) {
+                        vv[tg][jj].x = mask_pair(vv[tg][jj].x, 0, nv);
+                        vv[tg][jj].y = mask_pair(vv[tg][jj].y, 2, nv);
+                        vv[tg][jj].z = mask_pair(vv[tg][jj].z, 4, nv);
+                        vv[tg][jj].w = mask_pair(vv[tg][jj].w, 6, nv);
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; h += 2)
+                pv_2h<D>(acc[h], acc[h + 1], ph[h], pl[h], ph[h + 1], pl[h + 1], vv);
+            dpp_result_fence<G * DV>(&acc[0][0]);
+        };
+
+        // two buffers: sub-block k + 1 is requested before k is computed
+        uint4 kA[CQ], vA[2][DV], kB[CQ], vB[2][DV];
+        load_kv(0, kA, vA);
+        for (int k = 0; k < nmine; k += 2) {
+            load_kv(k + 1, kB, vB);
+            compute_sub(k, kA, vA);
+            load_kv(k + 2, kA, vA);
+            compute_sub(k + 1, kB, vB);
+        }
+    }
+}
+
+// Merge of the 4 waves' states (accumulators as in merge_waves, maxima and
+// weight sums per row head) in LDS, then emit(h, d, o, L) per (head, 4 dims)
+// as merge_waves does.
+template <int D, int G, int NWV, typename Emit>
+__device__ __forceinline__ void merge_waves_rh(WaveMergeLDS<D, G, NWV> &sm, int Ga,
+                                               const float (&m)[G / 4], const float (&lsum)[G / 4],
+                                               const float (&acc)[G][D / 64], Emit emit) {
+    constexpr int DV = D / 64, NR = G / 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, row = lane >> 4, col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const float l = row_sum16(lsum[i]);
+        if (col == 0) {
+            sm.m[wave][4 * i + row] = m[i];
+            sm.l[wave][4 * i + row] = l;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int jj = 0; jj < DV; jj++) sm.acc[wave][h][lane + 64 * jj] = acc[h][jj];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < Ga * (D / 4); idx += blockDim.x) {
+        const int h = idx / (D / 4), d = 4 * (idx % (D / 4));
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NWV; w++) M = fmax_nc(M, sm.m[w][h]);
+        const float Mr = M == kNegInf ? 0.f : M;
+        float o[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; w++) {
+            const float wt = fast_exp2(sm.m[w][h] - Mr);
+            const float4 a = *reinterpret_cast<const float4 *>(&sm.acc[w][h][d]);
+            o[0] += wt * a.x;
+            o[1] += wt * a.y;
+            o[2] += wt * a.z;
+            o[3] += wt * a.w;
+            den += wt * sm.l[w][h];
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] *= inv;
+        emit(h, d, o, L);
+    }
+}
+
+// The gathered-weight formulation serves the bf16 caches (shuffled and
+// standard) with 4, 8 or 16 query heads per kv head; the FP8 cache and
+// smaller groups use attend_range.
+template <int LAY, int G>
+constexpr bool uses_rh() { return (LAY == kLayShuffled || LAY == kLayStd) && G >= 4; }
+
+template <int D, int G, int LAY, int NWV = kWaves>
+using MergeLDS = WaveMergeLDS<D, G, NWV>;
+
+// Attention of this workgroup's waves over tokens [tb, te) of unit (s, g),
+// then the merge of the waves' states; emit(h, d, o, L) as in merge_waves.
+template <int D, int B, int G, int SUBS, int LAY, int NWV, typename Emit>
+__device__ __forceinline__ void attend_merge(const DecodeParams &p, int s, int g, int tb, int te,
+                                             int bt_first, const uint32_t (&qreg)[G],
+                                             MergeLDS<D, G, LAY, NWV> &sm, int Ga, Emit emit) {
+    if constexpr (uses_rh<LAY, G>()) {
+        constexpr int NR = G / 4, DV = D / 64;
+        float m[NR], lsum[NR], acc[G][DV];
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            m[i] = kNegInf;
+            lsum[i] = 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int jj = 0; jj < DV; jj++) acc[h][jj] = 0.f;
+        attend_range_rh<D, B, G, SUBS, true, LAY, NWV>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
+        merge_waves_rh<D, G, NWV>(sm, Ga, m, lsum, acc, emit);
+    } else {
+        constexpr int DV = D / 64;
+        float m[G], lsum[G], acc[G][DV];
+        reset_state<G, DV>(m, lsum, acc);
+        attend_range<D, B, G, SUBS, true, LAY, 2, NWV>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
+        merge_waves<D, G, NWV>(sm, Ga, m, lsum, acc, emit);
     }
 }
 
@@ -1013,16 +1446,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     const int nparts = (ctx + P - 1) / P;
     // the partition holding the last token writes the new token first
     if (p.slot_mapping && end == ctx) write_new_token<D, B, LAY>(p, s, g);
-    float m[G], lsum[G], acc[G][DV];
-    reset_state<G, DV>(m, lsum, acc);
-    attend_range<D, B, G, SUBS, true, LAY>(p, s, g, start, end, bt_first, qreg, m, lsum, acc);
-
-    __shared__ WaveMergeLDS<D, G> sm;
+    __shared__ MergeLDS<D, G, LAY, kWaves> sm;
     const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
     // partials of this unit's rows, addressed from its first row (32-bit offsets)
     const auto prs = coherent_rsrc(p.part_out + row0 * p.max_parts * D,
                                    (uint32_t)Ga * p.max_parts * D * 4);
-    merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, const float (&o)[4], float L) {
+    attend_merge<D, B, G, SUBS, LAY, kWaves>(p, s, g, start, end, bt_first, qreg, sm, Ga,
+                                     [&](int h, int d, const float (&o)[4], float L) {
         const size_t orow = row0 + h;
         if (nparts == 1) {
             store_out4(out + orow * D + d, o);
@@ -1119,8 +1549,8 @@ __device__ __forceinline__ void merge_unit_partials(const DecodeParams &p, size_
     }
 }
 
-template <int D, int B, int G, int LAY>
-__global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
+template <int D, int B, int G, int LAY, int NWV>
+__global__ __launch_bounds__(NWV * 64, 8 / NWV) void paged_decode_balanced_kernel(DecodeParams p) {
     constexpr int DV = D / 64;
     const int NW = gridDim.x, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -1161,7 +1591,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
         return n < (uint32_t)nsb ? (int)n : nsb;
     };
 
-    __shared__ WaveMergeLDS<D, G> sm;
+    __shared__ MergeLDS<D, G, LAY, NWV> sm;
     for (int64_t v = w; ; v += NW) {
         // find piece v (every wave computes the same)
         int s = -1, g = 0, k = 0, n = 1, a = 0, b = 0, ctx = 0, P_u = 0;
@@ -1197,16 +1627,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
         const int tb = a * kSub, te = min(b * kSub, ctx);
         // the piece holding the last token writes the new token first
         if (p.slot_mapping && te == ctx) write_new_token<D, B, LAY>(p, s, g);
-        const int bt_first = bt_entry<B, 1, true>(p, s, tb);
+        const int bt_first = bt_entry<B, 1, true, NWV>(p, s, tb);
         uint32_t qreg[G];
         load_queries<D, G>(p, s, g, Ga, qreg);
-        float m[G], lsum[G], acc[G][DV];
-        reset_state<G, DV>(m, lsum, acc);
-        attend_range<D, B, G, 1, true, LAY>(p, s, g, tb, te, bt_first, qreg, m, lsum, acc);
-
         const size_t row0 = (size_t)s * p.Hq + (size_t)g * Ga;
         const auto prs = coherent_rsrc(p.part_out + (size_t)v * Ga * D, (uint32_t)Ga * D * 4);
-        merge_waves<D, G>(sm, Ga, m, lsum, acc, [&](int h, int d, const float (&o)[4], float L) {
+        attend_merge<D, B, G, 1, LAY, NWV>(p, s, g, tb, te, bt_first, qreg, sm, Ga,
+                                      [&](int h, int d, const float (&o)[4], float L) {
             if (n == 1) {
                 store_out4(reinterpret_cast<uint16_t *>(p.out) + (row0 + h) * D + d, o);
                 if (d == 0 && p.lse) p.lse[row0 + h] = L;
@@ -1225,18 +1652,22 @@ template <int D, int B, int G, int LAY>
 hipError_t launch_partition(const DecodeParams &p, hipStream_t stream) {
     constexpr int kSubs = 1;  // waves take single sub-blocks in turn
     if (p.balanced_workgroups > 0) {
-        // one wave of workgroups: as many as are resident together
+        // one wave of workgroups: as many as are resident together, counted
+        // for the shuffled-layout instance and used for every layout, so the
+        // split (and the rounding) does not depend on the layout
         static const int per_cu = [] {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(&paged_decode_balanced_kernel<D, B, G, LAY>),
-                    256, 0) != hipSuccess || n < 1)
+                    &n,
+                    reinterpret_cast<const void *>(
+                        &paged_decode_balanced_kernel<D, B, G, kLayShuffled, kWaves>),
+                    kWaves * 64, 0) != hipSuccess || n < 1)
                 n = 1;
             return n;
         }();
         const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G, LAY>), dim3((unsigned)nw),
-                           dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, B, G, LAY, kWaves>),
+                           dim3((unsigned)nw), dim3(kWaves * 64), 0, stream, p);
         return hipGetLastError();
     }
     const int64_t units = (int64_t)p.max_parts * p.S * p.Hkv;
