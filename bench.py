@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="GQA decode cache element type: bf16, or FP8 E4M3 codes with "
                          "per-tensor scales (amax / 448), shuffled layout with x = 16")
+    ap.add_argument("--mla-engine", default="valu", choices=["valu", "mfma"],
+                    help="MLA decode: the VALU kernels (pa_mla_decode_attn*) or the matrix-core "
+                         "one (pa_mla_decode_attn_mfma)")
     ap.add_argument("--kv-layout", default="shuffled", choices=["shuffled", "standard"],
                     help="GQA decode cache layout: the pages' shuffled one, or the standard "
                          "[num_blocks, block_size, kv_heads, head_dim] it replaces (same "
@@ -499,9 +502,18 @@ def bench_mla(args, case, label):
     lse = torch.empty((case.S, case.Hq), dtype=torch.float32, device=dev)
 
     fused = not args.separate_cache_write
+    mfma = args.mla_engine == "mfma"
+    if mfma and f8:
+        raise SystemExit("the matrix-core MLA engine reads bf16 latents only")
 
     def decode(i):
-        if f8:
+        if mfma:
+            pa.mla_decode_attn_mfma(q, caches[i % pools], bt, cl, case.scale, max_ctx,
+                                    v_dim=case.Dv, partition_tokens=P,
+                                    new_latent=new_lat if fused else None,
+                                    slot_mapping=new_slots if fused else None, out=out, lse=lse,
+                                    workspace=ws)
+        elif f8:
             pa.mla_decode_attn_fp8(q, caches[i % pools], bt, cl, case.scale, max_ctx, kvs,
                                    v_dim=case.Dv, partition_tokens=P,
                                    new_latent=new_lat if fused else None,
@@ -541,7 +553,8 @@ def bench_mla(args, case, label):
             "hbm_gbps": algo / (dec_ms * 1e-3) / 1e9, "tflops": flops / (dec_ms * 1e-3) / 1e12,
             "pools": pools, "cache_write": "fused" if fused else "separate launch",
             "kv_scale": kvs if f8 else None,
-            "kernel": "mla_decode_balanced_kernel" if balanced else "mla_decode_kernel"}
+            "kernel": ("mla_decode_balanced_kernel" if balanced else "mla_decode_kernel")
+                      + ("<bf16, matrix cores>" if mfma else "")}
 
 
 def cpu_baseline_mla(case, seconds, kv_scale=None):
@@ -890,13 +903,27 @@ def main():
             rc = read_ceiling(r["algo_bytes"])
             rc["decode_frac_of_ceiling"] = r["hbm_gbps"] / rc["gbps"]
             line["hbm_read_ceiling"] = rc
-        line["roofline"] = {"bound": "alu", "kernel": r["kernel"], "achieved": r["tflops"],
-                            "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": r["tflops"] / VALU_PEAK_TFLOPS,
-                            "traffic": measured_traffic(
-                                args.config + ("_fp8" if args.kv_dtype == "fp8" else "")),
-                            "algo_flops_per_launch": r["algo_flops"],
-                            "algo_bytes_per_launch": r["algo_bytes"], "avg_launch_ms": r["decode_ms"]}
+        if args.mla_engine == "mfma":
+            # matrix cores: the latent read bounds it; the bf16 MFMA fraction
+            # (algorithmic flops; P.V runs twice, hi and lo parts) is reported beside
+            line["config"]["engine"] = "matrix cores"
+            line["roofline"] = {"bound": "hbm", "kernel": r["kernel"], "achieved": r["hbm_gbps"],
+                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
+                                "traffic": measured_traffic(args.config + "_mfma"),
+                                "algo_bytes_per_launch": r["algo_bytes"],
+                                "avg_launch_ms": r["decode_ms"],
+                                "mfma_tflops": r["tflops"],
+                                "mfma_frac_of_bf16_peak": r["tflops"] / MFMA_BF16_PEAK_TFLOPS}
+        else:
+            line["roofline"] = {"bound": "alu", "kernel": r["kernel"], "achieved": r["tflops"],
+                                "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": r["tflops"] / VALU_PEAK_TFLOPS,
+                                "traffic": measured_traffic(
+                                    args.config + ("_fp8" if args.kv_dtype == "fp8" else "")),
+                                "algo_flops_per_launch": r["algo_flops"],
+                                "algo_bytes_per_launch": r["algo_bytes"],
+                                "avg_launch_ms": r["decode_ms"]}
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds, r["kv_scale"])

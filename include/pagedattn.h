@@ -325,6 +325,27 @@ pa_status pa_mla_decode_attn_write(void *out, float *lse, const void *query,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Absorbed MLA paged decode on the matrix cores (MLA section of the "vLLM ROCm
+ * attention backends" blog: the assembly decode kernel of the pages keeps
+ * the latent read at memory speed).  The same operation as
+ * pa_mla_decode_attn, optionally with the fused latent write of
+ * pa_mla_decode_attn_write: new_latent and slot_mapping both NULL (no write)
+ * or both given.  QK (num_q_heads x 576 by 576 x tokens) and P.V (by
+ * tokens x 512) run as bf16 matrix products with fp32 accumulation, the
+ * weights as bf16 hi + lo parts; the result agrees with pa_mla_decode_attn
+ * to rounding.  Arguments, workspace (pa_mla_workspace_size), support and
+ * errors as for pa_mla_decode_attn; bf16 latents only.
+ */
+pa_status pa_mla_decode_attn_mfma(void *out, float *lse, const void *query,
+                                  const void *new_latent, const int64_t *slot_mapping,
+                                  void *kv_cache, const int32_t *block_table,
+                                  int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                  int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t latent_dim, int32_t v_dim, int32_t block_size,
+                                  int64_t num_blocks, float scale, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * FP8 latent cache (the MLA extend pseudocode of the "vLLM ROCm attention
  * backends" blog gathers the latent cache and may dequantise it; the code
  * format is that of pa_reshape_and_cache_fp8, with one scale for the whole

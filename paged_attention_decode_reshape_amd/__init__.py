@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     library,
     merge_attn_states,
     mla_decode_attn,
+    mla_decode_attn_mfma,
     mla_decode_attn_write,
     mixed_batch_attn,
     mixed_batch_plan,

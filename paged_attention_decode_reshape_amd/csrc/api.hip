@@ -370,7 +370,8 @@ size_t pa_mla_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t v_di
 
 // MLA decode, optionally with the fused cache write of each sequence's new
 // latent (new_latent / slot_mapping null: no write).
-static pa_status mla_impl(bool fp8, float kv_scale, void *out, float *lse, const void *query,
+static pa_status mla_impl(bool fp8, bool mfma, float kv_scale, void *out, float *lse,
+                          const void *query,
                           const void *new_latent,
                           const int64_t *slot_mapping, const void *kv_cache,
                           const int32_t *block_table, int32_t max_blocks_per_seq,
@@ -431,6 +432,7 @@ static pa_status mla_impl(bool fp8, float kv_scale, void *out, float *lse, const
     p.fp8 = fp8 ? 1 : 0;
     p.kv_scale = kv_scale;
     p.kv_inv = 1.0f / kv_scale;
+    p.mfma = mfma ? 1 : 0;
     return from_hip(launch_mla_decode(p, (hipStream_t)stream));
 }
 
@@ -441,7 +443,7 @@ pa_status pa_mla_decode_attn(void *out, float *lse, const void *query, const voi
                              int32_t v_dim, int32_t block_size, int64_t num_blocks, float scale,
                              int32_t partition_tokens, void *workspace, size_t workspace_bytes,
                              void *stream) {
-    return mla_impl(false, 1.f, out, lse, query, nullptr, nullptr, kv_cache, block_table,
+    return mla_impl(false, false, 1.f, out, lse, query, nullptr, nullptr, kv_cache, block_table,
                     max_blocks_per_seq,
                     context_lens, max_context_len, num_seqs, num_q_heads, latent_dim, v_dim,
                     block_size, num_blocks, scale, partition_tokens, workspace, workspace_bytes,
@@ -458,10 +460,28 @@ pa_status pa_mla_decode_attn_write(void *out, float *lse, const void *query,
                                    void *workspace, size_t workspace_bytes, void *stream) {
     if (!new_latent || !slot_mapping) return PA_ERR_INVALID_ARG;
     if (!aligned(new_latent, 16) || !aligned(slot_mapping, 8)) return PA_ERR_INVALID_ARG;
-    return mla_impl(false, 1.f, out, lse, query, new_latent, slot_mapping, kv_cache, block_table,
+    return mla_impl(false, false, 1.f, out, lse, query, new_latent, slot_mapping, kv_cache, block_table,
                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                     latent_dim, v_dim, block_size, num_blocks, scale, partition_tokens, workspace,
                     workspace_bytes, stream);
+}
+
+pa_status pa_mla_decode_attn_mfma(void *out, float *lse, const void *query,
+                                  const void *new_latent, const int64_t *slot_mapping,
+                                  void *kv_cache, const int32_t *block_table,
+                                  int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                  int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t latent_dim, int32_t v_dim, int32_t block_size,
+                                  int64_t num_blocks, float scale, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    const int given = (new_latent != nullptr) + (slot_mapping != nullptr);
+    if (given == 1) return PA_ERR_INVALID_ARG;
+    if (given == 2 && (!aligned(new_latent, 16) || !aligned(slot_mapping, 8)))
+        return PA_ERR_INVALID_ARG;
+    return mla_impl(false, true, 1.f, out, lse, query, new_latent, slot_mapping, kv_cache,
+                    block_table, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                    num_q_heads, latent_dim, v_dim, block_size, num_blocks, scale,
+                    partition_tokens, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_mla_decode_attn_fp8(void *out, float *lse, const void *query, const void *new_latent,
@@ -477,7 +497,7 @@ pa_status pa_mla_decode_attn_fp8(void *out, float *lse, const void *query, const
     if (given == 1) return PA_ERR_INVALID_ARG;
     if (given == 2 && (!aligned(new_latent, 16) || !aligned(slot_mapping, 8)))
         return PA_ERR_INVALID_ARG;
-    return mla_impl(true, kv_scale, out, lse, query, new_latent, slot_mapping, kv_cache,
+    return mla_impl(true, false, kv_scale, out, lse, query, new_latent, slot_mapping, kv_cache,
                     block_table, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                     num_q_heads, latent_dim, v_dim, block_size, num_blocks, scale,
                     partition_tokens, workspace, workspace_bytes, stream);

@@ -95,6 +95,8 @@ struct MLAParams {
     // (value = code * kv_scale; the fused write quantises with kv_inv)
     int32_t fp8;
     float kv_scale, kv_inv;
+    // nonzero: the matrix-core engine (bf16 latents only)
+    int32_t mfma;
 };
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream);

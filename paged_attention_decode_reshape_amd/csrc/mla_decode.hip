@@ -429,6 +429,274 @@ __device__ __forceinline__ void mla_write_empty(const MLAParams &p, int s) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core engine.  The 16 query heads over one shared latent make QK a
+// dense [16 x 576] x [576 x T] product and P.V a [16 x T] x [T x 512] one,
+// computed with v_mfma_f32_16x16x32_bf16 (QK, 18 steps of 32 dims per 16
+// tokens) and v_mfma_f32_16x16x16_bf16 (P.V, P in bf16 hi + lo parts).  A
+// workgroup of 4 waves walks its range 64 tokens at a time; wave w owns
+// tokens 16 w .. 16 w + 15 of each 64 and never exchanges data with the
+// other waves until the final merge.
+//   load  each lane of a wave gathers vectors of its own token's latent row
+//         (lane (g, m): token m, vectors 4 j + g, j < 18) straight into the
+//         wave's LDS region (global_load_lds: per-lane 64-bit addresses, so
+//         any pool size and block size), block j at slot 16 g + m, which is
+//         the QK A-operand layout: operand j is one conflict-free 1 KB read.
+//   QK    S^T = K Q^T: A = the 16 tokens' latents, B = the queries (resident
+//         registers: lane (g, m) holds head m's dims 32 j + 8 g .. + 7);
+//         lane (g, m) then holds head m's scores of tokens 4 g .. 4 g + 3.
+//   P.V   O = P V: A = P (lane (g, m): head m, tokens 4 g .. 4 g + 3, i.e.
+//         the lane's own weights), B = V through LDS transpose reads
+//         (ds_read_b64_tr_b16: within 16 lanes, lane 4 k + q reads token
+//         4 g + k, dims 4 q .. 4 q + 3 of the 16-dim output tile, and lane n
+//         receives dim n of the 4 tokens); 32 output tiles of 16 dims, whose
+//         accumulators (lane (g, n): heads 4 g .. 4 g + 3, dim 16 N + n) stay
+//         in registers.
+// Online softmax with the lazy reference of the VALU engine.  Query heads
+// beyond num_q_heads are zero rows whose outputs are not written.
+// ---------------------------------------------------------------------------
+constexpr int kMTok = 16;              // tokens per wave per round
+constexpr int kMRound = kWaves * kMTok;  // 64 tokens per round
+constexpr int kMSteps = kDl / 32;      // 18 QK steps
+constexpr int kMTiles = kDv / 16;      // 32 output tiles of 16 dims
+constexpr int kMMergeDims = 256;       // output dims merged per pass
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+struct MLAMfmaSmem {
+    union {
+        // per wave: block j holds, at slot 16 g + m, vector 4 j + g of token m
+        __align__(16) uint4 tile[kWaves][kMSteps][64];
+        // the final merge of the waves: one pass of output dims
+        __align__(16) float o[kWaves][16][kMMergeDims + 4];
+    };
+    float m[kWaves][16], l[kWaves][16];
+    float alpha[kWaves][16];  // rescale factors of the wave's heads (lazy softmax)
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Query operand registers: lane (g, m), step j: dims 32 j + 8 g .. + 7 of head m
+// (zero for heads >= num_q_heads).
+__device__ __forceinline__ void mla_mfma_queries(const MLAParams &p, int s, uint4 (&q)[kMSteps]) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const uint4 *qh = reinterpret_cast<const uint4 *>(p.query) + ((size_t)s * p.Hq + min(m, p.Hq - 1)) * kRowVec;
+#pragma unroll
+    for (int j = 0; j < kMSteps; j++) q[j] = m < p.Hq ? qh[4 * j + g] : make_uint4(0, 0, 0, 0);
+}
+
+// Latent row of token t of sequence s (-1: past `end` or an out-of-range block id).
+__device__ __forceinline__ int64_t mla_row(const MLAParams &p, int s, int t, int end) {
+    if (t >= end) return -1;
+    const int b = p.block_table[(size_t)s * p.max_blocks + min(t / p.B, p.max_blocks - 1)];
+    return b >= 0 && (int64_t)b < p.num_blocks ? (int64_t)b * p.B + t % p.B : -1;
+}
+
+// Attention of all heads over tokens [start, end) of sequence s, then the
+// merge of the 4 waves and the output: out rows (whole) or partials in the
+// layout merge_mla_partials reads (head h at po + h * hs, 16-byte vector
+// 64 i + c holding dims 8 c + 4 i .. + 3) with LSEs at pl + h * lhs.
+__device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &sm, int s,
+                                               int start, int end, bool whole, float *po,
+                                               size_t hs, float *pl, size_t lhs) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const float sl2 = p.scale * kLog2e;
+    const char *kv = reinterpret_cast<const char *>(p.kv_cache);
+    uint4 *region = &sm.tile[wave][0][0];
+
+    // stale LDS may hold any bits: tokens that are never loaded must read
+    // as zero rows, so the region starts zeroed
+    for (int i = lane; i < kMSteps * 64; i += 64) region[i] = make_uint4(0, 0, 0, 0);
+    // the gathers write LDS by another path: the zeros land first
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+
+    uint4 q[kMSteps];
+    bool have_q = false;  // the queries are requested after the first gather
+    f32x4_t o[kMTiles];
+#pragma unroll
+    for (int n = 0; n < kMTiles; n++) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mh = kNegInf, lsum = 0.f;  // head m: reference maximum (log2 units), lane's weight sum
+
+    // LDS byte offset (in the wave's region) of lane (g, 4 k + q)'s transpose
+    // read for output tile 0: token 4 g + k, dims 4 q .. 4 q + 3 (vector
+    // q / 2, half q % 2); tile N adds vector 2 N
+    const int kq = lane & 15, tk = 4 * g + (kq >> 2), qd = kq & 3;
+    auto tr_off = [&](int N) -> uint32_t {
+        const int v = 2 * N + (qd >> 1);
+        return (uint32_t)((v >> 2) * 1024 + (16 * (v & 3) + tk) * 16 + 8 * (qd & 1));
+    };
+
+    int64_t row = mla_row(p, s, start + kMTok * wave + m, end);
+    for (int r0 = start; r0 < end; r0 += kMRound) {
+        const int t0 = r0 + kMTok * wave;  // the wave's first token this round
+        // 16-bit mask of the wave's valid tokens
+        const uint32_t valid = (uint32_t)__ballot(row >= 0) & 0xffffu;
+        if (valid != 0) {
+            // gather: block j, lane (g, m) <- vector 4 j + g of token m's row
+            if (row >= 0) {
+                const char *src = kv + (size_t)row * (kDl * 2) + 16 * g;
+#pragma unroll
+                for (int j = 0; j < kMSteps; j++)
+                    __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(region + 64 * j), 16, 0, 0);
+            }
+        }
+        // the next round's row (in flight with the gather), and the queries
+        // behind the first gather in the memory queue
+        const int64_t next_row = mla_row(p, s, t0 + kMRound + m, end);
+        if (valid == 0) {
+            row = next_row;
+            continue;
+        }
+        if (!have_q) {
+            mla_mfma_queries(p, s, q);
+            have_q = true;
+        }
+        // the gather has landed (together with the next round's block-table
+        // entry, which may not have been requested at all)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        asm volatile("" ::: "memory");
+
+        // QK: two accumulator chains over the 18 steps
+        f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMSteps; j += 2) {
+            const uint4 ka = region[64 * j + lane], kb = region[64 * (j + 1) + lane];
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(q[j]), sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(q[j + 1]), sb, 0, 0, 0);
+        }
+        float z[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const bool ok = (valid >> (4 * g + i)) & 1u;
+            z[i] = ok ? (sa[i] + sb[i]) * sl2 : kNegInf;
+        }
+        // the round's maximum of head m over the wave's 16 tokens (4 per lane,
+        // 4 rows of lanes)
+        float zm = fmax_nc(fmax_nc(z[0], z[1]), fmax_nc(z[2], z[3]));
+        {
+            auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(zm), __float_as_uint(zm), false, false);
+            zm = fmax_nc(__uint_as_float(x[0]), __uint_as_float(x[1]));
+            auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(zm), __float_as_uint(zm), false, false);
+            zm = fmax_nc(__uint_as_float(y[0]), __uint_as_float(y[1]));
+        }
+        if (__ballot(zm > mh + kLazyLog2)) {
+            // rescale: alpha of head m (lanes (*, m)) -> accumulators of heads
+            // 4 g + i (lanes (g, *)) through LDS
+            float alpha = 1.f;
+            if (zm > mh + kLazyLog2) {
+                alpha = fast_exp2(mh - zm);  // 0 from -inf
+                mh = zm;
+            }
+            lsum *= alpha;
+            if (g == 0) sm.alpha[wave][m] = alpha;
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes have landed
+            float a4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) a4[i] = sm.alpha[wave][4 * g + i];
+#pragma unroll
+            for (int n = 0; n < kMTiles; n++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) o[n][i] *= a4[i];
+        }
+        float pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            pw[i] = fast_exp2(z[i] - mh);  // mh is finite here
+            lsum += pw[i];
+        }
+        // P as bf16 hi + lo parts: A operand of 16x16x16 (head m, tokens 4 g .. + 3)
+        uint2 ph, pl_;
+        ph.x = pack_bf16x2(pw[0], pw[1]);
+        ph.y = pack_bf16x2(pw[2], pw[3]);
+        pl_.x = pack_bf16x2(pw[0] - bf16_lo(ph.x), pw[1] - bf16_hi(ph.x));
+        pl_.y = pack_bf16x2(pw[2] - bf16_lo(ph.y), pw[3] - bf16_hi(ph.y));
+        const bf16x4_t pa = __builtin_bit_cast(bf16x4_t, ph), pb = __builtin_bit_cast(bf16x4_t, pl_);
+        // P.V over the 32 output tiles
+        const char *rb = reinterpret_cast<const char *>(region);
+#pragma unroll
+        for (int n = 0; n < kMTiles; n++) {
+            const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(rb + tr_off(n)));
+            const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, vt);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[n], 0, 0, 0);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, o[n], 0, 0, 0);
+        }
+        // every LDS read of this round's tile is done before the next gather
+        // overwrites it (the gather's LDS writes are not ordered after reads)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        row = next_row;
+    }
+
+    // merge of the 4 waves: weight sums of head m over the 4 rows of lanes
+    {
+        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+        float l2 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
+        lsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    }
+    __syncthreads();  // every wave is done with its tile region
+    if (g == 0) {
+        sm.m[wave][m] = mh;
+        sm.l[wave][m] = lsum;
+    }
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    for (int pass = 0; pass < kDv / kMMergeDims; pass++) {
+        constexpr int kTilesPerPass = kMMergeDims / 16;
+#pragma unroll
+        for (int n = 0; n < kTilesPerPass; n++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) sm.o[wave][4 * g + i][16 * n + m] = o[kTilesPerPass * pass + n][i];
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += blockDim.x) {
+            const int h = idx / (kMMergeDims / 4), d = 4 * (idx % (kMMergeDims / 4));
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
+            const float Mr = M == kNegInf ? 0.f : M;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) {
+                const float wt = fast_exp2(sm.m[w][h] - Mr);
+                const float4 a = *reinterpret_cast<const float4 *>(&sm.o[w][h][d]);
+                acc[0] += wt * a.x;
+                acc[1] += wt * a.y;
+                acc[2] += wt * a.z;
+                acc[3] += wt * a.w;
+                den += wt * sm.l[w][h];
+            }
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
+            const int dim = kMMergeDims * pass + d;
+            const size_t orow = (size_t)s * p.Hq + h;
+            if (whole) {
+                uint2 v;
+                v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                *reinterpret_cast<uint2 *>(out + orow * kDv + dim) = v;
+                if (dim == 0 && p.lse) p.lse[orow] = L;
+            } else {
+                // vector 64 i + c holds dims 8 c + 4 i .. + 3
+                const int vec = 64 * ((dim & 7) >> 2) + (dim >> 3);
+                const auto rs = coherent_rsrc(po + h * hs, kDv * 4);
+                store_coherent4(rs, (uint32_t)vec * 16, acc[0] * inv, acc[1] * inv, acc[2] * inv,
+                                acc[3] * inv);
+                if (dim == 0) store_coherent(&pl[h * lhs], L);
+            }
+        }
+        __syncthreads();  // the pass's LDS is read before the next one is written
+    }
+}
+
 __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW], float (&acc)[kHPW][8]) {
 #pragma unroll
     for (int j = 0; j < kHPW; j++) {
@@ -440,13 +708,14 @@ __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW],
 }
 
 // Fixed partitions: one workgroup per (partition, sequence).
-template <bool F8>
+template <bool F8, bool MFMA>
 __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
+    static_assert(!(F8 && MFMA), "the matrix-core engine reads bf16 latents");
     const int part = blockIdx.x / p.S;
     const int s = blockIdx.x - part * p.S;
     const int P = p.partition;
     const int start = part * P;
-    __shared__ MLASmem sm;
+    __shared__ std::conditional_t<MFMA, MLAMfmaSmem, MLASmem> sm;
 
     const int ctx = clamp_ctx(p, as_const<int32_t>(p.context_lens)[s]);
     if (start >= ctx) {
@@ -460,15 +729,20 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int nparts = (ctx + P - 1) / P;
     // the partition holding the last token writes the new token first
     if (p.slot_mapping && end == ctx) mla_write_new_token<F8>(p, s);
-    uint32_t qreg[kHPW][kSlices];
-    mla_load_queries(p, s, qreg);
-    float m[kHPW], lsum[kHPW], acc[kHPW][8];
-    mla_reset(m, lsum, acc);
-    mla_attend<F8>(p, sm, s, start, end, qreg, m, lsum, acc);
     // partials [S, Hq, max_parts, Dv] and [S, Hq, max_parts]
-    float *po = p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
-    float *pl = p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
-    mla_emit(p, s, nparts == 1, m, lsum, acc, po, (size_t)p.max_parts * kDv, pl, p.max_parts);
+    float *po = nparts == 1 ? nullptr : p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
+    float *pl = nparts == 1 ? nullptr : p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
+    if constexpr (MFMA) {
+        mla_mfma_piece(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv, pl,
+                       p.max_parts);
+    } else {
+        uint32_t qreg[kHPW][kSlices];
+        mla_load_queries(p, s, qreg);
+        float m[kHPW], lsum[kHPW], acc[kHPW][8];
+        mla_reset(m, lsum, acc);
+        mla_attend<F8>(p, sm, s, start, end, qreg, m, lsum, acc);
+        mla_emit(p, s, nparts == 1, m, lsum, acc, po, (size_t)p.max_parts * kDv, pl, p.max_parts);
+    }
     if (nparts == 1) return;
     if (!mla_count(p, s, nparts)) return;
     merge_mla_partials(p, s, p.part_out + (size_t)s * p.Hq * p.max_parts * kDv,
@@ -496,11 +770,12 @@ __device__ __forceinline__ int wave_prefix_sum_i(int v) {
 // else one, numbered sequence-major; workgroup w takes piece w (+ NW, ...).
 // Pieces P_u .. P_u + n - 1 of a sequence leave partials in those slots of
 // [NW, Hq, Dv] and [NW, Hq]; the last to finish merges them in order.
-template <bool F8>
+template <bool F8, bool MFMA>
 __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p) {
+    static_assert(!(F8 && MFMA), "the matrix-core engine reads bf16 latents");
     const int NW = gridDim.x, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    __shared__ MLASmem sm;
+    __shared__ std::conditional_t<MFMA, MLAMfmaSmem, MLASmem> sm;
     auto ctx_of = [&](int s) { return s < p.S ? clamp_ctx(p, p.context_lens[min(s, p.S - 1)]) : 0; };
     const int ctx_w0 = ctx_of(lane);
     auto ctx_in = [&](int c0) { return c0 == 0 ? ctx_w0 : ctx_of(c0 + lane); };
@@ -558,15 +833,22 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
         }
         if (s < 0) break;  // no piece left for this workgroup
 
-        uint32_t qreg[kHPW][kSlices];
-        mla_load_queries(p, s, qreg);
-        float m[kHPW], lsum[kHPW], acc[kHPW][8];
-        mla_reset(m, lsum, acc);
+        if (v != w) __syncthreads();  // the previous piece's LDS has been read
         // the piece holding the last token writes the new token first
         if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token<F8>(p, s);
-        mla_attend<F8>(p, sm, s, a * kTile, min(b * kTile, ctx), qreg, m, lsum, acc);
-        mla_emit(p, s, n == 1, m, lsum, acc, p.part_out + (size_t)v * p.Hq * kDv, kDv,
-                 p.part_lse + (size_t)v * p.Hq, 1);
+        if constexpr (MFMA) {
+            mla_mfma_piece(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
+                           p.part_out + (size_t)v * p.Hq * kDv, kDv, p.part_lse + (size_t)v * p.Hq,
+                           1);
+        } else {
+            uint32_t qreg[kHPW][kSlices];
+            mla_load_queries(p, s, qreg);
+            float m[kHPW], lsum[kHPW], acc[kHPW][8];
+            mla_reset(m, lsum, acc);
+            mla_attend<F8>(p, sm, s, a * kTile, min(b * kTile, ctx), qreg, m, lsum, acc);
+            mla_emit(p, s, n == 1, m, lsum, acc, p.part_out + (size_t)v * p.Hq * kDv, kDv,
+                     p.part_lse + (size_t)v * p.Hq, 1);
+        }
         if (n > 1 && mla_count(p, s, n))
             merge_mla_partials(p, s, p.part_out + (size_t)P_u * p.Hq * kDv, kDv,
                                (size_t)p.Hq * kDv, (uint32_t)n * p.Hq * kDv,
@@ -579,33 +861,34 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
 
 namespace {
 
-template <bool F8>
+template <bool F8, bool MFMA>
 hipError_t launch_mla(const MLAParams &p, hipStream_t stream) {
     if (p.balanced_workgroups > 0) {
         // one wave of workgroups: as many as are resident together
         static const int per_cu = [] {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(&mla_decode_balanced_kernel<F8>), 256, 0) !=
+                    &n, reinterpret_cast<const void *>(&mla_decode_balanced_kernel<F8, MFMA>), 256, 0) !=
                     hipSuccess || n < 1)
                 n = 1;
             return n;
         }();
         const int nw = min(p.balanced_workgroups, per_cu * p.num_cus);
-        hipLaunchKernelGGL(mla_decode_balanced_kernel<F8>, dim3((unsigned)nw), dim3(256), 0,
+        hipLaunchKernelGGL((mla_decode_balanced_kernel<F8, MFMA>), dim3((unsigned)nw), dim3(256), 0,
                            stream, p);
         return hipGetLastError();
     }
     const int64_t units = (int64_t)p.max_parts * p.S;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mla_decode_kernel<F8>, dim3((unsigned)units), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((mla_decode_kernel<F8, MFMA>), dim3((unsigned)units), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream) {
-    return p.fp8 ? launch_mla<true>(p, stream) : launch_mla<false>(p, stream);
+    if (p.mfma) return p.fp8 ? hipErrorInvalidValue : launch_mla<false, true>(p, stream);
+    return p.fp8 ? launch_mla<true, false>(p, stream) : launch_mla<false, false>(p, stream);
 }
 
 }  // namespace pa

@@ -57,6 +57,8 @@ _SIGS = {
                             _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
     "pa_mla_decode_attn_write": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
+    "pa_mla_decode_attn_mfma": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp], _i32),
     "pa_merge_attn_states": ([_vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp],
                              _i32),
     "pa_gather_cache_chunk": ([_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i64,
@@ -434,6 +436,52 @@ def mla_decode_attn_write(query: torch.Tensor, new_latent: torch.Tensor,
                                       int(max_context_len), S, Hq, Dl, v_dim, B, NB, float(scale),
                                       int(partition_tokens), _ptr(ws), nbytes, _stream(query))
     _check("mla_decode_attn_write", st)
+    return out, lse
+
+
+def mla_decode_attn_mfma(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                         context_lens: torch.Tensor, scale: float, max_context_len: int,
+                         v_dim: int = 512, partition_tokens: int = 0,
+                         new_latent: Optional[torch.Tensor] = None,
+                         slot_mapping: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Absorbed MLA decode on the matrix cores (same result as mla_decode_attn
+    to rounding), with the fused latent write when new_latent and
+    slot_mapping are given."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("kv_cache", kv_cache, torch.bfloat16, 3)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, Dl = query.shape
+    NB, B, Dl2 = kv_cache.shape
+    if Dl2 != Dl:
+        raise ValueError("kv_cache latent width differs from the query's")
+    if (new_latent is None) != (slot_mapping is None):
+        raise ValueError("new_latent and slot_mapping go together")
+    if new_latent is not None:
+        _gpu("new_latent", new_latent, torch.bfloat16, 2)
+        _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+        if tuple(new_latent.shape) != (S, Dl) or slot_mapping.numel() != S:
+            raise ValueError("new_latent [num_seqs, latent_dim] and one slot per sequence")
+    if out is None:
+        out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
+    _gpu("out", out, torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+    nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
+    ws = _workspace(nbytes, query.device, workspace)
+    st = lib.pa_mla_decode_attn_mfma(out.data_ptr(), _ptr(lse), query.data_ptr(),
+                                     _ptr(new_latent), _ptr(slot_mapping), kv_cache.data_ptr(),
+                                     block_table.data_ptr(), block_table.shape[1],
+                                     context_lens.data_ptr(), int(max_context_len), S, Hq, Dl,
+                                     v_dim, B, NB, float(scale), int(partition_tokens), _ptr(ws),
+                                     nbytes, _stream(query))
+    _check("mla_decode_attn_mfma", st)
     return out, lse
 
 

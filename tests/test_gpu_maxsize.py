@@ -1,5 +1,6 @@
 """GPU parity at the largest supported context, 2^20 tokens (the library's
-bound), with a ragged neighbour: GQA decode in four split modes, MLA decode,
+bound), with a ragged neighbour: GQA decode in four split modes, MLA decode
+(both engines, balanced and unsplit),
 and chunked extend over a 2^20-token context.  Every output is checked
 against the oracle.  Inputs are about 1 GB of KV per case."""
 import numpy as np
@@ -37,26 +38,34 @@ def test_decode_max_context(gqa_max, gqa_max_ref, partition):
     assert_attn_close(out, lse, gqa_max_ref[0], gqa_max_ref[1], what=f"max ctx P={partition}")
 
 
-def test_mla_max_context(orc):
+@pytest.fixture(scope="module")
+def mla_max(orc):
     case = W.mla_decode_cases("max_mla", 702, S=2, lens_range=None, lens=[MAX_CTX, 77], Hq=16,
                               Dl=576, Dv=512, block_sizes=(64,), scale=1.0 / 192 ** 0.5)[64]
-    say("mla decode at 2^20 tokens")
     dev = device()
     pg = case.paging
     kv = torch.full((pg.num_blocks, case.B, case.Dl), float("nan"), dtype=torch.bfloat16,
                     device=dev)
     pa.reshape_and_cache(case.latent.to(dev), None, kv, None,
                          torch.from_numpy(pg.slot_mapping).to(dev), layout=pa.LAYOUT_MLA_LATENT)
-    q = case.query.to(dev)
-    bt = torch.from_numpy(pg.block_table).to(dev)
-    cl = torch.from_numpy(pg.lens).to(dev)
-    out, lse = pa.mla_decode_attn(q, kv, bt, cl, case.scale, MAX_CTX, v_dim=512)
-    torch.cuda.synchronize()
+    g = (torch.from_numpy(pg.block_table).to(dev), torch.from_numpy(pg.lens).to(dev),
+         case.query.to(dev), kv)
     okv = np.full((pg.num_blocks, case.B, case.Dl), 0x7FC0, dtype=np.uint16)
     orc.cache_write_latent(W.bf16_bits(case.latent), pg.slot_mapping, okv, case.B)
-    ref_out, ref_lse = orc.paged_decode_mla(W.bf16_bits(case.query), okv, pg.block_table,
-                                            case.context_lens, case.B, case.Dv, case.scale)
-    assert_attn_close(out, lse, ref_out, ref_lse, what="mla max ctx")
+    ref = orc.paged_decode_mla(W.bf16_bits(case.query), okv, pg.block_table, case.context_lens,
+                               case.B, case.Dv, case.scale)
+    return case, g, ref
+
+
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
+@pytest.mark.parametrize("partition", [0, -1])
+def test_mla_max_context(mla_max, engine, partition):
+    case, (bt, cl, q, kv), (ref_out, ref_lse) = mla_max
+    say(f"mla decode at 2^20 tokens, {engine} engine, partition {partition}")
+    fn = pa.mla_decode_attn_mfma if engine == "mfma" else pa.mla_decode_attn
+    out, lse = fn(q, kv, bt, cl, case.scale, MAX_CTX, v_dim=512, partition_tokens=partition)
+    torch.cuda.synchronize()
+    assert_attn_close(out, lse, ref_out, ref_lse, what=f"mla max ctx {engine} P={partition}")
 
 
 def test_extend_max_context(orc):
