@@ -37,6 +37,17 @@
  *    sizes the arguments describe; the numerical result for such an entry
  *    is unspecified.
  *
+ *  - Workspaces.  Every workspace the library sizes (the *_workspace_size
+ *    queries) starts with the same region of PA_WORKSPACE_COUNTER_BYTES
+ *    bytes of int32 completion counters, one per split (sequence, kv head)
+ *    pair of a decode call; whatever else a call keeps in its workspace
+ *    lies after that region.  A decode call that splits leaves every
+ *    counter zero again and no call writes anything else into the region,
+ *    so a workspace zero-filled once (e.g. one hipMemset at allocation)
+ *    can serve any sequence of calls on one stream, of any shapes and any
+ *    entry points, as long as it is at least as large as each call's size
+ *    query.  Calls that may run concurrently must not share a workspace.
+ *
  * Shuffled KV layout (x = 16 bytes / sizeof(bf16) = 8 elements):
  *   k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x]
  *   v_cache [num_blocks, num_kv_heads, block_size / x, head_dim, x]
@@ -52,6 +63,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Size of the counter region at the start of every workspace; a split
+ * decode call supports at most PA_WORKSPACE_COUNTER_BYTES / 4 (sequence,
+ * kv head) pairs. */
+#define PA_WORKSPACE_COUNTER_BYTES ((size_t)1 << 20)
 
 typedef int32_t pa_status;
 enum {
@@ -112,9 +128,9 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
 int32_t pa_decode_uses_balanced_split(int32_t num_seqs, int32_t num_kv_heads,
                                       int32_t max_context_len, int32_t partition_tokens);
 
-/* Bytes of workspace pa_paged_decode_attn needs (0 if no split is needed).
- * For partition_tokens 0 and -2 the size depends on the current device's
- * compute-unit count. */
+/* Bytes of workspace pa_paged_decode_attn needs (0 if no split is needed;
+ * otherwise the counter region plus the partials).  For partition_tokens 0
+ * and -2 the size depends on the current device's compute-unit count. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len,
                                 int32_t partition_tokens);
@@ -142,12 +158,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *   whose tokens are split writes partial (out, lse) to the workspace;
  *   they are merged by log-sum-exp in token order.
  * workspace: device memory of at least pa_decode_workspace_size(...)
- *   bytes, 256-byte aligned.  It starts with a region of completion
- *   counters that must be zero-filled before the workspace is first used
- *   (e.g. one hipMemset at allocation); every call leaves it zero again.
- *   Calls that run concurrently must not share a workspace.
+ *   bytes, 256-byte aligned, whose counter region is zero (see
+ *   Workspaces above); the partials follow the counter region.
+ *   Unsplit calls need none (null is accepted).
  * Supported: head_dim in {64, 128}, block_size in {16, 32}, group size
- *   num_q_heads / num_kv_heads in 1..16, max_context_len <= 1 << 20.
+ *   num_q_heads / num_kv_heads in 1..16, max_context_len <= 1 << 20; a
+ *   split call with num_seqs * num_kv_heads above the counter capacity
+ *   returns PA_ERR_UNSUPPORTED (with partition_tokens 0 such a batch uses
+ *   fixed partitions, which need no split up to 4096 tokens).
  */
 pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
                                const void *v_cache, const int32_t *block_table,
@@ -388,9 +406,12 @@ pa_status pa_mla_decode_attn_fp8(void *out, float *lse, const void *query, const
  *
  * prefix_out, suffix_out [num_tokens, num_heads, head_dim] of in_dtype;
  * prefix_lse, suffix_lse [num_tokens, num_heads] f32; out of out_dtype,
- * out_lse f32 (nullable).  out may alias prefix_out or suffix_out when the
- * dtypes match (each element is read before it is written by the same
- * thread).  Supported: head_dim % 8 == 0, head_dim <= 1024.
+ * out_lse f32 (nullable).  out may be prefix_out or suffix_out itself (the
+ * same address) when the dtypes match: each element is read before it is
+ * written by the same thread.  Any other overlap between an output and an
+ * input, and in particular out_lse overlapping prefix_lse or suffix_lse (a
+ * row's LSEs are read by threads of several workgroups), returns
+ * PA_ERR_INVALID_ARG.  Supported: head_dim % 8 == 0, head_dim <= 1024.
  */
 pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,
                                const void *prefix_out, const float *prefix_lse,
@@ -457,7 +478,8 @@ size_t pa_extend_workspace_size(int32_t num_seqs, int32_t total_new_tokens, int3
  *   without a device read-back; the kernels read the device copies and stay
  *   in bounds if the two disagree).
  * A block-table entry outside [0, num_blocks) reads as zero K and V.
- * The workspace (pa_extend_workspace_size bytes, 256-byte aligned) holds the
+ * The workspace (pa_extend_workspace_size bytes, 256-byte aligned) holds,
+ *   after the counter region (which the call neither reads nor writes), the
  *   plan, the new tokens' V regrouped into 8-token groups and the pieces'
  *   fp32 partials; it needs no initialisation.
  * Supported: head_dim == 128, block_size in {16, 32}, group size 1..16,
@@ -520,7 +542,9 @@ size_t pa_mixed_batch_workspace_size(int32_t num_reqs, const int32_t *query_star
  *   device, with the same values in the _host copies (read during the call).
  * k_cache, v_cache: the shuffled caches; block_table [num_reqs,
  *   max_blocks_per_seq].  The workspace (pa_mixed_batch_workspace_size
- *   bytes, 256-byte aligned) needs no initialisation.
+ *   bytes, 256-byte aligned) needs no initialisation: the call zeroes the
+ *   counters its decode step uses, and like every call leaves the counter
+ *   region zero.
  * Supported: what the three paths support (head_dim 128 when an extend or
  *   prefill request is present).  Errors of a path are returned as they are;
  *   paths launched before it have run.

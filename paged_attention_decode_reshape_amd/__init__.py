@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     LAYOUT_SHUFFLED_KV,
     LAYOUT_STANDARD_KV,
     PagedAttnError,
+    WORKSPACE_COUNTER_BYTES,
     chunked_extend_attn,
     decode_partition_tokens,
     decode_uses_balanced_split,

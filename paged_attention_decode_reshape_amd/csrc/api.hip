@@ -18,6 +18,11 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+// [a, a + an) and [b, b + bn) share a byte
+inline bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return an > 0 && bn > 0 && x < y + bn && y < x + an;
+}
 
 // A workgroup's 4 waves take 16-token sub-blocks round-robin and a wave
 // tracks at most 64 of them, so a partition holds at most 4096 tokens.
@@ -41,6 +46,16 @@ int32_t partition_tokens_for(int32_t S, int32_t H, int32_t max_ctx, int32_t requ
     return P < kMaxPartition ? P : kMaxPartition;
 }
 
+// Every workspace the library sizes starts with the same fixed region of
+// completion counters (one int32 per split (sequence, kv head) pair);
+// call-specific data follows it.  The split kernels leave their counters
+// zero again, and no call writes anything else into the region, so one
+// workspace zero-filled once serves any sequence of calls, whatever their
+// shapes, and also when decode and extend calls share it.
+constexpr size_t kCounterBytes = PA_WORKSPACE_COUNTER_BYTES;
+constexpr int64_t kCounterCapacity = (int64_t)(kCounterBytes / sizeof(int32_t));
+static_assert(kCounterBytes % 256 == 0, "counter region keeps the data 256-byte aligned");
+
 struct Split {
     int32_t P;
     int32_t parts;
@@ -57,7 +72,7 @@ Split plan_split(int32_t S, int32_t Hq, int32_t H_units, int32_t Dv, int32_t max
         sp.parts = 1;
         sp.counter_bytes = sp.out_bytes = sp.lse_bytes = 0;
     } else {
-        sp.counter_bytes = align256((size_t)S * H_units * sizeof(int32_t));
+        sp.counter_bytes = kCounterBytes;
         sp.out_bytes = align256((size_t)S * Hq * sp.parts * Dv * sizeof(float));
         sp.lse_bytes = align256((size_t)S * Hq * sp.parts * sizeof(float));
     }
@@ -85,9 +100,17 @@ int32_t device_cus() {
 }
 int32_t balanced_workgroups() { return kBalancedMaxPerCU * device_cus(); }
 
+// A split call needs one counter per (sequence, kv head) pair.
+inline bool counters_fit(int32_t S, int32_t H_units) {
+    return (int64_t)S * H_units <= kCounterCapacity;
+}
+
 bool decode_uses_balanced(int32_t S, int32_t Hkv, int32_t max_ctx, int32_t requested) {
     if (requested == kRequestBalanced) return true;
     if (requested != 0) return false;
+    // auto with more pairs than counters: fixed partitions, which at this
+    // many pairs are whole sequences whenever the context allows it
+    if (!counters_fit(S, Hkv)) return false;
     const int32_t P = partition_tokens_for(S, Hkv, max_ctx, 0);
     const int64_t grid = (int64_t)S * Hkv * (max_ctx > 0 ? cdiv(max_ctx, P) : 1);
     return grid > (int64_t)kAutoPartitionedPerCU * device_cus();
@@ -98,7 +121,7 @@ Split plan_balanced(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t NW) {
     sp.P = 0;
     sp.parts = 0;
     const size_t Ga = (size_t)(Hq / Hkv);
-    sp.counter_bytes = align256((size_t)S * Hkv * sizeof(int32_t));
+    sp.counter_bytes = kCounterBytes;
     sp.out_bytes = align256((size_t)NW * Ga * D * sizeof(float));
     sp.lse_bytes = align256((size_t)NW * Ga * sizeof(float));
     return sp;
@@ -217,6 +240,8 @@ static pa_status decode_impl(int layout, float k_scale, float v_scale, void *out
     Split sp = balanced ? plan_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, NW)
                         : plan_split(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                      max_context_len, partition_tokens);
+    if ((balanced || sp.parts > 1) && !counters_fit(num_seqs, num_kv_heads))
+        return PA_ERR_UNSUPPORTED;
     if (sp.total() > 0) {
         if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
@@ -397,6 +422,7 @@ static pa_status mla_impl(bool fp8, bool mfma, float kv_scale, void *out, float 
     Split sp = balanced ? plan_balanced(num_seqs, num_q_heads, 1, v_dim, NW)
                         : plan_split(num_seqs, num_q_heads, 1, v_dim, max_context_len,
                                      partition_tokens);
+    if ((balanced || sp.parts > 1) && !counters_fit(num_seqs, 1)) return PA_ERR_UNSUPPORTED;
     if (sp.total() > 0) {
         if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
@@ -533,6 +559,26 @@ pa_status pa_merge_attn_states(void *out, float *out_lse, int32_t out_dtype,
         !aligned(prefix_lse, 4) || !aligned(suffix_lse, 4) || !aligned(out_lse, 4))
         return PA_ERR_INVALID_ARG;
     if (head_dim % 8 != 0 || head_dim > 1024) return PA_ERR_UNSUPPORTED;
+    // A row's LSEs are read by all of its threads, which may sit in several
+    // workgroups, while one of them writes out_lse: out_lse must not overlap
+    // an input LSE.  out may be an input itself (same address and dtype:
+    // each thread reads its vector before writing it), but no other overlap.
+    const size_t rows = (size_t)num_tokens * num_heads;
+    const size_t in_bytes = rows * head_dim * (in_dtype == PA_F32 ? 4 : 2);
+    const size_t out_bytes = rows * head_dim * (out_dtype == PA_F32 ? 4 : 2);
+    if (out_lse && (overlaps(out_lse, rows * 4, prefix_lse, rows * 4) ||
+                    overlaps(out_lse, rows * 4, suffix_lse, rows * 4) ||
+                    overlaps(out_lse, rows * 4, prefix_out, in_bytes) ||
+                    overlaps(out_lse, rows * 4, suffix_out, in_bytes) ||
+                    overlaps(out_lse, rows * 4, out, out_bytes)))
+        return PA_ERR_INVALID_ARG;
+    for (const void *in : {prefix_out, suffix_out}) {
+        const bool same = in == out && in_dtype == out_dtype;
+        if (!same && overlaps(out, out_bytes, in, in_bytes)) return PA_ERR_INVALID_ARG;
+    }
+    if (overlaps(out, out_bytes, prefix_lse, rows * 4) ||
+        overlaps(out, out_bytes, suffix_lse, rows * 4))
+        return PA_ERR_INVALID_ARG;
     if (num_tokens == 0) return PA_OK;
     return from_hip(launch_merge_pair(out, out_lse, out_dtype == PA_F32, prefix_out, prefix_lse,
                                       suffix_out, suffix_lse, in_dtype == PA_F32,
@@ -607,13 +653,15 @@ pa_status pa_gather_cache_chunk_fp8(void *k_out, void *v_out, const void *k_cach
                        block_size, num_blocks, iteration, chunk_tokens, stream);
 }
 
-// Extend workspace: the group prefix [S + 1], the new tokens' V in 8-token
-// groups, and fp32 partials (output, LSE) for up to kExtendMaxPieces context
-// pieces of every (new token, q head).
+// Extend workspace: the counter region (left untouched: extend keeps no
+// counters, but a workspace shared with decode calls keeps its counters
+// there), the group prefix [S + 1], the new tokens' V in 8-token groups, and
+// fp32 partials (output, LSE) for up to kExtendMaxPieces context pieces of
+// every (new token, q head).
 struct ExtendWorkspace {
     size_t prefix, vsh, part_out, part_lse;
     int32_t new_groups;
-    size_t total() const { return prefix + vsh + part_out + part_lse; }
+    size_t total() const { return kCounterBytes + prefix + vsh + part_out + part_lse; }
 };
 
 static ExtendWorkspace extend_workspace(int32_t S, int32_t Tn, int32_t Hq, int32_t Hkv) {
@@ -700,7 +748,7 @@ pa_status pa_chunked_extend_attn(void *out, float *lse, const void *query, const
         groups += (int64_t)extend_pieces(context_lens_host[r], p.piece_target, c, p.max_pieces,
                                          &len) * num_kv_heads;
     }
-    char *ws = (char *)workspace;
+    char *ws = (char *)workspace + kCounterBytes;
     p.q = query;
     p.k_new = k_new;
     p.v_new = v_new;

@@ -81,9 +81,13 @@ bool scan(int32_t R, const int32_t *qsl, const int32_t *ctx, Slices &sl) {
     return true;
 }
 
+// Layout: the decode call's workspace first, so that its counters sit in the
+// counter region every library workspace starts with (the region is
+// reserved even without decode requests), then the per-slice arrays, then
+// the extend call's workspace.
 struct RouteWorkspace {
-    size_t arrays, decode, extend;
-    size_t total() const { return arrays + decode + extend; }
+    size_t decode, arrays, extend;
+    size_t total() const { return decode + arrays + extend; }
 };
 
 RouteWorkspace route_workspace(int32_t R, const Slices &sl, int32_t Hq, int32_t Hkv, int32_t D,
@@ -92,6 +96,7 @@ RouteWorkspace route_workspace(int32_t R, const Slices &sl, int32_t Hq, int32_t 
     w.arrays = align256((size_t)(2 * R + 1) * sizeof(int32_t));
     w.decode = sl.nd ? align256(pa_decode_workspace_size(sl.nd, Hq, Hkv, D, sl.max_dec_len, 0))
                      : 0;
+    if (w.decode < PA_WORKSPACE_COUNTER_BYTES) w.decode = PA_WORKSPACE_COUNTER_BYTES;
     const int32_t nx = sl.ne + sl.np;
     w.extend = nx ? align256(pa_extend_workspace_size(nx, sl.te + sl.tp, Hq, Hkv, D, B, budget))
                   : 0;
@@ -171,12 +176,14 @@ pa_status pa_mixed_batch_attn(void *out, float *lse, const void *query, const vo
     if (s != PA_OK) return s;
 
     char *ws = (char *)workspace;
-    int32_t *dec_lens = (int32_t *)ws;
+    int32_t *dec_lens = (int32_t *)(ws + w.decode);
     int32_t *qsl_x = dec_lens + num_reqs;
     const int32_t nx = sl.ne + sl.np;
     // the decode workspace starts with one completion counter per (sequence, kv head)
-    int32_t *dec_ws = w.decode ? (int32_t *)(ws + w.arrays) : nullptr;
-    const int n_counters = w.decode ? sl.nd * num_kv_heads : 0;
+    int32_t *dec_ws = (int32_t *)ws;
+    const int n_counters = sl.nd * num_kv_heads < (int)(PA_WORKSPACE_COUNTER_BYTES / 4)
+                               ? sl.nd * num_kv_heads
+                               : (int)(PA_WORKSPACE_COUNTER_BYTES / 4);
     const int n = std::max({sl.nd, nx + 1, n_counters});
     hipLaunchKernelGGL(route_prepare_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        query_start_loc, context_lens, sl.nd, nx, dec_lens, qsl_x, dec_ws,
@@ -207,7 +214,7 @@ pa_status pa_mixed_batch_attn(void *out, float *lse, const void *query, const vo
                                    block_table + (size_t)r0 * max_blocks_per_seq,
                                    max_blocks_per_seq, context_lens + r0, context_lens_host + r0,
                                    nx, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                   scale, chunk_budget_tokens, ws + w.arrays + w.decode, w.extend,
+                                   scale, chunk_budget_tokens, ws + w.decode + w.arrays, w.extend,
                                    stream);
         if (s != PA_OK) return s;
     }

@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
 LAYOUT_SHUFFLED_KV = 0
 LAYOUT_MLA_LATENT = 1
 LAYOUT_STANDARD_KV = 2
+# Bytes of the completion-counter region at the start of every workspace
+# (PA_WORKSPACE_COUNTER_BYTES in the C header).
+WORKSPACE_COUNTER_BYTES = 1 << 20
 _BF16, _F32 = 0, 1
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
@@ -132,10 +135,59 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# Shape checks.  The C ABI receives bare pointers, so every tensor's shape is
+# checked against the sizes passed with it before anything is launched.
+
+def _shape(name: str, t: Optional[torch.Tensor], shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _shuffled_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, D: int, x: int):
+    """Shuffled caches for head_dim D with x elements per 16 bytes:
+    k_cache [NB, Hkv, D/x, B, x], v_cache [NB, Hkv, B/x, D, x]; returns
+    (NB, Hkv, B)."""
+    NB, Hkv, _, B, _ = k_cache.shape
+    if D % x or B % x:
+        raise ValueError(f"head_dim {D} and block size {B} must be multiples of {x}")
+    _shape("k_cache", k_cache, (NB, Hkv, D // x, B, x))
+    _shape("v_cache", v_cache, (NB, Hkv, B // x, D, x))
+    return NB, Hkv, B
+
+
+def _batch(S: int, block_table: torch.Tensor, context_lens: torch.Tensor):
+    if block_table.shape[0] < S:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for {S} sequences")
+    if block_table.shape[1] < 1:
+        raise ValueError("block_table needs at least one column")
+    if context_lens.numel() != S:
+        raise ValueError(f"context_lens has {context_lens.numel()} entries for {S} sequences")
+
+
+def _new_tokens(S: int, Hkv: int, D: int, new_key, new_value, slot_mapping):
+    _shape("new_key", new_key, (S, Hkv, D))
+    _shape("new_value", new_value, (S, Hkv, D))
+    if slot_mapping is not None and slot_mapping.numel() != S:
+        raise ValueError("slot_mapping must hold one slot per sequence")
+
+
+def _overlap(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """a and b share a byte of device memory."""
+    if a.device != b.device:
+        return False
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    an, bn = a.numel() * a.element_size(), b.numel() * b.element_size()
+    return an > 0 and bn > 0 and a0 < b0 + bn and b0 < a0 + an
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
-    """A caller-supplied workspace, or a fresh zero-filled one.  Workspaces
-    start with completion counters that must be zero before first use; the
-    library leaves them zero after every call, so a workspace can be reused."""
+    """A caller-supplied workspace, or a fresh zero-filled one.  Every
+    workspace starts with a fixed region of completion counters
+    (``WORKSPACE_COUNTER_BYTES``) that must be zero before its first use;
+    every call leaves the region zero and keeps its other data after it, so
+    one workspace, zero-filled once and at least as large as each call's size
+    query, can be reused across calls of any shape and any entry point on
+    one stream."""
     if nbytes == 0:
         return None
     if workspace is None:
@@ -232,14 +284,17 @@ def paged_decode_attn(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     _gpu("block_table", block_table, torch.int32, 2)
     _gpu("context_lens", context_lens, torch.int32, 1)
     S, Hq, D = query.shape
-    NB, Hkv, _, B, _ = k_cache.shape
+    NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)
+    _batch(S, block_table, context_lens)
     if out is None:
         out = torch.empty_like(query)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, D))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_paged_decode_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), k_cache.data_ptr(),
@@ -272,18 +327,18 @@ def paged_decode_attn_write(query: torch.Tensor, new_key: torch.Tensor, new_valu
     _gpu("block_table", block_table, torch.int32, 2)
     _gpu("context_lens", context_lens, torch.int32, 1)
     S, Hq, D = query.shape
-    NB, Hkv, _, B, _ = k_cache.shape
-    if tuple(new_key.shape) != (S, Hkv, D) or tuple(new_value.shape) != (S, Hkv, D):
-        raise ValueError("new_key / new_value must be [num_seqs, num_kv_heads, head_dim]")
-    if slot_mapping.numel() != S:
-        raise ValueError("slot_mapping must hold one slot per sequence")
+    NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)
+    _batch(S, block_table, context_lens)
+    _new_tokens(S, Hkv, D, new_key, new_value, slot_mapping)
     if out is None:
         out = torch.empty_like(query)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, D))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_paged_decode_attn_write(out.data_ptr(), _ptr(lse), query.data_ptr(),
@@ -323,9 +378,10 @@ def paged_decode_attn_layout(layout: int, query: torch.Tensor, k_cache: torch.Te
     elif layout == LAYOUT_SHUFFLED_KV:
         _gpu("k_cache", k_cache, torch.bfloat16, 5)
         _gpu("v_cache", v_cache, torch.bfloat16, 5)
-        NB, Hkv, _, B, _ = k_cache.shape
+        NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)
     else:
         raise ValueError(f"unsupported layout {layout}")
+    _batch(S, block_table, context_lens)
     given = [t is not None for t in (new_key, new_value, slot_mapping)]
     if any(given) and not all(given):
         raise ValueError("new_key, new_value and slot_mapping go together")
@@ -333,17 +389,16 @@ def paged_decode_attn_layout(layout: int, query: torch.Tensor, k_cache: torch.Te
         _gpu("new_key", new_key, torch.bfloat16, 3)
         _gpu("new_value", new_value, torch.bfloat16, 3)
         _gpu("slot_mapping", slot_mapping, torch.int64, 1)
-        if tuple(new_key.shape) != (S, Hkv, D) or tuple(new_value.shape) != (S, Hkv, D):
-            raise ValueError("new_key / new_value must be [num_seqs, num_kv_heads, head_dim]")
-        if slot_mapping.numel() != S:
-            raise ValueError("slot_mapping must hold one slot per sequence")
+        _new_tokens(S, Hkv, D, new_key, new_value, slot_mapping)
     if out is None:
         out = torch.empty_like(query)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, D))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_paged_decode_attn_layout(int(layout), out.data_ptr(), _ptr(lse), query.data_ptr(),
@@ -379,13 +434,16 @@ def mla_decode_attn(query: torch.Tensor, kv_cache: torch.Tensor, block_table: to
     NB, B, Dl2 = kv_cache.shape
     if Dl2 != Dl:
         raise ValueError("kv_cache latent width differs from the query's")
+    _batch(S, block_table, context_lens)
     if out is None:
         out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, v_dim))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_mla_decode_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), kv_cache.data_ptr(),
@@ -420,13 +478,16 @@ def mla_decode_attn_write(query: torch.Tensor, new_latent: torch.Tensor,
         raise ValueError("new_latent must be [num_seqs, latent_dim] of the cache's width")
     if slot_mapping.numel() != S:
         raise ValueError("slot_mapping must hold one slot per sequence")
+    _batch(S, block_table, context_lens)
     if out is None:
         out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, v_dim))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_mla_decode_attn_write(out.data_ptr(), _ptr(lse), query.data_ptr(),
@@ -466,13 +527,16 @@ def mla_decode_attn_mfma(query: torch.Tensor, kv_cache: torch.Tensor, block_tabl
         _gpu("slot_mapping", slot_mapping, torch.int64, 1)
         if tuple(new_latent.shape) != (S, Dl) or slot_mapping.numel() != S:
             raise ValueError("new_latent [num_seqs, latent_dim] and one slot per sequence")
+    _batch(S, block_table, context_lens)
     if out is None:
         out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, v_dim))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_mla_decode_attn_mfma(out.data_ptr(), _ptr(lse), query.data_ptr(),
@@ -507,10 +571,23 @@ def merge_attn_states(prefix_out: torch.Tensor, prefix_lse: torch.Tensor,
     if out is None:
         out = torch.empty((T, H, D), dtype=odt, device=prefix_out.device)
     _gpu("out", out, odt, 3)
+    _shape("out", out, (T, H, D))
     if out_lse is None and return_lse:
         out_lse = torch.empty((T, H), dtype=torch.float32, device=prefix_out.device)
     if out_lse is not None:
         _gpu("out_lse", out_lse, torch.float32, 2)
+        _shape("out_lse", out_lse, (T, H))
+        for name, t in (("prefix_lse", prefix_lse), ("suffix_lse", suffix_lse),
+                        ("prefix_out", prefix_out), ("suffix_out", suffix_out), ("out", out)):
+            if _overlap(out_lse, t):
+                raise ValueError(f"out_lse must not overlap {name}")
+    for name, t in (("prefix_out", prefix_out), ("suffix_out", suffix_out)):
+        same = out.data_ptr() == t.data_ptr() and out.dtype == t.dtype
+        if not same and _overlap(out, t):
+            raise ValueError(f"out may be {name} itself but must not partly overlap it")
+    for name, t in (("prefix_lse", prefix_lse), ("suffix_lse", suffix_lse)):
+        if _overlap(out, t):
+            raise ValueError(f"out must not overlap {name}")
     code = {torch.bfloat16: _BF16, torch.float32: _F32}
     st = lib.pa_merge_attn_states(out.data_ptr(), _ptr(out_lse), code[odt], prefix_out.data_ptr(),
                                   prefix_lse.data_ptr(), suffix_out.data_ptr(),
@@ -533,7 +610,9 @@ def gather_cache_chunk(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table
     _gpu("context_lens", context_lens, torch.int32, 1)
     NB, Hkv, C, B, x = k_cache.shape
     D = C * x
+    _shuffled_kv(k_cache, v_cache, D, 8)
     S = context_lens.shape[0]
+    _batch(S, block_table, context_lens)
     rows = S * chunk_tokens
     if k_out is None:
         k_out = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=k_cache.device)
@@ -543,6 +622,8 @@ def gather_cache_chunk(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table
     _gpu("v_out", v_out, torch.bfloat16, 3)
     if k_out.shape[0] < rows or v_out.shape[0] < rows:
         raise ValueError("output tensors need num_seqs * chunk_tokens rows")
+    if tuple(k_out.shape[1:]) != (Hkv, D) or tuple(v_out.shape[1:]) != (Hkv, D):
+        raise ValueError(f"k_out / v_out must be [rows, {Hkv}, {D}]")
     st = lib.pa_gather_cache_chunk(k_out.data_ptr(), v_out.data_ptr(), k_cache.data_ptr(),
                                    v_cache.data_ptr(), block_table.data_ptr(),
                                    block_table.shape[1], context_lens.data_ptr(), S, Hkv, D, B, NB,
@@ -586,21 +667,30 @@ def chunked_extend_attn(query: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
     _gpu("block_table", block_table, torch.int32, 2)
     _gpu("context_lens", context_lens, torch.int32, 1)
     Tn, Hq, D = query.shape
-    NB, Hkv, _, B, _ = k_cache.shape
+    NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)
     S = context_lens.shape[0]
+    _batch(S, block_table, context_lens)
+    _shape("k_new", k_new, (Tn, Hkv, D))
+    _shape("v_new", v_new, (Tn, Hkv, D))
+    if query_start_loc.numel() != S + 1:
+        raise ValueError("query_start_loc needs num_seqs + 1 entries")
     qsl_h = torch.as_tensor(query_start_loc_host, dtype=torch.int32).contiguous()
     cl_h = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous()
     if qsl_h.device.type != "cpu" or cl_h.device.type != "cpu":
         raise ValueError("host copies must be on the CPU")
     if qsl_h.numel() != S + 1 or cl_h.numel() != S:
         raise ValueError("host copies have the wrong length")
+    if int(qsl_h[-1]) != Tn:
+        raise ValueError(f"query_start_loc_host ends at {int(qsl_h[-1])}, query has {Tn} rows")
     if out is None:
         out = torch.empty_like(query)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (Tn, Hq, D))
     if lse is None and return_lse:
         lse = torch.empty((Tn, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (Tn, Hq))
     nbytes = extend_workspace_size(S, Tn, Hq, Hkv, D, B, chunk_budget_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_chunked_extend_attn(out.data_ptr(), _ptr(lse), query.data_ptr(), k_new.data_ptr(),
@@ -676,16 +766,25 @@ def mixed_batch_attn(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor
     ctx_h = _host_i32(context_lens_host)
     R = ctx_h.shape[0]
     T, Hq, D = query.shape
-    NB, Hkv, _, B, _ = k_cache.shape
+    NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)
     if qsl_h.shape[0] != R + 1 or int(qsl_h[-1]) != T or block_table.shape[0] != R:
         raise ValueError("batch arrays disagree")
+    _batch(R, block_table, context_lens)
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc needs num_reqs + 1 entries")
+    _shape("key", key, (T, Hkv, D))
+    _shape("value", value, (T, Hkv, D))
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must hold one slot per new token")
     if out is None:
         out = torch.empty_like(query)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (T, Hq, D))
     if lse is None and return_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (T, Hq))
     nbytes = int(lib.pa_mixed_batch_workspace_size(R, qsl_h.ctypes.data, ctx_h.ctypes.data, Hq,
                                                    Hkv, D, B, int(chunk_budget_tokens)))
     ws = _workspace(nbytes, query.device, workspace)
@@ -742,7 +841,8 @@ def paged_decode_attn_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     _gpu("block_table", block_table, torch.int32, 2)
     _gpu("context_lens", context_lens, torch.int32, 1)
     S, Hq, D = query.shape
-    NB, Hkv, _, B, _ = k_cache.shape
+    NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 16)
+    _batch(S, block_table, context_lens)
     given = [t is not None for t in (new_key, new_value, slot_mapping)]
     if any(given) and not all(given):
         raise ValueError("new_key, new_value and slot_mapping go together")
@@ -750,13 +850,16 @@ def paged_decode_attn_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: t
         _gpu("new_key", new_key, torch.bfloat16, 3)
         _gpu("new_value", new_value, torch.bfloat16, 3)
         _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+        _new_tokens(S, Hkv, D, new_key, new_value, slot_mapping)
     if out is None:
         out = torch.empty_like(query)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, D))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = decode_workspace_size(S, Hq, Hkv, D, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_paged_decode_attn_fp8(out.data_ptr(), _ptr(lse), query.data_ptr(), _ptr(new_key),
@@ -784,7 +887,9 @@ def gather_cache_chunk_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
     _gpu("context_lens", context_lens, torch.int32, 1)
     NB, Hkv, C, B, x = k_cache.shape
     D = C * x
+    _shuffled_kv(k_cache, v_cache, D, 16)
     S = context_lens.shape[0]
+    _batch(S, block_table, context_lens)
     rows = S * chunk_tokens
     if k_out is None:
         k_out = torch.empty((rows, Hkv, D), dtype=torch.bfloat16, device=k_cache.device)
@@ -794,6 +899,8 @@ def gather_cache_chunk_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
     _gpu("v_out", v_out, torch.bfloat16, 3)
     if k_out.shape[0] < rows or v_out.shape[0] < rows:
         raise ValueError("output tensors need num_seqs * chunk_tokens rows")
+    if tuple(k_out.shape[1:]) != (Hkv, D) or tuple(v_out.shape[1:]) != (Hkv, D):
+        raise ValueError(f"k_out / v_out must be [rows, {Hkv}, {D}]")
     st = lib.pa_gather_cache_chunk_fp8(k_out.data_ptr(), v_out.data_ptr(), k_cache.data_ptr(),
                                        v_cache.data_ptr(), block_table.data_ptr(),
                                        block_table.shape[1], context_lens.data_ptr(), S, Hkv, D,
@@ -845,13 +952,16 @@ def mla_decode_attn_fp8(query: torch.Tensor, kv_cache: torch.Tensor, block_table
         _gpu("slot_mapping", slot_mapping, torch.int64, 1)
         if tuple(new_latent.shape) != (S, Dl) or slot_mapping.numel() != S:
             raise ValueError("new_latent [num_seqs, latent_dim] and one slot per sequence")
+    _batch(S, block_table, context_lens)
     if out is None:
         out = torch.empty((S, Hq, v_dim), dtype=torch.bfloat16, device=query.device)
     _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, v_dim))
     if lse is None and return_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=query.device)
     if lse is not None:
         _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
     nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
     st = lib.pa_mla_decode_attn_fp8(out.data_ptr(), _ptr(lse), query.data_ptr(), _ptr(new_latent),

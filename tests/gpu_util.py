@@ -82,7 +82,9 @@ def attn_errors(out, lse, ref_out, ref_lse, rows=None):
         if rows is not None:
             l, rl = l[rows], rl[rows]
         both = np.isneginf(l) & np.isneginf(rl)
-        e_lse = float(np.max(np.where(both, 0.0, np.abs(l - rl)))) if l.size else 0.0
+        # mask the rows where both are -inf before subtracting
+        d = np.abs(np.where(both, 0.0, l) - np.where(both, 0.0, rl))
+        e_lse = float(np.max(d)) if l.size else 0.0
     if err.size == 0:
         return 0.0, 0.0, e_lse
     return float(np.nanmax(err)) if not np.isnan(err).any() else float("nan"), \

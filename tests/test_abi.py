@@ -82,7 +82,7 @@ def test_decode_workspace_sizes():
     assert pa.decode_partition_tokens(8, 4, 131072, 8192) == 4096
     assert pa.decode_partition_tokens(1, 1, 100000, -1) == 4096
     assert pa.decode_workspace_size(4, 4, 1, 128, 511, -1) == 0
-    # balanced split: counters [S, Hkv] + one partial per workgroup
+    # balanced split: the fixed counter region + one partial per workgroup
     # (at most four workgroups per compute unit; 256 CUs where no device is visible)
     cus = 256
     try:
@@ -93,8 +93,10 @@ def test_decode_workspace_sizes():
         pass
     a256 = lambda n: (n + 255) // 256 * 256
     nw = 4 * cus
+    region = pa.WORKSPACE_COUNTER_BYTES
+    assert region == 1 << 20
     assert pa.decode_workspace_size(64, 8, 1, 128, 2000, -2) == \
-        a256(64 * 4) + a256(nw * 8 * 128 * 4) + a256(nw * 8 * 4)
+        region + a256(nw * 8 * 128 * 4) + a256(nw * 8 * 4)
     # auto: 64 x 8 partitions of 256 tokens fit in one wave of workgroups;
     # 32 x 32 partitions of 4096 tokens do not
     assert not pa.decode_uses_balanced_split(64, 1, 2000, 0)
@@ -103,8 +105,26 @@ def test_decode_workspace_sizes():
     assert not pa.decode_uses_balanced_split(8, 4, 131072, 2048)
     parts = 4  # 511 tokens in 128-token partitions
     a256 = lambda n: (n + 255) // 256 * 256
-    want = a256(4 * 1 * 4) + a256(4 * 4 * parts * 128 * 4) + a256(4 * 4 * parts * 4)
+    want = region + a256(4 * 4 * parts * 128 * 4) + a256(4 * 4 * parts * 4)
     assert pa.decode_workspace_size(4, 4, 1, 128, 511, 128) == want
+    # the counter region holds one counter per (sequence, kv head) of a split call
+    cap = region // 4
+    # auto with more pairs than counters: fixed partitions, unsplit up to 4096 tokens
+    assert not pa.decode_uses_balanced_split(cap // 8 + 1, 8, 4096, 0)
+    assert pa.decode_workspace_size(cap // 8 + 1, 64, 8, 128, 4096, 0) == 0
+    assert pa.decode_uses_balanced_split(cap // 8, 8, 4096, 0)
+    # the extend workspace also starts with the (untouched) counter region
+    assert pa.extend_workspace_size(1, 8, 8, 2, 128, 16, 4096) > region
+
+
+def test_split_beyond_counter_capacity_is_unsupported():
+    """A split decode call with more (sequence, kv head) pairs than the
+    counter region holds returns PA_ERR_UNSUPPORTED before any launch."""
+    lib = pa.library()
+    S = pa.WORKSPACE_COUNTER_BYTES // 4 // 8 + 1     # 8 kv heads
+    big = 1 << 40
+    for P in (-2, 256):
+        assert _decode(lib, S=S, Hq=8, Hkv=8, maxctx=4096, P=P, ws=FAKE, wsb=big) == UNSUPPORTED
 
 
 def test_fused_decode_validation():
@@ -151,6 +171,26 @@ def test_merge_validation():
     assert f(FAKE, None, 5, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 128, None) == INVALID
     assert f(None, None, 0, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 128, None) == INVALID
     assert f(FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, 2, 128, None) == OK     # no rows
+
+
+def test_merge_rejects_overlapping_outputs():
+    """out_lse may not overlap an input LSE (a row's LSE is read by threads of
+    several workgroups); out may be an input itself, with the same dtype, but
+    may not partly overlap one.  All of these fail before any launch."""
+    f = pa.library().pa_merge_attn_states
+    T, H, D = 4, 2, 192                  # 24 vectors of 8 per row: a row spans workgroups
+    rows, F32 = T * H, 1
+    vo = rows * D * 4                    # bytes of one f32 output
+    po, so, out = FAKE, FAKE + vo, FAKE + 2 * vo
+    pl, sl = FAKE + 3 * vo, FAKE + 3 * vo + 256
+    assert f(out, pl, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID        # out_lse = prefix
+    assert f(out, sl, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID        # out_lse = suffix
+    assert f(out, sl + 16, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID   # partly
+    assert f(out, po + 64, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID   # in an input
+    assert f(out, out, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID       # in out
+    assert f(po + 32, None, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID  # out partly on po
+    assert f(po, None, 0, po, pl, so, sl, F32, T, H, D, None) == INVALID         # bf16 out on f32 po
+    assert f(pl - 64, None, F32, po, pl, so, sl, F32, T, H, D, None) == INVALID  # out on the LSEs
 
 
 def test_binding_refuses_cpu_tensors():

@@ -15,7 +15,7 @@ from gpu_util import assert_attn_close, device, empty_gpu_cache, say
 pytestmark = pytest.mark.gpu
 
 
-def run_routed(case):
+def run_routed(case, workspace=None):
     """Write the cached tokens, reorder the batch with the plan, run the
     routed call; returns (out, lse) in the case's own request order."""
     dev = device()
@@ -48,7 +48,8 @@ def run_routed(case):
     bt = torch.from_numpy(np.ascontiguousarray(pg.block_table[order])).to(dev)
     out, lse = pa.mixed_batch_attn(q, k, v, slots, torch.from_numpy(new_qsl).to(dev),
                                    torch.from_numpy(ctx).to(dev), kc, vc, bt, case.scale,
-                                   new_qsl, ctx, chunk_budget_tokens=case.chunk_budget_tokens)
+                                   new_qsl, ctx, chunk_budget_tokens=case.chunk_budget_tokens,
+                                   workspace=workspace)
     torch.cuda.synchronize()
     # back to the case's order
     inv = torch.empty(len(q_rows), dtype=torch.long)
