@@ -21,7 +21,9 @@
  * ---------------------------------------
  *  - Pointers are device pointers (HBM) unless the name ends in _host.
  *    The caller owns every buffer; the library never allocates or frees
- *    device memory, keeps no mutable global state and is re-entrant.
+ *    device memory, keeps no mutable global state and is re-entrant, with
+ *    one exception: pa_paged_decode_attn_write_noalloc works in a device
+ *    array of the library's own, shared by all its calls on a device.
  *  - `stream` is a hipStream_t (NULL: the null stream).  Work is enqueued
  *    on it asynchronously; nothing synchronises.
  *  - Tensors are dense, row-major, no padding.  bf16 is the storage type
@@ -202,6 +204,38 @@ pa_status pa_paged_decode_attn_write(void *out, float *lse, const void *query,
                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                      float scale, int32_t partition_tokens, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/* Bytes of the library's per-device scratch array used by
+ * pa_paged_decode_attn_write_noalloc (counter region included). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * pa_paged_decode_attn_write without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The call itself
+ * allocates nothing.  Its workspace is a file-scope device array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device, held
+ * from the library's load until the process ends; its device address is
+ * taken once per device on the first call there, which also enqueues a
+ * clear of the array's counter region on `stream` ahead of the call's own
+ * work.  Every other argument, the result and the errors are those of
+ * pa_paged_decode_attn_write; a call whose pa_decode_workspace_size
+ * exceeds PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE_TOO_SMALL with
+ * nothing enqueued.  All calls on one device share its array, which keeps
+ * the last call's contents: calls that overlap in time on one device
+ * (concurrent streams, threads or processes sharing the array's device
+ * memory) race and must be serialised by the caller.
+ */
+pa_status pa_paged_decode_attn_write_noalloc(void *out, float *lse, const void *query,
+                                             const void *new_key, const void *new_value,
+                                             const int64_t *slot_mapping, void *k_cache,
+                                             void *v_cache, const int32_t *block_table,
+                                             int32_t max_blocks_per_seq,
+                                             const int32_t *context_lens, int32_t max_context_len,
+                                             int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int64_t num_blocks, float scale,
+                                             int32_t partition_tokens, void *stream);
 
 /*
  * Paged GQA decode over a cache in either layout, with or without the fused

@@ -10,6 +10,7 @@ from .ops import (  # noqa: F401
     LAYOUT_MLA_LATENT,
     LAYOUT_SHUFFLED_KV,
     LAYOUT_STANDARD_KV,
+    NOALLOC_SCRATCH_BYTES,
     PagedAttnError,
     WORKSPACE_COUNTER_BYTES,
     chunked_extend_attn,
@@ -33,6 +34,7 @@ from .ops import (  # noqa: F401
     mla_decode_attn_fp8,
     paged_decode_attn_layout,
     paged_decode_attn_write,
+    paged_decode_attn_write_noalloc,
     reshape_and_cache,
     reshape_and_cache_fp8,
     reshape_and_cache_mla_fp8,

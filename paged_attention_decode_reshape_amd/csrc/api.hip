@@ -1,6 +1,7 @@
 // C ABI of libpagedattn (declared in include/pagedattn.h): host-side
 // argument checks, partition / chunk planning and kernel launches.
-// Nothing here allocates device memory or keeps state between calls.
+// Nothing here allocates device memory or keeps state between calls (the
+// one entry point with device state of its own is in noalloc.hip).
 #include <math.h>
 #include <stdint.h>
 
@@ -204,20 +205,22 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
     return sp.total();
 }
 
+}  // extern "C"
+
 // GQA decode, optionally with the fused cache write of each sequence's new
-// token (new_key / new_value / slot_mapping all null: no write).
+// token (new_key / new_value / slot_mapping all null: no write); shared by
+// the GQA decode entry points, including the one in noalloc.hip.
 // layout: 0 shuffled bf16, 1 standard bf16, 2 shuffled FP8 (k_scale,
 // v_scale used only there)
-static pa_status decode_impl(int layout, float k_scale, float v_scale, void *out, float *lse,
-                             const void *query, const void *new_key,
-                             const void *new_value, const int64_t *slot_mapping,
-                             const void *k_cache, const void *v_cache,
-                             const int32_t *block_table, int32_t max_blocks_per_seq,
-                             const int32_t *context_lens, int32_t max_context_len,
-                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                             float scale, int32_t partition_tokens, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+int32_t pa::decode_impl(int layout, float k_scale, float v_scale, void *out, float *lse,
+                        const void *query, const void *new_key, const void *new_value,
+                        const int64_t *slot_mapping, const void *k_cache, const void *v_cache,
+                        const int32_t *block_table, int32_t max_blocks_per_seq,
+                        const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, float scale,
+                        int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                        void *stream, bool dry_run) {
     if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
         num_blocks < 1 || max_context_len < 0 || partition_tokens < kRequestBalanced ||
         !isfinite(scale))
@@ -243,10 +246,11 @@ static pa_status decode_impl(int layout, float k_scale, float v_scale, void *out
     if ((balanced || sp.parts > 1) && !counters_fit(num_seqs, num_kv_heads))
         return PA_ERR_UNSUPPORTED;
     if (sp.total() > 0) {
-        if (!workspace || workspace_bytes < sp.total()) return PA_ERR_WORKSPACE_TOO_SMALL;
+        if ((!workspace && !dry_run) || workspace_bytes < sp.total())
+            return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
     }
-    if (num_seqs == 0) return PA_OK;
+    if (num_seqs == 0 || dry_run) return PA_OK;
     DecodeParams p;
     p.out = out;
     p.lse = lse;
@@ -283,6 +287,8 @@ static pa_status decode_impl(int layout, float k_scale, float v_scale, void *out
     p.v_inv = 1.0f / v_scale;
     return from_hip(launch_paged_decode(p, (hipStream_t)stream));
 }
+
+extern "C" {
 
 pa_status pa_paged_decode_attn(void *out, float *lse, const void *query, const void *k_cache,
                                const void *v_cache, const int32_t *block_table,

@@ -66,6 +66,21 @@ struct DecodeParams {
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
 
+// The checks, split planning and launch behind every GQA decode entry point
+// (api.hip): returns a pa_status.  layout: 0 shuffled bf16, 1 standard
+// bf16, 2 shuffled FP8.  The workspace starts with the counter region.
+// dry_run: every check (the workspace may be null, its size still counts),
+// nothing enqueued.
+int32_t decode_impl(int layout, float k_scale, float v_scale, void *out, float *lse,
+                    const void *query, const void *new_key, const void *new_value,
+                    const int64_t *slot_mapping, const void *k_cache, const void *v_cache,
+                    const int32_t *block_table, int32_t max_blocks_per_seq,
+                    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, float scale,
+                    int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                    void *stream, bool dry_run = false);
+
 struct MLAParams {
     void *out;                 // bf16 [S, Hq, Dv]
     float *lse;                // f32 [S, Hq] or null

@@ -23,6 +23,9 @@ LAYOUT_STANDARD_KV = 2
 # Bytes of the completion-counter region at the start of every workspace
 # (PA_WORKSPACE_COUNTER_BYTES in the C header).
 WORKSPACE_COUNTER_BYTES = 1 << 20
+# Bytes of the per-device array paged_decode_attn_write_noalloc works in
+# (PA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 _BF16, _F32 = 0, 1
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
@@ -52,6 +55,9 @@ _SIGS = {
     "pa_paged_decode_attn_write": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                     _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp,
                                     _sz, _vp], _i32),
+    "pa_paged_decode_attn_write_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                            _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                                            _i32, _vp], _i32),
     "pa_paged_decode_attn_layout": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                      _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32,
                                      _vp, _sz, _vp], _i32),
@@ -349,6 +355,47 @@ def paged_decode_attn_write(query: torch.Tensor, new_key: torch.Tensor, new_valu
                                         int(max_context_len), S, Hq, Hkv, D, B, NB, float(scale),
                                         int(partition_tokens), _ptr(ws), nbytes, _stream(query))
     _check("paged_decode_attn_write", st)
+    return out, lse
+
+
+def paged_decode_attn_write_noalloc(query: torch.Tensor, new_key: torch.Tensor,
+                                    new_value: torch.Tensor, slot_mapping: torch.Tensor,
+                                    k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                    block_table: torch.Tensor, context_lens: torch.Tensor,
+                                    scale: float, max_context_len: int, partition_tokens: int = 0,
+                                    out: Optional[torch.Tensor] = None,
+                                    lse: Optional[torch.Tensor] = None
+                                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """paged_decode_attn_write with the workspace in the library's own
+    per-device array (NOALLOC_SCRATCH_BYTES), for callers that cannot allocate
+    device memory.  Pass `out` (and `lse`) to allocate nothing here either;
+    calls that overlap in time on one device race."""
+    lib = library()
+    _gpu("query", query, torch.bfloat16, 3)
+    _gpu("new_key", new_key, torch.bfloat16, 3)
+    _gpu("new_value", new_value, torch.bfloat16, 3)
+    _gpu("slot_mapping", slot_mapping, torch.int64, 1)
+    _gpu("k_cache", k_cache, torch.bfloat16, 5)
+    _gpu("v_cache", v_cache, torch.bfloat16, 5)
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    S, Hq, D = query.shape
+    NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)
+    _batch(S, block_table, context_lens)
+    _new_tokens(S, Hkv, D, new_key, new_value, slot_mapping)
+    if out is None:
+        out = torch.empty_like(query)
+    _gpu("out", out, torch.bfloat16, 3)
+    _shape("out", out, (S, Hq, D))
+    if lse is not None:
+        _gpu("lse", lse, torch.float32, 2)
+        _shape("lse", lse, (S, Hq))
+    st = lib.pa_paged_decode_attn_write_noalloc(
+        out.data_ptr(), _ptr(lse), query.data_ptr(), new_key.data_ptr(), new_value.data_ptr(),
+        slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        block_table.shape[1], context_lens.data_ptr(), int(max_context_len), S, Hq, Hkv, D, B, NB,
+        float(scale), int(partition_tokens), _stream(query))
+    _check("paged_decode_attn_write_noalloc", st)
     return out, lse
 
 

@@ -339,3 +339,19 @@ def test_mla_fp8_entry_validation():
     assert d(ks=-1.0) == INVALID and d(ks=float("inf")) == INVALID
     assert d(Dv=448) == UNSUPPORTED
     assert d(P=-2) == WS_SMALL
+
+
+def test_noalloc_decode_validation():
+    """The no-allocation decode entry checks everything, the size of its
+    array included, before it touches the device."""
+    f = pa.library().pa_paged_decode_attn_write_noalloc
+    args = lambda nk, S, Hq, maxctx, P: (FAKE, None, FAKE, nk, FAKE, FAKE, FAKE, FAKE, FAKE, 256,
+                                         FAKE, maxctx, S, Hq, 2, 128, 16, 4096, 0.1, P, None)
+    assert f(*args(None, 4, 8, 100, -1)) == INVALID               # no new key
+    assert f(*args(FAKE + 8, 4, 8, 100, -1)) == INVALID           # new key misaligned
+    assert f(*args(FAKE, 4, 7, 100, -1)) == INVALID               # 7 q heads on 2 kv heads
+    assert f(*args(FAKE, 4, 8, 100, -3)) == INVALID
+    # 64 x 16 heads x 64 partitions of fp32 partials: more than the array holds
+    assert pa.decode_workspace_size(64, 16, 2, 128, 4096, 64) > pa.NOALLOC_SCRATCH_BYTES
+    assert f(*args(FAKE, 64, 16, 4096, 64)) == WS_SMALL
+    assert pa.NOALLOC_SCRATCH_BYTES == 32 << 20
