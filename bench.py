@@ -55,17 +55,55 @@ MEASURED_TRAFFIC = {
 }
 
 
-def measured_traffic(config):
-    """The counter-measured bytes per launch, or None once the kernel changed."""
+def sources_sha(sources) -> str:
+    """sha256 prefix of the concatenated source files (tags measurements)."""
     import hashlib
-    if config not in MEASURED_TRAFFIC:
-        return None
-    sources, sha, nbytes = MEASURED_TRAFFIC[config]
     h = hashlib.sha256()
     for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    return nbytes if h.hexdigest()[:16] == sha else None
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """The counter-measured bytes per launch, or None once the kernel changed."""
+    if config not in MEASURED_TRAFFIC:
+        return None
+    sources, sha, nbytes = MEASURED_TRAFFIC[config]
+    return nbytes if sources_sha(sources) == sha else None
+
+
+# The sources of each workload's kernels, for the tag the JSON line carries.
+KERNEL_SOURCES = {
+    "gqa": (_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
+    "mla": (_CSRC + "mla_decode.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
+    "extend": (_CSRC + "extend.hip", _CSRC + "decode_common.h"),
+    "merge": (_CSRC + "merge.hip",),
+    "cache_write": (_CSRC + "cache_write.hip", _CSRC + "fp8.h"),
+}
+
+
+def trace_summary(path, top=12):
+    """Per-kernel duration statistics (count, mean, median, p10, p90, min,
+    max in microseconds) from a rocprofv3 kernel-trace CSV, as a markdown
+    table, longest total time first."""
+    import csv
+    durs = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("Kernel-Name") or row.get("KernelName")
+            t0 = int(row.get("Start_Timestamp") or row.get("Start-Timestamp"))
+            t1 = int(row.get("End_Timestamp") or row.get("End-Timestamp"))
+            durs.setdefault(name, []).append((t1 - t0) / 1000.0)
+    lines = ["| kernel | launches | mean us | median us | p10 us | p90 us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        a = np.array(d)
+        short = name if len(name) <= 110 else name[:107] + "..."
+        lines.append(f"| `{short}` | {a.size} | {a.mean():.2f} | {np.median(a):.2f} | "
+                     f"{np.percentile(a, 10):.2f} | {np.percentile(a, 90):.2f} | {a.min():.2f} | "
+                     f"{a.max():.2f} |")
+    return "\n".join(lines)
 
 
 HBM_PEAK_GBPS = 8000.0
@@ -104,6 +142,9 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="decode split (GQA and MLA): 0 auto, -2 balanced, > 0 fixed "
                          "partitions, -1 unsplit (default: the workload's own)")
+    ap.add_argument("--trace-summary", default=None, metavar="CSV",
+                    help="print per-kernel duration statistics of a rocprofv3 kernel-trace CSV "
+                         "and exit (no GPU needed)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after the bench, run plain device copies of this many MiB (a known "
                          "byte count for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -150,6 +191,63 @@ def time_launches(launch, n):
     e1.record(cur)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _gate(ms):
+    """Hold the current stream for about `ms` with torch's bounded spin
+    kernel, so that launches enqueued meanwhile then run back to back."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(2_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
+def launch_stats(launch, n=240, batch=20):
+    """Device time per launch (ms) of n launches run back to back: the
+    stream is held by a short spin while they are enqueued.  mean_ms comes
+    from one pair of HIP events around all n on the launch stream; a second
+    pass records an event after every `batch` launches and reports the
+    spread of the per-batch means (an event after every single launch would
+    add its own few microseconds to each).  Per-launch percentiles come from
+    rocprofv3 kernel traces."""
+    import torch
+    cur = torch.cuda.current_stream()
+    for i in range(5):
+        launch(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    _gate(max(2.0, 0.03 * n))
+    e0.record(cur)
+    for i in range(n):
+        launch(i)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / n
+    nb = max(1, n // batch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    _gate(max(2.0, 0.03 * n))
+    ev[0].record(cur)
+    for b in range(nb):
+        for j in range(batch):
+            launch(b * batch + j)
+        ev[b + 1].record(cur)
+    torch.cuda.synchronize()
+    d = np.array([ev[b].elapsed_time(ev[b + 1]) / batch for b in range(nb)])
+    return {"launches": n, "mean_ms": mean, "batch": batch,
+            "batch_mean_median_ms": float(np.median(d)),
+            "batch_mean_p10_ms": float(np.percentile(d, 10)),
+            "batch_mean_p90_ms": float(np.percentile(d, 90)),
+            "method": "HIP events on the launch stream around back-to-back launches"}
 
 
 def read_ceiling(nbytes, grids=(1024, 2048, 4096, 8192), n=200):
@@ -238,7 +336,7 @@ def bench_gqa(args, case, label):
 
     fused = not args.separate_cache_write
 
-    def decode(i):
+    def decode_call(i):
         kc, vc = caches[i % pools]
         if f8:
             pa.paged_decode_attn_fp8(q, kc, vc, bt, cl, case.scale, max_ctx, k_scale, v_scale,
@@ -258,6 +356,13 @@ def bench_gqa(args, case, label):
         else:
             pa.paged_decode_attn(q, kc, vc, bt, cl, case.scale, max_ctx, partition_tokens=P,
                                  out=out, lse=lse, workspace=ws)
+
+    # each pool's call checked and marshalled once (pa.prepare); a launch is
+    # then one C call, so the host enqueues faster than the GPU runs them
+    prepared = [pa.prepare(decode_call, i) for i in range(pools)]
+
+    def decode(i):
+        prepared[i % pools]()
 
     def step(i):
         if not fused:
@@ -315,9 +420,10 @@ def bench_gqa(args, case, label):
         torch.cuda.synchronize()
         graph_ok = bool(torch.equal(out.view(torch.int16), ref_out.view(torch.int16)))
 
-    # the decode kernel's own duration: HIP events on the launch stream around
-    # back-to-back launches (rotating pools), averaged per launch
-    dec_ms = time_launches(decode, min(args.steps, 400))
+    # the decode kernel's own duration: HIP events on the launch stream between
+    # back-to-back launches (rotating pools)
+    stats = launch_stats(decode, 240)
+    dec_ms = stats["mean_ms"]
 
     algo = gqa_algorithmic_bytes(case, with_write=fused, kv_bytes=kv_bytes)
     achieved = algo / (dec_ms * 1e-3) / 1e9
@@ -327,6 +433,7 @@ def bench_gqa(args, case, label):
         "ms_per_step": ms_per_step,
         "graph_replay_matches_eager": graph_ok,
         "decode_ms": dec_ms,
+        "launch_stats": stats,
         "hbm_gbps": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "algo_bytes": algo,
@@ -340,6 +447,58 @@ def bench_gqa(args, case, label):
         "partition_tokens": ("balanced" if pa.decode_uses_balanced_split(case.S, case.Hkv, max_ctx, P)
                              else pa.decode_partition_tokens(case.S, case.Hkv, max_ctx, P)),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def time_oracle(step, units, unit, seconds, sample, omp=True):
+    """The oracle's throughput on this host: one untimed warm-up step, then
+    three runs of about seconds/4 each (the median is the value), then a run
+    of about seconds/4 on one thread.  `units` counted per step.  omp: the
+    step is the C oracle (OpenMP threads); otherwise numpy on one BLAS
+    thread throughout."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    orc = oracle.get()
+
+    def run(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            step()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return units * reps / el, reps, el
+
+    cores = orc.max_threads() if omp else 1
+    with threadpool_limits(1, user_api="blas"):
+        step()
+        runs = [run(seconds / 4) for _ in range(3)]
+        if omp:
+            orc.set_threads(1)
+            try:
+                one = run(seconds / 4)
+            finally:
+                orc.set_threads(cores)
+        else:
+            one = sorted(runs)[1]
+    vals = sorted(r[0] for r in runs)
+    return {"value": vals[1], "unit": unit, "cores": cores, "kind": "oracle",
+            "runs": [r[0] for r in runs], "one_thread_value": one[0],
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "sample": f"{sample}; median of 3 runs ({sum(r[1] for r in runs)} steps in "
+                      f"{sum(r[2] for r in runs):.1f} s) after a warm-up step, then "
+                      f"{one[1]} step(s) on one thread, fp64"}
 
 
 def cpu_baseline_gqa(case, seconds, kv_layout="shuffled", kv_scales=None):
@@ -386,25 +545,12 @@ def cpu_baseline_gqa(case, seconds, kv_layout="shuffled", kv_scales=None):
             orc.cache_write_shuffled(nk, nv, ns, kc, vc, case.B)
             orc.paged_decode_gqa(qb, kc, vc, pg.block_table, case.context_lens, case.B,
                                  case.scale)
-    from threadpoolctl import threadpool_limits
-    reps = 0
-    t0 = time.perf_counter()
-    # numpy's BLAS on one thread, so the FP8 oracle's `cores` is exact (the C
-    # oracle's OpenMP threads are not limited)
-    with threadpool_limits(1, user_api="blas"):
-        while True:
-            step()
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
     what = ("FP8 numpy oracle, every 8th request" if kv_scales is not None else
             "standard-layout cache, shuffled on the fly" if kv_layout == "standard" else
             "shuffled bf16 cache")
-    return {"value": len(seqs) * reps / el, "unit": "tok/s",
-            "cores": orc.max_threads() if kv_scales is None else 1, "kind": "oracle",
-            "sample": f"{reps} decode steps of the same workload ({len(seqs)} of {case.S} "
-                      f"requests per step, {what}) in {el:.1f} s, fp64"}
+    return time_oracle(step, len(seqs), "tok/s", seconds,
+                       f"decode steps of the same workload ({len(seqs)} of {case.S} requests "
+                       f"per step, {what})", omp=kv_scales is None)
 
 
 def cpu_baseline_mixed(case, seconds):
@@ -421,20 +567,12 @@ def cpu_baseline_mixed(case, seconds):
     rows = case.new_rows()
     kn, vn = kb[rows], vb[rows]
     qb = W.bf16_bits(case.query)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+    def step():
         orc.extend(qb, kn, vn, case.query_start_loc, kc, vc, case.paging.block_table,
                    case.ctx_lens, case.B, case.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
     tokens = int(case.query_start_loc[-1])
-    return {"value": tokens * reps / el, "unit": "new tok/s", "cores": orc.max_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} passes over the whole mixed batch ({tokens} new tokens) in "
-                      f"{el:.1f} s, fp64"}
+    return time_oracle(step, tokens, "new tok/s", seconds,
+                       f"passes over the whole mixed batch ({tokens} new tokens)")
 
 
 # ---------------------------------------------------------------------------
@@ -506,7 +644,7 @@ def bench_mla(args, case, label):
     if mfma and f8:
         raise SystemExit("the matrix-core MLA engine reads bf16 latents only")
 
-    def decode(i):
+    def decode_call(i):
         if mfma:
             pa.mla_decode_attn_mfma(q, caches[i % pools], bt, cl, case.scale, max_ctx,
                                     v_dim=case.Dv, partition_tokens=P,
@@ -527,6 +665,11 @@ def bench_mla(args, case, label):
             pa.mla_decode_attn(q, caches[i % pools], bt, cl, case.scale, max_ctx, v_dim=case.Dv,
                                partition_tokens=P, out=out, lse=lse, workspace=ws)
 
+    prepared = [pa.prepare(decode_call, i) for i in range(pools)]
+
+    def decode(i):
+        prepared[i % pools]()
+
     def step(i):
         if not fused and f8:
             pa.reshape_and_cache_mla_fp8(new_lat, caches[i % pools], new_slots, kvs)
@@ -543,13 +686,14 @@ def bench_mla(args, case, label):
         step(i)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    dec_ms = time_launches(decode, min(args.steps, 200))
+    stats = launch_stats(decode, 240)
+    dec_ms = stats["mean_ms"]
     algo = mla_algorithmic_bytes(case, with_write=fused, kv_bytes=kv_bytes)
     flops = mla_algorithmic_flops(case)
     # MLA picks its split like GQA decode with one unit per sequence
     balanced = pa.decode_uses_balanced_split(case.S, 1, max_ctx, P)
     return {"value": case.S / (ms_per_step * 1e-3), "ms_per_step": ms_per_step,
-            "decode_ms": dec_ms, "algo_bytes": algo, "algo_flops": flops,
+            "decode_ms": dec_ms, "launch_stats": stats, "algo_bytes": algo, "algo_flops": flops,
             "hbm_gbps": algo / (dec_ms * 1e-3) / 1e9, "tflops": flops / (dec_ms * 1e-3) / 1e12,
             "pools": pools, "cache_write": "fused" if fused else "separate launch",
             "kv_scale": kvs if f8 else None,
@@ -580,21 +724,10 @@ def cpu_baseline_mla(case, seconds, kv_scale=None):
         def step():
             OF.paged_decode_mla(qb, kv, case.paging.block_table, case.context_lens, case.Dv,
                                 case.scale, kv_scale)
-    from threadpoolctl import threadpool_limits
-    reps = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(1, user_api="blas"):
-        while True:
-            step()
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    return {"value": case.S * reps / el, "unit": "tok/s",
-            "cores": orc.max_threads() if kv_scale is None else 1, "kind": "oracle",
-            "sample": f"{reps} full MLA decode steps of the same workload ({case.S} requests"
-                      f"{', FP8 numpy oracle' if kv_scale is not None else ''}) "
-                      f"in {el:.1f} s, fp64"}
+    return time_oracle(step, case.S, "tok/s", seconds,
+                       f"full MLA decode steps of the same workload ({case.S} requests"
+                       f"{', FP8 numpy oracle' if kv_scale is not None else ''})",
+                       omp=kv_scale is None)
 
 
 # ---------------------------------------------------------------------------
@@ -704,12 +837,13 @@ def bench_cache_write(args):
         k, v = srcs[i % pools]
         pa.reshape_and_cache(k, v, kc, vc, slots)
 
-    ms = time_launches(launch, min(args.steps, 400))
+    stats = launch_stats(launch, 240)
+    ms = stats["mean_ms"]
     T = pg.total_tokens
     nbytes = T * case.Hkv * case.D * 2 * 2 * 2 + T * 8
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"value": T / (ms * 1e-3), "ms_per_step": ms, "algo_bytes": nbytes, "gbps": gbps,
-            "tokens": T, "pools": pools}
+            "tokens": T, "pools": pools, "launch_stats": stats}
 
 
 def bench_merge(args):
@@ -739,11 +873,12 @@ def bench_merge(args):
         po, pl, so, sl = sets[i % copies]
         pa.merge_attn_states(po, pl, so, sl, out=out, out_lse=lse)
 
-    ms = time_launches(launch, min(args.steps, 400))
+    stats = launch_stats(launch, 240)
+    ms = stats["mean_ms"]
     nbytes = per + T * H * D * 2 + T * H * 4
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"value": T / (ms * 1e-3), "ms_per_step": ms, "algo_bytes": nbytes, "gbps": gbps,
-            "copies": copies}
+            "copies": copies, "launch_stats": stats}
 
 
 def bench_extend(args, case, label):
@@ -785,7 +920,8 @@ def bench_extend(args, case, label):
         call(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    ev_ms = time_launches(call, args.steps)
+    stats = launch_stats(call, 200)
+    ev_ms = stats["mean_ms"]
     flops = extend_algorithmic_flops(case)
 
     # The context gather on its own (pa_gather_cache_chunk, the pages'
@@ -802,7 +938,8 @@ def bench_extend(args, case, label):
 
     g_ms = time_launches(gather_pass, max(3, args.steps // 20))
     g_bytes = int(case.ctx_lens.astype(np.int64).sum()) * case.Hkv * case.D * 2 * 2 * 2
-    return {"value": Tn / (ms * 1e-3), "ms_per_step": ms, "call_ms": ev_ms, "algo_flops": flops,
+    return {"value": Tn / (ms * 1e-3), "ms_per_step": ms, "call_ms": ev_ms, "launch_stats": stats,
+            "algo_flops": flops,
             "tflops": flops / (ev_ms * 1e-3) / 1e12,
             "gather": {"kernel": "gather_chunk_kernel", "chunk_tokens": c, "iterations": iters,
                        "ms_per_pass": g_ms, "algo_bytes_per_pass": g_bytes,
@@ -810,31 +947,25 @@ def bench_extend(args, case, label):
 
 
 def cpu_baseline_extend(case, seconds):
-    """The oracle's extend (the definition, fp64) on a bounded sample: the
-    first request's first new tokens, as many as fit the time budget."""
+    """The oracle's extend (the definition, fp64) on a bounded sample: two
+    new tokens (all 64 q heads) over the first request's context."""
     import oracle
     from paged_attention_decode_reshape_amd import workloads as W
 
     orc = oracle.get()
-    sub = W.extend_case("extend_sample", 1005, ctx_lens=[int(case.ctx_lens[0])], new_tokens=[8],
+    sub = W.extend_case("extend_sample", 1005, ctx_lens=[int(case.ctx_lens[0])], new_tokens=[2],
                         Hq=case.Hq, Hkv=case.Hkv, D=case.D, block_size=case.B)
     rows = sub.new_rows()
     kc, vc = orc.empty_shuffled_cache(sub.paging.num_blocks, sub.Hkv, sub.D, sub.B)
     orc.cache_write_shuffled(W.bf16_bits(sub.key), W.bf16_bits(sub.value), sub.paging.slot_mapping,
                              kc, vc, sub.B)
     kn, vn, qb = W.bf16_bits(sub.key)[rows], W.bf16_bits(sub.value)[rows], W.bf16_bits(sub.query)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+    def step():
         orc.extend(qb, kn, vn, sub.query_start_loc, kc, vc, sub.paging.block_table, sub.ctx_lens,
                    sub.B, sub.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": 8 * reps / el, "unit": "new tok/s", "cores": orc.max_threads(), "kind": "oracle",
-            "sample": f"{reps} runs of 8 new tokens over a {int(case.ctx_lens[0])}-token context "
-                      f"(64 q heads) in {el:.1f} s, fp64"}
+    return time_oracle(step, 2, "new tok/s", seconds,
+                       f"runs of 2 new tokens over a {int(case.ctx_lens[0])}-token context "
+                       f"(64 q heads)")
 
 
 def copy_calibration(mb):
@@ -852,6 +983,9 @@ def copy_calibration(mb):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library's "
               "path has no multi-GPU leg", file=sys.stderr)
@@ -913,6 +1047,7 @@ def main():
                                 "traffic": measured_traffic(args.config + "_mfma"),
                                 "algo_bytes_per_launch": r["algo_bytes"],
                                 "avg_launch_ms": r["decode_ms"],
+                                "launch_stats": r["launch_stats"],
                                 "mfma_tflops": r["tflops"],
                                 "mfma_frac_of_bf16_peak": r["tflops"] / MFMA_BF16_PEAK_TFLOPS}
         else:
@@ -923,11 +1058,12 @@ def main():
                                     args.config + ("_fp8" if args.kv_dtype == "fp8" else "")),
                                 "algo_flops_per_launch": r["algo_flops"],
                                 "algo_bytes_per_launch": r["algo_bytes"],
-                                "avg_launch_ms": r["decode_ms"]}
+                                "avg_launch_ms": r["decode_ms"],
+                                "launch_stats": r["launch_stats"]}
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_mla(case, args.cpu_seconds, r["kv_scale"])
-        print(json.dumps(line), flush=True)
+        emit(line, ("mla",))
         return
     elif args.config == "cache_write":
         r = bench_cache_write(args)
@@ -939,8 +1075,9 @@ def main():
                             "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
                             "algo_bytes_per_launch": r["algo_bytes"],
-                            "avg_launch_ms": r["ms_per_step"]}
-        print(json.dumps(line), flush=True)
+                            "avg_launch_ms": r["ms_per_step"],
+                            "launch_stats": r["launch_stats"]}
+        emit(line, ("cache_write",))
         return
     elif args.config == "merge":
         r = bench_merge(args)
@@ -953,12 +1090,13 @@ def main():
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
                             "algo_bytes_per_launch": r["algo_bytes"],
-                            "avg_launch_ms": r["ms_per_step"]}
+                            "avg_launch_ms": r["ms_per_step"],
+                            "launch_stats": r["launch_stats"]}
         if not args.no_read_ceiling:
             rc = read_ceiling(r["algo_bytes"])
             rc["decode_frac_of_ceiling"] = r["gbps"] / rc["gbps"]
             line["hbm_read_ceiling"] = rc
-        print(json.dumps(line), flush=True)
+        emit(line, ("merge",))
         return
     elif args.config == "mixed":
         r = bench_mixed(args)
@@ -971,7 +1109,7 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_mixed(mixed_case(), args.cpu_seconds)
-        print(json.dumps(line), flush=True)
+        emit(line, ("gqa", "extend"))
         return
     else:  # extend
         case = W.chunked_extend()
@@ -986,12 +1124,13 @@ def main():
                             "traffic": measured_traffic(args.config),
                             "traffic_kernel": "extend_attn_kernel",
                             "algo_flops_per_call": r["algo_flops"],
-                            "avg_call_ms": r["call_ms"]}
+                            "avg_call_ms": r["call_ms"],
+                            "launch_stats": r["launch_stats"]}
         line["gather_pass"] = r["gather"]
         if not args.no_cpu_baseline:
             log("[bench] timing the oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_extend(case, args.cpu_seconds)
-        print(json.dumps(line), flush=True)
+        emit(line, ("extend",))
         return
 
     line = base_line(args, r, workload)
@@ -1016,6 +1155,7 @@ def main():
                         if r["kv_layout"] == "shuffled" else None),
             "algo_bytes_per_launch": r["algo_bytes"],
             "avg_launch_ms": r["decode_ms"],
+            "launch_stats": r["launch_stats"],
         },
     })
     if not args.no_read_ceiling:
@@ -1026,6 +1166,15 @@ def main():
         log("[bench] timing the oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds, r["kv_layout"],
                                                 r["kv_scales"])
+    emit(line, ("gqa",))
+
+
+def emit(line, kinds):
+    """Tag the line with the sha of the kernel sources it measured; print it."""
+    files = []
+    for k in kinds:
+        files += [f for f in KERNEL_SOURCES[k] if f not in files]
+    line["kernel_sources_sha16"] = sources_sha(files)
     print(json.dumps(line), flush=True)
 
 

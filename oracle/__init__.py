@@ -87,8 +87,10 @@ class Oracle:
                                           _i32, _i32, _i32, _f64, _i32, _c_f64p, _c_f64p]
         lib.oracle_extend.argtypes = [_c_u16p, _c_u16p, _c_u16p, _c_i32p, _c_u16p, _c_u16p,
                                       _c_i32p, _i32, _c_i32p, _i32, _i32, _i32, _i32, _i32,
-                                      _i32, _f64, _c_f64p, _c_f64p]
+                                      _i32, _f64, _c_vp, _c_f64p, _c_f64p]
         lib.oracle_max_threads.restype = _i32
+        lib.oracle_set_threads.argtypes = [_i32]
+        lib.oracle_set_threads.restype = None
         for f in ("oracle_cache_write_shuffled", "oracle_cache_write_latent",
                   "oracle_gather_shuffled", "oracle_paged_attn_gqa", "oracle_paged_attn_mla",
                   "oracle_merge", "oracle_dense_attn", "oracle_extend"):
@@ -96,6 +98,10 @@ class Oracle:
 
     def max_threads(self) -> int:
         return int(self.lib.oracle_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads of the C oracle's parallel loops from now on."""
+        self.lib.oracle_set_threads(int(n))
 
     # ---- caches ----------------------------------------------------------
     @staticmethod
@@ -248,8 +254,9 @@ class Oracle:
         return out, lse
 
     def extend(self, q, k_new, v_new, query_start_loc, k_cache, v_cache, block_table, ctx_lens,
-               B: int, scale: float, x: int = 8):
-        """Extend attention by its definition (no chunking)."""
+               B: int, scale: float, x: int = 8, row_mask: Optional[np.ndarray] = None):
+        """Extend attention by its definition (no chunking).  row_mask [Tn, Hq]
+        selects the (new token, head) rows to compute; the rest stay zero."""
         q, k_new, v_new = _u16(q), _u16(k_new), _u16(v_new)
         Tn, Hq, D = q.shape
         Hkv = k_new.shape[1]
@@ -257,8 +264,13 @@ class Oracle:
         cl = _i32a(ctx_lens)
         out = np.zeros((Tn, Hq, D), dtype=np.float64)
         lse = np.zeros((Tn, Hq), dtype=np.float64)
+        mask = None
+        if row_mask is not None:
+            mask = np.ascontiguousarray(row_mask, dtype=np.uint8)
+            assert mask.shape == (Tn, Hq)
         self.lib.oracle_extend(q, k_new, v_new, _i32a(query_start_loc), k_cache, v_cache, bt,
-                               bt.shape[1], cl, len(cl), Hq, Hkv, D, B, x, float(scale), out, lse)
+                               bt.shape[1], cl, len(cl), Hq, Hkv, D, B, x, float(scale),
+                               None if mask is None else mask.ctypes.data, out, lse)
         return out, lse
 
     def extend_chunked(self, q, k_new, v_new, query_start_loc, k_cache, v_cache, block_table,

@@ -306,11 +306,14 @@ void oracle_dense_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * Request r has ctx_lens[r] cached tokens (read through block_table from
  * the shuffled cache) and new tokens at query rows qsl[r] .. qsl[r+1]
  * whose K/V are k_new/v_new at the same rows.  New token i sees every
- * cached token and the new tokens 0..i. */
+ * cached token and the new tokens 0..i.  row_mask [Tn, Hq] (nullable)
+ * selects the (row, head) outputs to compute; the others are left as they
+ * are. */
 void oracle_extend(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                    const int32_t *qsl, const uint16_t *k_cache, const uint16_t *v_cache,
                    const int32_t *block_table, int max_blocks, const int32_t *ctx_lens, int S,
-                   int Hq, int Hkv, int D, int B, int x, double scale, double *out, double *lse)
+                   int Hq, int Hkv, int D, int B, int x, double scale, const uint8_t *row_mask,
+                   double *out, double *lse)
 {
     int group = Hq / Hkv;
     for (int r = 0; r < S; r++) {
@@ -320,6 +323,8 @@ void oracle_extend(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_n
             for (int h = 0; h < Hq; h++) {
                 int g = h / group;
                 int64_t qi = qsl[r] + i;
+                if (row_mask && !row_mask[qi * Hq + h])
+                    continue;
                 int64_t n = c + i + 1;
                 double *z = (double *)malloc(sizeof(double) * (size_t)n);
                 double *V = (double *)malloc(sizeof(double) * (size_t)n * D);
@@ -355,5 +360,17 @@ int oracle_max_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads the oracle's parallel loops use from now on (for timing it on one
+ * core); no effect on its results, which do not depend on the split. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
 #endif
 }

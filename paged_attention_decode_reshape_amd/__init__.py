@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     LAYOUT_STANDARD_KV,
     NOALLOC_SCRATCH_BYTES,
     PagedAttnError,
+    PreparedCall,
     WORKSPACE_COUNTER_BYTES,
     chunked_extend_attn,
     decode_partition_tokens,
@@ -35,6 +36,7 @@ from .ops import (  # noqa: F401
     paged_decode_attn_layout,
     paged_decode_attn_write,
     paged_decode_attn_write_noalloc,
+    prepare,
     reshape_and_cache,
     reshape_and_cache_fp8,
     reshape_and_cache_mla_fp8,

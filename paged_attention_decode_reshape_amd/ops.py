@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import threading
 from typing import Optional, Tuple
 
 import numpy as np
@@ -95,11 +96,17 @@ _SIGS = {
                              _vp], _i32),
 }
 
+# Entries that only compute on the host (sizes, plans, strings); every other
+# entry enqueues work on a stream.
+_HOST_ONLY = {"pa_status_string", "pa_decode_partition_tokens", "pa_decode_uses_balanced_split",
+              "pa_decode_workspace_size", "pa_mla_workspace_size", "pa_extend_workspace_size",
+              "pa_extend_chunk_tokens", "pa_mixed_batch_plan", "pa_mixed_batch_workspace_size"}
+
 _lib = None
+_tls = threading.local()  # .capture: the prepare() record in progress, if any
 
 
-def library() -> ctypes.CDLL:
-    """The loaded libpagedattn.so; raises if it has not been built."""
+def _load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -112,6 +119,81 @@ def library() -> ctypes.CDLL:
             f.restype = res
         _lib = lib
     return _lib
+
+
+class _Capture:
+    """Stands in for the library while prepare() runs a wrapper: host-only
+    entries run, the one enqueuing entry is recorded instead of called."""
+
+    def __init__(self, lib):
+        self.lib = lib
+        self.calls = []
+        self.keep = []  # objects the recorded pointers point into
+
+    def __getattr__(self, name):
+        if name in _HOST_ONLY:
+            return getattr(self.lib, name)
+        f = getattr(self.lib, name)
+
+        def record(*args):
+            self.calls.append((name, f, args))
+            return 0
+        return record
+
+
+def library():
+    """The loaded libpagedattn.so; raises if it has not been built."""
+    lib = _load()
+    cap = getattr(_tls, "capture", None)
+    return cap if cap is not None else lib
+
+
+def _keep(obj):
+    """Keep obj alive for as long as a prepared call that points into it."""
+    cap = getattr(_tls, "capture", None)
+    if cap is not None:
+        cap.keep.append(obj)
+    return obj
+
+
+class PreparedCall:
+    """One library call whose arguments were checked and marshalled once by
+    prepare(); calling it enqueues the same work again, on the same tensors
+    and the stream that was current when it was prepared, and returns what
+    the wrapper returned (e.g. the (out, lse) it writes)."""
+
+    def __init__(self, name, fn, args, keep, result):
+        self.name = name
+        self._fn = fn
+        self._args = tuple(None if a is None else t(a) for t, a in zip(fn.argtypes, args))
+        self._keep = keep
+        self.result = result
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise PagedAttnError(self.name[3:] if self.name.startswith("pa_") else self.name, st)
+        return self.result
+
+
+def prepare(wrapper, *args, **kwargs) -> PreparedCall:
+    """Run a wrapper of this module (e.g. paged_decode_attn_write) once for
+    its checks, sizing and marshalling, without enqueuing anything; returns a
+    PreparedCall that enqueues that call each time it is called.  Tensors the
+    caller passes must stay alive and keep their storage while the prepared
+    call is used; outputs and workspaces the wrapper allocates are kept by
+    the PreparedCall."""
+    cap = _Capture(_load())
+    _tls.capture = cap
+    try:
+        result = wrapper(*args, **kwargs)
+    finally:
+        _tls.capture = None
+    if len(cap.calls) != 1:
+        raise ValueError(f"prepare() needs a wrapper that makes exactly one enqueuing call, "
+                         f"got {len(cap.calls)}")
+    name, fn, cargs = cap.calls[0]
+    return PreparedCall(name, fn, cargs, cap.keep + [result], result)
 
 
 def _check(fn: str, status: int):
@@ -197,7 +279,7 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if nbytes == 0:
         return None
     if workspace is None:
-        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return _keep(torch.zeros(nbytes, dtype=torch.uint8, device=device))
     _gpu("workspace", workspace)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
@@ -721,8 +803,8 @@ def chunked_extend_attn(query: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
     _shape("v_new", v_new, (Tn, Hkv, D))
     if query_start_loc.numel() != S + 1:
         raise ValueError("query_start_loc needs num_seqs + 1 entries")
-    qsl_h = torch.as_tensor(query_start_loc_host, dtype=torch.int32).contiguous()
-    cl_h = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous()
+    qsl_h = _keep(torch.as_tensor(query_start_loc_host, dtype=torch.int32).contiguous())
+    cl_h = _keep(torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous())
     if qsl_h.device.type != "cpu" or cl_h.device.type != "cpu":
         raise ValueError("host copies must be on the CPU")
     if qsl_h.numel() != S + 1 or cl_h.numel() != S:
@@ -809,8 +891,8 @@ def mixed_batch_attn(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor
     _gpu("k_cache", k_cache, torch.bfloat16, 5)
     _gpu("v_cache", v_cache, torch.bfloat16, 5)
     _gpu("block_table", block_table, torch.int32, 2)
-    qsl_h = _host_i32(query_start_loc_host)
-    ctx_h = _host_i32(context_lens_host)
+    qsl_h = _keep(_host_i32(query_start_loc_host))
+    ctx_h = _keep(_host_i32(context_lens_host))
     R = ctx_h.shape[0]
     T, Hq, D = query.shape
     NB, Hkv, B = _shuffled_kv(k_cache, v_cache, D, 8)

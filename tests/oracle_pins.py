@@ -620,6 +620,16 @@ def pin_extend_vs_numpy(orc):
                                case.paging.seq_start, case.ctx_lens, case.new_lens, case.scale)
     _close(out, rout, 1e-12, "extend out")
     _close(lse, rlse, 1e-12, "extend lse")
+    # a row selection computes exactly the selected rows and leaves the rest zero
+    mask = np.zeros(lse.shape, dtype=np.uint8)
+    mask[::3, 1] = 1
+    mask[-1, :] = 1
+    mo, ml = orc.extend(qb, kn, vn, case.query_start_loc, kc, vc, case.paging.block_table,
+                        case.ctx_lens, case.B, case.scale, row_mask=mask)
+    sel = mask.astype(bool)
+    _close(mo[sel], rout[sel], 1e-12, "masked extend out")
+    _close(ml[sel], rlse[sel], 1e-12, "masked extend lse")
+    assert not mo[~sel].any() and not ml[~sel].any()
     # the chunked recipe equals the definition for any chunk length
     for chunk in (16, 64, 160, 4096):
         cout, clse = orc.extend_chunked(qb, kn, vn, case.query_start_loc, kc, vc,

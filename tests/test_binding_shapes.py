@@ -339,3 +339,25 @@ def test_merge_shapes_and_aliasing(rec):
     with pytest.raises(ValueError, match="overlap"):
         ops.merge_attn_states(po, pl, so, sl, out=over, out_dtype=bf16)
     assert len(rec.launches) == 2
+
+
+def test_prepare_records_one_call_and_checks_first(monkeypatch):
+    """prepare() runs the wrapper's checks and marshalling against the real
+    library without enqueuing: exactly one entry is recorded, host-only
+    queries run, a shape mismatch raises at prepare time."""
+    monkeypatch.setattr(ops, "_gpu", lambda name, t, dtype=None, ndim=None: t)
+    monkeypatch.setattr(ops, "_stream", lambda t: 0)
+    a = decode_args(partition_tokens=64, max_context_len=200)
+    call = ops.prepare(ops.paged_decode_attn, **a)
+    assert isinstance(call, ops.PreparedCall) and call.name == "pa_paged_decode_attn"
+    out, lse = call.result
+    assert tuple(out.shape) == (S, Hq, D) and tuple(lse.shape) == (S, Hq)
+    # the split call's workspace (counter region + partials) is held by the call
+    nbytes = ops.decode_workspace_size(S, Hq, Hkv, D, 200, 64)
+    assert nbytes > ops.WORKSPACE_COUNTER_BYTES
+    assert any(isinstance(k, torch.Tensor) and k.numel() == nbytes for k in call._keep)
+    with pytest.raises(ValueError):
+        ops.prepare(ops.paged_decode_attn, **decode_args(block_table=z(1, MAXB, dtype=i32)))
+    with pytest.raises(ValueError, match="exactly one"):
+        ops.prepare(lambda: None)
+    assert getattr(ops._tls, "capture", None) is None

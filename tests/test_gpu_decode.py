@@ -267,15 +267,20 @@ def test_decode_qwen3_full(orc):
 
 def test_decode_long_context_sampled(orc):
     """8 requests up to 131072 tokens, 2048-token partitions, K outliers:
-    sampled (seq, head) rows vs the oracle, plus partition-size invariance."""
+    sampled (seq, head) rows (every kv head of every sequence) vs the oracle,
+    plus partition-size invariance."""
     case = W.long_context_decode()
     say(f"decode long context, lens {case.context_lens.tolist()}")
     g = GpuGQA(case)
     out, lse = g.decode()
     rng = np.random.default_rng(31)
     mask = np.zeros((case.S, case.Hq), dtype=np.uint8)
+    grp = case.Hq // case.Hkv
     for s in range(case.S):
-        mask[s, rng.choice(case.Hq, size=3, replace=False)] = 1
+        # one q head of every kv head's group, plus one more anywhere
+        for kv in range(case.Hkv):
+            mask[s, kv * grp + int(rng.integers(grp))] = 1
+        mask[s, int(rng.integers(case.Hq))] = 1
     ref_out, ref_lse = oracle_gqa(orc, case, row_mask=mask)
     rows = np.nonzero(mask)
     assert_attn_close(out, lse, ref_out, ref_lse, rows=rows, what="long context sampled")
