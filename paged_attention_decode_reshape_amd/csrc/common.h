@@ -57,6 +57,15 @@ __device__ __forceinline__ float load_coherent(const float *p) {
 // acknowledged); also a compiler barrier for memory.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for reusing LDS: every wave's LDS accesses are done when
+// any wave passes it.  Unlike __syncthreads() (whose workgroup-scope release
+// also waits for the wave's global stores to be acknowledged) it leaves
+// global stores in flight; a release that publishes them still has to wait
+// for them itself.  Called by every wave of the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // A zero the compiler cannot see through.  Adding it to an address keeps a
 // loop-invariant scalar load inside the loop (re-read from the scalar cache
 // each iteration) instead of being hoisted and spilled.

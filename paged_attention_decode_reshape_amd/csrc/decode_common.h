@@ -109,15 +109,15 @@ __device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32
 // in index order, so the result does not depend on which workgroup merges.
 // Partials are read with device-coherent 16-byte loads (they were written by
 // other workgroups of the same kernel), addressed from the first row so the
-// offsets fit 32 bits.
-template <int D, int DPT, int BATCH>
+// offsets fit 32 bits.  NT: threads of the calling workgroup.
+template <int D, int DPT, int BATCH, int NT>
 __device__ __forceinline__ void merge_partition_rows(const float *part_out, const float *part_lse,
                                                      int max_parts, uint16_t *outp, float *lse,
                                                      size_t row0, int nrows, int nparts) {
     static_assert(DPT % 4 == 0, "16-byte partial loads");
     const auto rs = coherent_rsrc(part_out + row0 * max_parts * D,
                                   (uint32_t)nrows * max_parts * D * 4);
-    for (int it = threadIdx.x; it < nrows * (D / DPT); it += blockDim.x) {
+    for (int it = threadIdx.x; it < nrows * (D / DPT); it += NT) {
         const int h = it / (D / DPT), d0 = (it % (D / DPT)) * DPT;
         const size_t row = row0 + h;
         const float *pl = part_lse + row * max_parts;

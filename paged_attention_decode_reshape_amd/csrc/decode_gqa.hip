@@ -884,7 +884,7 @@ __device__ __forceinline__ void merge_waves(WaveMergeLDS<D, G, NWV> &sm, int Ga,
         for (int jj = 0; jj < DV; jj++) sm.acc[wave][h][lane + 64 * jj] = acc[h][jj];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < Ga * (D / 4); idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < Ga * (D / 4); idx += NWV * 64) {
         const int h = idx / (D / 4), d = 4 * (idx % (D / 4));
         float M = kNegInf;
 #pragma unroll
@@ -1249,7 +1249,7 @@ __device__ __forceinline__ void merge_waves_rh(WaveMergeLDS<D, G, NWV> &sm, int 
 #pragma unroll
         for (int jj = 0; jj < DV; jj++) sm.acc[wave][h][lane + 64 * jj] = acc[h][jj];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < Ga * (D / 4); idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < Ga * (D / 4); idx += NWV * 64) {
         const int h = idx / (D / 4), d = 4 * (idx % (D / 4));
         float M = kNegInf;
 #pragma unroll
@@ -1465,8 +1465,8 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     });
     if (nparts == 1) return;
     if (!count_finished(p.counters + (size_t)s * p.Hkv + g, nparts)) return;
-    merge_partition_rows<D, 4, 16>(p.part_out, p.part_lse, p.max_parts, out, p.lse, row0, Ga,
-                                   nparts);
+    merge_partition_rows<D, 4, 16, kWaves * 64>(p.part_out, p.part_lse, p.max_parts, out, p.lse,
+                                                 row0, Ga, nparts);
 }
 
 // Balanced split.  The grid has NW workgroups (as many as are resident at
@@ -1500,12 +1500,12 @@ __device__ __forceinline__ int wave_prefix_sum_i(int v) {
 // Merge of a unit's piece partials (slots P_u .. P_u + nparts - 1, in that
 // order) into rows row0 .. row0 + Ga - 1: thread -> (head, 4 dims), 16
 // partials per round trip.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void merge_unit_partials(const DecodeParams &p, size_t row0, int Ga,
                                                     int P_u, int nparts, int NW) {
     constexpr int kBatch = 16;
     const auto rs = coherent_rsrc(p.part_out, (uint32_t)NW * Ga * D * 4);
-    for (int it = threadIdx.x; it < Ga * (D / 4); it += blockDim.x) {
+    for (int it = threadIdx.x; it < Ga * (D / 4); it += NT) {
         const int h = it / (D / 4), d0 = (it % (D / 4)) * 4;
         float M = kNegInf, den = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
         for (int b = 0; b < nparts; b += kBatch) {
@@ -1643,7 +1643,7 @@ __global__ __launch_bounds__(NWV * 64, 8 / NWV) void paged_decode_balanced_kerne
             }
         });
         if (n > 1 && count_finished(p.counters + (size_t)s * Hkv + g, n))
-            merge_unit_partials<D>(p, row0, Ga, P_u, n, NW);
+            merge_unit_partials<D, NWV * 64>(p, row0, Ga, P_u, n, NW);
         if (split) break;  // one piece per workgroup
     }
 }

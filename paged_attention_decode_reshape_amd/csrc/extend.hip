@@ -598,7 +598,7 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(ExtendParams p) {
     const int64_t rows = (int64_t)(q1 - q0) * p.Hq;
     const int64_t first = (int64_t)blockIdx.x * 8;
     if (first >= rows) return;
-    merge_partition_rows<kD, 4, kExtendMaxPieces>(
+    merge_partition_rows<kD, 4, kExtendMaxPieces, 256>(
         p.part_out, p.part_lse, p.max_pieces, reinterpret_cast<uint16_t *>(p.out), p.lse,
         (size_t)q0 * p.Hq + first, (int)min<int64_t>(8, rows - first), npieces);
 }

@@ -228,7 +228,7 @@ __device__ __forceinline__ void mla_attend(const MLAParams &p, MLASmem &sm, int 
     for (int w0 = start; w0 < end; w0 += kMaxPartition) {
         const int wend = min(w0 + kMaxPartition, end);
         __syncthreads();  // the previous window's rows and tile are no longer read
-        for (int i = threadIdx.x; i < wend - w0; i += blockDim.x) {
+        for (int i = threadIdx.x; i < wend - w0; i += kWaves * 64) {
             const int t = w0 + i;
             const int b = p.block_table[(size_t)s * p.max_blocks + t / p.B];
             sm.row[i] = b >= 0 && (int64_t)b < p.num_blocks ? b * p.B + t % p.B : -1;
@@ -423,7 +423,7 @@ __device__ __forceinline__ bool mla_count(const MLAParams &p, int s, int nparts)
 
 __device__ __forceinline__ void mla_write_empty(const MLAParams &p, int s) {
     uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-    for (int idx = threadIdx.x; idx < p.Hq * kDv; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < p.Hq * kDv; idx += kWaves * 64) {
         out[((size_t)s * p.Hq + idx / kDv) * kDv + idx % kDv] = 0;
         if (idx % kDv == 0 && p.lse) p.lse[(size_t)s * p.Hq + idx / kDv] = kNegInf;
     }
@@ -644,21 +644,28 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
         lsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
     }
-    __syncthreads();  // every wave is done with its tile region
+    lds_barrier();  // every wave is done with its tile region
     if (g == 0) {
         sm.m[wave][m] = mh;
         sm.l[wave][m] = lsum;
     }
     uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    // partials of all heads through one descriptor made outside the loops
+    // (a per-head descriptor is per-lane to the compiler, which then wraps
+    // each store in a loop over distinct descriptors)
+    const auto prs = coherent_rsrc(po, whole ? 0u : (uint32_t)(((p.Hq - 1) * hs + kDv) * 4));
     for (int pass = 0; pass < kDv / kMMergeDims; pass++) {
         constexpr int kTilesPerPass = kMMergeDims / 16;
 #pragma unroll
         for (int n = 0; n < kTilesPerPass; n++)
 #pragma unroll
             for (int i = 0; i < 4; i++) sm.o[wave][4 * g + i][16 * n + m] = o[kTilesPerPass * pass + n][i];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += blockDim.x) {
-            const int h = idx / (kMMergeDims / 4), d = 4 * (idx % (kMMergeDims / 4));
+        lds_barrier();
+        // a wave's 64 consecutive indices share one head (the bound is a
+        // multiple of 64)
+        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += kWaves * 64) {
+            const int h = __builtin_amdgcn_readfirstlane(idx / (kMMergeDims / 4));
+            const int d = 4 * (idx % (kMMergeDims / 4));
             float M = kNegInf;
 #pragma unroll
             for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
@@ -687,13 +694,14 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
             } else {
                 // vector 64 i + c holds dims 8 c + 4 i .. + 3
                 const int vec = 64 * ((dim & 7) >> 2) + (dim >> 3);
-                const auto rs = coherent_rsrc(po + h * hs, kDv * 4);
-                store_coherent4(rs, (uint32_t)vec * 16, acc[0] * inv, acc[1] * inv, acc[2] * inv,
-                                acc[3] * inv);
+                store_coherent4(prs, (uint32_t)(h * hs * 4 + vec * 16), acc[0] * inv,
+                                acc[1] * inv, acc[2] * inv, acc[3] * inv);
                 if (dim == 0) store_coherent(&pl[h * lhs], L);
             }
         }
-        __syncthreads();  // the pass's LDS is read before the next one is written
+        // the pass's LDS is read before the next one is written (its partial
+        // stores stay in flight: the count that publishes them waits for them)
+        lds_barrier();
     }
 }
 
