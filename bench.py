@@ -123,7 +123,7 @@ def parse():
                          "per-tensor scales (amax / 448), shuffled layout with x = 16")
     ap.add_argument("--mla-engine", default="valu", choices=["valu", "mfma"],
                     help="MLA decode: the VALU kernels (pa_mla_decode_attn*) or the matrix-core "
-                         "one (pa_mla_decode_attn_mfma)")
+                         "ones (pa_mla_decode_attn_mfma, pa_mla_decode_attn_fp8_mfma)")
     ap.add_argument("--kv-layout", default="shuffled", choices=["shuffled", "standard"],
                     help="GQA decode cache layout: the pages' shuffled one, or the standard "
                          "[num_blocks, block_size, kv_heads, head_dim] it replaces (same "
@@ -641,11 +641,15 @@ def bench_mla(args, case, label):
 
     fused = not args.separate_cache_write
     mfma = args.mla_engine == "mfma"
-    if mfma and f8:
-        raise SystemExit("the matrix-core MLA engine reads bf16 latents only")
 
     def decode_call(i):
-        if mfma:
+        if mfma and f8:
+            pa.mla_decode_attn_fp8_mfma(q, caches[i % pools], bt, cl, case.scale, max_ctx, kvs,
+                                        v_dim=case.Dv, partition_tokens=P,
+                                        new_latent=new_lat if fused else None,
+                                        slot_mapping=new_slots if fused else None, out=out,
+                                        lse=lse, workspace=ws)
+        elif mfma:
             pa.mla_decode_attn_mfma(q, caches[i % pools], bt, cl, case.scale, max_ctx,
                                     v_dim=case.Dv, partition_tokens=P,
                                     new_latent=new_lat if fused else None,
@@ -698,7 +702,7 @@ def bench_mla(args, case, label):
             "pools": pools, "cache_write": "fused" if fused else "separate launch",
             "kv_scale": kvs if f8 else None,
             "kernel": ("mla_decode_balanced_kernel" if balanced else "mla_decode_kernel")
-                      + ("<bf16, matrix cores>" if mfma else "")}
+                      + (f"<{'fp8' if f8 else 'bf16'}, matrix cores>" if mfma else "")}
 
 
 def cpu_baseline_mla(case, seconds, kv_scale=None):
@@ -1044,7 +1048,9 @@ def main():
             line["roofline"] = {"bound": "hbm", "kernel": r["kernel"], "achieved": r["hbm_gbps"],
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-                                "traffic": measured_traffic(args.config + "_mfma"),
+                                "traffic": measured_traffic(
+                                    args.config + ("_fp8" if args.kv_dtype == "fp8" else "")
+                                    + "_mfma"),
                                 "algo_bytes_per_launch": r["algo_bytes"],
                                 "avg_launch_ms": r["decode_ms"],
                                 "launch_stats": r["launch_stats"],

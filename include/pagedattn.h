@@ -386,7 +386,8 @@ pa_status pa_mla_decode_attn_write(void *out, float *lse, const void *query,
  * tokens x 512) run as bf16 matrix products with fp32 accumulation, the
  * weights as bf16 hi + lo parts; the result agrees with pa_mla_decode_attn
  * to rounding.  Arguments, workspace (pa_mla_workspace_size), support and
- * errors as for pa_mla_decode_attn; bf16 latents only.
+ * errors as for pa_mla_decode_attn; bf16 latents (FP8 latents:
+ * pa_mla_decode_attn_fp8_mfma).
  */
 pa_status pa_mla_decode_attn_mfma(void *out, float *lse, const void *query,
                                   const void *new_latent, const int64_t *slot_mapping,
@@ -430,6 +431,24 @@ pa_status pa_mla_decode_attn_fp8(void *out, float *lse, const void *query, const
                                  int32_t v_dim, int32_t block_size, int64_t num_blocks,
                                  float scale, float kv_scale, int32_t partition_tokens,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_mla_decode_attn_fp8 on the matrix cores: the operation and arguments of
+ * pa_mla_decode_attn_fp8 (FP8 latent cache, kv_scale, optional fused write),
+ * computed as pa_mla_decode_attn_mfma computes it, the codes widened exactly
+ * to bf16 on chip and kv_scale folded into the softmax scale and the output.
+ * Workspace (pa_mla_workspace_size), support and errors as for
+ * pa_mla_decode_attn_fp8.
+ */
+pa_status pa_mla_decode_attn_fp8_mfma(void *out, float *lse, const void *query,
+                                      const void *new_latent, const int64_t *slot_mapping,
+                                      void *kv_cache, const int32_t *block_table,
+                                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t latent_dim, int32_t v_dim,
+                                      int32_t block_size, int64_t num_blocks, float scale,
+                                      float kv_scale, int32_t partition_tokens, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 /*
  * Log-sum-exp merge of two partial attention results (merge_attn_states;

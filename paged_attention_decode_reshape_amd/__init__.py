@@ -33,6 +33,7 @@ from .ops import (  # noqa: F401
     paged_decode_attn,
     paged_decode_attn_fp8,
     mla_decode_attn_fp8,
+    mla_decode_attn_fp8_mfma,
     paged_decode_attn_layout,
     paged_decode_attn_write,
     paged_decode_attn_write_noalloc,

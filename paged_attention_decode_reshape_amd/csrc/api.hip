@@ -535,6 +535,26 @@ pa_status pa_mla_decode_attn_fp8(void *out, float *lse, const void *query, const
                     partition_tokens, workspace, workspace_bytes, stream);
 }
 
+pa_status pa_mla_decode_attn_fp8_mfma(void *out, float *lse, const void *query,
+                                      const void *new_latent, const int64_t *slot_mapping,
+                                      void *kv_cache, const int32_t *block_table,
+                                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t latent_dim, int32_t v_dim,
+                                      int32_t block_size, int64_t num_blocks, float scale,
+                                      float kv_scale, int32_t partition_tokens, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    if (!valid_scale(kv_scale)) return PA_ERR_INVALID_ARG;
+    const int given = (new_latent != nullptr) + (slot_mapping != nullptr);
+    if (given == 1) return PA_ERR_INVALID_ARG;
+    if (given == 2 && (!aligned(new_latent, 16) || !aligned(slot_mapping, 8)))
+        return PA_ERR_INVALID_ARG;
+    return mla_impl(true, true, kv_scale, out, lse, query, new_latent, slot_mapping, kv_cache,
+                    block_table, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                    num_q_heads, latent_dim, v_dim, block_size, num_blocks, scale,
+                    partition_tokens, workspace, workspace_bytes, stream);
+}
+
 pa_status pa_reshape_and_cache_mla_fp8(const void *latent, void *kv_cache,
                                        const int64_t *slot_mapping, int64_t num_tokens,
                                        int32_t latent_dim, int32_t block_size, int64_t num_blocks,

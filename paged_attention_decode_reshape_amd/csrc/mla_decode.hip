@@ -454,6 +454,11 @@ __device__ __forceinline__ void mla_write_empty(const MLAParams &p, int s) {
 //         in registers.
 // Online softmax with the lazy reference of the VALU engine.  Query heads
 // beyond num_q_heads are zero rows whose outputs are not written.
+// FP8 latents: a row is 576 codes (36 vectors of 16); lane (g, m) gathers
+// vectors 4 j + g, j < 9, into blocks 9 + j, the second half of the wave's
+// region, and after the gather lands the codes are widened in place into the
+// bf16 blocks above (exact: every E4M3 value is a bf16), so QK and P.V run
+// unchanged; the cache scale folds into the softmax scale and the output.
 // ---------------------------------------------------------------------------
 constexpr int kMTok = 16;              // tokens per wave per round
 constexpr int kMRound = kWaves * kMTok;  // 64 tokens per round
@@ -502,12 +507,13 @@ __device__ __forceinline__ int64_t mla_row(const MLAParams &p, int s, int t, int
 // merge of the 4 waves and the output: out rows (whole) or partials in the
 // layout merge_mla_partials reads (head h at po + h * hs, 16-byte vector
 // 64 i + c holding dims 8 c + 4 i .. + 3) with LSEs at pl + h * lhs.
+template <bool F8>
 __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &sm, int s,
                                                int start, int end, bool whole, float *po,
                                                size_t hs, float *pl, size_t lhs) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
-    const float sl2 = p.scale * kLog2e;
+    const float sl2 = p.scale * kLog2e * (F8 ? p.kv_scale : 1.f);
     const char *kv = reinterpret_cast<const char *>(p.kv_cache);
     uint4 *region = &sm.tile[wave][0][0];
 
@@ -542,10 +548,20 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         if (valid != 0) {
             // gather: block j, lane (g, m) <- vector 4 j + g of token m's row
             if (row >= 0) {
-                const char *src = kv + (size_t)row * (kDl * 2) + 16 * g;
+                if constexpr (F8) {
+                    const char *src = kv + (size_t)row * kDl + 16 * g;
 #pragma unroll
-                for (int j = 0; j < kMSteps; j++)
-                    __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(region + 64 * j), 16, 0, 0);
+                    for (int j = 0; j < kMSteps / 2; j++)
+                        __builtin_amdgcn_global_load_lds(src + 64 * j,
+                                                         (lds_void_t *)(region + 64 * (kMSteps / 2 + j)),
+                                                         16, 0, 0);
+                } else {
+                    const char *src = kv + (size_t)row * (kDl * 2) + 16 * g;
+#pragma unroll
+                    for (int j = 0; j < kMSteps; j++)
+                        __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(region + 64 * j),
+                                                         16, 0, 0);
+                }
             }
         }
         // the next round's row (in flight with the gather), and the queries
@@ -563,6 +579,30 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         // entry, which may not have been requested at all)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         asm volatile("" ::: "memory");
+        if constexpr (F8) {
+            // codes of vector 4 jc + g (dims 64 jc + 16 g .. + 15) of token m
+            // -> bf16 vectors 8 jc + 2 g and + 1, i.e. block 2 jc + g / 2, slots
+            // 16 (2 (g % 2)) + m and 16 (2 (g % 2) + 1) + m; tokens not
+            // gathered this round become zero rows.  Code block 9 + jc is read
+            // before bf16 blocks 2 jc and 2 jc + 1 are written, and no code
+            // block still to be read lies below 2 jc + 2.
+            const bool ok = (valid >> m) & 1u;
+            const int gp = 2 * (g & 1);
+#pragma unroll
+            for (int jc = 0; jc < kMSteps / 2; jc++) {
+                const uint4 codes = region[64 * (kMSteps / 2 + jc) + lane];
+                uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+                if (ok) {
+                    fp8x4_to_bf16x2(codes.x, lo.x, lo.y);
+                    fp8x4_to_bf16x2(codes.y, lo.z, lo.w);
+                    fp8x4_to_bf16x2(codes.z, hi.x, hi.y);
+                    fp8x4_to_bf16x2(codes.w, hi.z, hi.w);
+                }
+                const int j = 2 * jc + (g >> 1);
+                region[64 * j + 16 * gp + m] = lo;
+                region[64 * j + 16 * (gp + 1) + m] = hi;
+            }
+        }
 
         // QK: two accumulator chains over the 18 steps
         f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -637,6 +677,12 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         row = next_row;
     }
 
+    if constexpr (F8) {  // the value rows were summed as unscaled codes
+#pragma unroll
+        for (int n = 0; n < kMTiles; n++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) o[n][i] *= p.kv_scale;
+    }
     // merge of the 4 waves: weight sums of head m over the 4 rows of lanes
     {
         auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
@@ -718,7 +764,6 @@ __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW],
 // Fixed partitions: one workgroup per (partition, sequence).
 template <bool F8, bool MFMA>
 __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
-    static_assert(!(F8 && MFMA), "the matrix-core engine reads bf16 latents");
     const int part = blockIdx.x / p.S;
     const int s = blockIdx.x - part * p.S;
     const int P = p.partition;
@@ -741,7 +786,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     float *po = nparts == 1 ? nullptr : p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
     float *pl = nparts == 1 ? nullptr : p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
     if constexpr (MFMA) {
-        mla_mfma_piece(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv, pl,
+        mla_mfma_piece<F8>(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv, pl,
                        p.max_parts);
     } else {
         uint32_t qreg[kHPW][kSlices];
@@ -780,7 +825,6 @@ __device__ __forceinline__ int wave_prefix_sum_i(int v) {
 // [NW, Hq, Dv] and [NW, Hq]; the last to finish merges them in order.
 template <bool F8, bool MFMA>
 __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p) {
-    static_assert(!(F8 && MFMA), "the matrix-core engine reads bf16 latents");
     const int NW = gridDim.x, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
     __shared__ std::conditional_t<MFMA, MLAMfmaSmem, MLASmem> sm;
@@ -845,7 +889,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
         // the piece holding the last token writes the new token first
         if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token<F8>(p, s);
         if constexpr (MFMA) {
-            mla_mfma_piece(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
+            mla_mfma_piece<F8>(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
                            p.part_out + (size_t)v * p.Hq * kDv, kDv, p.part_lse + (size_t)v * p.Hq,
                            1);
         } else {
@@ -895,7 +939,7 @@ hipError_t launch_mla(const MLAParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_mla_decode(const MLAParams &p, hipStream_t stream) {
-    if (p.mfma) return p.fp8 ? hipErrorInvalidValue : launch_mla<false, true>(p, stream);
+    if (p.mfma) return p.fp8 ? launch_mla<true, true>(p, stream) : launch_mla<false, true>(p, stream);
     return p.fp8 ? launch_mla<true, false>(p, stream) : launch_mla<false, false>(p, stream);
 }
 

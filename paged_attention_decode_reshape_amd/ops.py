@@ -89,6 +89,9 @@ _SIGS = {
     "pa_reshape_and_cache_mla_fp8": ([_vp, _vp, _vp, _i64, _i32, _i32, _i64, _f32, _vp], _i32),
     "pa_mla_decode_attn_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i64, _f32, _f32, _i32, _vp, _sz, _vp], _i32),
+    "pa_mla_decode_attn_fp8_mfma": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _i64, _f32, _f32, _i32, _vp, _sz,
+                                     _vp], _i32),
     "pa_mixed_batch_plan": ([_i32, _vp, _vp, _vp, _vp], _i32),
     "pa_mixed_batch_workspace_size": ([_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_mixed_batch_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -1065,6 +1068,28 @@ def mla_decode_attn_fp8(query: torch.Tensor, kv_cache: torch.Tensor, block_table
                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Absorbed MLA decode over an FP8 latent cache (rows = code * kv_scale), with
     the fused quantised write when new_latent and slot_mapping are given."""
+    return _mla_fp8("pa_mla_decode_attn_fp8", query, kv_cache, block_table, context_lens, scale,
+                    max_context_len, kv_scale, v_dim, partition_tokens, new_latent, slot_mapping,
+                    out, lse, return_lse, workspace)
+
+
+def mla_decode_attn_fp8_mfma(query: torch.Tensor, kv_cache: torch.Tensor,
+                             block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                             max_context_len: int, kv_scale: float, v_dim: int = 512,
+                             partition_tokens: int = 0, new_latent: Optional[torch.Tensor] = None,
+                             slot_mapping: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                             workspace: Optional[torch.Tensor] = None
+                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """mla_decode_attn_fp8 on the matrix cores (codes widened to bf16 on chip)."""
+    return _mla_fp8("pa_mla_decode_attn_fp8_mfma", query, kv_cache, block_table, context_lens,
+                    scale, max_context_len, kv_scale, v_dim, partition_tokens, new_latent,
+                    slot_mapping, out, lse, return_lse, workspace)
+
+
+def _mla_fp8(fn, query, kv_cache, block_table, context_lens, scale, max_context_len, kv_scale,
+             v_dim, partition_tokens, new_latent, slot_mapping, out, lse, return_lse, workspace):
     lib = library()
     _gpu("query", query, torch.bfloat16, 3)
     _gpu("kv_cache", kv_cache, torch.uint8, 3)
@@ -1093,11 +1118,10 @@ def mla_decode_attn_fp8(query: torch.Tensor, kv_cache: torch.Tensor, block_table
         _shape("lse", lse, (S, Hq))
     nbytes = mla_workspace_size(S, Hq, v_dim, max_context_len, partition_tokens)
     ws = _workspace(nbytes, query.device, workspace)
-    st = lib.pa_mla_decode_attn_fp8(out.data_ptr(), _ptr(lse), query.data_ptr(), _ptr(new_latent),
-                                    _ptr(slot_mapping), kv_cache.data_ptr(),
-                                    block_table.data_ptr(), block_table.shape[1],
-                                    context_lens.data_ptr(), int(max_context_len), S, Hq, Dl,
-                                    v_dim, B, NB, float(scale), float(kv_scale),
-                                    int(partition_tokens), _ptr(ws), nbytes, _stream(query))
-    _check("mla_decode_attn_fp8", st)
+    st = getattr(lib, fn)(out.data_ptr(), _ptr(lse), query.data_ptr(), _ptr(new_latent),
+                          _ptr(slot_mapping), kv_cache.data_ptr(), block_table.data_ptr(),
+                          block_table.shape[1], context_lens.data_ptr(), int(max_context_len), S,
+                          Hq, Dl, v_dim, B, NB, float(scale), float(kv_scale),
+                          int(partition_tokens), _ptr(ws), nbytes, _stream(query))
+    _check(fn[3:], st)
     return out, lse

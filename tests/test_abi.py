@@ -339,6 +339,13 @@ def test_mla_fp8_entry_validation():
     assert d(ks=-1.0) == INVALID and d(ks=float("inf")) == INVALID
     assert d(Dv=448) == UNSUPPORTED
     assert d(P=-2) == WS_SMALL
+    m = lambda nl=None, sm=None, ks=0.01, Dv=512, P=-1: lib.pa_mla_decode_attn_fp8_mfma(
+        FAKE, None, FAKE, nl, sm, FAKE, FAKE, 8, FAKE, 100, 4, 16, 576, Dv, 16, 64, 0.07, ks, P,
+        None, 0, None)
+    assert m(nl=FAKE) == INVALID and m(sm=FAKE) == INVALID
+    assert m(ks=0.0) == INVALID and m(ks=float("nan")) == INVALID
+    assert m(Dv=448) == UNSUPPORTED
+    assert m(P=-2) == WS_SMALL
 
 
 def test_noalloc_decode_validation():

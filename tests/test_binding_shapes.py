@@ -210,13 +210,14 @@ def test_mla_write(rec, bad):
         assert rec.launches == ["pa_mla_decode_attn_write"]
 
 
-def test_mla_fp8(rec):
+@pytest.mark.parametrize("fn", ["mla_decode_attn_fp8", "mla_decode_attn_fp8_mfma"])
+def test_mla_fp8(rec, fn):
     a = mla_args(kv_cache=z(NB, 64, 576, dtype=u8), kv_scale=0.5)
-    ops.mla_decode_attn_fp8(**a)
-    assert rec.launches == ["pa_mla_decode_attn_fp8"]
+    getattr(ops, fn)(**a)
+    assert rec.launches == ["pa_" + fn]
     a["block_table"] = z(S - 1, MAXB, dtype=i32)
     with pytest.raises(ValueError):
-        ops.mla_decode_attn_fp8(**a)
+        getattr(ops, fn)(**a)
     assert len(rec.launches) == 1
 
 

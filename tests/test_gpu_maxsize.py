@@ -92,13 +92,14 @@ def test_extend_max_context(orc):
     assert_attn_close(out, lse, ref_out, ref_lse, what="extend max ctx")
 
 
-def test_mla_fp8_max_context():
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
+def test_mla_fp8_max_context(engine):
     """MLA decode over an FP8 latent cache at 2^20 tokens (row offsets past
-    2^29 bytes) against the FP8 oracle."""
+    2^29 bytes) against the FP8 oracle, on either engine."""
     from oracle import fp8 as OF
     case = W.mla_decode_cases("max_mla8", 703, S=2, lens_range=None, lens=[MAX_CTX, 77], Hq=16,
                               Dl=576, Dv=512, block_sizes=(64,), scale=1.0 / 192 ** 0.5)[64]
-    say("mla fp8 decode at 2^20 tokens")
+    say(f"mla fp8 decode at 2^20 tokens, {engine} engine")
     dev = device()
     pg = case.paging
     kvs = float(np.float32(case.latent.float().abs().max().item() / 448.0))
@@ -108,11 +109,12 @@ def test_mla_fp8_max_context():
     q = case.query.to(dev)
     bt = torch.from_numpy(pg.block_table).to(dev)
     cl = torch.from_numpy(pg.lens).to(dev)
-    out, lse = pa.mla_decode_attn_fp8(q, kv, bt, cl, case.scale, MAX_CTX, kvs, v_dim=512)
+    fn = pa.mla_decode_attn_fp8_mfma if engine == "mfma" else pa.mla_decode_attn_fp8
+    out, lse = fn(q, kv, bt, cl, case.scale, MAX_CTX, kvs, v_dim=512)
     torch.cuda.synchronize()
     okv = np.full((pg.num_blocks, case.B, case.Dl), 0x7F, dtype=np.uint8)
     OF.cache_write_latent(W.bf16_bits(case.latent), pg.slot_mapping, okv, kvs)
     assert np.array_equal(kv.cpu().numpy(), okv)
     ref_out, ref_lse = OF.paged_decode_mla(W.bf16_bits(case.query), okv, pg.block_table,
                                            case.context_lens, case.Dv, case.scale, kvs)
-    assert_attn_close(out, lse, ref_out, ref_lse, what="mla fp8 max ctx")
+    assert_attn_close(out, lse, ref_out, ref_lse, what=f"mla fp8 max ctx {engine}")

@@ -1,8 +1,9 @@
 """GPU parity of absorbed MLA decode over an FP8 (E4M3) latent cache against
 the oracle (oracle/fp8.py): the quantising latent write bit for bit, decode
-to the usual tolerance at block sizes 1, 64 and 5 and every split, the
-fused write + decode equal to the write followed by decode.  Calls go
-through the C ABI."""
+on the vector ALUs (pa_mla_decode_attn_fp8) and on the matrix cores
+(pa_mla_decode_attn_fp8_mfma) to the usual tolerance at block sizes 1, 64
+and 5 and every split, the fused write + decode equal to the write followed
+by decode.  Calls go through the C ABI."""
 import math
 
 import numpy as np
@@ -18,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 SCALE = 1.0 / math.sqrt(192.0)
 KVS = 0.0123  # not a power of two: the products round
+ENGINES = {"valu": pa.mla_decode_attn_fp8, "mfma": pa.mla_decode_attn_fp8_mfma}
 LENS = [1, 31, 32, 33, 0, 100, 257, 700]
 
 
@@ -51,10 +53,9 @@ class GpuMLAFp8:
                               pg.slot_mapping if slots is None else slots, kv, self.kvs)
         return kv
 
-    def decode(self, partition, **kw):
-        return pa.mla_decode_attn_fp8(self.q, self.kv, self.bt, self.cl, self.case.scale,
-                                      self.max_ctx, self.kvs, v_dim=self.case.Dv,
-                                      partition_tokens=partition, **kw)
+    def decode(self, partition, engine="valu", **kw):
+        return ENGINES[engine](self.q, self.kv, self.bt, self.cl, self.case.scale, self.max_ctx,
+                               self.kvs, v_dim=self.case.Dv, partition_tokens=partition, **kw)
 
     def oracle(self, kv=None, seqs=None):
         c = self.case
@@ -82,25 +83,28 @@ def test_mla_fp8_cache_write_bitexact():
     assert np.array_equal(g.kv.cpu().numpy(), g.oracle_cache())
 
 
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
 @pytest.mark.parametrize("Hq", [16, 3])
 @pytest.mark.parametrize("partition", [-1, 64, 0, -2])
-def test_mla_fp8_small(Hq, partition):
+def test_mla_fp8_small(Hq, partition, engine):
     cases = halved(W.mla_decode_cases("mla8", 431 + Hq, S=len(LENS), lens_range=None, lens=LENS,
                                       Hq=Hq, Dl=576, Dv=512, block_sizes=(1, 64, 5), scale=SCALE))
     ref = None
     for B, case in cases.items():
-        say(f"mla fp8 Hq={Hq} B={B} P={partition}")
+        say(f"mla fp8 {engine} Hq={Hq} B={B} P={partition}")
         g = GpuMLAFp8(case)
-        out, lse = g.decode(partition)
+        out, lse = g.decode(partition, engine)
         if ref is None:
             ref = g.oracle()
-        assert_attn_close(out, lse, ref[0], ref[1], what=f"mla fp8 Hq={Hq} B={B} P={partition}")
+        assert_attn_close(out, lse, ref[0], ref[1],
+                          what=f"mla fp8 {engine} Hq={Hq} B={B} P={partition}")
         s0 = LENS.index(0)
         assert torch.all(out[s0] == 0) and torch.all(torch.isneginf(lse[s0]))
 
 
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
 @pytest.mark.parametrize("partition", [-1, 64, -2])
-def test_mla_fp8_fused_cache_write(partition):
+def test_mla_fp8_fused_cache_write(partition, engine):
     """One launch (quantised write of each sequence's new latent, then
     decode) equals the write followed by decode, bits of output, LSE and
     cache, and matches the oracle."""
@@ -109,7 +113,7 @@ def test_mla_fp8_fused_cache_write(partition):
                                       Hq=16, Dl=576, Dv=512, block_sizes=(1, 64, 5), scale=SCALE))
     dev = device()
     for B, case in cases.items():
-        say(f"mla fp8 fused cache write B={B} P={partition}")
+        say(f"mla fp8 {engine} fused cache write B={B} P={partition}")
         g = GpuMLAFp8(case)
         rows = case.new_token_rows()
         nl = case.latent[torch.from_numpy(rows)].to(dev).contiguous()
@@ -118,32 +122,66 @@ def test_mla_fp8_fused_cache_write(partition):
         junk = torch.randn(tuple(nl.shape), generator=gen).to(torch.bfloat16).to(dev)
         pa.reshape_and_cache_mla_fp8(junk, g.kv, slots, KVS)
         kv2 = g.kv.clone()
-        o1, l1 = g.decode(partition, new_latent=nl, slot_mapping=slots)
+        o1, l1 = g.decode(partition, engine, new_latent=nl, slot_mapping=slots)
         pa.reshape_and_cache_mla_fp8(nl, kv2, slots, KVS)
-        o2, l2 = pa.mla_decode_attn_fp8(g.q, kv2, g.bt, g.cl, case.scale, g.max_ctx, KVS,
-                                        v_dim=case.Dv, partition_tokens=partition)
+        o2, l2 = ENGINES[engine](g.q, kv2, g.bt, g.cl, case.scale, g.max_ctx, KVS,
+                                 v_dim=case.Dv, partition_tokens=partition)
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
         assert torch.equal(g.kv, kv2)
         ref_out, ref_lse = g.oracle()
-        assert_attn_close(o1, l1, ref_out, ref_lse, what=f"mla fp8 fused B={B} P={partition}")
+        assert_attn_close(o1, l1, ref_out, ref_lse,
+                          what=f"mla fp8 {engine} fused B={B} P={partition}")
 
 
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
 @pytest.mark.parametrize("B", [1, 64])
-def test_mla_fp8_deepseek_sampled(B):
+def test_mla_fp8_deepseek_sampled(B, engine):
     """64 requests, 16 heads, lengths U[1024,4096], in the benchmark's launch
     configuration (scale amax / 448): 8 whole requests vs the oracle."""
     case = W.deepseek_mla_decode(block_sizes=(B,))[B]
     kvs = float(np.float32(case.latent.float().abs().max().item() / 448.0))
-    say(f"mla fp8 deepseek B={B} kv_scale={kvs:.4g}")
+    say(f"mla fp8 {engine} deepseek B={B} kv_scale={kvs:.4g}")
     g = GpuMLAFp8(case, kv_scale=kvs)
-    out, lse = g.decode(0)
+    out, lse = g.decode(0, engine)
     seqs = np.random.default_rng(83).choice(case.S, size=8, replace=False)
     ref_out, ref_lse = g.oracle(kv=g.kv.cpu().numpy(), seqs=seqs)
     mask = np.zeros((case.S, case.Hq), dtype=bool)
     mask[seqs] = True
     assert_attn_close(out, lse, ref_out, ref_lse, rows=np.nonzero(mask),
-                      what=f"mla fp8 deepseek bs{B}")
+                      what=f"mla fp8 {engine} deepseek bs{B}")
+
+
+def test_mla_fp8_mfma_balanced_more_sequences_than_workgroups():
+    """The balanced split when the sequences outnumber the resident
+    workgroups (one whole sequence per piece, in turn), matrix-core engine."""
+    lens = np.random.default_rng(434).integers(0, 80, size=1500)
+    case = halved(W.mla_decode_cases("mla8many", 434, S=len(lens), lens_range=None,
+                                     lens=lens.tolist(), Hq=4, Dl=576, Dv=512, block_sizes=(16,),
+                                     scale=SCALE))[16]
+    say("mla fp8 mfma balanced 1500 sequences")
+    g = GpuMLAFp8(case)
+    out, lse = g.decode(-2, "mfma")
+    ref_out, ref_lse = g.oracle()
+    assert_attn_close(out, lse, ref_out, ref_lse, what="mla fp8 mfma balanced, many sequences")
+
+
+def test_mla_fp8_mfma_out_of_range_blocks():
+    """Block ids outside the pool read as zero rows (weight exp(-max) on a
+    zero value) in both engines: the two agree to rounding."""
+    case = halved(W.mla_decode_cases("mla8oor", 435, S=3, lens_range=None, lens=[40, 70, 33],
+                                     Hq=16, Dl=576, Dv=512, block_sizes=(16,), scale=SCALE))[16]
+    g = GpuMLAFp8(case)
+    bt = g.bt.clone()
+    bt[0, 1] = case.paging.num_blocks + 5
+    bt[1, 0] = -3
+    say("mla fp8 out-of-range block ids, both engines")
+    o1, l1 = pa.mla_decode_attn_fp8(g.q, g.kv, bt, g.cl, SCALE, g.max_ctx, KVS)
+    o2, l2 = pa.mla_decode_attn_fp8_mfma(g.q, g.kv, bt, g.cl, SCALE, g.max_ctx, KVS)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all() and torch.isfinite(l2).all()
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-3
 
 
 def test_mla_fp8_rejects_bad_arguments():
@@ -156,3 +194,6 @@ def test_mla_fp8_rejects_bad_arguments():
     with pytest.raises(pa.PagedAttnError) as e:
         pa.mla_decode_attn_fp8(g.q, g.kv, g.bt, g.cl, SCALE, g.max_ctx, KVS, v_dim=448)
     assert e.value.status == 2
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.mla_decode_attn_fp8_mfma(g.q, g.kv, g.bt, g.cl, SCALE, g.max_ctx, float("nan"))
+    assert e.value.status == 1
