@@ -454,11 +454,6 @@ __device__ __forceinline__ void mla_write_empty(const MLAParams &p, int s) {
 //         in registers.
 // Online softmax with the lazy reference of the VALU engine.  Query heads
 // beyond num_q_heads are zero rows whose outputs are not written.
-// FP8 latents: a row is 576 codes (36 vectors of 16); lane (g, m) gathers
-// vectors 4 j + g, j < 9, into blocks 9 + j, the second half of the wave's
-// region, and after the gather lands the codes are widened in place into the
-// bf16 blocks above (exact: every E4M3 value is a bf16), so QK and P.V run
-// unchanged; the cache scale folds into the softmax scale and the output.
 // ---------------------------------------------------------------------------
 constexpr int kMTok = 16;              // tokens per wave per round
 constexpr int kMRound = kWaves * kMTok;  // 64 tokens per round
@@ -482,6 +477,16 @@ struct MLAMfmaSmem {
     float m[kWaves][16], l[kWaves][16];
     float alpha[kWaves][16];  // rescale factors of the wave's heads (lazy softmax)
 };
+
+// The matrix-core engine over FP8 latents keeps its stage buffers in
+// objects of their own; the workgroup shares only the softmax state.
+struct MLAMfmaF8Smem {
+    float m[kWaves][16], l[kWaves][16];
+    float alpha[kWaves][16];  // rescale factors of the wave's heads (lazy softmax)
+};
+template <bool F8, bool MFMA>
+using MLASmemOf = std::conditional_t<MFMA, std::conditional_t<F8, MLAMfmaF8Smem, MLAMfmaSmem>, MLASmem>;
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
     return __builtin_bit_cast(bf16x8_t, v);
@@ -507,13 +512,12 @@ __device__ __forceinline__ int64_t mla_row(const MLAParams &p, int s, int t, int
 // merge of the 4 waves and the output: out rows (whole) or partials in the
 // layout merge_mla_partials reads (head h at po + h * hs, 16-byte vector
 // 64 i + c holding dims 8 c + 4 i .. + 3) with LSEs at pl + h * lhs.
-template <bool F8>
 __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &sm, int s,
                                                int start, int end, bool whole, float *po,
                                                size_t hs, float *pl, size_t lhs) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
-    const float sl2 = p.scale * kLog2e * (F8 ? p.kv_scale : 1.f);
+    const float sl2 = p.scale * kLog2e;
     const char *kv = reinterpret_cast<const char *>(p.kv_cache);
     uint4 *region = &sm.tile[wave][0][0];
 
@@ -548,20 +552,10 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         if (valid != 0) {
             // gather: block j, lane (g, m) <- vector 4 j + g of token m's row
             if (row >= 0) {
-                if constexpr (F8) {
-                    const char *src = kv + (size_t)row * kDl + 16 * g;
+                const char *src = kv + (size_t)row * (kDl * 2) + 16 * g;
 #pragma unroll
-                    for (int j = 0; j < kMSteps / 2; j++)
-                        __builtin_amdgcn_global_load_lds(src + 64 * j,
-                                                         (lds_void_t *)(region + 64 * (kMSteps / 2 + j)),
-                                                         16, 0, 0);
-                } else {
-                    const char *src = kv + (size_t)row * (kDl * 2) + 16 * g;
-#pragma unroll
-                    for (int j = 0; j < kMSteps; j++)
-                        __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(region + 64 * j),
-                                                         16, 0, 0);
-                }
+                for (int j = 0; j < kMSteps; j++)
+                    __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(region + 64 * j), 16, 0, 0);
             }
         }
         // the next round's row (in flight with the gather), and the queries
@@ -579,30 +573,6 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         // entry, which may not have been requested at all)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         asm volatile("" ::: "memory");
-        if constexpr (F8) {
-            // codes of vector 4 jc + g (dims 64 jc + 16 g .. + 15) of token m
-            // -> bf16 vectors 8 jc + 2 g and + 1, i.e. block 2 jc + g / 2, slots
-            // 16 (2 (g % 2)) + m and 16 (2 (g % 2) + 1) + m; tokens not
-            // gathered this round become zero rows.  Code block 9 + jc is read
-            // before bf16 blocks 2 jc and 2 jc + 1 are written, and no code
-            // block still to be read lies below 2 jc + 2.
-            const bool ok = (valid >> m) & 1u;
-            const int gp = 2 * (g & 1);
-#pragma unroll
-            for (int jc = 0; jc < kMSteps / 2; jc++) {
-                const uint4 codes = region[64 * (kMSteps / 2 + jc) + lane];
-                uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-                if (ok) {
-                    fp8x4_to_bf16x2(codes.x, lo.x, lo.y);
-                    fp8x4_to_bf16x2(codes.y, lo.z, lo.w);
-                    fp8x4_to_bf16x2(codes.z, hi.x, hi.y);
-                    fp8x4_to_bf16x2(codes.w, hi.z, hi.w);
-                }
-                const int j = 2 * jc + (g >> 1);
-                region[64 * j + 16 * gp + m] = lo;
-                region[64 * j + 16 * (gp + 1) + m] = hi;
-            }
-        }
 
         // QK: two accumulator chains over the 18 steps
         f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -677,12 +647,6 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         row = next_row;
     }
 
-    if constexpr (F8) {  // the value rows were summed as unscaled codes
-#pragma unroll
-        for (int n = 0; n < kMTiles; n++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) o[n][i] *= p.kv_scale;
-    }
     // merge of the 4 waves: weight sums of head m over the 4 rows of lanes
     {
         auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
@@ -751,6 +715,275 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core engine over FP8 latents.  The same products as above, with
+// the codes gathered into two stage buffers per wave (9 KB each: block j
+// holds, at slot 16 g + m, code vector 4 j + g, i.e. codes 64 j + 16 g ..
+// + 15, of token m), so that the next round's gather is in flight while the
+// current round is computed; at 72 KB of stages per workgroup two
+// workgroups still share a compute unit.  Codes are widened to bf16 in
+// registers (exact: every E4M3 value is a bf16):
+//   QK   A operand of step j: 8 codes (one 64-bit LDS read) of token m,
+//        dims 32 j + 8 g .. + 7;
+//   P.V  B operands of output tiles N and N + 1 (N even) from one 8-bit
+//        transpose read (ds_read_b64_tr_b8: within 16 lanes, lane 2 b + h
+//        gives the address of row b, lane n receives byte n of every row);
+//        row b is token 4 g + b % 4 at dims 16 (N + b / 4) + 8 h .. + 7, so
+//        lane (g, n) receives dim 16 N + n (first word) and 16 (N + 1) + n
+//        (second word) of tokens 4 g .. 4 g + 3.
+// Every round issues exactly one block-table load (for two rounds ahead,
+// index clamped) and nine gather loads, so "all but the newest ten vector
+// memory operations are done" means the current round has landed.  Lanes
+// whose token is past the end (or whose block id is out of range) gather a
+// harmless in-pool row; their scores are masked and their code bytes zeroed
+// before the P.V products.  The cache scale folds into the softmax scale and
+// the output.
+// ---------------------------------------------------------------------------
+constexpr int kF8Blocks = kDl / 64;  // 9 blocks of 64 code vectors per wave and round
+
+struct F8Stage {
+    __align__(16) uint4 t[kWaves][kF8Blocks][64];
+};
+
+// "All but the newest n vector memory operations have completed."
+#define PA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8Smem &sm, int s,
+                                                  int start, int end, bool whole, float *po,
+                                                  size_t hs, float *pl, size_t lhs) {
+    __shared__ F8Stage st0, st1;  // two objects: a read of one need not wait for a gather into the other
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const float sl2 = p.scale * kLog2e * p.kv_scale;
+    const char *kv = reinterpret_cast<const char *>(p.kv_cache);
+    char *const b0 = reinterpret_cast<char *>(&st0.t[wave][0][0]);
+    char *const b1 = reinterpret_cast<char *>(&st1.t[wave][0][0]);
+    const int nr = end > start ? (end - start + kMRound - 1) / kMRound : 0;  // rounds of the piece
+    const int32_t *bt = p.block_table + (size_t)s * p.max_blocks;
+
+    // the lane's token in round r, its block-table entry (always loaded: the
+    // index is clamped) and its latent row (-1: no token)
+    auto token = [&](int r) { return start + kMRound * r + kMTok * wave + m; };
+    auto entry = [&](int r) {
+        const int t = min(token(r), end - 1);
+        return bt[min(t / p.B, p.max_blocks - 1)];
+    };
+    auto row_of = [&](int r, int b) -> int64_t {
+        const int t = token(r);
+        return t < end && b >= 0 && (int64_t)b < p.num_blocks ? (int64_t)b * p.B + t % p.B : -1;
+    };
+    auto gather = [&](char *stage, int64_t row) {
+        const char *src = kv + (size_t)(row < 0 ? 0 : row) * kDl + 16 * g;
+#pragma unroll
+        for (int j = 0; j < kF8Blocks; j++)
+            __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(stage + 1024 * j), 16, 0, 0);
+    };
+
+    // QK operand offsets (step j adds 1024 * (j / 2) + 256 * (j % 2)... see
+    // below) and the transpose-read offset of tile pair 0 for this lane
+    const int qk_off = (16 * (g >> 1) + m) * 16 + 8 * (g & 1);  // step 0: vector g / 2
+    const int tb = (lane & 15) >> 1, th = lane & 1;              // transpose row, half
+    const int tr_tok = 4 * g + (tb & 3);
+    // tile pair N, N + 1 (N even): vector N + tb / 4
+
+    uint4 q[kMSteps];
+    f32x4_t o[kMTiles];
+#pragma unroll
+    for (int n = 0; n < kMTiles; n++) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mh = kNegInf, lsum = 0.f;
+
+    int e1 = 0;  // entry of round r + 1
+    int64_t row = -1;
+    if (nr > 0) {
+        row = row_of(0, entry(0));
+        e1 = entry(min(1, nr - 1));
+        gather(b0, row);
+        mla_mfma_queries(p, s, q);
+    }
+    // one round; which stage is current is a compile-time fact, so that the
+    // compiler can tell the stage read from the one being gathered into
+    auto round = [&](int r, auto in_st0) {
+        constexpr bool kSt0 = decltype(in_st0)::value;
+        char *cur = kSt0 ? b0 : b1;
+        char *nxt = kSt0 ? b1 : b0;
+        const uint32_t valid = (uint32_t)__ballot(row >= 0) & 0xffffu;
+        int64_t row1 = -1;
+        asm volatile("" ::: "memory");
+        if (r + 1 < nr) {
+            // the next round: its entry is in (loaded before this round's
+            // gather), the one after is requested first
+            const int e2 = entry(min(r + 2, nr - 1));
+            row1 = row_of(r + 1, e1);
+            gather(nxt, row1);
+            e1 = e2;
+            asm volatile("" ::: "memory");
+            PA_WAIT_VM(10);
+        } else {
+            PA_WAIT_VM(0);
+        }
+        asm volatile("" ::: "memory");
+        if (valid != 0) {
+            // QK: two accumulator chains over the 18 steps
+            f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kMSteps; j += 2) {
+                // step j: vector 2 j + g / 2 = 4 (j / 2) + g / 2; step j + 1: + 2
+                const char *base = cur + 1024 * (j / 2) + qk_off;
+                const uint2 ca = *reinterpret_cast<const uint2 *>(base);
+                const uint2 cb = *reinterpret_cast<const uint2 *>(base + 2 * 16 * 16);
+                uint4 ka, kb;
+                fp8x4_to_bf16x2(ca.x, ka.x, ka.y);
+                fp8x4_to_bf16x2(ca.y, ka.z, ka.w);
+                fp8x4_to_bf16x2(cb.x, kb.x, kb.y);
+                fp8x4_to_bf16x2(cb.y, kb.z, kb.w);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(q[j]), sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(q[j + 1]), sb, 0, 0, 0);
+            }
+            float z[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const bool ok = (valid >> (4 * g + i)) & 1u;
+                z[i] = ok ? (sa[i] + sb[i]) * sl2 : kNegInf;
+            }
+            float zm = fmax_nc(fmax_nc(z[0], z[1]), fmax_nc(z[2], z[3]));
+            {
+                auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(zm), __float_as_uint(zm), false, false);
+                zm = fmax_nc(__uint_as_float(x[0]), __uint_as_float(x[1]));
+                auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(zm), __float_as_uint(zm), false, false);
+                zm = fmax_nc(__uint_as_float(y[0]), __uint_as_float(y[1]));
+            }
+            if (__ballot(zm > mh + kLazyLog2)) {
+                float alpha = 1.f;
+                if (zm > mh + kLazyLog2) {
+                    alpha = fast_exp2(mh - zm);  // 0 from -inf
+                    mh = zm;
+                }
+                lsum *= alpha;
+                if (g == 0) sm.alpha[wave][m] = alpha;
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes have landed
+                float a4[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) a4[i] = sm.alpha[wave][4 * g + i];
+#pragma unroll
+                for (int n = 0; n < kMTiles; n++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) o[n][i] *= a4[i];
+            }
+            float pw[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                pw[i] = fast_exp2(z[i] - mh);  // mh is finite here
+                lsum += pw[i];
+            }
+            uint2 ph, pl_;
+            ph.x = pack_bf16x2(pw[0], pw[1]);
+            ph.y = pack_bf16x2(pw[2], pw[3]);
+            pl_.x = pack_bf16x2(pw[0] - bf16_lo(ph.x), pw[1] - bf16_hi(ph.x));
+            pl_.y = pack_bf16x2(pw[2] - bf16_lo(ph.y), pw[3] - bf16_hi(ph.y));
+            const bf16x4_t pa = __builtin_bit_cast(bf16x4_t, ph), pb = __builtin_bit_cast(bf16x4_t, pl_);
+            // code bytes of tokens 4 g .. 4 g + 3 that are not this round's:
+            // zeroed (the gathered stand-in row may hold any code)
+            const uint32_t nib = (valid >> (4 * g)) & 0xfu;
+            const uint32_t bm = ((nib * 0x00204081u) & 0x01010101u) * 0xffu;
+#pragma unroll
+            for (int n = 0; n < kMTiles; n += 2) {
+                const int v = n + (tb >> 2);  // code vector of the lane's transpose row
+                const int off = (v >> 2) * 1024 + (16 * (v & 3) + tr_tok) * 16 + 8 * th;
+                const v2i32_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i32_t *)(cur + off));
+                uint2 w0, w1;
+                fp8x4_to_bf16x2((uint32_t)c[0] & bm, w0.x, w0.y);
+                fp8x4_to_bf16x2((uint32_t)c[1] & bm, w1.x, w1.y);
+                const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, w0), v1 = __builtin_bit_cast(bf16x4_t, w1);
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v0, o[n], 0, 0, 0);
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, v0, o[n], 0, 0, 0);
+                o[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v1, o[n + 1], 0, 0, 0);
+                o[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, v1, o[n + 1], 0, 0, 0);
+            }
+        }
+        // every LDS read of this round's stage is done before the gather two
+        // rounds on overwrites it (the gather's LDS writes are not ordered
+        // after reads)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        row = row1;
+    };
+    for (int r = 0; r < nr; r += 2) {
+        round(r, std::true_type{});
+        if (r + 1 < nr) round(r + 1, std::false_type{});
+    }
+#pragma unroll
+    for (int n = 0; n < kMTiles; n++)  // the value rows were summed as unscaled codes
+#pragma unroll
+        for (int i = 0; i < 4; i++) o[n][i] *= p.kv_scale;
+
+    // merge of the 4 waves (as in the bf16 engine); the stages, no longer
+    // read, hold each wave's pass of output dims: waves 0, 1 in st0, 2, 3 in st1
+    auto obuf = [&](int w) -> float * {
+        return reinterpret_cast<float *>(w < 2 ? &st0 : &st1) + (w & 1) * 16 * (kMMergeDims + 4);
+    };
+    {
+        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+        float l2 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
+        lsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    }
+    lds_barrier();  // every wave is done with its stages
+    if (g == 0) {
+        sm.m[wave][m] = mh;
+        sm.l[wave][m] = lsum;
+    }
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    const auto prs = coherent_rsrc(po, whole ? 0u : (uint32_t)(((p.Hq - 1) * hs + kDv) * 4));
+    float *mine = obuf(wave);
+    for (int pass = 0; pass < kDv / kMMergeDims; pass++) {
+        constexpr int kTilesPerPass = kMMergeDims / 16;
+#pragma unroll
+        for (int n = 0; n < kTilesPerPass; n++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                mine[(4 * g + i) * (kMMergeDims + 4) + 16 * n + m] = o[kTilesPerPass * pass + n][i];
+        lds_barrier();
+        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += kWaves * 64) {
+            const int h = __builtin_amdgcn_readfirstlane(idx / (kMMergeDims / 4));
+            const int d = 4 * (idx % (kMMergeDims / 4));
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
+            const float Mr = M == kNegInf ? 0.f : M;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) {
+                const float wt = fast_exp2(sm.m[w][h] - Mr);
+                const float4 a = *reinterpret_cast<const float4 *>(obuf(w) + h * (kMMergeDims + 4) + d);
+                acc[0] += wt * a.x;
+                acc[1] += wt * a.y;
+                acc[2] += wt * a.z;
+                acc[3] += wt * a.w;
+                den += wt * sm.l[w][h];
+            }
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
+            const int dim = kMMergeDims * pass + d;
+            const size_t orow = (size_t)s * p.Hq + h;
+            if (whole) {
+                uint2 v;
+                v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                *reinterpret_cast<uint2 *>(out + orow * kDv + dim) = v;
+                if (dim == 0 && p.lse) p.lse[orow] = L;
+            } else {
+                const int vec = 64 * ((dim & 7) >> 2) + (dim >> 3);
+                store_coherent4(prs, (uint32_t)(h * hs * 4 + vec * 16), acc[0] * inv,
+                                acc[1] * inv, acc[2] * inv, acc[3] * inv);
+                if (dim == 0) store_coherent(&pl[h * lhs], L);
+            }
+        }
+        lds_barrier();
+    }
+}
+
 __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW], float (&acc)[kHPW][8]) {
 #pragma unroll
     for (int j = 0; j < kHPW; j++) {
@@ -768,7 +1001,7 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     const int s = blockIdx.x - part * p.S;
     const int P = p.partition;
     const int start = part * P;
-    __shared__ std::conditional_t<MFMA, MLAMfmaSmem, MLASmem> sm;
+    __shared__ MLASmemOf<F8, MFMA> sm;
 
     const int ctx = clamp_ctx(p, as_const<int32_t>(p.context_lens)[s]);
     if (start >= ctx) {
@@ -786,8 +1019,12 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     float *po = nparts == 1 ? nullptr : p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
     float *pl = nparts == 1 ? nullptr : p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
     if constexpr (MFMA) {
-        mla_mfma_piece<F8>(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv, pl,
-                       p.max_parts);
+        if constexpr (F8)
+            mla_mfma_piece_f8(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv,
+                              pl, p.max_parts);
+        else
+            mla_mfma_piece(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv, pl,
+                           p.max_parts);
     } else {
         uint32_t qreg[kHPW][kSlices];
         mla_load_queries(p, s, qreg);
@@ -827,7 +1064,7 @@ template <bool F8, bool MFMA>
 __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p) {
     const int NW = gridDim.x, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    __shared__ std::conditional_t<MFMA, MLAMfmaSmem, MLASmem> sm;
+    __shared__ MLASmemOf<F8, MFMA> sm;
     auto ctx_of = [&](int s) { return s < p.S ? clamp_ctx(p, p.context_lens[min(s, p.S - 1)]) : 0; };
     const int ctx_w0 = ctx_of(lane);
     auto ctx_in = [&](int c0) { return c0 == 0 ? ctx_w0 : ctx_of(c0 + lane); };
@@ -889,9 +1126,14 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
         // the piece holding the last token writes the new token first
         if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token<F8>(p, s);
         if constexpr (MFMA) {
-            mla_mfma_piece<F8>(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
-                           p.part_out + (size_t)v * p.Hq * kDv, kDv, p.part_lse + (size_t)v * p.Hq,
-                           1);
+            if constexpr (F8)
+                mla_mfma_piece_f8(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
+                                  p.part_out + (size_t)v * p.Hq * kDv, kDv,
+                                  p.part_lse + (size_t)v * p.Hq, 1);
+            else
+                mla_mfma_piece(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
+                               p.part_out + (size_t)v * p.Hq * kDv, kDv,
+                               p.part_lse + (size_t)v * p.Hq, 1);
         } else {
             uint32_t qreg[kHPW][kSlices];
             mla_load_queries(p, s, qreg);
