@@ -508,6 +508,90 @@ __device__ __forceinline__ int64_t mla_row(const MLAParams &p, int s, int t, int
     return b >= 0 && (int64_t)b < p.num_blocks ? (int64_t)b * p.B + t % p.B : -1;
 }
 
+// Merge of the 4 waves of a matrix-core workgroup and the output: each
+// wave's accumulators (lane (g, n): heads 4 g .. 4 g + 3, dim 16 N + n of tile
+// N), reference maxima (mh, head m) and weight sums (lsum, lane's share of
+// head m) are combined by log-sum-exp, written as output rows (whole) or as
+// partials at po + h * hs (16-byte vector 64 i + c holding dims 8 c + 4 i ..
+// + 3) with LSEs at pl + h * lhs.  The output dims go through LDS in passes of
+// kMMergeDims; obuf(w) is wave w's [16][kMMergeDims + 4] float area.
+template <typename OBuf>
+__device__ __forceinline__ void mla_mfma_emit(const MLAParams &p, int s, bool whole, float *po,
+                                              size_t hs, float *pl, size_t lhs,
+                                              const f32x4_t (&o)[kMTiles], float mh, float lsum,
+                                              float (&sm_m)[kWaves][16],
+                                              float (&sm_l)[kWaves][16], OBuf obuf) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    {  // weight sums of head m over the 4 rows of lanes
+        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+        float l2 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
+        lsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    }
+    lds_barrier();  // every wave is done with the LDS that obuf reuses
+    if (g == 0) {
+        sm_m[wave][m] = mh;
+        sm_l[wave][m] = lsum;
+    }
+    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
+    // partials of all heads through one descriptor made outside the loops
+    // (a per-head descriptor is per-lane to the compiler, which then wraps
+    // each store in a loop over distinct descriptors)
+    const auto prs = coherent_rsrc(po, whole ? 0u : (uint32_t)(((p.Hq - 1) * hs + kDv) * 4));
+    constexpr int kStride = kMMergeDims + 4;
+    float *mine = obuf(wave);
+    for (int pass = 0; pass < kDv / kMMergeDims; pass++) {
+        constexpr int kTilesPerPass = kMMergeDims / 16;
+#pragma unroll
+        for (int n = 0; n < kTilesPerPass; n++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) mine[(4 * g + i) * kStride + 16 * n + m] = o[kTilesPerPass * pass + n][i];
+        lds_barrier();
+        // a wave's 64 consecutive indices share one head (the bound is a
+        // multiple of 64)
+        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += kWaves * 64) {
+            const int h = __builtin_amdgcn_readfirstlane(idx / (kMMergeDims / 4));
+            const int d = 4 * (idx % (kMMergeDims / 4));
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm_m[w][h]);
+            const float Mr = M == kNegInf ? 0.f : M;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) {
+                const float wt = fast_exp2(sm_m[w][h] - Mr);
+                const float4 a = *reinterpret_cast<const float4 *>(obuf(w) + h * kStride + d);
+                acc[0] += wt * a.x;
+                acc[1] += wt * a.y;
+                acc[2] += wt * a.z;
+                acc[3] += wt * a.w;
+                den += wt * sm_l[w][h];
+            }
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
+            const int dim = kMMergeDims * pass + d;
+            const size_t orow = (size_t)s * p.Hq + h;
+            if (whole) {
+                uint2 v;
+                v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                *reinterpret_cast<uint2 *>(out + orow * kDv + dim) = v;
+                if (dim == 0 && p.lse) p.lse[orow] = L;
+            } else {
+                // vector 64 i + c holds dims 8 c + 4 i .. + 3
+                const int vec = 64 * ((dim & 7) >> 2) + (dim >> 3);
+                store_coherent4(prs, (uint32_t)(h * hs * 4 + vec * 16), acc[0] * inv,
+                                acc[1] * inv, acc[2] * inv, acc[3] * inv);
+                if (dim == 0) store_coherent(&pl[h * lhs], L);
+            }
+        }
+        // the pass's LDS is read before the next one is written (its partial
+        // stores stay in flight: the count that publishes them waits for them)
+        lds_barrier();
+    }
+}
+
 // Attention of all heads over tokens [start, end) of sequence s, then the
 // merge of the 4 waves and the output: out rows (whole) or partials in the
 // layout merge_mla_partials reads (head h at po + h * hs, 16-byte vector
@@ -647,72 +731,8 @@ __device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &
         row = next_row;
     }
 
-    // merge of the 4 waves: weight sums of head m over the 4 rows of lanes
-    {
-        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
-        float l2 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
-        lsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    }
-    lds_barrier();  // every wave is done with its tile region
-    if (g == 0) {
-        sm.m[wave][m] = mh;
-        sm.l[wave][m] = lsum;
-    }
-    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-    // partials of all heads through one descriptor made outside the loops
-    // (a per-head descriptor is per-lane to the compiler, which then wraps
-    // each store in a loop over distinct descriptors)
-    const auto prs = coherent_rsrc(po, whole ? 0u : (uint32_t)(((p.Hq - 1) * hs + kDv) * 4));
-    for (int pass = 0; pass < kDv / kMMergeDims; pass++) {
-        constexpr int kTilesPerPass = kMMergeDims / 16;
-#pragma unroll
-        for (int n = 0; n < kTilesPerPass; n++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) sm.o[wave][4 * g + i][16 * n + m] = o[kTilesPerPass * pass + n][i];
-        lds_barrier();
-        // a wave's 64 consecutive indices share one head (the bound is a
-        // multiple of 64)
-        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += kWaves * 64) {
-            const int h = __builtin_amdgcn_readfirstlane(idx / (kMMergeDims / 4));
-            const int d = 4 * (idx % (kMMergeDims / 4));
-            float M = kNegInf;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
-            const float Mr = M == kNegInf ? 0.f : M;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) {
-                const float wt = fast_exp2(sm.m[w][h] - Mr);
-                const float4 a = *reinterpret_cast<const float4 *>(&sm.o[w][h][d]);
-                acc[0] += wt * a.x;
-                acc[1] += wt * a.y;
-                acc[2] += wt * a.z;
-                acc[3] += wt * a.w;
-                den += wt * sm.l[w][h];
-            }
-            const float inv = den > 0.f ? 1.f / den : 0.f;
-            const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
-            const int dim = kMMergeDims * pass + d;
-            const size_t orow = (size_t)s * p.Hq + h;
-            if (whole) {
-                uint2 v;
-                v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-                v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-                *reinterpret_cast<uint2 *>(out + orow * kDv + dim) = v;
-                if (dim == 0 && p.lse) p.lse[orow] = L;
-            } else {
-                // vector 64 i + c holds dims 8 c + 4 i .. + 3
-                const int vec = 64 * ((dim & 7) >> 2) + (dim >> 3);
-                store_coherent4(prs, (uint32_t)(h * hs * 4 + vec * 16), acc[0] * inv,
-                                acc[1] * inv, acc[2] * inv, acc[3] * inv);
-                if (dim == 0) store_coherent(&pl[h * lhs], L);
-            }
-        }
-        // the pass's LDS is read before the next one is written (its partial
-        // stores stay in flight: the count that publishes them waits for them)
-        lds_barrier();
-    }
+    mla_mfma_emit(p, s, whole, po, hs, pl, lhs, o, mh, lsum, sm.m, sm.l,
+                  [&](int w) { return &sm.o[w][0][0]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -812,6 +832,8 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
         if (r + 1 < nr) {
             // the next round: its entry is in (loaded before this round's
             // gather), the one after is requested first
+            PA_WAIT_VM(9);  // e1, loaded before the current round's gather
+            asm volatile("" ::: "memory");
             const int e2 = entry(min(r + 2, nr - 1));
             row1 = row_of(r + 1, e1);
             gather(nxt, row1);
@@ -918,70 +940,11 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
 #pragma unroll
         for (int i = 0; i < 4; i++) o[n][i] *= p.kv_scale;
 
-    // merge of the 4 waves (as in the bf16 engine); the stages, no longer
-    // read, hold each wave's pass of output dims: waves 0, 1 in st0, 2, 3 in st1
-    auto obuf = [&](int w) -> float * {
+    // the stages, no longer read, hold each wave's pass of output dims:
+    // waves 0, 1 in st0, 2, 3 in st1
+    mla_mfma_emit(p, s, whole, po, hs, pl, lhs, o, mh, lsum, sm.m, sm.l, [&](int w) -> float * {
         return reinterpret_cast<float *>(w < 2 ? &st0 : &st1) + (w & 1) * 16 * (kMMergeDims + 4);
-    };
-    {
-        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
-        float l2 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
-        lsum = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    }
-    lds_barrier();  // every wave is done with its stages
-    if (g == 0) {
-        sm.m[wave][m] = mh;
-        sm.l[wave][m] = lsum;
-    }
-    uint16_t *out = reinterpret_cast<uint16_t *>(p.out);
-    const auto prs = coherent_rsrc(po, whole ? 0u : (uint32_t)(((p.Hq - 1) * hs + kDv) * 4));
-    float *mine = obuf(wave);
-    for (int pass = 0; pass < kDv / kMMergeDims; pass++) {
-        constexpr int kTilesPerPass = kMMergeDims / 16;
-#pragma unroll
-        for (int n = 0; n < kTilesPerPass; n++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                mine[(4 * g + i) * (kMMergeDims + 4) + 16 * n + m] = o[kTilesPerPass * pass + n][i];
-        lds_barrier();
-        for (int idx = threadIdx.x; idx < p.Hq * (kMMergeDims / 4); idx += kWaves * 64) {
-            const int h = __builtin_amdgcn_readfirstlane(idx / (kMMergeDims / 4));
-            const int d = 4 * (idx % (kMMergeDims / 4));
-            float M = kNegInf;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) M = fmax_nc(M, sm.m[w][h]);
-            const float Mr = M == kNegInf ? 0.f : M;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) {
-                const float wt = fast_exp2(sm.m[w][h] - Mr);
-                const float4 a = *reinterpret_cast<const float4 *>(obuf(w) + h * (kMMergeDims + 4) + d);
-                acc[0] += wt * a.x;
-                acc[1] += wt * a.y;
-                acc[2] += wt * a.z;
-                acc[3] += wt * a.w;
-                den += wt * sm.l[w][h];
-            }
-            const float inv = den > 0.f ? 1.f / den : 0.f;
-            const float L = den > 0.f ? (M + fast_log2(den)) * kLn2 : kNegInf;
-            const int dim = kMMergeDims * pass + d;
-            const size_t orow = (size_t)s * p.Hq + h;
-            if (whole) {
-                uint2 v;
-                v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-                v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-                *reinterpret_cast<uint2 *>(out + orow * kDv + dim) = v;
-                if (dim == 0 && p.lse) p.lse[orow] = L;
-            } else {
-                const int vec = 64 * ((dim & 7) >> 2) + (dim >> 3);
-                store_coherent4(prs, (uint32_t)(h * hs * 4 + vec * 16), acc[0] * inv,
-                                acc[1] * inv, acc[2] * inv, acc[3] * inv);
-                if (dim == 0) store_coherent(&pl[h * lhs], L);
-            }
-        }
-        lds_barrier();
-    }
+    });
 }
 
 __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW], float (&acc)[kHPW][8]) {

@@ -135,11 +135,14 @@ def test_graph_mla_step():
     check_graph(step, [out, lse])
 
 
-def test_graph_mla_fp8_step():
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
+def test_graph_mla_fp8_step(engine):
     """The fused MLA decode step over an FP8 latent cache (the quantised
-    write of the new latents included), captured and replayed."""
+    write of the new latents included), captured and replayed, on either
+    engine."""
     case = W.deepseek_mla_decode(S=16, block_sizes=(64,))[64]
-    say("graph: fused MLA decode step, FP8 cache")
+    say(f"graph: fused MLA decode step, FP8 cache, {engine} engine")
+    fn = pa.mla_decode_attn_fp8_mfma if engine == "mfma" else pa.mla_decode_attn_fp8
     dev = device()
     pg = case.paging
     kvs = float(np.float32(case.latent.float().abs().max().item() / 448.0))
@@ -162,8 +165,8 @@ def test_graph_mla_fp8_step():
     pa.reshape_and_cache_mla_fp8(nl, kv_exp, slots, kvs)
 
     def step():
-        pa.mla_decode_attn_fp8(q, kv, bt, cl, case.scale, mc, kvs, new_latent=nl,
-                               slot_mapping=slots, out=out, lse=lse, workspace=ws)
+        fn(q, kv, bt, cl, case.scale, mc, kvs, new_latent=nl, slot_mapping=slots, out=out,
+           lse=lse, workspace=ws)
     check_graph(step, [out, lse])
     assert torch.equal(kv, kv_exp)
 
