@@ -434,26 +434,48 @@ __device__ __forceinline__ void mla_write_empty(const MLAParams &p, int s) {
 // dense [16 x 576] x [576 x T] product and P.V a [16 x T] x [T x 512] one,
 // computed with v_mfma_f32_16x16x32_bf16 (QK, 18 steps of 32 dims per 16
 // tokens) and v_mfma_f32_16x16x16_bf16 (P.V, P in bf16 hi + lo parts).  A
-// workgroup of 4 waves walks its range 64 tokens at a time; wave w owns
-// tokens 16 w .. 16 w + 15 of each 64 and never exchanges data with the
-// other waves until the final merge.
-//   load  each lane of a wave gathers vectors of its own token's latent row
-//         (lane (g, m): token m, vectors 4 j + g, j < 18) straight into the
-//         wave's LDS region (global_load_lds: per-lane 64-bit addresses, so
-//         any pool size and block size), block j at slot 16 g + m, which is
-//         the QK A-operand layout: operand j is one conflict-free 1 KB read.
+// workgroup of 4 waves walks its range 64 tokens at a time (a round); wave w
+// owns tokens 16 w .. 16 w + 15 of each round and never exchanges data with
+// the other waves until the final merge.
+//   load  each lane of a wave gathers 16-byte vectors of its own token's
+//         latent row (lane (g, m): token m, vectors 4 j + g) straight into
+//         one of the wave's two stage buffers (global_load_lds: per-lane
+//         64-bit addresses, so any pool size and block size): block j holds,
+//         at slot 16 g + m, vector 4 j + g of token m.  The next round's
+//         gather is in flight while the current round is computed; the two
+//         stages are separate LDS objects, so a read of one need not wait
+//         for a gather into the other.
 //   QK    S^T = K Q^T: A = the 16 tokens' latents, B = the queries (resident
 //         registers: lane (g, m) holds head m's dims 32 j + 8 g .. + 7);
 //         lane (g, m) then holds head m's scores of tokens 4 g .. 4 g + 3.
 //   P.V   O = P V: A = P (lane (g, m): head m, tokens 4 g .. 4 g + 3, i.e.
-//         the lane's own weights), B = V through LDS transpose reads
-//         (ds_read_b64_tr_b16: within 16 lanes, lane 4 k + q reads token
-//         4 g + k, dims 4 q .. 4 q + 3 of the 16-dim output tile, and lane n
-//         receives dim n of the 4 tokens); 32 output tiles of 16 dims, whose
-//         accumulators (lane (g, n): heads 4 g .. 4 g + 3, dim 16 N + n) stay
-//         in registers.
-// Online softmax with the lazy reference of the VALU engine.  Query heads
-// beyond num_q_heads are zero rows whose outputs are not written.
+//         the lane's own weights), B = V through LDS transpose reads; 32
+//         output tiles of 16 dims, whose accumulators (lane (g, n): heads
+//         4 g .. 4 g + 3, dim 16 N + n) stay in registers.
+// bf16 latents: 18 blocks (18 KB) per stage, 144 KB of stages per workgroup
+// (one workgroup per compute unit); operand j of QK is one conflict-free
+// 1 KB read of block j; the P.V operand of tile N comes from
+// ds_read_b64_tr_b16 (within 16 lanes, lane 4 k + q reads token 4 g + k,
+// dims 4 q .. 4 q + 3 of the tile, and lane n receives dim n of the 4
+// tokens).
+// FP8 latents (576 codes a row): 9 blocks (9 KB) per stage, 72 KB per
+// workgroup (two per compute unit); codes are widened to bf16 in registers
+// (exact: every E4M3 value is a bf16): the QK operand of step j is 8 codes
+// (one 64-bit read) of dims 32 j + 8 g .. + 7; the B operands of tiles N
+// and N + 1 (N even) come from one ds_read_b64_tr_b8 (within 16 lanes,
+// lane 2 b + h gives the address of row b, lane n receives byte n of every
+// row) whose row b is token 4 g + b % 4 at dims 16 (N + b / 4) + 8 h .. + 7,
+// so lane (g, n) receives dim 16 N + n (first word) and 16 (N + 1) + n
+// (second word) of tokens 4 g .. 4 g + 3; the cache scale folds into the
+// softmax scale and the output.
+// Every round issues exactly one block-table load (for two rounds ahead,
+// index clamped) and one gather load per stage block, so "all but the
+// newest (blocks + 1) vector memory operations are done" means the current
+// round has landed.  Lanes whose token is past the end (or whose block id
+// is out of range) gather a stand-in in-pool row; their scores are masked
+// and their values zeroed before the P.V products.  Online softmax with the
+// lazy reference of the VALU engine.  Query heads beyond num_q_heads are
+// zero rows whose outputs are not written.
 // ---------------------------------------------------------------------------
 constexpr int kMTok = 16;              // tokens per wave per round
 constexpr int kMRound = kWaves * kMTok;  // 64 tokens per round
@@ -467,25 +489,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Workgroup state of the matrix-core engine besides its stage buffers.
 struct MLAMfmaSmem {
-    union {
-        // per wave: block j holds, at slot 16 g + m, vector 4 j + g of token m
-        __align__(16) uint4 tile[kWaves][kMSteps][64];
-        // the final merge of the waves: one pass of output dims
-        __align__(16) float o[kWaves][16][kMMergeDims + 4];
-    };
-    float m[kWaves][16], l[kWaves][16];
-    float alpha[kWaves][16];  // rescale factors of the wave's heads (lazy softmax)
-};
-
-// The matrix-core engine over FP8 latents keeps its stage buffers in
-// objects of their own; the workgroup shares only the softmax state.
-struct MLAMfmaF8Smem {
     float m[kWaves][16], l[kWaves][16];
     float alpha[kWaves][16];  // rescale factors of the wave's heads (lazy softmax)
 };
 template <bool F8, bool MFMA>
-using MLASmemOf = std::conditional_t<MFMA, std::conditional_t<F8, MLAMfmaF8Smem, MLAMfmaSmem>, MLASmem>;
+using MLASmemOf = std::conditional_t<MFMA, MLAMfmaSmem, MLASmem>;
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
@@ -592,189 +602,30 @@ __device__ __forceinline__ void mla_mfma_emit(const MLAParams &p, int s, bool wh
     }
 }
 
-// Attention of all heads over tokens [start, end) of sequence s, then the
-// merge of the 4 waves and the output: out rows (whole) or partials in the
-// layout merge_mla_partials reads (head h at po + h * hs, 16-byte vector
-// 64 i + c holding dims 8 c + 4 i .. + 3) with LSEs at pl + h * lhs.
-__device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &sm, int s,
-                                               int start, int end, bool whole, float *po,
-                                               size_t hs, float *pl, size_t lhs) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
-    const float sl2 = p.scale * kLog2e;
-    const char *kv = reinterpret_cast<const char *>(p.kv_cache);
-    uint4 *region = &sm.tile[wave][0][0];
+// Stage blocks of 64 16-byte vectors per wave and round: 9 of codes, 18 of bf16.
+template <bool F8>
+constexpr int kStageBlocks = F8 ? kDl / 64 : kDl / 32;
 
-    // stale LDS may hold any bits: tokens that are never loaded must read
-    // as zero rows, so the region starts zeroed
-    for (int i = lane; i < kMSteps * 64; i += 64) region[i] = make_uint4(0, 0, 0, 0);
-    // the gathers write LDS by another path: the zeros land first
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-
-    uint4 q[kMSteps];
-    bool have_q = false;  // the queries are requested after the first gather
-    f32x4_t o[kMTiles];
-#pragma unroll
-    for (int n = 0; n < kMTiles; n++) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mh = kNegInf, lsum = 0.f;  // head m: reference maximum (log2 units), lane's weight sum
-
-    // LDS byte offset (in the wave's region) of lane (g, 4 k + q)'s transpose
-    // read for output tile 0: token 4 g + k, dims 4 q .. 4 q + 3 (vector
-    // q / 2, half q % 2); tile N adds vector 2 N
-    const int kq = lane & 15, tk = 4 * g + (kq >> 2), qd = kq & 3;
-    auto tr_off = [&](int N) -> uint32_t {
-        const int v = 2 * N + (qd >> 1);
-        return (uint32_t)((v >> 2) * 1024 + (16 * (v & 3) + tk) * 16 + 8 * (qd & 1));
-    };
-
-    int64_t row = mla_row(p, s, start + kMTok * wave + m, end);
-    for (int r0 = start; r0 < end; r0 += kMRound) {
-        const int t0 = r0 + kMTok * wave;  // the wave's first token this round
-        // 16-bit mask of the wave's valid tokens
-        const uint32_t valid = (uint32_t)__ballot(row >= 0) & 0xffffu;
-        if (valid != 0) {
-            // gather: block j, lane (g, m) <- vector 4 j + g of token m's row
-            if (row >= 0) {
-                const char *src = kv + (size_t)row * (kDl * 2) + 16 * g;
-#pragma unroll
-                for (int j = 0; j < kMSteps; j++)
-                    __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(region + 64 * j), 16, 0, 0);
-            }
-        }
-        // the next round's row (in flight with the gather), and the queries
-        // behind the first gather in the memory queue
-        const int64_t next_row = mla_row(p, s, t0 + kMRound + m, end);
-        if (valid == 0) {
-            row = next_row;
-            continue;
-        }
-        if (!have_q) {
-            mla_mfma_queries(p, s, q);
-            have_q = true;
-        }
-        // the gather has landed (together with the next round's block-table
-        // entry, which may not have been requested at all)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        asm volatile("" ::: "memory");
-
-        // QK: two accumulator chains over the 18 steps
-        f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kMSteps; j += 2) {
-            const uint4 ka = region[64 * j + lane], kb = region[64 * (j + 1) + lane];
-            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(q[j]), sa, 0, 0, 0);
-            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(q[j + 1]), sb, 0, 0, 0);
-        }
-        float z[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const bool ok = (valid >> (4 * g + i)) & 1u;
-            z[i] = ok ? (sa[i] + sb[i]) * sl2 : kNegInf;
-        }
-        // the round's maximum of head m over the wave's 16 tokens (4 per lane,
-        // 4 rows of lanes)
-        float zm = fmax_nc(fmax_nc(z[0], z[1]), fmax_nc(z[2], z[3]));
-        {
-            auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(zm), __float_as_uint(zm), false, false);
-            zm = fmax_nc(__uint_as_float(x[0]), __uint_as_float(x[1]));
-            auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(zm), __float_as_uint(zm), false, false);
-            zm = fmax_nc(__uint_as_float(y[0]), __uint_as_float(y[1]));
-        }
-        if (__ballot(zm > mh + kLazyLog2)) {
-            // rescale: alpha of head m (lanes (*, m)) -> accumulators of heads
-            // 4 g + i (lanes (g, *)) through LDS
-            float alpha = 1.f;
-            if (zm > mh + kLazyLog2) {
-                alpha = fast_exp2(mh - zm);  // 0 from -inf
-                mh = zm;
-            }
-            lsum *= alpha;
-            if (g == 0) sm.alpha[wave][m] = alpha;
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS writes have landed
-            float a4[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) a4[i] = sm.alpha[wave][4 * g + i];
-#pragma unroll
-            for (int n = 0; n < kMTiles; n++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) o[n][i] *= a4[i];
-        }
-        float pw[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            pw[i] = fast_exp2(z[i] - mh);  // mh is finite here
-            lsum += pw[i];
-        }
-        // P as bf16 hi + lo parts: A operand of 16x16x16 (head m, tokens 4 g .. + 3)
-        uint2 ph, pl_;
-        ph.x = pack_bf16x2(pw[0], pw[1]);
-        ph.y = pack_bf16x2(pw[2], pw[3]);
-        pl_.x = pack_bf16x2(pw[0] - bf16_lo(ph.x), pw[1] - bf16_hi(ph.x));
-        pl_.y = pack_bf16x2(pw[2] - bf16_lo(ph.y), pw[3] - bf16_hi(ph.y));
-        const bf16x4_t pa = __builtin_bit_cast(bf16x4_t, ph), pb = __builtin_bit_cast(bf16x4_t, pl_);
-        // P.V over the 32 output tiles
-        const char *rb = reinterpret_cast<const char *>(region);
-#pragma unroll
-        for (int n = 0; n < kMTiles; n++) {
-            const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t *)(rb + tr_off(n)));
-            const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, vt);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, o[n], 0, 0, 0);
-        }
-        // every LDS read of this round's tile is done before the next gather
-        // overwrites it (the gather's LDS writes are not ordered after reads)
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        asm volatile("" ::: "memory");
-        row = next_row;
-    }
-
-    mla_mfma_emit(p, s, whole, po, hs, pl, lhs, o, mh, lsum, sm.m, sm.l,
-                  [&](int w) { return &sm.o[w][0][0]; });
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core engine over FP8 latents.  The same products as above, with
-// the codes gathered into two stage buffers per wave (9 KB each: block j
-// holds, at slot 16 g + m, code vector 4 j + g, i.e. codes 64 j + 16 g ..
-// + 15, of token m), so that the next round's gather is in flight while the
-// current round is computed; at 72 KB of stages per workgroup two
-// workgroups still share a compute unit.  Codes are widened to bf16 in
-// registers (exact: every E4M3 value is a bf16):
-//   QK   A operand of step j: 8 codes (one 64-bit LDS read) of token m,
-//        dims 32 j + 8 g .. + 7;
-//   P.V  B operands of output tiles N and N + 1 (N even) from one 8-bit
-//        transpose read (ds_read_b64_tr_b8: within 16 lanes, lane 2 b + h
-//        gives the address of row b, lane n receives byte n of every row);
-//        row b is token 4 g + b % 4 at dims 16 (N + b / 4) + 8 h .. + 7, so
-//        lane (g, n) receives dim 16 N + n (first word) and 16 (N + 1) + n
-//        (second word) of tokens 4 g .. 4 g + 3.
-// Every round issues exactly one block-table load (for two rounds ahead,
-// index clamped) and nine gather loads, so "all but the newest ten vector
-// memory operations are done" means the current round has landed.  Lanes
-// whose token is past the end (or whose block id is out of range) gather a
-// harmless in-pool row; their scores are masked and their code bytes zeroed
-// before the P.V products.  The cache scale folds into the softmax scale and
-// the output.
-// ---------------------------------------------------------------------------
-constexpr int kF8Blocks = kDl / 64;  // 9 blocks of 64 code vectors per wave and round
-
-struct F8Stage {
-    __align__(16) uint4 t[kWaves][kF8Blocks][64];
+template <bool F8>
+struct MfmaStage {
+    __align__(16) uint4 t[kWaves][kStageBlocks<F8>][64];
 };
 
 // "All but the newest n vector memory operations have completed."
 #define PA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-__device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8Smem &sm, int s,
+// Attention of all heads over tokens [start, end) of sequence s, then the
+// merge of the 4 waves and the output (mla_mfma_emit).
+template <bool F8>
+__device__ __forceinline__ void mla_mfma_piece(const MLAParams &p, MLAMfmaSmem &sm, int s,
                                                   int start, int end, bool whole, float *po,
                                                   size_t hs, float *pl, size_t lhs) {
-    __shared__ F8Stage st0, st1;  // two objects: a read of one need not wait for a gather into the other
+    // two objects: a read of one need not wait for a gather into the other
+    __shared__ MfmaStage<F8> st0, st1;
+    constexpr int kLoads = kStageBlocks<F8>;  // gather loads per round
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
-    const float sl2 = p.scale * kLog2e * p.kv_scale;
+    const float sl2 = p.scale * kLog2e * (F8 ? p.kv_scale : 1.f);
     const char *kv = reinterpret_cast<const char *>(p.kv_cache);
     char *const b0 = reinterpret_cast<char *>(&st0.t[wave][0][0]);
     char *const b1 = reinterpret_cast<char *>(&st1.t[wave][0][0]);
@@ -793,18 +644,22 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
         return t < end && b >= 0 && (int64_t)b < p.num_blocks ? (int64_t)b * p.B + t % p.B : -1;
     };
     auto gather = [&](char *stage, int64_t row) {
-        const char *src = kv + (size_t)(row < 0 ? 0 : row) * kDl + 16 * g;
+        const char *src = kv + (size_t)(row < 0 ? 0 : row) * (F8 ? kDl : 2 * kDl) + 16 * g;
 #pragma unroll
-        for (int j = 0; j < kF8Blocks; j++)
+        for (int j = 0; j < kLoads; j++)
             __builtin_amdgcn_global_load_lds(src + 64 * j, (lds_void_t *)(stage + 1024 * j), 16, 0, 0);
     };
 
-    // QK operand offsets (step j adds 1024 * (j / 2) + 256 * (j % 2)... see
-    // below) and the transpose-read offset of tile pair 0 for this lane
-    const int qk_off = (16 * (g >> 1) + m) * 16 + 8 * (g & 1);  // step 0: vector g / 2
-    const int tb = (lane & 15) >> 1, th = lane & 1;              // transpose row, half
+    // FP8 QK operand of steps j, j + 1 (j even): vector 2 j + g / 2 (+ 2),
+    // i.e. block j / 2, slot 16 (g / 2) (+ 32) + m, half g % 2
+    const int qk_off = (16 * (g >> 1) + m) * 16 + 8 * (g & 1);
+    // FP8 transpose row (tb) and half (th) of the lane: tile pair N, N + 1
+    // (N even) reads vector N + tb / 4 of token 4 g + tb % 4
+    const int tb = (lane & 15) >> 1, th = lane & 1;
     const int tr_tok = 4 * g + (tb & 3);
-    // tile pair N, N + 1 (N even): vector N + tb / 4
+    // bf16 transpose read of tile N: lane (g, 4 k + q) reads token 4 g + k,
+    // dims 4 q .. 4 q + 3 (vector 2 N + q / 2, half q % 2)
+    const int kq = lane & 15, tk = 4 * g + (kq >> 2), qd = kq & 3;
 
     uint4 q[kMSteps];
     f32x4_t o[kMTiles];
@@ -832,14 +687,14 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
         if (r + 1 < nr) {
             // the next round: its entry is in (loaded before this round's
             // gather), the one after is requested first
-            PA_WAIT_VM(9);  // e1, loaded before the current round's gather
+            PA_WAIT_VM(kLoads);  // e1, loaded before the current round's gather
             asm volatile("" ::: "memory");
             const int e2 = entry(min(r + 2, nr - 1));
             row1 = row_of(r + 1, e1);
             gather(nxt, row1);
             e1 = e2;
             asm volatile("" ::: "memory");
-            PA_WAIT_VM(10);
+            PA_WAIT_VM(kLoads + 1);
         } else {
             PA_WAIT_VM(0);
         }
@@ -849,17 +704,31 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
             f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < kMSteps; j += 2) {
-                // step j: vector 2 j + g / 2 = 4 (j / 2) + g / 2; step j + 1: + 2
-                const char *base = cur + 1024 * (j / 2) + qk_off;
-                const uint2 ca = *reinterpret_cast<const uint2 *>(base);
-                const uint2 cb = *reinterpret_cast<const uint2 *>(base + 2 * 16 * 16);
-                uint4 ka, kb;
-                fp8x4_to_bf16x2(ca.x, ka.x, ka.y);
-                fp8x4_to_bf16x2(ca.y, ka.z, ka.w);
-                fp8x4_to_bf16x2(cb.x, kb.x, kb.y);
-                fp8x4_to_bf16x2(cb.y, kb.z, kb.w);
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(q[j]), sa, 0, 0, 0);
-                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(q[j + 1]), sb, 0, 0, 0);
+                if constexpr (F8) {
+                    uint4 ka, kb;
+                    const char *base = cur + 1024 * (j / 2) + qk_off;
+                    const uint2 ca = *reinterpret_cast<const uint2 *>(base);
+                    const uint2 cb = *reinterpret_cast<const uint2 *>(base + 2 * 16 * 16);
+                    fp8x4_to_bf16x2(ca.x, ka.x, ka.y);
+                    fp8x4_to_bf16x2(ca.y, ka.z, ka.w);
+                    fp8x4_to_bf16x2(cb.x, kb.x, kb.y);
+                    fp8x4_to_bf16x2(cb.y, kb.z, kb.w);
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(q[j]), sa, 0, 0, 0);
+                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(q[j + 1]), sb, 0, 0, 0);
+                } else if (j % 6 == 0) {
+                    // six steps at a time: their operand reads are issued
+                    // together (block j, slot lane: vector 4 j + g of token m)
+                    uint4 kk[6];
+#pragma unroll
+                    for (int i = 0; i < 6; i++)
+                        kk[i] = *reinterpret_cast<const uint4 *>(cur + 1024 * (j + i) + 16 * lane);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 6; i += 2) {
+                        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[i]), as_bf16x8(q[j + i]), sa, 0, 0, 0);
+                        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[i + 1]), as_bf16x8(q[j + i + 1]), sb, 0, 0, 0);
+                    }
+                }
             }
             float z[4];
 #pragma unroll
@@ -904,24 +773,50 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
             pl_.x = pack_bf16x2(pw[0] - bf16_lo(ph.x), pw[1] - bf16_hi(ph.x));
             pl_.y = pack_bf16x2(pw[2] - bf16_lo(ph.y), pw[3] - bf16_hi(ph.y));
             const bf16x4_t pa = __builtin_bit_cast(bf16x4_t, ph), pb = __builtin_bit_cast(bf16x4_t, pl_);
-            // code bytes of tokens 4 g .. 4 g + 3 that are not this round's:
-            // zeroed (the gathered stand-in row may hold any code)
+            // values of tokens 4 g .. 4 g + 3 that are not this round's are
+            // zeroed (the gathered stand-in row may hold any bits)
             const uint32_t nib = (valid >> (4 * g)) & 0xfu;
-            const uint32_t bm = ((nib * 0x00204081u) & 0x01010101u) * 0xffu;
+            if constexpr (F8) {
+                const uint32_t bm = ((nib * 0x00204081u) & 0x01010101u) * 0xffu;  // byte k: token k
 #pragma unroll
-            for (int n = 0; n < kMTiles; n += 2) {
-                const int v = n + (tb >> 2);  // code vector of the lane's transpose row
-                const int off = (v >> 2) * 1024 + (16 * (v & 3) + tr_tok) * 16 + 8 * th;
-                const v2i32_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i32_t *)(cur + off));
-                uint2 w0, w1;
-                fp8x4_to_bf16x2((uint32_t)c[0] & bm, w0.x, w0.y);
-                fp8x4_to_bf16x2((uint32_t)c[1] & bm, w1.x, w1.y);
-                const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, w0), v1 = __builtin_bit_cast(bf16x4_t, w1);
-                o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v0, o[n], 0, 0, 0);
-                o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, v0, o[n], 0, 0, 0);
-                o[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v1, o[n + 1], 0, 0, 0);
-                o[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, v1, o[n + 1], 0, 0, 0);
+                for (int n = 0; n < kMTiles; n += 2) {
+                    const int v = n + (tb >> 2);  // code vector of the lane's transpose row
+                    const int off = (v >> 2) * 1024 + (16 * (v & 3) + tr_tok) * 16 + 8 * th;
+                    const v2i32_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i32_t *)(cur + off));
+                    uint2 w0, w1;
+                    fp8x4_to_bf16x2((uint32_t)c[0] & bm, w0.x, w0.y);
+                    fp8x4_to_bf16x2((uint32_t)c[1] & bm, w1.x, w1.y);
+                    const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, w0), v1 = __builtin_bit_cast(bf16x4_t, w1);
+                    o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v0, o[n], 0, 0, 0);
+                    o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, v0, o[n], 0, 0, 0);
+                    o[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v1, o[n + 1], 0, 0, 0);
+                    o[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, v1, o[n + 1], 0, 0, 0);
+                }
+            } else {
+                // 16-bit half k of the pair: token k (first word 0, 1; second 2, 3)
+                const uint32_t hm0 = ((nib & 1u) ? 0xffffu : 0u) | ((nib & 2u) ? 0xffff0000u : 0u);
+                const uint32_t hm1 = ((nib & 4u) ? 0xffffu : 0u) | ((nib & 8u) ? 0xffff0000u : 0u);
+#pragma unroll
+                for (int n0 = 0; n0 < kMTiles; n0 += 8) {  // 8 tiles' reads issued together
+                    uint2 w[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const int v = 2 * (n0 + i) + (qd >> 1);
+                        const int off = (v >> 2) * 1024 + (16 * (v & 3) + tk) * 16 + 8 * (qd & 1);
+                        w[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_t *)(cur + off)));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        w[i].x &= hm0;
+                        w[i].y &= hm1;
+                        const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, w[i]);
+                        o[n0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[n0 + i], 0, 0, 0);
+                        o[n0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, o[n0 + i], 0, 0, 0);
+                    }
+                }
             }
         }
         // every LDS read of this round's stage is done before the gather two
@@ -935,10 +830,12 @@ __device__ __forceinline__ void mla_mfma_piece_f8(const MLAParams &p, MLAMfmaF8S
         round(r, std::true_type{});
         if (r + 1 < nr) round(r + 1, std::false_type{});
     }
+    if constexpr (F8) {  // the value rows were summed as unscaled codes
 #pragma unroll
-    for (int n = 0; n < kMTiles; n++)  // the value rows were summed as unscaled codes
+        for (int n = 0; n < kMTiles; n++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) o[n][i] *= p.kv_scale;
+            for (int i = 0; i < 4; i++) o[n][i] *= p.kv_scale;
+    }
 
     // the stages, no longer read, hold each wave's pass of output dims:
     // waves 0, 1 in st0, 2, 3 in st1
@@ -959,7 +856,7 @@ __device__ __forceinline__ void mla_reset(float (&m)[kHPW], float (&lsum)[kHPW],
 
 // Fixed partitions: one workgroup per (partition, sequence).
 template <bool F8, bool MFMA>
-__global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
+__global__ __launch_bounds__(256, (MFMA && !F8) ? 1 : 2) void mla_decode_kernel(MLAParams p) {
     const int part = blockIdx.x / p.S;
     const int s = blockIdx.x - part * p.S;
     const int P = p.partition;
@@ -982,12 +879,8 @@ __global__ __launch_bounds__(256, 2) void mla_decode_kernel(MLAParams p) {
     float *po = nparts == 1 ? nullptr : p.part_out + ((size_t)s * p.Hq * p.max_parts + part) * kDv;
     float *pl = nparts == 1 ? nullptr : p.part_lse + (size_t)s * p.Hq * p.max_parts + part;
     if constexpr (MFMA) {
-        if constexpr (F8)
-            mla_mfma_piece_f8(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv,
+        mla_mfma_piece<F8>(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv,
                               pl, p.max_parts);
-        else
-            mla_mfma_piece(p, sm, s, start, end, nparts == 1, po, (size_t)p.max_parts * kDv, pl,
-                           p.max_parts);
     } else {
         uint32_t qreg[kHPW][kSlices];
         mla_load_queries(p, s, qreg);
@@ -1024,7 +917,7 @@ __device__ __forceinline__ int wave_prefix_sum_i(int v) {
 // Pieces P_u .. P_u + n - 1 of a sequence leave partials in those slots of
 // [NW, Hq, Dv] and [NW, Hq]; the last to finish merges them in order.
 template <bool F8, bool MFMA>
-__global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p) {
+__global__ __launch_bounds__(256, (MFMA && !F8) ? 1 : 2) void mla_decode_balanced_kernel(MLAParams p) {
     const int NW = gridDim.x, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
     __shared__ MLASmemOf<F8, MFMA> sm;
@@ -1089,14 +982,9 @@ __global__ __launch_bounds__(256, 2) void mla_decode_balanced_kernel(MLAParams p
         // the piece holding the last token writes the new token first
         if (p.slot_mapping && min(b * kTile, ctx) == ctx) mla_write_new_token<F8>(p, s);
         if constexpr (MFMA) {
-            if constexpr (F8)
-                mla_mfma_piece_f8(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
+            mla_mfma_piece<F8>(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
                                   p.part_out + (size_t)v * p.Hq * kDv, kDv,
                                   p.part_lse + (size_t)v * p.Hq, 1);
-            else
-                mla_mfma_piece(p, sm, s, a * kTile, min(b * kTile, ctx), n == 1,
-                               p.part_out + (size_t)v * p.Hq * kDv, kDv,
-                               p.part_lse + (size_t)v * p.Hq, 1);
         } else {
             uint32_t qreg[kHPW][kSlices];
             mla_load_queries(p, s, qreg);
