@@ -42,16 +42,32 @@ METRIC = "paged decode attn: achieved HBM GB/s (% of peak) and decode tok/s, 64 
 # valid only for the kernel sources it was measured on:
 # workload -> (sources, sha256 prefix of those sources, bytes per launch).
 _CSRC = "paged_attention_decode_reshape_amd/csrc/"
+# The sources of each workload's kernels, for the tag the JSON line carries.
+KERNEL_SOURCES = {
+    "gqa": (_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
+    "mla": (_CSRC + "mla_decode.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
+    "extend": (_CSRC + "extend.hip", _CSRC + "decode_common.h"),
+    "merge": (_CSRC + "merge.hip",),
+    "cache_write": (_CSRC + "cache_write.hip", _CSRC + "fp8.h"),
+}
+
+# HBM bytes per launch of the line's dominant kernel from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE runs (one counter per run, each scaled by what it reads for a
+# plain 64 MiB device copy in the same process), for the workload's default
+# launch: key -> (source group, sha256 prefix of that group when measured,
+# bytes).  Keys name the variant: workload, then _fp8 (FP8 cache) and _mfma
+# (matrix-core MLA engine).
 MEASURED_TRAFFIC = {
-    "qwen3": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h"), "c7875b7c37b66cf0", 52.39e6),
-    "qwen3_fp8": ((_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
-                  "9ce2920c1d3b0562", 28.39e6),
-    "merge": ((_CSRC + "merge.hip",), "5767d743027acd19", 340.74e6),
-    "cache_write": ((_CSRC + "cache_write.hip", _CSRC + "fp8.h"), "409d000f5c585fba", 107.43e6),
-    "mla": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77", 237.19e6),
-    "mla_fp8": ((_CSRC + "mla_decode.hip", _CSRC + "decode_common.h"), "a258b7c31811cc77",
-                139.27e6),
-    "extend": ((_CSRC + "extend.hip", _CSRC + "decode_common.h"), "74420352bf28f086", 1294.40e6),
+    "qwen3": ("gqa", "716929696c53bbde", 52.34e6),
+    "qwen3_fp8": ("gqa", "716929696c53bbde", 28.38e6),
+    "long_context": ("gqa", "716929696c53bbde", 1148.44e6),
+    "mla": ("mla", "30dd7bded0e5261d", 237.19e6),
+    "mla_mfma": ("mla", "30dd7bded0e5261d", 216.86e6),
+    "mla_fp8": ("mla", "30dd7bded0e5261d", 139.29e6),
+    "mla_fp8_mfma": ("mla", "30dd7bded0e5261d", 145.71e6),
+    "extend": ("extend", "f2417c33dd0081bc", 1294.48e6),
+    "merge": ("merge", "5767d743027acd19", 340.74e6),
+    "cache_write": ("cache_write", "409d000f5c585fba", 107.43e6),
 }
 
 
@@ -65,22 +81,20 @@ def sources_sha(sources) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config):
-    """The counter-measured bytes per launch, or None once the kernel changed."""
-    if config not in MEASURED_TRAFFIC:
+def default_launch(args) -> bool:
+    """Whether the line times the launch the counters were taken on: the
+    workload's own split, the fused cache write and the shuffled layout."""
+    return (args.partition_tokens is None and not args.separate_cache_write
+            and args.kv_layout == "shuffled")
+
+
+def measured_traffic(key, default_launch=True):
+    """The counter-measured bytes per launch, or None for a launch other than
+    the measured one (another split or layout) or once the kernel changed."""
+    if not default_launch or key not in MEASURED_TRAFFIC:
         return None
-    sources, sha, nbytes = MEASURED_TRAFFIC[config]
-    return nbytes if sources_sha(sources) == sha else None
-
-
-# The sources of each workload's kernels, for the tag the JSON line carries.
-KERNEL_SOURCES = {
-    "gqa": (_CSRC + "decode_gqa.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
-    "mla": (_CSRC + "mla_decode.hip", _CSRC + "decode_common.h", _CSRC + "fp8.h"),
-    "extend": (_CSRC + "extend.hip", _CSRC + "decode_common.h"),
-    "merge": (_CSRC + "merge.hip",),
-    "cache_write": (_CSRC + "cache_write.hip", _CSRC + "fp8.h"),
-}
+    group, sha, nbytes = MEASURED_TRAFFIC[key]
+    return nbytes if sources_sha(KERNEL_SOURCES[group]) == sha else None
 
 
 def trace_summary(path, top=12):
@@ -1050,7 +1064,7 @@ def main():
                                 "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
                                 "traffic": measured_traffic(
                                     args.config + ("_fp8" if args.kv_dtype == "fp8" else "")
-                                    + "_mfma"),
+                                    + "_mfma", default_launch(args)),
                                 "algo_bytes_per_launch": r["algo_bytes"],
                                 "avg_launch_ms": r["decode_ms"],
                                 "launch_stats": r["launch_stats"],
@@ -1061,7 +1075,8 @@ def main():
                                 "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                                 "frac": r["tflops"] / VALU_PEAK_TFLOPS,
                                 "traffic": measured_traffic(
-                                    args.config + ("_fp8" if args.kv_dtype == "fp8" else "")),
+                                    args.config + ("_fp8" if args.kv_dtype == "fp8" else ""),
+                                    default_launch(args)),
                                 "algo_flops_per_launch": r["algo_flops"],
                                 "algo_bytes_per_launch": r["algo_bytes"],
                                 "avg_launch_ms": r["decode_ms"],
@@ -1079,7 +1094,8 @@ def main():
         line = base_line(args, r, workload, unit="tokens/s")
         line["roofline"] = {"bound": "hbm", "kernel": "cache_write_shuffled_kernel",
                             "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
+                            "frac": r["gbps"] / HBM_PEAK_GBPS,
+                            "traffic": measured_traffic(args.config, default_launch(args)),
                             "algo_bytes_per_launch": r["algo_bytes"],
                             "avg_launch_ms": r["ms_per_step"],
                             "launch_stats": r["launch_stats"]}
@@ -1094,7 +1110,8 @@ def main():
         line["dtype"] = "f32"
         line["roofline"] = {"bound": "hbm", "kernel": "merge_pair_kernel", "achieved": r["gbps"],
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
+                            "frac": r["gbps"] / HBM_PEAK_GBPS,
+                            "traffic": measured_traffic(args.config, default_launch(args)),
                             "algo_bytes_per_launch": r["algo_bytes"],
                             "avg_launch_ms": r["ms_per_step"],
                             "launch_stats": r["launch_stats"]}
@@ -1127,7 +1144,7 @@ def main():
         line["roofline"] = {"bound": "mfma", "kernel": "extend_attn_kernel (+ plan, new-V shuffle, merge)",
                             "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS,
-                            "traffic": measured_traffic(args.config),
+                            "traffic": measured_traffic(args.config, default_launch(args)),
                             "traffic_kernel": "extend_attn_kernel",
                             "algo_flops_per_call": r["algo_flops"],
                             "avg_call_ms": r["call_ms"],
@@ -1157,8 +1174,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": r["hbm_gbps"] / HBM_PEAK_GBPS,
-            "traffic": (measured_traffic(args.config + ("_fp8" if r["kv_dtype"] == "fp8" else ""))
-                        if r["kv_layout"] == "shuffled" else None),
+            "traffic": measured_traffic(args.config + ("_fp8" if r["kv_dtype"] == "fp8" else ""),
+                                        default_launch(args)),
             "algo_bytes_per_launch": r["algo_bytes"],
             "avg_launch_ms": r["decode_ms"],
             "launch_stats": r["launch_stats"],
