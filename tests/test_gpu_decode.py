@@ -255,6 +255,21 @@ def test_decode_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("partition", [0, 128, 64])
+def test_decode_repeated_launches_identical(partition):
+    """Which workgroup merges a split unit's partials depends on timing (the
+    last to finish); the partitions combine in index order whoever merges,
+    so 20 launches of the 64-request decode must agree bit for bit (8, 16
+    and 32 partitions per request)."""
+    case = W.qwen3_decode()
+    g = GpuGQA(case)
+    o1, l1 = g.decode(partition_tokens=partition)
+    for _ in range(20):
+        o2, l2 = g.decode(partition_tokens=partition)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
 def test_decode_qwen3_full(orc):
     """64 requests, GQA 8:1, lengths U[1000,2000]: every output vs the oracle."""
     case = W.qwen3_decode()
