@@ -17,7 +17,10 @@ is measured with HIP events on the stream it is launched on.
 
 The decode lines also carry hbm_read_ceiling: the time of a plain
 streaming read (pa_stream_read) of the same number of bytes on the same GPU,
-i.e. what the memory system delivers at this transfer size.
+i.e. what the memory system delivers at this transfer size; the GQA lines
+over the preshuffled cache also carry hbm_gather_ceiling: the time of
+reading exactly the blocks the decode reads, through its block table over
+the same rotating pools, with no arithmetic (pa_gather_read).
 
 Prints one JSON line.  Other workloads: --config long_context | mla | extend.
 """
@@ -444,7 +447,22 @@ def bench_gqa(args, case, label):
     algo = gqa_algorithmic_bytes(case, with_write=fused, kv_bytes=kv_bytes)
     achieved = algo / (dec_ms * 1e-3) / 1e9
     tok_s = case.S / (ms_per_step * 1e-3)
+    # the same blocks read through the same block table over the same
+    # rotating pools, with no arithmetic (preshuffled layouts only)
+    gather = None
+    if not args.no_read_ceiling and not std:
+        gsink = torch.empty(case.S * case.Hkv * ((bt.shape[1] + 3) // 4), dtype=torch.int32,
+                            device=dev)
+        gstats = launch_stats(lambda i: pa.gather_read(caches[i % pools][0], caches[i % pools][1],
+                                                       bt, cl, gsink, verify=False), 240)
+        gather = {"kernel": "gather_read_kernel (pa_gather_read)",
+                  "avg_launch_ms": gstats["avg_ms"],
+                  "gbps": algo / (gstats["avg_ms"] * 1e-3) / 1e9,
+                  "decode_frac_of_gather": gstats["avg_ms"] / dec_ms,
+                  "note": "K and V of every block a decode reads, one wave per block, "
+                          "no arithmetic; gbps counts the decode's algorithmic bytes"}
     return {
+        "gather_ceiling": gather,
         "value": tok_s,
         "ms_per_step": ms_per_step,
         "graph_replay_matches_eager": graph_ok,
@@ -1187,6 +1205,8 @@ def main():
         rc = read_ceiling(r["algo_bytes"])
         rc["decode_frac_of_ceiling"] = r["hbm_gbps"] / rc["gbps"]
         line["hbm_read_ceiling"] = rc
+        if r["gather_ceiling"] is not None:
+            line["hbm_gather_ceiling"] = r["gather_ceiling"]
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline_gqa(case, args.cpu_seconds, r["kv_layout"],

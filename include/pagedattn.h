@@ -630,6 +630,34 @@ pa_status pa_mixed_batch_attn(void *out, float *lse, const void *query, const vo
 pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups,
                          int32_t verify, void *stream);
 
+/*
+ * Block-table gather read (a measurement aid, not a step of the method):
+ * for every sequence s < num_seqs and kv head g < num_kv_heads, reads the
+ * K and V units of the blocks that hold the sequence's first
+ * context_lens[s] tokens -- unit_bytes each from k_cache and from v_cache
+ * at byte (block_table[s * max_blocks_per_seq + b] * num_kv_heads + g) *
+ * unit_bytes, b < ceil(context_lens[s] / block_size), the bytes a decode
+ * over the preshuffled cache reads (unit_bytes = head_dim * block_size *
+ * element size) -- one wave per block, four blocks per workgroup of 256
+ * threads, grid ordered block-major like the decode's partition-major grid,
+ * in 16-byte vectors folded into xor words.  Its time is the yardstick for
+ * the decode's bandwidth on its own access pattern: the same blocks, no
+ * arithmetic.  Context lengths are clamped to [0, max_blocks_per_seq *
+ * block_size]; block ids outside [0, num_blocks) are skipped.  sink: device,
+ * one uint32 per workgroup (num_seqs * num_kv_heads *
+ * ceil(max_blocks_per_seq / 4) words): with verify nonzero workgroup
+ * (b4 * num_seqs * num_kv_heads + s * num_kv_heads + g) stores the xor of
+ * every 32-bit word it read (the K and V units of blocks 4 b4 .. 4 b4 + 3
+ * of (s, g)); with verify 0 the contents are meaningless, as in
+ * pa_stream_read.  Caches 16-byte aligned; unit_bytes a multiple of 1024 in
+ * [1024, 65536].
+ * Errors: PA_ERR_INVALID_ARG (nothing launched), PA_ERR_HIP.
+ */
+pa_status pa_gather_read(const void *k_cache, const void *v_cache, const int32_t *block_table,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks,
+                         int32_t unit_bytes, uint32_t *sink, int32_t verify, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,4 +42,5 @@ from .ops import (  # noqa: F401
     reshape_and_cache_fp8,
     reshape_and_cache_mla_fp8,
     stream_read,
+    gather_read,
 )

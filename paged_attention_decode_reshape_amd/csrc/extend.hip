@@ -438,20 +438,23 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
         if (i + 1 < ntiles) load_tile(i + 1, tile_block(i + 1), nk, nv);
         // S^T = K Q^T for the two 32-key blocks of the tile
         f32x16_t s[2];
+        // A-operand row l32 holds tile key 32 kb + pi(l32), pi swapping bits
+        // 2 and 3 (run 2 kb + l32 / 16 of the LDS tile); then the result rows
+        // a lane holds are 8 consecutive keys per 16-key step, the layout of
+        // the P^T operand, and no regrouping of P across lanes is needed.
+        // The two key blocks' accumulations alternate, so that consecutive
+        // matrix instructions are independent.
+        const int pr = (l32 & 3) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+        const uint4 *kr = sk + (l32 >> 4) * 256 + 16 * hl + pr;
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
+        for (int kb = 0; kb < 2; kb++)
 #pragma unroll
             for (int e = 0; e < 16; e++) s[kb][e] = 0.f;
-            // A-operand row l32 holds tile key 32 kb + pi(l32), pi swapping
-            // bits 2 and 3 (run 2 kb + l32 / 16 of the LDS tile); then the
-            // result rows a lane holds are 8 consecutive keys per 16-key
-            // step, the layout of the P^T operand, and no regrouping of P
-            // across lanes is needed
-            const int pr = (l32 & 3) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-            const uint4 *kr = sk + (2 * kb + (l32 >> 4)) * 256 + 16 * hl + pr;
 #pragma unroll
-            for (int ks = 0; ks < 8; ks++) s[kb] = mfma32(as_bf16x8(kr[32 * ks]), qf[ks], s[kb]);
-        }
+        for (int ks = 0; ks < 8; ks++)
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+                s[kb] = mfma32(as_bf16x8(kr[2 * kb * 256 + 32 * ks]), qf[ks], s[kb]);
         // s[kb][e]: tile key 32 kb + 16 (e / 8) + 8 hl + e % 8 of query qi.
         // Visible keys: tile keys below `lim` (context end; new tokens: the
         // causal bound and the request's end).
@@ -528,14 +531,19 @@ __global__ __launch_bounds__(256, 2) void extend_attn_kernel(ExtendParams p) {
                 if constexpr (HILO)
                     pbl = as_bf16x8(make_uint4(pl[kb][4 * sp], pl[kb][4 * sp + 1],
                                                pl[kb][4 * sp + 2], pl[kb][4 * sp + 3]));
-                // V^T operand: dims 32 db + l32, tokens of group 4 kb + 2 sp + hl
+                // V^T operand: dims 32 db + l32, tokens of group 4 kb + 2 sp + hl;
+                // the hi products of the 4 dim blocks go first, then the lo
+                // ones, so that consecutive matrix instructions are independent
                 const uint4 *vr = sv + (4 * kb + 2 * sp + hl) * kD + l32;
+                bf16x8_t va[4];
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
-                    const bf16x8_t va = as_bf16x8(vr[32 * db]);
-                    o[db] = mfma32(va, pb, o[db]);
-                    if constexpr (HILO) o[db] = mfma32(va, pbl, o[db]);
+                    va[db] = as_bf16x8(vr[32 * db]);
+                    o[db] = mfma32(va[db], pb, o[db]);
                 }
+                if constexpr (HILO)
+#pragma unroll
+                    for (int db = 0; db < 4; db++) o[db] = mfma32(va[db], pbl, o[db]);
             }
         if (i + 1 < ntiles) {
             wait_dma();

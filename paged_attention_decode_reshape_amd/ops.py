@@ -79,6 +79,8 @@ _SIGS = {
                                 _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp, _sz, _vp],
                                _i32),
     "pa_stream_read": ([_vp, _sz, _vp, _i32, _i32, _vp], _i32),
+    "pa_gather_read": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp, _i32, _vp],
+                       _i32),
     "pa_reshape_and_cache_fp8": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _f32,
                                   _f32, _vp], _i32),
     "pa_paged_decode_attn_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
@@ -852,6 +854,43 @@ def stream_read(src: torch.Tensor, workgroups: int, sink: Optional[torch.Tensor]
         raise ValueError("sink needs one word per workgroup")
     _check("stream_read", lib.pa_stream_read(src.data_ptr(), nbytes, sink.data_ptr(),
                                              int(workgroups), int(bool(verify)), _stream(src)))
+    return sink
+
+
+def gather_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                context_lens: torch.Tensor, sink: Optional[torch.Tensor] = None,
+                verify: bool = True) -> torch.Tensor:
+    """Read the K and V blocks that a decode over the preshuffled cache reads
+    (every kv head's unit of each block holding a sequence's context),
+    through the block table, with no arithmetic: the library's gather-read
+    kernel (a bandwidth yardstick, not part of attention).  Caches
+    [num_blocks, kv_heads, ...] of either preshuffled shape; with `verify`
+    the per-workgroup xor words are stored in the returned sink."""
+    lib = library()
+    _gpu("k_cache", k_cache)
+    _gpu("v_cache", v_cache)
+    if k_cache.shape[:2] != v_cache.shape[:2] or k_cache.numel() != v_cache.numel():
+        raise ValueError("k_cache and v_cache must hold the same units")
+    if k_cache.dim() != 5 or not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("caches must be contiguous [num_blocks, kv_heads, a, b, x] tensors")
+    _gpu("block_table", block_table, torch.int32, 2)
+    _gpu("context_lens", context_lens, torch.int32, 1)
+    NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    B = int(k_cache.shape[3])
+    unit = (k_cache.numel() // (NB * Hkv)) * k_cache.element_size()
+    S, maxb = int(context_lens.shape[0]), int(block_table.shape[1])
+    if block_table.shape[0] < S:
+        raise ValueError("block_table needs a row per sequence")
+    words = S * Hkv * ((maxb + 3) // 4)
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=k_cache.device)
+    _gpu("sink", sink, torch.int32, 1)
+    if sink.numel() < words:
+        raise ValueError("sink needs one word per workgroup")
+    _check("gather_read", lib.pa_gather_read(k_cache.data_ptr(), v_cache.data_ptr(),
+                                             block_table.data_ptr(), context_lens.data_ptr(), S,
+                                             Hkv, maxb, B, NB, int(unit), sink.data_ptr(),
+                                             int(bool(verify)), _stream(k_cache)))
     return sink
 
 

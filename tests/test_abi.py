@@ -212,6 +212,28 @@ def test_stream_read_validation(args):
     assert pa.library().pa_stream_read(*args, 1, None) == INVALID
 
 
+# (k, v, block_table, context_lens, S, Hkv, max_blocks, block_size, num_blocks, unit_bytes, sink)
+_GR = (FAKE, FAKE, FAKE, FAKE, 4, 1, 8, 16, 64, 4096, FAKE)
+
+
+@pytest.mark.parametrize("i,value", [
+    (0, None), (1, None), (2, None), (3, None), (10, None),
+    (0, FAKE + 8),      # cache not 16-byte aligned
+    (4, -1),            # negative sequence count
+    (5, 0),             # no kv heads
+    (6, 0),             # no block-table columns
+    (7, 0),             # block size 0
+    (8, 0),             # no blocks
+    (9, 512),           # unit below one 16-byte vector per lane
+    (9, 3000),          # unit not whole 1 KiB
+    (9, 1 << 17),       # unit above 64 KiB
+])
+def test_gather_read_validation(i, value):
+    args = list(_GR)
+    args[i] = value
+    assert pa.library().pa_gather_read(*args, 1, None) == INVALID
+
+
 def _decode_layout(lib, layout=0, nk=None, nv=None, sm=None, **kw):
     a = dict(out=FAKE, lse=None, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxb=8, cl=FAKE, maxctx=100,
              S=4, Hq=8, Hkv=1, D=128, B=16, NB=64, scale=0.1, P=-1, ws=None, wsb=0)
