@@ -68,7 +68,7 @@ MEASURED_TRAFFIC = {
     "mla_mfma": ("mla", "30dd7bded0e5261d", 216.86e6),
     "mla_fp8": ("mla", "30dd7bded0e5261d", 139.29e6),
     "mla_fp8_mfma": ("mla", "30dd7bded0e5261d", 145.71e6),
-    "extend": ("extend", "f2417c33dd0081bc", 1294.48e6),
+    "extend": ("extend", "f06b1df214d4f57b", 1295.49e6),
     "merge": ("merge", "5767d743027acd19", 340.74e6),
     "cache_write": ("cache_write", "409d000f5c585fba", 107.43e6),
 }
