@@ -403,8 +403,18 @@ constexpr float kLazyLog2 = 8.f;  // softmax reference lag allowed (log2 units)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
+// Cache policy of the KV tile loads.  In the preshuffled layouts every load
+// instruction covers whole cache lines (a K instruction 4 runs of 16 tokens'
+// 16-byte vectors, a V instruction 64 consecutive vectors) and each line is
+// read once per launch, so those loads skip the vector L1 (sc0) and are
+// marked non-temporal in L2 (nt): 3% faster on the 64-request decode and 1-2%
+// on the long-context one than the default policy.  The standard layout
+// reads a token's row in four instructions, which the L1 serves together:
+// there the default policy is kept (sc0 + nt made it 30% slower).
+constexpr int kStreamPolicy = 1 | 2, kCachedPolicy = 0;
+template <int POLICY = kStreamPolicy>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -456,7 +466,7 @@ __device__ __forceinline__ void load_rows_std(const char *cache, size_t first, i
     const char *base = cache + first * (size_t)D * 2;
     const auto r = tile_rsrc(base, live ? (uint32_t)((15 * Hkv + 1) * D * 2) : 0u);
 #pragma unroll
-    for (int i = 0; i < CQ; i++) kq[i] = buf_load16(r, lane_off + i * 16);
+    for (int i = 0; i < CQ; i++) kq[i] = buf_load16<kCachedPolicy>(r, lane_off + i * 16);
 }
 // byte offset of lane (row, col) inside a standard-layout sub-block
 template <int D>
