@@ -20,6 +20,10 @@
 
 namespace pa {
 
+// Four dwords as one 16-byte vector value, the type the non-temporal access
+// builtins take.
+typedef unsigned int dw4_t __attribute__((ext_vector_type(4)));
+
 // Lanes are laid out so that 8 neighbouring lanes take 8 consecutive tokens
 // of the same 8 dims (lane = 8 * (chunk % 8) + token % 8): when those tokens
 // go to consecutive slots (a prefill or a bulk fill), the 2-byte V values of
@@ -48,14 +52,19 @@ __global__ __launch_bounds__(256) void cache_write_shuffled_kernel(
     if (slot < 0 || slot >= num_blocks * B) return;
     const int64_t p = slot / B;
     const int o = (int)(slot % B);
-    const uint4 kv = key[idx];
-    const uint4 vv = value[idx];
+    // The source is read once and the K vectors are written whole, so both
+    // are non-temporal accesses; V's 2-byte stores keep the default policy,
+    // under which L2 combines them into whole vectors (measured on a 93k-token
+    // bulk fill: 6.5% faster than the default policy throughout; non-temporal
+    // V stores made it 55% slower).
+    const dw4_t kv = __builtin_nontemporal_load(reinterpret_cast<const dw4_t *>(key) + idx);
+    const dw4_t vv = __builtin_nontemporal_load(reinterpret_cast<const dw4_t *>(value) + idx);
     // K vector (dims c*8 .. c*8+7 of token o) -> k_cache[p][g][c][o][0..8)
-    uint4 *kdst = reinterpret_cast<uint4 *>(k_cache) + ((p * Hkv + g) * C + c) * B + o;
-    *kdst = kv;
+    dw4_t *kdst = reinterpret_cast<dw4_t *>(k_cache) + ((p * Hkv + g) * C + c) * B + o;
+    __builtin_nontemporal_store(kv, kdst);
     // V: dim d = c*8 + e of token o -> v_cache[p][g][o / 8][d][o % 8]
     uint16_t *vdst = v_cache + (((p * Hkv + g) * (B / 8) + o / 8) * D + c * 8) * 8 + (o % 8);
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    const uint32_t w[4] = {vv[0], vv[1], vv[2], vv[3]};
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         const uint32_t word = w[e / 2];
