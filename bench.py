@@ -61,16 +61,16 @@ KERNEL_SOURCES = {
 # bytes).  Keys name the variant: workload, then _fp8 (FP8 cache) and _mfma
 # (matrix-core MLA engine).
 MEASURED_TRAFFIC = {
-    "qwen3": ("gqa", "716929696c53bbde", 52.34e6),
-    "qwen3_fp8": ("gqa", "716929696c53bbde", 28.38e6),
-    "long_context": ("gqa", "716929696c53bbde", 1148.44e6),
-    "mla": ("mla", "30dd7bded0e5261d", 237.19e6),
-    "mla_mfma": ("mla", "30dd7bded0e5261d", 216.86e6),
-    "mla_fp8": ("mla", "30dd7bded0e5261d", 139.29e6),
-    "mla_fp8_mfma": ("mla", "30dd7bded0e5261d", 145.71e6),
-    "extend": ("extend", "f06b1df214d4f57b", 1295.49e6),
+    "qwen3": ("gqa", "f191010d0e01bce8", 52.32e6),
+    "qwen3_fp8": ("gqa", "f191010d0e01bce8", 28.38e6),
+    "long_context": ("gqa", "f191010d0e01bce8", 1147.93e6),
+    "mla": ("mla", "30dd7bded0e5261d", 237.16e6),
+    "mla_mfma": ("mla", "30dd7bded0e5261d", 216.84e6),
+    "mla_fp8": ("mla", "30dd7bded0e5261d", 139.27e6),
+    "mla_fp8_mfma": ("mla", "30dd7bded0e5261d", 145.69e6),
+    "extend": ("extend", "f06b1df214d4f57b", 1295.37e6),
     "merge": ("merge", "5767d743027acd19", 340.74e6),
-    "cache_write": ("cache_write", "409d000f5c585fba", 107.43e6),
+    "cache_write": ("cache_write", "43249f5a74c4bd74", 109.87e6),
 }
 
 
