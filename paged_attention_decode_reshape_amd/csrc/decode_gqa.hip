@@ -1475,8 +1475,14 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeParams p) {
     });
     if (nparts == 1) return;
     if (!count_finished(p.counters + (size_t)s * p.Hkv + g, nparts)) return;
-    merge_partition_rows<D, 4, 16, kWaves * 64>(p.part_out, p.part_lse, p.max_parts, out, p.lse,
-                                                 row0, Ga, nparts);
+    // up to 8 partitions (the automatic split's usual count) in one batch of
+    // 8: the same sums as a batch of 16, whose extra entries add exact zeros
+    if (nparts <= 8)
+        merge_partition_rows<D, 4, 8, kWaves * 64>(p.part_out, p.part_lse, p.max_parts, out, p.lse,
+                                                    row0, Ga, nparts);
+    else
+        merge_partition_rows<D, 4, 16, kWaves * 64>(p.part_out, p.part_lse, p.max_parts, out,
+                                                     p.lse, row0, Ga, nparts);
 }
 
 // Balanced split.  The grid has NW workgroups (as many as are resident at
