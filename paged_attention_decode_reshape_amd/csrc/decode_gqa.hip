@@ -1086,14 +1086,18 @@ __device__ __forceinline__ void attend_range_rh(const DecodeParams &p, int s, in
     constexpr int DV = D / 64;        // output dims per lane
     constexpr int NR = G / 4;         // heads per row
     constexpr int kWindow = (SHARED ? NWV : 1) * 64 * kSub;  // tokens per window
-    constexpr bool STD = LAY == kLayStd;
+    constexpr bool STD = LAY == kLayStd, FP8 = LAY == kLayFp8;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int row = lane >> 4, col = lane & 15;
-    const float sl2 = p.scale * kLog2e;
+    // FP8: the codes are widened to bf16 exactly; K's scale goes into the
+    // score scale and V's multiplies the output at the end
+    const float sl2 = p.scale * kLog2e * (FP8 ? p.k_scale : 1.f);
     const char *kc = reinterpret_cast<const char *>(p.k_cache);
     const char *vc = reinterpret_cast<const char *>(p.v_cache);
-    const uint32_t k_off = STD ? std_lane_off<D>(row, col, p.Hkv) : k_lane_off<D, B>(row, col);
+    const uint32_t k_off = STD   ? std_lane_off<D>(row, col, p.Hkv)
+                           : FP8 ? (uint32_t)((row * (D / 64) * B + col) * 16)
+                                 : k_lane_off<D, B>(row, col);
     const uint32_t v_off = STD ? k_off : (uint32_t)lane * 16;
     char *vt_region = nullptr;
     if constexpr (STD) {
@@ -1134,11 +1138,18 @@ __device__ __forceinline__ void attend_range_rh(const DecodeParams &p, int s, in
                 size_t tile;
                 int half;
                 locate(k, tile, half);
-                load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
-                load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
+                if constexpr (FP8) {
+                    load_k_sub8<D, B>(kc, tile, half, k < nmine, k_off, kq);
+                    load_v_sub8<D, B>(vc, tile, half, k < nmine, v_off, vv);
+                } else {
+                    load_k_sub<D, B>(kc, tile, half, k < nmine, k_off, kq);
+                    load_v_sub<D, B>(vc, tile, half, k < nmine, v_off, vv);
+                }
             }
         };
-        constexpr int LK = CQ, LV = 2 * DV;
+        // loads per sub-block (FP8: CQ / 2 K vectors of 16 codes, one V vector
+        // of the sub-block's 16 tokens per dim)
+        constexpr int LK = FP8 ? CQ / 2 : CQ, LV = FP8 ? DV : 2 * DV;
 
         auto compute_sub = [&](int k, const uint4 (&kq)[CQ], const uint4 (&vin)[2][DV]) {
             const int t0 = start + sub_t0<SUBS, SHARED, NWV>(k, wave);
@@ -1147,11 +1158,14 @@ __device__ __forceinline__ void attend_range_rh(const DecodeParams &p, int s, in
             if (nvalid <= 0) return;
             // in flight: this sub-block's K and V, then the next one's
             wait_vm_loads<LV + LK + LV>();
+            uint4 kconv[CQ];
+            if constexpr (FP8) k_fp8_to_bf16<D>(kq, kconv);
+            const uint4 (&kb)[CQ] = FP8 ? kconv : kq;
             float z[NR];
 #pragma unroll
             for (int i = 0; i < NR; i++) {
                 float a[4] = {0.f, 0.f, 0.f, 0.f};
-                qk_4h<D>(a, &qreg[4 * i], kq);
+                qk_4h<D>(a, &qreg[4 * i], kb);
                 z[i] = rows_to_heads(a[0], a[1], a[2], a[3]) * sl2;
             }
             if (nvalid < kSub) {
@@ -1197,6 +1211,17 @@ __device__ __forceinline__ void attend_range_rh(const DecodeParams &p, int s, in
             uint4 vv[2][DV];
             if constexpr (STD) {
                 transpose_v_std<D>(vt_region, reinterpret_cast<const uint4(&)[CQ]>(vin), vv);
+            } else if constexpr (FP8) {
+                // the 16-token vector of dim l + 64 jj -> the two 8-token
+                // groups' bf16 pairs (token 2 w in the low half of word w)
+#pragma unroll
+                for (int jj = 0; jj < DV; jj++) {
+                    const uint4 raw = vin[0][jj];
+                    fp8x4_to_bf16x2(raw.x, vv[0][jj].x, vv[0][jj].y);
+                    fp8x4_to_bf16x2(raw.y, vv[0][jj].z, vv[0][jj].w);
+                    fp8x4_to_bf16x2(raw.z, vv[1][jj].x, vv[1][jj].y);
+                    fp8x4_to_bf16x2(raw.w, vv[1][jj].z, vv[1][jj].w);
+                }
             } else {
 #pragma unroll
                 for (int tg = 0; tg < 2; tg++)
@@ -1233,6 +1258,12 @@ __device__ __forceinline__ void attend_range_rh(const DecodeParams &p, int s, in
             load_kv(k + 2, kA, vA);
             compute_sub(k + 1, kB, vB);
         }
+    }
+    if constexpr (FP8) {  // V codes were summed unscaled
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int jj = 0; jj < DV; jj++) acc[h][jj] *= p.v_scale;
     }
 }
 
@@ -1284,11 +1315,11 @@ __device__ __forceinline__ void merge_waves_rh(WaveMergeLDS<D, G, NWV> &sm, int 
     }
 }
 
-// The gathered-weight formulation serves the bf16 caches (shuffled and
-// standard) with 4, 8 or 16 query heads per kv head; the FP8 cache and
-// smaller groups use attend_range.
+// The gathered-weight formulation serves 4, 8 or 16 query heads per kv head
+// over every cache (FP8 codes widened to bf16 after the load); smaller
+// groups use attend_range.
 template <int LAY, int G>
-constexpr bool uses_rh() { return (LAY == kLayShuffled || LAY == kLayStd) && G >= 4; }
+constexpr bool uses_rh() { return G >= 4; }
 
 template <int D, int G, int LAY, int NWV = kWaves>
 using MergeLDS = WaveMergeLDS<D, G, NWV>;
