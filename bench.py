@@ -61,9 +61,9 @@ KERNEL_SOURCES = {
 # bytes).  Keys name the variant: workload, then _fp8 (FP8 cache) and _mfma
 # (matrix-core MLA engine).
 MEASURED_TRAFFIC = {
-    "qwen3": ("gqa", "f191010d0e01bce8", 52.32e6),
-    "qwen3_fp8": ("gqa", "f191010d0e01bce8", 28.38e6),
-    "long_context": ("gqa", "f191010d0e01bce8", 1147.93e6),
+    "qwen3": ("gqa", "9809f6225010d674", 52.32e6),
+    "qwen3_fp8": ("gqa", "9809f6225010d674", 28.37e6),
+    "long_context": ("gqa", "9809f6225010d674", 1147.95e6),
     "mla": ("mla", "30dd7bded0e5261d", 237.16e6),
     "mla_mfma": ("mla", "30dd7bded0e5261d", 216.84e6),
     "mla_fp8": ("mla", "30dd7bded0e5261d", 139.27e6),
