@@ -1112,7 +1112,7 @@ def main():
                     "kv_heads": 1, "head_dim": 128, "block_size": 16, "layout": "shuffled",
                     "pools": r["pools"]}
         line = base_line(args, r, workload, unit="tokens/s")
-        line["roofline"] = {"bound": "hbm", "kernel": "cache_write_shuffled_kernel",
+        line["roofline"] = {"bound": "hbm", "kernel": "cache_write_runs_kernel",
                             "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": r["gbps"] / HBM_PEAK_GBPS,
                             "traffic": measured_traffic(args.config, default_launch(args)),

@@ -37,6 +37,45 @@ def test_cache_write_bitexact(orc, mk):
     assert np.array_equal(_bits(g.vc), vc)
 
 
+@pytest.mark.parametrize("D,B,Hkv", [(128, 16, 1), (64, 32, 3), (128, 32, 2)])
+def test_cache_write_mixed_slot_runs(orc, D, B, Hkv):
+    """Bulk write whose slot mapping mixes every case of an 8-slot V group:
+    runs that start mid-group and mid-block, aligned runs of exactly 8, runs
+    crossing a 32-token chunk boundary, scattered single slots, skipped (-1)
+    and out-of-range slots, and a token count that is not a multiple of 32;
+    into NaN-filled pools, bit for bit against the oracle's write."""
+    rng = np.random.default_rng(D + B + Hkv)
+    nb = 48
+    perm = rng.permutation(nb)
+    slots = []
+    def run(block, start, n):
+        slots.extend(int(perm[block]) * B + start + j for j in range(n))
+    run(0, 3, B - 3)          # mid-block start, to the block's end
+    run(1, 0, 8)              # exactly one aligned group
+    run(2, 0, B)              # a whole block, then the next block of the same run
+    run(3, 0, B)
+    slots.extend(int(perm[5]) * B + int(o) for o in rng.choice(B, size=5, replace=False))
+    slots.extend([-1, nb * B + 3, -1])
+    run(6, 5, 2)              # a short run inside one group
+    run(7, 0, 13)             # an aligned run ending mid-group
+    run(8, 8, 8)              # the second group of a block
+    run(9, 1, 30 if B == 32 else 15)
+    T = len(slots)
+    assert T % 32 != 0
+    assert len(set(s for s in slots if 0 <= s < nb * B)) == sum(1 for s in slots if 0 <= s < nb * B)
+    dev = device()
+    key = torch.randn(T, Hkv, D, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    value = torch.randn(T, Hkv, D, generator=torch.Generator().manual_seed(8)).to(torch.bfloat16)
+    kc = torch.full((nb, Hkv, D // 8, B, 8), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full((nb, Hkv, B // 8, D, 8), float("nan"), dtype=torch.bfloat16, device=dev)
+    sm = np.array(slots, dtype=np.int64)
+    pa.reshape_and_cache(key.to(dev), value.to(dev), kc, vc, torch.from_numpy(sm).to(dev))
+    torch.cuda.synchronize()
+    okc, ovc = orc.empty_shuffled_cache(nb, Hkv, D, B)
+    orc.cache_write_shuffled(W.bf16_bits(key), W.bf16_bits(value), sm, okc, ovc, B)
+    assert np.array_equal(_bits(kc), okc) and np.array_equal(_bits(vc), ovc)
+
+
 def test_cache_write_skips_bad_slots(orc):
     dev = device()
     case = W.gqa_decode_case("skip", 203, [20], Hq=2, Hkv=2, D=128, block_size=16)
