@@ -37,29 +37,37 @@ def test_cache_write_bitexact(orc, mk):
     assert np.array_equal(_bits(g.vc), vc)
 
 
+@pytest.mark.parametrize("reps", [1, 128], ids=["small", "bulk"])
 @pytest.mark.parametrize("D,B,Hkv", [(128, 16, 1), (64, 32, 3), (128, 32, 2)])
-def test_cache_write_mixed_slot_runs(orc, D, B, Hkv):
+def test_cache_write_mixed_slot_runs(orc, D, B, Hkv, reps):
     """Bulk write whose slot mapping mixes every case of an 8-slot V group:
     runs that start mid-group and mid-block, aligned runs of exactly 8, runs
     crossing a 32-token chunk boundary, scattered single slots, skipped (-1)
     and out-of-range slots, and a token count that is not a multiple of 32;
-    into NaN-filled pools, bit for bit against the oracle's write."""
+    into NaN-filled pools, bit for bit against the oracle's write.  The
+    pattern is repeated over fresh blocks ``reps`` times: once stays below
+    12288 token-heads (one thread per source vector), 128 times goes above
+    (32-token chunks staged in LDS)."""
     rng = np.random.default_rng(D + B + Hkv)
-    nb = 48
+    nb = 48 * reps
     perm = rng.permutation(nb)
     slots = []
-    def run(block, start, n):
-        slots.extend(int(perm[block]) * B + start + j for j in range(n))
-    run(0, 3, B - 3)          # mid-block start, to the block's end
-    run(1, 0, 8)              # exactly one aligned group
-    run(2, 0, B)              # a whole block, then the next block of the same run
-    run(3, 0, B)
-    slots.extend(int(perm[5]) * B + int(o) for o in rng.choice(B, size=5, replace=False))
-    slots.extend([-1, nb * B + 3, -1])
-    run(6, 5, 2)              # a short run inside one group
-    run(7, 0, 13)             # an aligned run ending mid-group
-    run(8, 8, 8)              # the second group of a block
-    run(9, 1, 30 if B == 32 else 15)
+    for rep in range(reps):
+        def run(block, start, n):
+            slots.extend(int(perm[48 * rep + block]) * B + start + j for j in range(n))
+        run(0, 3, B - 3)          # mid-block start, to the block's end
+        run(1, 0, 8)              # exactly one aligned group
+        run(2, 0, B)              # a whole block, then the next block of the same run
+        run(3, 0, B)
+        slots.extend(int(perm[48 * rep + 5]) * B + int(o)
+                     for o in rng.choice(B, size=5, replace=False))
+        slots.extend([-1, nb * B + 3, -1])
+        run(6, 5, 2)              # a short run inside one group
+        run(7, 0, 13)             # an aligned run ending mid-group
+        run(8, 8, 8)              # the second group of a block
+        run(9, 1, 30 if B == 32 else 15)
+    slots.extend(int(perm[10]) * B + j for j in range(5))  # a ragged tail on an unused block
+    assert (len(slots) * Hkv >= 12288) == (reps > 1)
     T = len(slots)
     assert T % 32 != 0
     assert len(set(s for s in slots if 0 <= s < nb * B)) == sum(1 for s in slots if 0 <= s < nb * B)
