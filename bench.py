@@ -70,7 +70,7 @@ MEASURED_TRAFFIC = {
     "mla_fp8_mfma": ("mla", "30dd7bded0e5261d", 145.69e6),
     "extend": ("extend", "f06b1df214d4f57b", 1295.37e6),
     "merge": ("merge", "5767d743027acd19", 340.74e6),
-    "cache_write": ("cache_write", "2cc04fc5b2348afb", 113.80e6),
+    "cache_write": ("cache_write", "a6f4db786c645612", 107.92e6),
 }
 
 

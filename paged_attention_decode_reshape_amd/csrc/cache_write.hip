@@ -102,8 +102,13 @@ __global__ __launch_bounds__(256) void cache_write_runs_kernel(
     __shared__ int64_t kb[kRun], vb[kRun];     // cache offsets of chunk token r for dim 0
     __shared__ int64_t vs[kRun];               // vb[r] if token r's V is stored 2 bytes a dim, else -1
     __shared__ __align__(16) uint16_t vl[kRun + kExt][D];
-    const int g = (int)(blockIdx.x % Hkv);
-    const int64_t t_begin = (int64_t)(blockIdx.x / Hkv) * kRun;
+    // workgroups go round-robin over the 8 XCDs: give each XCD a contiguous
+    // range of chunks, so that the 8 tokens a chunk stages past its end are
+    // read by the L2 that also holds the next chunk
+    const uint32_t n = gridDim.x, per = n / 8, rem = n % 8, x = blockIdx.x % 8;
+    const uint32_t wg = x * per + min(x, rem) + blockIdx.x / 8;
+    const int g = (int)(wg % Hkv);
+    const int64_t t_begin = (int64_t)(wg / Hkv) * kRun;
     const int tid = threadIdx.x;
     const int64_t cap = num_blocks * B;
     // Every global load is issued before the first wait: the slots, V of
