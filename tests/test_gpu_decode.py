@@ -27,7 +27,8 @@ def _bits(t):
     lambda: W.gqa_decode_case("d64b32", 201, [1, 31, 32, 33, 200], Hq=8, Hkv=4, D=64,
                               block_size=32),
     lambda: W.gqa_decode_case("h3", 202, [5, 17, 64, 65], Hq=6, Hkv=3, D=128, block_size=16),
-], ids=["tiny", "d64b32_hkv4", "hkv3"])
+    lambda: W.qwen3_decode(),
+], ids=["tiny", "d64b32_hkv4", "hkv3", "qwen3_64req_93k_tokens"])
 def test_cache_write_bitexact(orc, mk):
     case = mk()
     say(f"cache write {case.name}")
